@@ -1,0 +1,10 @@
+"""Gated DeltaNet layer core for MI355X (gfx950).
+
+The compute lives in the HIP library ``libgdn.so`` (built from ``csrc/``),
+reached through its C ABI (``include/gdn.h``).  ``binding`` marshals torch
+tensors to that ABI; ``inputs`` draws seeded synthetic inputs.  The library
+is loaded on first use; if it has not been built, that first call raises.
+"""
+from .binding import (  # noqa: F401
+    GdnError, layer_core, layer_core_workspace_bytes, lib, prep, recurrent,
+)

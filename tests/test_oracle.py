@@ -1,0 +1,482 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is pinned to things other than itself:
+  * a hand-worked example with exact dyadic values (tests/golden/);
+  * an independent formulation of the recurrence (the affine matrix form
+    S_t = S_{t-1} A_t + B_t, with A_t = g_t (I - beta_t k_t k_t^T) and
+    B_t = beta_t v_t k_t^T, y_t = S_t q_t), evaluated with numpy matmuls;
+  * closed forms and invariants of the gated delta rule;
+  * library routines (torch conv1d, silu, rms_norm, logaddexp, sigmoid; torch's
+    bfloat16 conversion) for the prologue pieces.
+Each test is chosen so that a plausible slip (dropped decay, read-out before
+decay, output before update, transposed state, wrong GQA order, flipped conv
+taps, wrong eps placement, wrong rounding tie rule) fails at least one.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_recurrence_prep_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(seed):
+    return np.random.default_rng(seed)
+
+
+def rand_recurrence(seed, B, T, Hk, Hv, Dk, Dv, state=True, gscale=1.0):
+    r = rnd(seed)
+    q = r.standard_normal((B, T, Hk, Dk)) / math.sqrt(Dk)
+    k = r.standard_normal((B, T, Hk, Dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((B, T, Hv, Dv))
+    g = r.uniform(0.0, 1.0, (B, T, Hv)) * gscale
+    beta = r.uniform(0.0, 1.0, (B, T, Hv))
+    s0 = r.standard_normal((B, Hv, Dv, Dk)) * 0.1 if state else None
+    return q, k, v, g, beta, s0
+
+
+def matrix_form(q, k, v, g, beta, s0):
+    """Independent formulation: S_t = S_{t-1} A_t + B_t, y_t = S_t q_t."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    rep = Hv // Hk
+    y = np.zeros((B, T, Hv, Dv))
+    sT = np.zeros((B, Hv, Dv, Dk))
+    for b in range(B):
+        for h in range(Hv):
+            hk = h // rep
+            S = np.zeros((Dv, Dk)) if s0 is None else s0[b, h].copy()
+            for t in range(T):
+                kt = k[b, t, hk][:, None]
+                A = g[b, t, h] * (np.eye(Dk) - beta[b, t, h] * (kt @ kt.T))
+                Bm = beta[b, t, h] * (v[b, t, h][:, None] @ kt.T)
+                S = S @ A + Bm
+                y[b, t, h] = S @ q[b, t, hk]
+            sT[b, h] = S
+    return y, sT
+
+
+def relerr(a, b):
+    return np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
+
+
+# ------------------------------------------------------------------ formats
+
+def test_bf16_rounding_ties_and_edges():
+    f = oracle.lib().oracle_f64_to_bf16
+    assert f(1.0) == 0x3F80
+    assert f(1.0 + 2 ** -8) == 0x3F80            # tie -> even (down)
+    assert f(1.0 + 3 * 2 ** -8) == 0x3F82        # tie -> even (up)
+    assert f(1.0 + 2 ** -8 + 2 ** -40) == 0x3F81  # just above the tie
+    assert f(-2.5) == 0xC020
+    assert f(2.0 ** -133) == 0x0001              # smallest subnormal
+    assert f(2.0 ** -134) == 0x0000              # tie between 0 and 2^-133 -> even
+    assert f(3 * 2.0 ** -134) == 0x0002          # tie between 1 and 2 ulps -> even
+    assert f(2.0 ** -126) == 0x0080              # smallest normal
+    assert f(3.3895313892515355e38) == 0x7F7F    # largest finite bf16
+    assert f(2.0 ** 128) == 0x7F80
+    assert f(-math.inf) == 0xFF80
+    assert f(math.nan) & 0x7FC0 == 0x7FC0
+    assert f(-0.0) == 0x8000
+
+
+def test_bf16_roundtrip_all_patterns():
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    x = oracle.bf16_to_f64(bits)
+    back = oracle.round_bf16(x)
+    finite = np.isfinite(x)
+    assert np.array_equal(back[finite], bits[finite])
+    assert np.all(np.isnan(x[~finite]) | np.isinf(x[~finite]))
+
+
+def test_bf16_rounding_matches_torch_on_f32_values():
+    # torch's float32 -> bfloat16 conversion rounds to nearest even; on values
+    # that are exactly float32 the direct-from-double rounding must agree.
+    r = rnd(7)
+    x = (r.standard_normal(200000) * np.exp(r.uniform(-60, 60, 200000))).astype(np.float32)
+    x[:1000] = (np.float32(1.0) + np.arange(1000, dtype=np.float32) * np.float32(2 ** -9))
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------- recurrence
+
+def test_golden_hand_worked_2x2():
+    vals = {}
+    with open(os.path.join(GOLDEN, "recurrence_2x2.txt")) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            key, rest = line.split(":")
+            vals[key] = np.array([float(x) for x in rest.split()])
+    q = vals["q"].reshape(1, 2, 1, 2)
+    k = vals["k"].reshape(1, 2, 1, 2)
+    v = vals["v"].reshape(1, 2, 1, 2)
+    g = vals["g"].reshape(1, 2, 1)
+    beta = vals["beta"].reshape(1, 2, 1)
+    s0 = vals["S0"].reshape(1, 1, 2, 2)
+    y, s = oracle.recurrent(q, k, v, g, beta, s0)
+    assert np.array_equal(y.ravel(), vals["y"])
+    assert np.array_equal(s.ravel(), vals["S_T"])
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 5, 1, 1, 4, 3), (2, 7, 1, 2, 8, 5), (1, 9, 2, 4, 6, 6), (1, 4, 3, 3, 5, 2),
+])
+@pytest.mark.parametrize("state", [True, False])
+def test_recurrence_matches_matrix_form(shape, state):
+    B, T, Hk, Hv, Dk, Dv = shape
+    args = rand_recurrence(sum(shape) + state, B, T, Hk, Hv, Dk, Dv, state)
+    y, s = oracle.recurrent(*args)
+    y2, s2 = matrix_form(*args)
+    assert relerr(y, y2) < 1e-12
+    assert relerr(s, s2) < 1e-12
+
+
+def test_recurrence_matrix_form_on_tiny_workload():
+    w = inputs.WORKLOADS["tiny"]
+    raw = inputs.workload("tiny")
+    ri = oracle.recurrence_inputs(raw)
+    args = (oracle.bf16_to_f64(ri["q"]), oracle.bf16_to_f64(ri["k"]), oracle.bf16_to_f64(ri["v"]),
+            ri["g"].astype(np.float64), ri["beta"].astype(np.float64), raw["state"].astype(np.float64))
+    y, s = oracle.recurrent(*args)
+    y2, s2 = matrix_form(*args)
+    assert y.shape == (1, 64, w["Hv"], w["Dv"])
+    assert relerr(y, y2) < 1e-12
+    assert relerr(s, s2) < 1e-12
+
+
+def test_I1_beta0_g1_leaves_state():
+    q, k, v, g, beta, s0 = rand_recurrence(11, 2, 6, 2, 4, 8, 5)
+    g[:] = 1.0
+    beta[:] = 0.0
+    y, s = oracle.recurrent(q, k, v, g, beta, s0)
+    assert np.array_equal(s, s0)
+    rep = 2
+    for b in range(2):
+        for h in range(4):
+            for t in range(6):
+                np.testing.assert_allclose(y[b, t, h], s0[b, h] @ q[b, t, h // rep], rtol=1e-13, atol=1e-15)
+
+
+def test_I2_g0_resets_state():
+    q, k, v, g, beta, s0 = rand_recurrence(12, 1, 1, 1, 1, 8, 6)
+    g[:] = 0.0
+    _, s_a = oracle.recurrent(q, k, v, g, beta, s0)
+    _, s_b = oracle.recurrent(q, k, v, g, beta, s0 * 1000.0 + 3.0)
+    ref = np.outer(v[0, 0, 0] * beta[0, 0, 0], k[0, 0, 0])
+    assert np.array_equal(s_a[0, 0], ref)
+    assert np.array_equal(s_b[0, 0], ref)
+
+
+def test_I3_unit_key_writes_value():
+    q, k, v, g, beta, s0 = rand_recurrence(13, 1, 1, 1, 1, 16, 7)
+    g[:] = 1.0
+    beta[:] = 1.0
+    _, s = oracle.recurrent(q, k, v, g, beta, s0)
+    np.testing.assert_allclose(s[0, 0] @ k[0, 0, 0], v[0, 0, 0], rtol=0, atol=64 * 2.0 ** -52)
+
+
+def test_I4_gqa_equals_repeated_heads():
+    q, k, v, g, beta, s0 = rand_recurrence(14, 2, 5, 2, 6, 8, 4)
+    y, s = oracle.recurrent(q, k, v, g, beta, s0)
+    qr = np.repeat(q, 3, axis=2)
+    kr = np.repeat(k, 3, axis=2)
+    y2, s2 = oracle.recurrent(qr, kr, v, g, beta, s0)
+    assert np.array_equal(y, y2) and np.array_equal(s, s2)
+    # the tiled order (hk = hv mod Hk) is a different map and must differ
+    y3, _ = oracle.recurrent(np.tile(q, (1, 1, 3, 1)), np.tile(k, (1, 1, 3, 1)), v, g, beta, s0)
+    assert not np.allclose(y, y3)
+
+
+def test_I5_single_step_from_zero():
+    q, k, v, g, beta, _ = rand_recurrence(15, 1, 1, 1, 1, 8, 5, state=False)
+    y, s = oracle.recurrent(q, k, v, g, beta, None)
+    expect = beta[0, 0, 0] * (q[0, 0, 0] @ k[0, 0, 0]) * v[0, 0, 0]
+    np.testing.assert_allclose(y[0, 0, 0], expect, rtol=1e-14, atol=1e-16)
+    np.testing.assert_allclose(s[0, 0], beta[0, 0, 0] * np.outer(v[0, 0, 0], k[0, 0, 0]), rtol=1e-15)
+
+
+def test_I6_beta0_pure_decay():
+    q, k, v, g, beta, s0 = rand_recurrence(16, 1, 9, 1, 1, 6, 4)
+    beta[:] = 0.0
+    y, s = oracle.recurrent(q, k, v, g, beta, s0)
+    cum = np.cumprod(g[0, :, 0])
+    np.testing.assert_allclose(s[0, 0], cum[-1] * s0[0, 0], rtol=1e-13)
+    for t in range(9):
+        np.testing.assert_allclose(y[0, t, 0], cum[t] * (s0[0, 0] @ q[0, t, 0]), rtol=1e-12, atol=1e-300)
+
+
+def test_I7_time_split_is_exact():
+    q, k, v, g, beta, s0 = rand_recurrence(17, 2, 12, 1, 2, 8, 6)
+    y, s = oracle.recurrent(q, k, v, g, beta, s0)
+    y1, s1 = oracle.recurrent(q[:, :5], k[:, :5], v[:, :5], g[:, :5], beta[:, :5], s0)
+    y2, s2 = oracle.recurrent(q[:, 5:], k[:, 5:], v[:, 5:], g[:, 5:], beta[:, 5:], s1)
+    assert np.array_equal(np.concatenate([y1, y2], axis=1), y)
+    assert np.array_equal(s2, s)
+
+
+def test_I8_linear_in_state_and_values():
+    q, k, v, g, beta, s0 = rand_recurrence(18, 1, 7, 1, 2, 8, 5)
+    r = rnd(19)
+    v2 = r.standard_normal(v.shape)
+    s02 = r.standard_normal(s0.shape)
+    ya, sa = oracle.recurrent(q, k, v, g, beta, s0)
+    yb, sb = oracle.recurrent(q, k, v2, g, beta, s02)
+    yc, sc = oracle.recurrent(q, k, 2 * v - 3 * v2, g, beta, 2 * s0 - 3 * s02)
+    np.testing.assert_allclose(yc, 2 * ya - 3 * yb, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sc, 2 * sa - 3 * sb, rtol=0, atol=1e-12)
+
+
+def test_I9_batch_and_head_permutation():
+    q, k, v, g, beta, s0 = rand_recurrence(20, 3, 4, 2, 4, 8, 5)
+    y, s = oracle.recurrent(q, k, v, g, beta, s0)
+    pb = np.array([2, 0, 1])
+    # permute k-heads and their v-head groups together (GQA groups of 2)
+    phk = np.array([1, 0])
+    phv = np.array([2, 3, 0, 1])
+    y2, s2 = oracle.recurrent(q[pb][:, :, phk], k[pb][:, :, phk], v[pb][:, :, phv],
+                              g[pb][:, :, phv], beta[pb][:, :, phv], s0[pb][:, phv])
+    assert np.array_equal(y2, y[pb][:, :, phv])
+    assert np.array_equal(s2, s[pb][:, phv])
+
+
+def test_I10_orthonormal_keys_write_columns():
+    Dk, Dv, T = 6, 4, 5
+    q, k, v, g, beta, s0 = rand_recurrence(21, 1, T, 1, 1, Dk, Dv)
+    cols = [3, 0, 5, 3, 1]
+    k[:] = 0.0
+    for t, j in enumerate(cols):
+        k[0, t, 0, j] = 1.0
+    g[:] = 1.0
+    beta[:] = 1.0
+    _, s = oracle.recurrent(q, k, v, g, beta, s0)
+    last = {}
+    for t, j in enumerate(cols):
+        last[j] = t
+    for j in range(Dk):
+        if j in last:
+            np.testing.assert_allclose(s[0, 0, :, j], v[0, last[j], 0], rtol=2 ** -52, atol=0)
+        else:
+            assert np.array_equal(s[0, 0, :, j], s0[0, 0, :, j])
+
+
+def test_rows_are_independent_subproblems():
+    # One state row only depends on its own v entry: slicing Dv rows and one
+    # head gives bit-identical results (used by the sampled parity checks).
+    q, k, v, g, beta, s0 = rand_recurrence(22, 2, 8, 2, 4, 8, 6)
+    y, s = oracle.recurrent(q, k, v, g, beta, s0)
+    b, hv, rows = 1, 3, [1, 4, 5]
+    hk = hv // 2
+    ys, ss = oracle.recurrent(q[b:b + 1, :, hk:hk + 1], k[b:b + 1, :, hk:hk + 1],
+                              v[b:b + 1, :, hv:hv + 1][..., rows], g[b:b + 1, :, hv:hv + 1],
+                              beta[b:b + 1, :, hv:hv + 1], s0[b:b + 1, hv:hv + 1][:, :, rows])
+    assert np.array_equal(ys[0, :, 0], y[b, :, hv][:, rows])
+    assert np.array_equal(ss[0, 0], s[b, hv][rows])
+
+
+def test_zero_length_and_empty_batch():
+    q, k, v, g, beta, s0 = rand_recurrence(23, 2, 0, 1, 2, 4, 3)
+    y, s = oracle.recurrent(q, k, v, g, beta, s0)
+    assert y.shape == (2, 0, 2, 3) and np.array_equal(s, s0)
+    y, s = oracle.recurrent(q, k, v, g, beta, None)
+    assert np.array_equal(s, np.zeros_like(s0))
+
+
+# ---------------------------------------------------------------- prologue
+
+def small_layer(seed, B=2, T=9, Hk=2, Hv=4, Dk=8, Dv=4, K=4, conv_state=True, state=True):
+    return inputs.layer_raw(B=B, T=T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, K=K, workload_id=90 + seed,
+                            state=state, conv_state=conv_state)
+
+
+def torch_prologue(raw, Hk, Hv, Dk, Dv, q_scale, k_scale, eps):
+    """Library-routine evaluation of the prologue in float64 on the CPU."""
+    f = lambda h: torch.from_numpy(oracle.bf16_to_f64(h))
+    x = f(raw["qkv"])                      # [B,T,C]
+    B, T, C = x.shape
+    w = f(raw["conv_w"])                   # [C,K]
+    K = w.shape[1]
+    cs = f(raw["conv_state"]) if raw["conv_state"] is not None else torch.zeros(B, K - 1, C, dtype=torch.float64)
+    xp = torch.cat([cs, x], dim=1).transpose(1, 2)            # [B,C,T+K-1]
+    u = torch.nn.functional.conv1d(xp, w[:, None, :], groups=C).transpose(1, 2)
+    act = torch.nn.functional.silu(u)
+    q = act[..., :Hk * Dk].reshape(B, T, Hk, Dk)
+    k = act[..., Hk * Dk:2 * Hk * Dk].reshape(B, T, Hk, Dk)
+    v = act[..., 2 * Hk * Dk:].reshape(B, T, Hv, Dv)
+    q = torch.nn.functional.rms_norm(q, (Dk,), eps=eps) * q_scale
+    k = torch.nn.functional.rms_norm(k, (Dk,), eps=eps) * k_scale
+    a = f(raw["a"]) + torch.from_numpy(raw["dt_bias"].astype(np.float64))
+    sp = torch.logaddexp(a, torch.zeros_like(a))
+    g = torch.exp(-torch.exp(torch.from_numpy(raw["A_log"].astype(np.float64))) * sp)
+    beta = torch.sigmoid(f(raw["b"]))
+    tail = torch.cat([cs, x], dim=1)[:, T:]
+    return dict(q=q.numpy(), k=k.numpy(), v=v.numpy(), g=g.numpy(), beta=beta.numpy(),
+                tail=tail.numpy())
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+@pytest.mark.parametrize("conv_state", [True, False])
+def test_prologue_matches_torch_library(K, conv_state):
+    Hk, Hv, Dk, Dv = 2, 4, 8, 4
+    raw = small_layer(K, K=K, conv_state=conv_state)
+    qs, ks = 0.125, 0.3
+    out = oracle.prep(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
+                      raw["A_log"], raw["dt_bias"], Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv,
+                      q_scale=qs, k_scale=ks, eps=1e-6)
+    ref = torch_prologue(raw, Hk, Hv, Dk, Dv, qs, ks, 1e-6)
+    for name in ("q", "k", "v", "g", "beta"):
+        np.testing.assert_allclose(out[name], ref[name], rtol=1e-13, atol=1e-15, err_msg=name)
+    assert np.array_equal(oracle.bf16_to_f64(out["conv_state"]), ref["tail"])
+
+
+def test_conv_delta_weights_identity_and_shift():
+    Hk, Hv, Dk, Dv, K = 1, 1, 4, 4, 4
+    raw = small_layer(5, B=1, T=6, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, K=K)
+    C = raw["qkv"].shape[-1]
+    one = np.uint16(0x3F80)
+    x = oracle.bf16_to_f64(raw["qkv"])[0]
+    cs = oracle.bf16_to_f64(raw["conv_state"])[0]
+    silu = lambda u: torch.nn.functional.silu(torch.from_numpy(u)).numpy()
+    # w = e_{K-1}: the newest tap only -> act = silu(x_t)
+    w = np.zeros((C, K), np.uint16)
+    w[:, K - 1] = one
+    out = oracle.prep(raw["qkv"], w, raw["conv_state"], raw["a"], raw["b"], raw["A_log"],
+                      raw["dt_bias"], Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=1, k_scale=1)
+    np.testing.assert_allclose(out["v"][0, :, 0], silu(x[:, 2 * Dk:]), rtol=1e-15)
+    # w = e_0: the oldest tap -> act_t = silu(xpad_t), xpad = [conv_state; x]
+    w = np.zeros((C, K), np.uint16)
+    w[:, 0] = one
+    out = oracle.prep(raw["qkv"], w, raw["conv_state"], raw["a"], raw["b"], raw["A_log"],
+                      raw["dt_bias"], Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=1, k_scale=1)
+    xpad = np.concatenate([cs, x])
+    np.testing.assert_allclose(out["v"][0, :, 0], silu(xpad[:6, 2 * Dk:]), rtol=1e-15)
+
+
+def test_norm_identity_and_gate_closed_forms():
+    Hk, Hv, Dk, Dv = 2, 2, 16, 8
+    raw = small_layer(6, B=1, T=5, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv)
+    ks, eps = 0.25, 1e-6
+    out = oracle.prep(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
+                      raw["A_log"], raw["dt_bias"], Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv,
+                      q_scale=1.0, k_scale=ks, eps=eps)
+    # mean(q_hat^2) = ms / (ms + eps) just below 1 at scale 1, and
+    # ||k_hat||^2 = Dk ks^2 ms / (ms + eps) just below Dk ks^2.  (The eps
+    # placement itself is pinned by the torch rms_norm cross-check.)
+    msq = np.mean(out["q"] ** 2, axis=-1)
+    assert np.all(msq < 1.0) and np.all(msq > 1.0 - 1e-3)
+    n2 = np.sum(out["k"] ** 2, axis=-1)
+    assert np.all(n2 < Dk * ks * ks) and np.all(n2 > Dk * ks * ks * (1 - 1e-3))
+    # a + dt_bias = 0 and A_log = 0 -> softplus = ln 2, g = exp(-ln 2) = 1/2
+    g, beta = oracle.gates(np.zeros((3, 2), np.uint16), np.zeros((3, 2), np.uint16),
+                           np.zeros(2, np.float32), np.zeros(2, np.float32))
+    np.testing.assert_allclose(g, 0.5, rtol=2 ** -52)
+    assert np.all(beta == 0.5)
+    # A_log = log 3 (as stored f32): g = 2^(-exp(A_log))
+    al = np.array([math.log(3.0)], np.float32)
+    g, _ = oracle.gates(np.zeros((1, 1), np.uint16), np.zeros((1, 1), np.uint16), al,
+                        np.zeros(1, np.float32))
+    np.testing.assert_allclose(g[0, 0], 2.0 ** (-math.exp(float(al[0]))), rtol=1e-15)
+    # large negative a: softplus -> e^x, g -> 1; large positive: g = exp(-E x) (tiny)
+    a = np.array([[0xC2C8, 0x42C8]], np.uint16)     # -100, +100 in bf16
+    g, beta = oracle.gates(a, a, np.zeros(2, np.float32), np.zeros(2, np.float32))
+    np.testing.assert_allclose(g[0, 0], math.exp(-math.exp(-100.0)), rtol=1e-15)
+    np.testing.assert_allclose(g[0, 1], math.exp(-100.0), rtol=1e-13)
+    np.testing.assert_allclose(beta[0], [math.exp(-100.0), 1.0], rtol=1e-13)
+
+
+def test_prologue_time_split_and_conv_state_tail():
+    Hk, Hv, Dk, Dv = 1, 2, 8, 4
+    for K in (2, 4):
+        raw = small_layer(7 + K, B=2, T=11, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, K=K)
+        kw = dict(Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=0.5, k_scale=0.25)
+        y, s, cs = oracle.layer_core(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
+                                     raw["A_log"], raw["dt_bias"], raw["state"], **kw)
+        for T1 in (0, 1, K - 2, 5):
+            sl = lambda x, lo, hi: None if x is None else np.ascontiguousarray(x[:, lo:hi])
+            y1, s1, c1 = oracle.layer_core(sl(raw["qkv"], 0, T1), raw["conv_w"], raw["conv_state"],
+                                           sl(raw["a"], 0, T1), sl(raw["b"], 0, T1), raw["A_log"],
+                                           raw["dt_bias"], raw["state"], **kw)
+            y2, s2, c2 = oracle.layer_core(sl(raw["qkv"], T1, 11), raw["conv_w"], c1,
+                                           sl(raw["a"], T1, 11), sl(raw["b"], T1, 11), raw["A_log"],
+                                           raw["dt_bias"], s1, **kw)
+            assert np.array_equal(np.concatenate([y1, y2], axis=1), y)
+            assert np.array_equal(s2, s) and np.array_equal(c2, cs)
+        # the tail is the last K-1 raw input rows
+        assert np.array_equal(cs, raw["qkv"][:, -(K - 1):])
+
+
+def test_layer_core_is_prep_then_rounded_recurrence():
+    Hk, Hv, Dk, Dv = 2, 4, 8, 4
+    raw = small_layer(8, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv)
+    kw = dict(Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=0.125, k_scale=0.35)
+    p = oracle.prep(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
+                    raw["A_log"], raw["dt_bias"], **kw)
+    r = lambda x: oracle.bf16_to_f64(oracle.round_bf16(x))
+    y, s = oracle.recurrent(r(p["q"]), r(p["k"]), r(p["v"]), oracle.round_f32(p["g"]),
+                            oracle.round_f32(p["beta"]), raw["state"])
+    y2, s2, _ = oracle.layer_core(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
+                                  raw["A_log"], raw["dt_bias"], raw["state"], **kw)
+    assert np.array_equal(y, y2) and np.array_equal(s, s2)
+
+
+def test_prologue_channel_subproblem_is_exact():
+    # q/k head hk, k head hk and a subset of v channels of one v-head form a
+    # self-contained prologue (the conv is depthwise, the norm is per head).
+    Hk, Hv, Dk, Dv = 2, 4, 8, 6
+    raw = small_layer(9, B=1, T=7, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv)
+    kw = dict(q_scale=0.125, k_scale=0.35)
+    full = oracle.prep(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
+                       raw["A_log"], raw["dt_bias"], Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, **kw)
+    hv, rows = 3, [0, 2, 5]
+    hk = hv // 2
+    ch = list(range(hk * Dk, (hk + 1) * Dk)) + list(range(Hk * Dk + hk * Dk, Hk * Dk + (hk + 1) * Dk)) \
+        + [2 * Hk * Dk + hv * Dv + r for r in rows]
+    sub = oracle.prep(raw["qkv"][..., ch], raw["conv_w"][ch], raw["conv_state"][..., ch],
+                      raw["a"][..., hv:hv + 1], raw["b"][..., hv:hv + 1], raw["A_log"][hv:hv + 1],
+                      raw["dt_bias"][hv:hv + 1], Hk=1, Hv=1, Dk=Dk, Dv=len(rows), **kw)
+    assert np.array_equal(sub["q"][:, :, 0], full["q"][:, :, hk])
+    assert np.array_equal(sub["k"][:, :, 0], full["k"][:, :, hk])
+    assert np.array_equal(sub["v"][:, :, 0], full["v"][:, :, hv][..., rows])
+    assert np.array_equal(sub["g"][..., 0], full["g"][..., hv])
+
+
+def test_mutations_are_caught_by_the_pins():
+    """Plant plausible slips in a Python transcription of the per-step order
+    and confirm the independent matrix form tells them apart: read-out before
+    decay, output before update, missing decay."""
+    q, k, v, g, beta, s0 = rand_recurrence(30, 1, 6, 1, 1, 5, 4)
+    y_ref, _ = matrix_form(q, k, v, g, beta, s0)
+
+    def variant(kind):
+        S = s0[0, 0].copy()
+        ys = []
+        for t in range(6):
+            kt, qt, vt, gt, bt = k[0, t, 0], q[0, t, 0], v[0, t, 0], g[0, t, 0], beta[0, t, 0]
+            if kind == "readout_before_decay":
+                kv = S @ kt
+                S = gt * S
+            elif kind == "no_decay":
+                kv = S @ kt
+            else:
+                S = gt * S
+                kv = S @ kt
+            d = (vt - kv) * bt
+            if kind == "output_before_update":
+                ys.append(S @ qt)
+                S = S + np.outer(d, kt)
+            else:
+                S = S + np.outer(d, kt)
+                ys.append(S @ qt)
+        return np.array(ys)
+
+    assert relerr(variant("ok"), y_ref[0, :, 0]) < 1e-12
+    for kind in ("readout_before_decay", "no_decay", "output_before_update"):
+        assert relerr(variant(kind), y_ref[0, :, 0]) > 1e-3, kind
