@@ -1,0 +1,321 @@
+"""Benchmark of the Gated DeltaNet layer core on one MI355X.
+
+One step = one gdn_layer_core call (prologue + recurrence, every step of the
+hot path) over the prefill workload: B=1, T=4096, Hk=16, Hv=32, Dk=Dv=128,
+conv K=4, zero conv and recurrent state, seeded synthetic inputs resident in
+HBM before timing.  Metric: recurrence tokens/s*head = B*T*Hv / step time.
+
+Also measured in the same run (same JSON line):
+  * the dominant kernel (the recurrence) timed alone with HIP events on the
+    stream it is launched on -> roofline against the FP32 vector peak;
+  * batched decode, B=64, T=1 (layer core, 8 rotating sets of state and conv
+    state, 1 GiB, so the 256 MB last-level cache cannot hold them) -> HBM
+    roofline of its recurrence kernel;
+  * the CPU oracle on a bounded sample of the prefill workload, one thread.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CU x 4 SIMD x 16 lanes x 2 (packed) x 2 (FMA) x 2.4 GHz
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--kernel-only", default=None, choices=[None, "recurrent", "prep", "decode", "copy"],
+                    help="launch only this kernel (for counter collection)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path needs no collectives; run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_attention_recurrence_prep_amd import binding, inputs
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    binding.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    # ------------------------------------------------------------ prefill
+    w = inputs.WORKLOADS["prefill"]
+    B, T, Hk, Hv, Dk, Dv, K = (w[k] for k in ("B", "T", "Hk", "Hv", "Dk", "Dv", "K"))
+    C = 2 * Hk * Dk + Hv * Dv
+    qs, ks = inputs.scales(Dk)
+    eps = 1e-6
+    raw = inputs.workload("prefill")
+    d = {k: up(raw[k]) for k in ("qkv", "conv_w", "conv_state", "a", "b", "A_log", "dt_bias", "state")}
+    y = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+    s_out = torch.empty(B, Hv, Dv, Dk, dtype=torch.float32, device=dev)
+    cs_out = torch.empty(B, K - 1, C, dtype=torch.int16, device=dev)
+    ws = torch.empty(binding.layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        binding.layer_core(d["qkv"], d["conv_w"], d["conv_state"], cs_out, d["a"], d["b"], d["A_log"],
+                           d["dt_bias"], d["state"], s_out, y, ws, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv,
+                           q_scale=qs, k_scale=ks, eps=eps)
+
+    # prologue outputs for timing the recurrence kernel alone
+    pq = torch.empty(B, T, Hk, Dk, dtype=torch.int16, device=dev)
+    pk = torch.empty_like(pq)
+    pv = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+    pg = torch.empty(B, T, Hv, dtype=torch.float32, device=dev)
+    pb = torch.empty_like(pg)
+
+    def prep_only():
+        binding.prep(d["qkv"], d["conv_w"], d["conv_state"], cs_out, d["a"], d["b"], d["A_log"],
+                     d["dt_bias"], pq, pk, pv, pg, pb, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs,
+                     k_scale=ks, eps=eps)
+
+    def rec_only():
+        binding.recurrent(pq, pk, pv, pg, pb, None, s_out, y)
+
+    prep_only()
+    torch.cuda.synchronize()
+
+    if args.kernel_only:
+        return kernel_only(args, torch, dev, prep_only, rec_only, up, inputs, binding, np)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] prefill warmup done ({args.warmup})", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    value = B * T * Hv / (ms_step * 1e-3)
+    print(f"[bench] prefill layer core {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+
+    # dominant kernel alone, events on the stream it runs on
+    rec_us = time_kernel(torch, stream, rec_only, args.steps)
+    prep_us = time_kernel(torch, stream, prep_only, args.steps)
+    flops = 7 * B * T * Hv * Dk * Dv
+    achieved_tflops = flops / (rec_us * 1e-6) / 1e12
+    rec_bytes = (2 * B * T * Hk * Dk * 2 + B * T * Hv * Dv * 2 + 2 * B * T * Hv * 4 + B * T * Hv * Dv * 2
+                 + B * Hv * Dv * Dk * 4)
+    prep_bytes = (B * T * C * 2 + C * K * 2 + 2 * B * T * Hv * 2 + 2 * Hv * 4 + 2 * B * T * Hk * Dk * 2
+                  + B * T * Hv * Dv * 2 + 2 * B * T * Hv * 4 + B * (K - 1) * C * 2)
+    print(f"[bench] recurrent kernel {rec_us:.1f} us ({achieved_tflops:.1f} TFLOP/s), "
+          f"prep kernel {prep_us:.1f} us ({prep_bytes / prep_us / 1e3:.0f} GB/s)", file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------- decode
+    decode = bench_decode(args, torch, dev, up, inputs, binding, np)
+
+    # -------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(raw, Hk, Hv, Dk, Dv, qs, ks, eps)
+
+    line = {
+        "metric": "recurrence tokens/s*head (prefill T=4096, layer core incl. prologue)",
+        "value": value,
+        "unit": "token*head/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (bf16 q/k/v/y storage)",
+        "data": "synthetic (seeded)",
+        "config": {"workload": "prefill B=1 T=4096 Hk=16 Hv=32 Dk=Dv=128 K=4, zero conv/recurrent state",
+                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "alu", "kernel": "recurrent_kernel<128,32>",
+                     "achieved": achieved_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                     "flops_per_launch": flops, "avg_launch_us": rec_us},
+        "prologue": {"kernel": "prep_kernel<128,4>", "avg_launch_us": prep_us,
+                     "bytes_per_launch": prep_bytes, "achieved_GBs": prep_bytes / prep_us / 1e3,
+                     "frac_hbm": prep_bytes / prep_us / 1e3 / HBM_PEAK_GBS},
+        "decode_b64": decode,
+        "cpu_baseline": cpu,
+        "wall_s_timed": t_wall,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def time_kernel(torch, stream, fn, n):
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
+
+
+def bench_decode(args, torch, dev, up, inputs, binding, np):
+    """Batched decode B=64, T=1 through the layer core, rotating 8 state sets."""
+    B, T, Hk, Hv, Dk, Dv, K = 64, 1, 16, 32, 128, 128, 4
+    C = 2 * Hk * Dk + Hv * Dv
+    qs, ks = inputs.scales(Dk)
+    R = 8
+    raw = inputs.layer_raw(B=B, T=T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, K=K, workload_id=2, state=True,
+                           conv_state=True)
+    common = {k: up(raw[k]) for k in ("conv_w", "A_log", "dt_bias")}
+    sets = []
+    for r in range(R):
+        sets.append(dict(qkv=up(raw["qkv"]).clone(), a=up(raw["a"]).clone(), b=up(raw["b"]).clone(),
+                         cs=up(raw["conv_state"]).clone(), st=up(raw["state"]).clone()))
+    y = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+    ws = torch.empty(binding.layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv), dtype=torch.uint8,
+                     device=dev)
+    # recurrence kernel alone: q,k,v,g,beta prepared once per set
+    pq = torch.empty(B, T, Hk, Dk, dtype=torch.int16, device=dev)
+    pk, pv = torch.empty_like(pq), torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+    pg = torch.empty(B, T, Hv, dtype=torch.float32, device=dev)
+    pb = torch.empty_like(pg)
+    binding.prep(sets[0]["qkv"], common["conv_w"], sets[0]["cs"], None, sets[0]["a"], sets[0]["b"],
+                 common["A_log"], common["dt_bias"], pq, pk, pv, pg, pb, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv,
+                 q_scale=qs, k_scale=ks)
+
+    def step(i):
+        s = sets[i % R]
+        binding.layer_core(s["qkv"], common["conv_w"], s["cs"], s["cs"], s["a"], s["b"], common["A_log"],
+                           common["dt_bias"], s["st"], s["st"], y, ws, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv,
+                           q_scale=qs, k_scale=ks)
+
+    def rec(i):
+        s = sets[i % R]
+        binding.recurrent(pq, pk, pv, pg, pb, s["st"], s["st"], y)
+
+    stream = torch.cuda.current_stream(dev)
+    n = args.decode_steps
+    out = {}
+    for name, fn in (("layer_core", step), ("recurrent", rec)):
+        for i in range(2 * R):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        out[name] = a.elapsed_time(b) * 1e3 / n
+    state_bytes = 2 * B * Hv * Dv * Dk * 4
+    rec_bytes = state_bytes + 2 * B * T * Hk * Dk * 2 + 2 * B * T * Hv * Dv * 2 + 2 * B * T * Hv * 4
+    core_bytes = (state_bytes + B * T * C * 2 + 2 * B * (K - 1) * C * 2 + C * K * 2 + 2 * B * T * Hv * 2
+                  + B * T * Hv * Dv * 2)
+    gbs = rec_bytes / out["recurrent"] / 1e3
+    print(f"[bench] decode B=64: layer core {out['layer_core']:.1f} us, recurrent kernel "
+          f"{out['recurrent']:.1f} us ({gbs:.0f} GB/s)", file=sys.stderr, flush=True)
+    return {
+        "workload": "decode B=64 T=1 Hk=16 Hv=32 Dk=Dv=128, 8 rotating state sets (1 GiB)",
+        "value": B * T * Hv / (out["layer_core"] * 1e-6),
+        "unit": "token*head/s",
+        "us_per_step": out["layer_core"],
+        "layer_core_GBs": core_bytes / out["layer_core"] / 1e3,
+        "roofline": {"bound": "hbm", "kernel": "recurrent_kernel<128,1>", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": rec_bytes, "avg_launch_us": out["recurrent"]},
+    }
+
+
+def cpu_baseline(raw, Hk, Hv, Dk, Dv, qs, ks, eps):
+    """The oracle (as it stands) on a bounded sample of the prefill workload:
+    the full layer core (prologue of the head's channels + recurrence) for
+    a fixed set of v-heads over all T tokens, on one host thread."""
+    import numpy as np
+
+    import oracle
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    heads = list(range(Hv))
+    T = raw["qkv"].shape[1]
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+    oracle.lib()
+    t0 = time.perf_counter()
+    for hv in heads:
+        hk = hv // (Hv // Hk)
+        ch = (list(range(hk * Dk, (hk + 1) * Dk)) + list(range(Hk * Dk + hk * Dk, Hk * Dk + (hk + 1) * Dk))
+              + list(range(2 * Hk * Dk + hv * Dv, 2 * Hk * Dk + (hv + 1) * Dv)))
+        oracle.layer_core(np.ascontiguousarray(raw["qkv"][..., ch]), np.ascontiguousarray(raw["conv_w"][ch]),
+                          None, np.ascontiguousarray(raw["a"][..., hv:hv + 1]),
+                          np.ascontiguousarray(raw["b"][..., hv:hv + 1]), raw["A_log"][hv:hv + 1].copy(),
+                          raw["dt_bias"][hv:hv + 1].copy(), None, Hk=1, Hv=1, Dk=Dk, Dv=Dv,
+                          q_scale=qs, k_scale=ks, eps=eps)
+    dt = time.perf_counter() - t0
+    print(f"[bench] cpu oracle: {len(heads)} heads x {T} tokens in {dt:.1f} s", file=sys.stderr, flush=True)
+    return {"value": len(heads) * T / dt, "unit": "token*head/s", "cores": 1, "kind": "oracle",
+            "sample": f"the whole prefill workload, computed per v-head (all {len(heads)}): prologue of the head's channels + recurrence "
+                      f"over all {T} tokens, fp64, one thread",
+            "seconds": dt, "host": platform.processor() or platform.machine(),
+            "host_cpus": os.cpu_count()}
+
+
+def kernel_only(args, torch, dev, prep_only, rec_only, up, inputs, binding, np):
+    """Launch one kernel a few times (for rocprofv3 counter passes)."""
+    n = max(args.steps, 1)
+    if args.kernel_only == "recurrent":
+        fn = rec_only
+    elif args.kernel_only == "prep":
+        fn = prep_only
+    elif args.kernel_only == "copy":
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)   # 256 MiB
+        dst = torch.empty_like(src)
+
+        def fn():
+            dst.copy_(src)
+    else:
+        B, T, Hk, Hv, Dk, Dv = 64, 1, 16, 32, 128, 128
+        pq = torch.zeros(B, T, Hk, Dk, dtype=torch.int16, device=dev)
+        pk, pv = torch.zeros_like(pq), torch.zeros(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+        pg = torch.ones(B, T, Hv, dtype=torch.float32, device=dev)
+        pb = torch.zeros_like(pg)
+        st = torch.zeros(B, Hv, Dv, Dk, dtype=torch.float32, device=dev)
+        yy = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+
+        def fn():
+            binding.recurrent(pq, pk, pv, pg, pb, st, st, yy)
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    print(f"[bench] kernel-only {args.kernel_only}: {n} launches", file=sys.stderr, flush=True)
+
+
+if __name__ == "__main__":
+    main()

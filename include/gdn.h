@@ -1,0 +1,158 @@
+/*
+ * gdn.h -- C ABI of the Gated DeltaNet layer-core library for MI355X (gfx950).
+ *
+ * The library computes the data-parallel prologue and the per-timestep gated
+ * delta-rule recurrence of the Gated DeltaNet linear-attention layer, as
+ * defined by "mlex 0.1.2 -- src/models/gated_delta.rs" (GatedDeltaNet::forward)
+ * and "mlx-bun 0.4.0 -> 1.0.0, package/src/model/qwen3-delta.ts" (the
+ * layout/dtype contract in its file header, compute_g and gated_delta_step).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are DEVICE pointers (HIP device memory of the current device),
+ *   row-major and contiguous.  bf16 tensors are raw bfloat16 bit patterns
+ *   (gdn_bf16).  Every tensor pointer must be 16-byte aligned.
+ * - Ownership: the caller owns every buffer.  The library never allocates,
+ *   frees or retains device memory and keeps no pointer after returning.
+ * - Execution: every call only enqueues kernels on `stream` (a hipStream_t
+ *   passed as void*; NULL is the null stream) and returns without
+ *   synchronising.  Outputs are valid once the stream reaches that point.
+ * - Errors: all argument validation happens before any launch; on a non-zero
+ *   status no kernel was enqueued and no output was touched.  The status is
+ *   one of gdn_status; gdn_last_error() returns a thread-local description of
+ *   the most recent failure on the calling thread.  A GDN_ERR_HIP status means
+ *   a launch failed; the stream may then hold partial work.
+ * - Aliasing: outputs must not overlap any other argument, with two
+ *   exceptions: state_out may equal state_in exactly (in-place state update),
+ *   and conv_state_out may equal conv_state_in exactly.
+ * - Dimensions: B >= 0 and T >= 0 (zero is allowed, see each call);
+ *   Hk >= 1, Hv >= 1, Hv % Hk == 0 (GQA: v-head hv reads k-head
+ *   hk = hv / (Hv / Hk), the repeat order of the pages); Dk in
+ *   {32, 64, 128, 256}; Dv a multiple of 8 in [8, 4096]; conv kernel size K
+ *   in {2, 3, 4}.
+ * - Concurrency: calls on different streams or threads are independent; the
+ *   library holds no global mutable state other than the thread-local error.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t gdn_bf16; /* raw bfloat16 bits */
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_NULL_POINTER = -1, /* a required pointer is NULL */
+    GDN_ERR_BAD_DIMS = -2,     /* negative/zero size, Hv % Hk != 0, overflow */
+    GDN_ERR_UNSUPPORTED = -3,  /* Dk, Dv or K outside the supported set */
+    GDN_ERR_MISALIGNED = -4,   /* a tensor pointer is not 16-byte aligned */
+    GDN_ERR_OVERLAP = -5,      /* an output overlaps another argument */
+    GDN_ERR_WORKSPACE = -6,    /* workspace missing or too small */
+    GDN_ERR_BAD_VALUE = -7,    /* non-finite or negative scale / eps */
+    GDN_ERR_HIP = -8           /* a kernel launch failed */
+} gdn_status;
+
+/* Library ABI version (incremented on any signature change). */
+int gdn_version(void);
+
+/* Static name of a status code. */
+const char *gdn_status_string(int status);
+
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char *gdn_last_error(void);
+
+/*
+ * gdn_recurrent -- the gated delta rule over T steps.
+ * ("mlex ... gated_delta.rs", recurrence loop of GatedDeltaNet::forward;
+ *  "mlx-bun ... qwen3-delta.ts", gated_delta_step and gatedDeltaUpdate.)
+ *
+ * For each batch row b, v-head hv (k-head hk = hv / (Hv/Hk)) and t = 0..T-1:
+ *   S <- g_t S;  kv = S k_t;  delta = (v_t - kv) beta_t;
+ *   S <- S + delta k_t^T;  y_t = S q_t (rounded to bf16, nearest even).
+ * S is fp32 [Dv, Dk] per (b, hv), held on chip across the T loop.
+ *
+ *   q, k      [B,T,Hk,Dk] bf16   (already normalised and scaled)
+ *   v         [B,T,Hv,Dv] bf16
+ *   g, beta   [B,T,Hv]    f32
+ *   state_in  [B,Hv,Dv,Dk] f32, or NULL for a zero initial state
+ *   state_out [B,Hv,Dv,Dk] f32, may equal state_in
+ *   y         [B,T,Hv,Dv] bf16
+ * T == 0 copies state_in (or zeros) to state_out; B == 0 does nothing.
+ * q, k, v, g, beta and y may be NULL only when B*T == 0.
+ */
+gdn_status gdn_recurrent(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_bf16 *v,
+                         const float *g, const float *beta,
+                         const float *state_in, float *state_out, gdn_bf16 *y,
+                         int B, int T, int Hk, int Hv, int Dk, int Dv, void *stream);
+
+/*
+ * gdn_prep -- the data-parallel prologue.
+ * ("mlex ... gated_delta.rs", GatedDeltaNet::forward from the conv-state
+ *  splice through g; "mlx-bun ... qwen3-delta.ts", compute_g.)
+ *
+ *   xpad = [conv_state_in (zeros if NULL) ; qkv[b]] along T      (T+K-1 rows)
+ *   u[t,c] = sum_j conv_w[c,j] xpad[t+j,c]   (cross-correlation, no bias)
+ *   x = u sigmoid(u)                                              (SiLU)
+ *   q = x[:, 0:Hk*Dk], k = x[:, Hk*Dk:2*Hk*Dk], v = x[:, 2*Hk*Dk:]
+ *   q_hat = q / sqrt(mean_Dk(q^2) + eps) * q_scale (per head), k_hat likewise
+ *   with k_scale; q_hat, k_hat, v rounded once to bf16 (nearest even).
+ *   g = exp(-exp(A_log[hv]) softplus(a + dt_bias[hv])), beta = sigmoid(b), f32.
+ *   conv_state_out = the last K-1 rows of xpad.
+ *
+ *   qkv            [B,T,C] bf16, C = 2*Hk*Dk + Hv*Dv
+ *   conv_w         [C,K] bf16
+ *   conv_state_in  [B,K-1,C] bf16 or NULL (zeros)
+ *   conv_state_out [B,K-1,C] bf16 or NULL (not written); may equal
+ *                  conv_state_in
+ *   a, b           [B,T,Hv] bf16
+ *   A_log, dt_bias [Hv] f32
+ *   q, k           [B,T,Hk,Dk] bf16 out;  v [B,T,Hv,Dv] bf16 out
+ *   g, beta        [B,T,Hv] f32 out
+ *   q_scale, k_scale finite; eps finite and >= 0.
+ * T == 0 only writes conv_state_out (a copy of conv_state_in, or zeros).
+ */
+gdn_status gdn_prep(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
+                    const gdn_bf16 *conv_state_in, gdn_bf16 *conv_state_out,
+                    const gdn_bf16 *a, const gdn_bf16 *b,
+                    const float *A_log, const float *dt_bias,
+                    gdn_bf16 *q, gdn_bf16 *k, gdn_bf16 *v, float *g, float *beta,
+                    int B, int T, int Hk, int Hv, int Dk, int Dv, int K,
+                    float q_scale, float k_scale, float eps, void *stream);
+
+/*
+ * Bytes of device workspace gdn_layer_core needs for these sizes (the bf16
+ * q, k, v and f32 g, beta of the prologue, each 256-byte aligned).  Returns 0
+ * for invalid sizes (and when B*T == 0).
+ */
+size_t gdn_layer_core_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv);
+
+/*
+ * gdn_layer_core -- gdn_prep followed by gdn_recurrent, defined as exactly
+ * that composition (same roundings), on one stream.
+ * ("mlex ... gated_delta.rs", GatedDeltaNet::forward between the input
+ *  projections and the output normalisation.)
+ *
+ * Arguments as gdn_prep (inputs) and gdn_recurrent (state_in, state_out, y).
+ * workspace: device buffer of at least gdn_layer_core_workspace_bytes(...)
+ * bytes, 256-byte aligned, owned by the caller, not read before it is
+ * written; it may be NULL when that size is 0.
+ */
+gdn_status gdn_layer_core(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
+                          const gdn_bf16 *conv_state_in, gdn_bf16 *conv_state_out,
+                          const gdn_bf16 *a, const gdn_bf16 *b,
+                          const float *A_log, const float *dt_bias,
+                          const float *state_in, float *state_out, gdn_bf16 *y,
+                          void *workspace, size_t workspace_bytes,
+                          int B, int T, int Hk, int Hv, int Dk, int Dv, int K,
+                          float q_scale, float k_scale, float eps, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,3 +1,185 @@
-class GdnError(RuntimeError): pass
-def lib(): raise NotImplementedError
-prep = recurrent = layer_core = layer_core_workspace_bytes = lib
+"""ctypes binding of ``libgdn.so`` (C ABI in ``include/gdn.h``).
+
+Argument marshalling only: checks dtype / shape / device / contiguity of the
+torch tensors, passes raw device pointers, sizes and the current HIP stream,
+and raises :class:`GdnError` on a non-zero status.  Every step of the method
+runs in the library's kernels.  The library is loaded on first use from the
+package directory; if it has not been built, that first call raises.
+
+bf16 tensors may be ``torch.bfloat16`` or raw ``torch.int16``/``uint16`` bit
+patterns; both are passed through as bits.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "gdn.h")
+
+_lib = None
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def lib():
+    """The loaded library (ctypes.CDLL).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m linear_attention_recurrence_prep_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.gdn_version.restype = _i
+        L.gdn_status_string.argtypes = [_i]
+        L.gdn_status_string.restype = ctypes.c_char_p
+        L.gdn_last_error.restype = ctypes.c_char_p
+        L.gdn_recurrent.argtypes = [_p] * 8 + [_i] * 6 + [_p]
+        L.gdn_recurrent.restype = _i
+        L.gdn_prep.argtypes = [_p] * 13 + [_i] * 7 + [_f] * 3 + [_p]
+        L.gdn_prep.restype = _i
+        L.gdn_layer_core_workspace_bytes.argtypes = [_i] * 6
+        L.gdn_layer_core_workspace_bytes.restype = ctypes.c_size_t
+        L.gdn_layer_core.argtypes = [_p] * 12 + [ctypes.c_size_t] + [_i] * 7 + [_f] * 3 + [_p]
+        L.gdn_layer_core.restype = _i
+        _lib = L
+    return _lib
+
+
+def header_functions():
+    """Names of the functions declared in include/gdn.h."""
+    with open(HEADER) as fh:
+        text = fh.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_0-9]+)\s*\(", text)))
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise GdnError(status, f"{L.gdn_status_string(status).decode()}: {L.gdn_last_error().decode()}")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _ptr(t, name, dtypes, shape, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(device, stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def recurrent(q, k, v, g, beta, state_in, state_out, y, *, stream=None):
+    """Gated delta rule over T steps (gdn_recurrent).  q,k [B,T,Hk,Dk] bf16;
+    v [B,T,Hv,Dv] bf16; g,beta [B,T,Hv] f32; state_in [B,Hv,Dv,Dk] f32 or
+    None; state_out like state_in (may be the same tensor); y [B,T,Hv,Dv]
+    bf16 (written)."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dev = q.device
+    args = [
+        _ptr(q, "q", _BF16, (B, T, Hk, Dk), dev),
+        _ptr(k, "k", _BF16, (B, T, Hk, Dk), dev),
+        _ptr(v, "v", _BF16, (B, T, Hv, Dv), dev),
+        _ptr(g, "g", (torch.float32,), (B, T, Hv), dev),
+        _ptr(beta, "beta", (torch.float32,), (B, T, Hv), dev),
+        _ptr(state_in, "state_in", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(state_out, "state_out", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
+    ]
+    _check(lib().gdn_recurrent(*args, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream)))
+
+
+def prep(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, q, k, v, g, beta, *,
+         Hk, Hv, Dk, Dv, q_scale, k_scale, eps=1e-6, stream=None):
+    """Prologue (gdn_prep).  qkv [B,T,C] bf16, conv_w [C,K] bf16,
+    conv_state_in/out [B,K-1,C] bf16 or None, a,b [B,T,Hv] bf16, A_log,
+    dt_bias [Hv] f32; outputs q,k [B,T,Hk,Dk] bf16, v [B,T,Hv,Dv] bf16,
+    g,beta [B,T,Hv] f32."""
+    B, T, C = qkv.shape
+    K = conv_w.shape[1]
+    dev = qkv.device
+    args = [
+        _ptr(qkv, "qkv", _BF16, (B, T, C), dev),
+        _ptr(conv_w, "conv_w", _BF16, (C, K), dev),
+        _ptr(conv_state_in, "conv_state_in", _BF16, (B, K - 1, C), dev),
+        _ptr(conv_state_out, "conv_state_out", _BF16, (B, K - 1, C), dev),
+        _ptr(a, "a", _BF16, (B, T, Hv), dev),
+        _ptr(b, "b", _BF16, (B, T, Hv), dev),
+        _ptr(A_log, "A_log", (torch.float32,), (Hv,), dev),
+        _ptr(dt_bias, "dt_bias", (torch.float32,), (Hv,), dev),
+        _ptr(q, "q", _BF16, (B, T, Hk, Dk), dev),
+        _ptr(k, "k", _BF16, (B, T, Hk, Dk), dev),
+        _ptr(v, "v", _BF16, (B, T, Hv, Dv), dev),
+        _ptr(g, "g", (torch.float32,), (B, T, Hv), dev),
+        _ptr(beta, "beta", (torch.float32,), (B, T, Hv), dev),
+    ]
+    _check(lib().gdn_prep(*args, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps,
+                          _stream(dev, stream)))
+
+
+def layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv) -> int:
+    return int(lib().gdn_layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv))
+
+
+def layer_core(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias,
+               state_in, state_out, y, workspace, *, Hk, Hv, Dk, Dv, q_scale, k_scale,
+               eps=1e-6, stream=None):
+    """Prologue then recurrence (gdn_layer_core).  Arguments as ``prep`` and
+    ``recurrent``; ``workspace`` is a uint8/int8 device tensor of at least
+    ``layer_core_workspace_bytes(...)`` bytes (or None when that is 0)."""
+    B, T, C = qkv.shape
+    K = conv_w.shape[1]
+    dev = qkv.device
+    ws_bytes = 0
+    ws_ptr = None
+    if workspace is not None:
+        if workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        ws_ptr = workspace.data_ptr() if ws_bytes else None
+    args = [
+        _ptr(qkv, "qkv", _BF16, (B, T, C), dev),
+        _ptr(conv_w, "conv_w", _BF16, (C, K), dev),
+        _ptr(conv_state_in, "conv_state_in", _BF16, (B, K - 1, C), dev),
+        _ptr(conv_state_out, "conv_state_out", _BF16, (B, K - 1, C), dev),
+        _ptr(a, "a", _BF16, (B, T, Hv), dev),
+        _ptr(b, "b", _BF16, (B, T, Hv), dev),
+        _ptr(A_log, "A_log", (torch.float32,), (Hv,), dev),
+        _ptr(dt_bias, "dt_bias", (torch.float32,), (Hv,), dev),
+        _ptr(state_in, "state_in", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(state_out, "state_out", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
+        ws_ptr,
+    ]
+    _check(lib().gdn_layer_core(*args, ws_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps,
+                                _stream(dev, stream)))

@@ -1,0 +1,69 @@
+"""Build ``libgdn.so`` (gfx950 kernels + C ABI) in-tree with hipcc.
+
+Usage: ``python -m linear_attention_recurrence_prep_amd.build`` (or call
+``build()``).  Objects go to ``_build/``; the library is written next to
+this file so it travels with the source tree.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OUT_DIR = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libgdn.so")
+
+SOURCES = ["gdn_api.cpp", "prep.hip", "recurrent.hip"]
+
+ARCH = "gfx950"
+# Packed FP32 instructions are disabled for every HIP translation unit: the
+# compiler then emits only scalar v_fma_f32 / v_mul_f32 / v_add_f32 forms.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
+def _hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    extra = list(extra_flags or [])
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+    failed = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        text = out.decode(errors="replace")
+        # hipcc's host pass does not know the packed-fp32 feature; drop that note
+        lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l or "error" in l]
+        if lines and (verbose or p.returncode):
+            print("\n".join(lines), flush=True)
+        if p.returncode:
+            failed.append(src)
+    if failed:
+        raise RuntimeError(f"hipcc failed for {failed}")
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
+    print(LIB)

@@ -1,0 +1,97 @@
+// Device helpers shared by the gfx950 kernels of the Gated DeltaNet library:
+// bf16 <-> f32 conversion and cross-lane butterfly sums on 64-wide wavefronts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// ---------------------------------------------------------------- bf16 ----
+
+// bf16 bits in the low / high half of a 32-bit word, widened exactly.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// f32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// 8 bf16 (one 16-byte vector) -> 8 floats.
+__device__ __forceinline__ void unpack8(const uint4 w, float* f) {
+    f[0] = bf16lo(w.x); f[1] = bf16hi(w.x);
+    f[2] = bf16lo(w.y); f[3] = bf16hi(w.y);
+    f[4] = bf16lo(w.z); f[5] = bf16hi(w.z);
+    f[6] = bf16lo(w.w); f[7] = bf16hi(w.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+}
+
+// ------------------------------------------------------------ cross-lane ----
+
+// DPP controls (GCN/CDNA encoding): quad permutations, mirrors inside a
+// 16-lane row and inside each 8-lane half-row.
+enum : int {
+    DPP_QUAD_XOR1 = 0xB1,  // quad_perm [1,0,3,2]
+    DPP_QUAD_XOR2 = 0x4E,  // quad_perm [2,3,0,1]
+    DPP_ROW_MIRROR = 0x140,
+    DPP_ROW_HALF_MIRROR = 0x141,
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W lanes (W in {4, 8, 16, 32}); every lane of a
+// group receives the group's total.  Within a 16-lane row the steps are DPP
+// permutations (no LDS traffic); the 32-lane step uses ds_swizzle.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(W == 4 || W == 8 || W == 16 || W == 32, "group width");
+    x += dpp_mov<DPP_QUAD_XOR1>(x);
+    x += dpp_mov<DPP_QUAD_XOR2>(x);
+    if constexpr (W >= 8) x += dpp_mov<DPP_ROW_HALF_MIRROR>(x);
+    if constexpr (W >= 16) x += dpp_mov<DPP_ROW_MIRROR>(x);
+    if constexpr (W >= 32) {
+        // bitmask swizzle inside 32-lane halves: lane ^ 16
+        x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+    }
+    return x;
+}
+
+// Two independent group sums interleaved, so their latency chains overlap.
+template <int W>
+__device__ __forceinline__ void group_sum2(float& x, float& y) {
+    static_assert(W == 4 || W == 8 || W == 16 || W == 32, "group width");
+    float a = dpp_mov<DPP_QUAD_XOR1>(x), b = dpp_mov<DPP_QUAD_XOR1>(y);
+    x += a; y += b;
+    a = dpp_mov<DPP_QUAD_XOR2>(x); b = dpp_mov<DPP_QUAD_XOR2>(y);
+    x += a; y += b;
+    if constexpr (W >= 8) {
+        a = dpp_mov<DPP_ROW_HALF_MIRROR>(x); b = dpp_mov<DPP_ROW_HALF_MIRROR>(y);
+        x += a; y += b;
+    }
+    if constexpr (W >= 16) {
+        a = dpp_mov<DPP_ROW_MIRROR>(x); b = dpp_mov<DPP_ROW_MIRROR>(y);
+        x += a; y += b;
+    }
+    if constexpr (W >= 32) {
+        a = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+        b = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(y), 0x401F));
+        x += a; y += b;
+    }
+}
+
+}  // namespace gdn

@@ -1,0 +1,47 @@
+// Internal launchers of the Gated DeltaNet kernels.  Arguments are validated
+// by the C ABI layer (gdn_api.cpp) before these are called.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct RecurrentArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* g;
+    const float* beta;
+    const float* state_in;   // may be null (zeros)
+    float* state_out;
+    uint16_t* y;
+    int B, T, Hk, Hv, Dk, Dv;
+};
+
+struct PrepArgs {
+    const uint16_t* qkv;
+    const uint16_t* conv_w;
+    const uint16_t* conv_state_in;   // may be null (zeros)
+    uint16_t* conv_state_out;        // may be null (not written)
+    const uint16_t* a;
+    const uint16_t* b;
+    const float* A_log;
+    const float* dt_bias;
+    uint16_t* q;
+    uint16_t* k;
+    uint16_t* v;
+    float* g;
+    float* beta;
+    int B, T, Hk, Hv, Dk, Dv, K;
+    float q_scale, k_scale, eps;
+};
+
+// Number of blocks each launcher would use (for grid-size validation).
+int64_t recurrent_blocks(int B, int Hv, int Dk, int Dv);
+int64_t prep_blocks(int B, int T, int Hk, int Hv, int Dk, int Dv);
+
+hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream);
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
+
+}  // namespace gdn

@@ -1,0 +1,200 @@
+// Data-parallel prologue of the Gated DeltaNet layer on gfx950
+// ("mlex 0.1.2 -- src/models/gated_delta.rs", GatedDeltaNet::forward from the
+//  conv-state splice through g; "mlx-bun 0.4.0 -> 1.0.0, qwen3-delta.ts",
+//  compute_g and the dtype contract in its header).
+//
+// HBM-bound: every qkv element is read once and every q/k/v element written
+// once.  A thread owns 8 consecutive channels (one 16-byte vector) over TT
+// consecutive tokens and slides a (K-1)-row window of the spliced input
+// through registers, so the conv halo costs K-1 extra rows per TT tokens.
+// A 64-lane wave covers 512 channels; q/k heads (Dk channels = Dk/8 lanes)
+// are aligned lane groups, so the per-head sum of squares is a DPP butterfly.
+// Gates (g, beta) are computed by extra blocks of the same launch.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+constexpr int PREP_NT = 256;   // threads per block: 2048 channels
+constexpr int PREP_TT = 16;    // tokens per thread
+
+template <int DK, int K>
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int t_chunks,
+                                                    int64_t conv_blocks) {
+    const int tid = threadIdx.x;
+    const int64_t bid = blockIdx.x;
+    const int T = p.T, Hk = p.Hk, Hv = p.Hv, Dv = p.Dv;
+
+    if (bid >= conv_blocks) {
+        // g = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b)
+        const int64_t i = (bid - conv_blocks) * PREP_NT + tid;
+        if (i < (int64_t)p.B * T * Hv) {
+            const int h = (int)(i % Hv);
+            const float x = bf16lo(p.a[i]) + p.dt_bias[h];
+            const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+            p.g[i] = expf(-expf(p.A_log[h]) * sp);
+            p.beta[i] = 1.f / (1.f + expf(-bf16lo(p.b[i])));
+        }
+        return;
+    }
+
+    const int HKDK = Hk * DK;
+    const int C = 2 * HKDK + Hv * Dv;
+    const int groups = C >> 3;
+    const int ct = (int)(bid % c_tiles);
+    const int64_t rest = bid / c_tiles;
+    const int tc = (int)(rest % t_chunks);
+    const int b = (int)(rest / t_chunks);
+    const int cg = ct * PREP_NT + tid;
+    const bool valid = cg < groups;
+    const int c0 = cg * 8;
+    const int t0 = tc * PREP_TT;
+    const int t1 = min(T, t0 + PREP_TT);
+    const uint16_t* xb = p.qkv + (int64_t)b * T * C + c0;
+    const uint16_t* csb = p.conv_state_in ? p.conv_state_in + (int64_t)b * (K - 1) * C + c0 : nullptr;
+
+    // conv weights of the 8 channels: conv_w[c0 + i][j] -> w[j][i]
+    float w[K][8];
+    if (valid) {
+        const uint4* wp = reinterpret_cast<const uint4*>(p.conv_w + (int64_t)c0 * K);
+        float f[8 * K];
+#pragma unroll
+        for (int v4 = 0; v4 < K; ++v4) unpack8(wp[v4], f + 8 * v4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < K; ++j) w[j][i] = f[i * K + j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[j][i] = 0.f;
+    }
+
+    // spliced input row p (0 <= p < T + K - 1): conv state rows, then qkv rows
+    auto xpad_row = [&](int pr) -> uint4 {
+        if (!valid) return make_uint4(0, 0, 0, 0);
+        if (pr >= K - 1) return *reinterpret_cast<const uint4*>(xb + (int64_t)(pr - (K - 1)) * C);
+        if (csb) return *reinterpret_cast<const uint4*>(csb + (int64_t)pr * C);
+        return make_uint4(0, 0, 0, 0);
+    };
+
+    // window = xpad rows t0 .. t0+K-2
+    float h[K - 1][8];
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j) unpack8(xpad_row(t0 + j), h[j]);
+
+    // the new conv state: last K-1 rows of xpad (read before any write, so
+    // conv_state_out may alias conv_state_in)
+    if (tc == 0 && valid && p.conv_state_out) {
+        uint4 tail[K - 1];
+#pragma unroll
+        for (int i = 0; i < K - 1; ++i) tail[i] = xpad_row(T + i);
+        uint16_t* out = p.conv_state_out + (int64_t)b * (K - 1) * C + c0;
+#pragma unroll
+        for (int i = 0; i < K - 1; ++i) *reinterpret_cast<uint4*>(out + (int64_t)i * C) = tail[i];
+    }
+
+    uint4 rows[PREP_TT];
+#pragma unroll
+    for (int i = 0; i < PREP_TT; ++i)
+        rows[i] = (valid && t0 + i < t1) ? *reinterpret_cast<const uint4*>(xb + (int64_t)(t0 + i) * C)
+                                         : make_uint4(0, 0, 0, 0);
+
+    // region of this lane's channels
+    int region;      // 0 = q, 1 = k, 2 = v
+    if (c0 < HKDK) region = 0;
+    else if (c0 < 2 * HKDK) region = 1;
+    else region = 2;
+    const float scale = region == 0 ? p.q_scale : p.k_scale;
+
+#pragma unroll
+    for (int i = 0; i < PREP_TT; ++i) {
+        if (t0 + i >= t1) break;   // uniform across the block
+        const int t = t0 + i;
+        float x[8];
+        unpack8(rows[i], x);
+        float act[8];
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float u = 0.f;
+#pragma unroll
+            for (int j = 0; j < K - 1; ++j) u = fmaf(w[j][e], h[j][e], u);
+            u = fmaf(w[K - 1][e], x[e], u);
+            act[e] = u / (1.f + expf(-u));
+            ss = fmaf(act[e], act[e], ss);
+        }
+        ss = group_sum<DK / 8>(ss);
+        // slide the window
+#pragma unroll
+        for (int j = 0; j < K - 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[j][e] = h[j + 1][e];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[K - 2][e] = x[e];
+
+        if (!valid) continue;
+        const int64_t tok = (int64_t)b * T + t;
+        if (region < 2) {
+            const float r = 1.f / sqrtf(ss / (float)DK + p.eps);
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = act[e] * r * scale;
+            uint16_t* dst = region == 0 ? p.q + tok * HKDK + c0 : p.k + tok * HKDK + (c0 - HKDK);
+            *reinterpret_cast<uint4*>(dst) = pack8(o);
+        } else {
+            *reinterpret_cast<uint4*>(p.v + tok * Hv * Dv + (c0 - 2 * HKDK)) = pack8(act);
+        }
+    }
+}
+
+static void prep_grid(int B, int T, int Hk, int Hv, int Dk, int Dv, int& c_tiles, int& t_chunks,
+                      int64_t& conv_blocks, int64_t& gate_blocks) {
+    const int64_t C = 2LL * Hk * Dk + (int64_t)Hv * Dv;
+    c_tiles = (int)((C / 8 + PREP_NT - 1) / PREP_NT);
+    t_chunks = T > 0 ? (T + PREP_TT - 1) / PREP_TT : 1;
+    conv_blocks = (int64_t)B * t_chunks * c_tiles;
+    gate_blocks = ((int64_t)B * T * Hv + PREP_NT - 1) / PREP_NT;
+}
+
+int64_t prep_blocks(int B, int T, int Hk, int Hv, int Dk, int Dv) {
+    int ct, tcn;
+    int64_t cb, gb;
+    prep_grid(B, T, Hk, Hv, Dk, Dv, ct, tcn, cb, gb);
+    return cb + gb;
+}
+
+template <int DK, int K>
+static hipError_t launch_prep_t(const PrepArgs& a, hipStream_t stream) {
+    int c_tiles, t_chunks;
+    int64_t conv_blocks, gate_blocks;
+    prep_grid(a.B, a.T, a.Hk, a.Hv, a.Dk, a.Dv, c_tiles, t_chunks, conv_blocks, gate_blocks);
+    const int64_t blocks = conv_blocks + gate_blocks;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((prep_kernel<DK, K>), dim3((unsigned)blocks), dim3(PREP_NT), 0, stream,
+                       a, c_tiles, t_chunks, conv_blocks);
+    return hipGetLastError();
+}
+
+template <int DK>
+static hipError_t launch_prep_k(const PrepArgs& a, hipStream_t stream) {
+    switch (a.K) {
+        case 2: return launch_prep_t<DK, 2>(a, stream);
+        case 3: return launch_prep_t<DK, 3>(a, stream);
+        case 4: return launch_prep_t<DK, 4>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream) {
+    switch (a.Dk) {
+        case 32: return launch_prep_k<32>(a, stream);
+        case 64: return launch_prep_k<64>(a, stream);
+        case 128: return launch_prep_k<128>(a, stream);
+        case 256: return launch_prep_k<256>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gdn

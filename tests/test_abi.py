@@ -1,0 +1,171 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/gdn.h declares, and rejects bad arguments with the documented
+status before any launch (these calls never reach HIP).  Pointers here are
+fake addresses: validation never dereferences them."""
+import ctypes
+import os
+
+import pytest
+
+from linear_attention_recurrence_prep_amd import binding
+
+OK, NULLP, DIMS, UNSUP, ALIGN, OVERLAP, WS, VALUE, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(binding.LIB_PATH):
+        from linear_attention_recurrence_prep_amd.build import build
+        build()
+    return binding.lib()
+
+
+def test_exports_every_header_function(L):
+    names = binding.header_functions()
+    assert set(names) >= {"gdn_recurrent", "gdn_prep", "gdn_layer_core",
+                          "gdn_layer_core_workspace_bytes", "gdn_last_error",
+                          "gdn_status_string", "gdn_version"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    assert L.gdn_version() >= 1
+    for code, name in [(OK, "GDN_OK"), (NULLP, "GDN_ERR_NULL_POINTER"), (DIMS, "GDN_ERR_BAD_DIMS"),
+                       (UNSUP, "GDN_ERR_UNSUPPORTED"), (ALIGN, "GDN_ERR_MISALIGNED"),
+                       (OVERLAP, "GDN_ERR_OVERLAP"), (WS, "GDN_ERR_WORKSPACE"),
+                       (VALUE, "GDN_ERR_BAD_VALUE"), (HIP, "GDN_ERR_HIP")]:
+        assert L.gdn_status_string(code).decode() == name
+    assert L.gdn_status_string(123).decode() == "GDN_ERR_UNKNOWN"
+
+
+# Fake, well-separated, 256-byte aligned "device" addresses.
+BASE = 1 << 40
+SPAN = 1 << 34
+
+
+def addr(i):
+    return BASE + i * SPAN
+
+
+def rec_args(B=2, T=8, Hk=2, Hv=4, Dk=64, Dv=32, **over):
+    p = dict(q=addr(0), k=addr(1), v=addr(2), g=addr(3), beta=addr(4), state_in=addr(5),
+             state_out=addr(6), y=addr(7))
+    p.update({k: v for k, v in over.items() if k in p})
+    dims = dict(B=B, T=T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv)
+    dims.update({k: v for k, v in over.items() if k in dims})
+    return p, dims
+
+
+def call_rec(L, **over):
+    p, d = rec_args(**over)
+    return L.gdn_recurrent(p["q"], p["k"], p["v"], p["g"], p["beta"], p["state_in"], p["state_out"],
+                           p["y"], d["B"], d["T"], d["Hk"], d["Hv"], d["Dk"], d["Dv"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=-1), DIMS), (dict(T=-3), DIMS), (dict(Hk=0), DIMS), (dict(Hv=0), DIMS),
+    (dict(Hk=3, Hv=4), DIMS), (dict(Dk=48), UNSUP), (dict(Dk=16), UNSUP), (dict(Dk=512), UNSUP),
+    (dict(Dv=12), UNSUP), (dict(Dv=0), UNSUP), (dict(Dv=4104), UNSUP),
+    (dict(q=None), NULLP), (dict(k=None), NULLP), (dict(v=None), NULLP), (dict(g=None), NULLP),
+    (dict(beta=None), NULLP), (dict(y=None), NULLP), (dict(state_out=None), NULLP),
+    (dict(q=addr(0) + 8), ALIGN), (dict(state_out=addr(6) + 4), ALIGN),
+    (dict(y=addr(2)), OVERLAP), (dict(state_out=addr(5) + 16), OVERLAP), (dict(y=addr(6)), OVERLAP),
+    (dict(B=1 << 30, T=1 << 30), DIMS),
+])
+def test_recurrent_rejects(L, over, code):
+    assert call_rec(L, **over) == code
+    assert L.gdn_last_error().decode() != ""
+
+
+def test_recurrent_noop_and_null_inputs_allowed(L):
+    # B == 0 returns before any launch; T == 0 still needs state_out only
+    assert call_rec(L, B=0) == OK
+    assert call_rec(L, B=0, q=None, k=None, v=None, g=None, beta=None, y=None, state_out=None) == OK
+    assert L.gdn_last_error().decode() == ""
+
+
+def prep_args(**over):
+    p = dict(qkv=addr(0), conv_w=addr(1), cs_in=addr(2), cs_out=addr(3), a=addr(4), b=addr(5),
+             A_log=addr(6), dt_bias=addr(7), q=addr(8), k=addr(9), v=addr(10), g=addr(11),
+             beta=addr(12))
+    d = dict(B=2, T=5, Hk=2, Hv=4, Dk=32, Dv=16, K=4, q_scale=0.1, k_scale=0.2, eps=1e-6)
+    for k_, v_ in over.items():
+        (p if k_ in p else d)[k_] = v_
+    return p, d
+
+
+def call_prep(L, **over):
+    p, d = prep_args(**over)
+    return L.gdn_prep(p["qkv"], p["conv_w"], p["cs_in"], p["cs_out"], p["a"], p["b"], p["A_log"],
+                      p["dt_bias"], p["q"], p["k"], p["v"], p["g"], p["beta"], d["B"], d["T"], d["Hk"],
+                      d["Hv"], d["Dk"], d["Dv"], d["K"], d["q_scale"], d["k_scale"], d["eps"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(K=1), UNSUP), (dict(K=5), UNSUP), (dict(Dk=100), UNSUP), (dict(Hv=3), DIMS),
+    (dict(eps=-1.0), VALUE), (dict(eps=float("nan")), VALUE), (dict(q_scale=float("inf")), VALUE),
+    (dict(qkv=None), NULLP), (dict(conv_w=None), NULLP), (dict(a=None), NULLP), (dict(b=None), NULLP),
+    (dict(A_log=None), NULLP), (dict(dt_bias=None), NULLP), (dict(q=None), NULLP),
+    (dict(k=None), NULLP), (dict(v=None), NULLP), (dict(g=None), NULLP), (dict(beta=None), NULLP),
+    (dict(qkv=addr(0) + 2), ALIGN), (dict(conv_w=addr(1) + 8), ALIGN),
+    (dict(q=addr(0)), OVERLAP), (dict(k=addr(8) + 32), OVERLAP), (dict(cs_out=addr(2) + 16), OVERLAP),
+    (dict(g=addr(12)), OVERLAP),
+])
+def test_prep_rejects(L, over, code):
+    assert call_prep(L, **over) == code
+
+
+def test_prep_allows_in_place_conv_state_and_empty_batch(L):
+    assert call_prep(L, B=0) == OK
+    # exact alias passes validation; B=0 keeps it launch-free
+    assert call_prep(L, B=0, cs_out=addr(2)) == OK
+    assert call_prep(L, B=0, cs_in=None, cs_out=None) == OK
+
+
+def test_workspace_bytes(L):
+    f = L.gdn_layer_core_workspace_bytes
+    up = lambda x: (x + 255) // 256 * 256
+    B, T, Hk, Hv, Dk, Dv = 1, 4096, 16, 32, 128, 128
+    expect = 2 * up(B * T * Hk * Dk * 2) + up(B * T * Hv * Dv * 2) + 2 * up(B * T * Hv * 4)
+    assert f(B, T, Hk, Hv, Dk, Dv) == expect
+    assert f(1, 0, 16, 32, 128, 128) == 0
+    assert f(0, 10, 16, 32, 128, 128) == 0
+    assert f(1, 10, 3, 32, 128, 128) == 0     # invalid dims
+    assert f(1, 10, 16, 32, 100, 128) == 0
+
+
+def call_core(L, ws=addr(20), ws_bytes=1 << 30, **over):
+    p, d = prep_args(**over)
+    si = over.get("state_in", addr(13))
+    so = over.get("state_out", addr(14))
+    y = over.get("y", addr(15))
+    return L.gdn_layer_core(p["qkv"], p["conv_w"], p["cs_in"], p["cs_out"], p["a"], p["b"], p["A_log"],
+                            p["dt_bias"], si, so, y, ws, ctypes.c_size_t(ws_bytes), d["B"], d["T"],
+                            d["Hk"], d["Hv"], d["Dk"], d["Dv"], d["K"], d["q_scale"], d["k_scale"],
+                            d["eps"], None)
+
+
+def test_layer_core_rejects(L):
+    assert call_core(L, ws=None) == WS
+    assert call_core(L, ws_bytes=100) == WS
+    assert call_core(L, ws=addr(20) + 16) == ALIGN
+    assert call_core(L, ws=addr(0)) == OVERLAP            # workspace over qkv
+    assert call_core(L, y=addr(20)) == OVERLAP            # y inside workspace
+    assert call_core(L, state_out=addr(13) + 16) == OVERLAP
+    assert call_core(L, K=7) == UNSUP
+    assert call_core(L, qkv=None) == NULLP
+    assert call_core(L, state_out=None) == NULLP
+    assert call_core(L, B=0) == OK
+    assert call_core(L, B=0, state_out=addr(13)) == OK    # exact in-place alias allowed
+
+
+def test_binding_argument_checks_on_cpu():
+    import torch
+    q = torch.zeros(1, 2, 1, 32, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        binding._ptr(q.float(), "q", binding._BF16, (1, 2, 1, 32), q.device)
+    with pytest.raises(ValueError):
+        binding._ptr(q, "q", binding._BF16, (1, 2, 1, 64), q.device)
+    with pytest.raises(ValueError):
+        binding._ptr(q.transpose(1, 3), "q", binding._BF16, (1, 32, 1, 2), q.device)

@@ -1,0 +1,377 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs.  Tolerances (see tests/helpers.py):
+  y      within 1 bf16 ulp of the fp64 value + 1e-3 absolute;
+  state  per-head normwise max |dS| / max |S| <= 1e-4 (T <= 4096), 1e-3 beyond;
+  GQA, batch/head permutation, time split, in-place and NULL-state runs are
+  compared bit for bit against the GPU's own reference run.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_recurrence_prep_amd import binding, inputs
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = 0x7FC0   # quiet-NaN bf16 pattern (fits int16)
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    binding.lib()   # raises if the HIP library is not built
+    yield
+    torch.cuda.synchronize()
+
+
+def rec_inputs(B, T, Hk, Hv, Dk, Dv, wid, state=True):
+    raw = inputs.recurrence_raw(B=B, T=T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, workload_id=wid, state=state)
+    ri = oracle.recurrence_inputs(raw)
+    ri["state"] = raw["state"]
+    return ri
+
+
+def gpu_recurrent(ri, state_dev="copy", y_guard=True):
+    """Run gdn_recurrent on device copies of ri; returns (y bits, state f32)."""
+    B, T, Hk, Dk = ri["q"].shape
+    Hv, Dv = ri["v"].shape[2:]
+    d = {k: H.to_dev(ri[k]) for k in ("q", "k", "v", "g", "beta")}
+    s_in = H.to_dev(ri["state"]) if ri["state"] is not None else None
+    yfull, y = H.guarded((B, T, Hv, Dv), torch.int16, NAN_BF16)
+    sfull, s_out = H.guarded((B, Hv, Dv, Dk), torch.float32, float("nan"))
+    binding.recurrent(d["q"], d["k"], d["v"], d["g"], d["beta"], s_in, s_out, y)
+    torch.cuda.synchronize()
+    assert H.guards_intact(yfull, NAN_BF16) and H.guards_intact(sfull, float("nan")), "guard band written"
+    return H.bits(y), H.f32(s_out)
+
+
+def oracle_recurrent(ri):
+    f = oracle.bf16_to_f64
+    s0 = None if ri["state"] is None else ri["state"].astype(np.float64)
+    return oracle.recurrent(f(ri["q"]), f(ri["k"]), f(ri["v"]), ri["g"].astype(np.float64),
+                            ri["beta"].astype(np.float64), s0)
+
+
+# ------------------------------------------------------------ recurrence
+
+REC_CASES = [
+    # B, T, Hk, Hv, Dk, Dv, wid           (wid = generator workload id)
+    (1, 64, 2, 4, 32, 32, 0),              # tiny workload
+    (1, 1, 16, 32, 128, 128, 1),           # decode, B=1
+    (64, 1, 16, 32, 128, 128, 2),          # batched decode
+    (2, 37, 1, 2, 64, 24, 100),            # ragged T (chunk tail), Dv < rows/block
+    (1, 100, 2, 2, 128, 40, 101),          # Dv not a multiple of the block rows
+    (1, 19, 1, 1, 256, 8, 102),            # Dk = 256 (32-lane rows)
+    (3, 5, 2, 4, 128, 128, 103),           # just above the short-sequence path
+    (2, 4, 4, 8, 32, 64, 104),             # short-sequence path, GQA 2
+    (1, 70, 1, 4, 64, 64, 105),            # GQA 4, two chunks + tail
+    (1, 33, 2, 2, 128, 256, 106),          # Dv = 256, one step past a chunk
+]
+
+
+@pytest.mark.parametrize("case", REC_CASES, ids=lambda c: "B%dT%dHk%dHv%dDk%dDv%d" % c[:6])
+def test_recurrent_matches_oracle(case):
+    B, T, Hk, Hv, Dk, Dv, wid = case
+    say("recurrent", case)
+    ri = rec_inputs(B, T, Hk, Hv, Dk, Dv, wid)
+    y_bits, s = gpu_recurrent(ri)
+    y_ref, s_ref = oracle_recurrent(ri)
+    H.check_y(y_bits, y_ref, str(case))
+    H.check_state(s, s_ref, 1e-4, str(case))
+
+
+def test_recurrent_zero_state_and_null_state():
+    say("recurrent NULL state")
+    ri = rec_inputs(1, 50, 2, 4, 64, 32, 110, state=False)
+    y_bits, s = gpu_recurrent(ri)
+    y_ref, s_ref = oracle_recurrent(ri)
+    H.check_y(y_bits, y_ref)
+    H.check_state(s, s_ref, 1e-4)
+    ri2 = dict(ri, state=np.zeros((1, 4, 32, 64), np.float32))
+    y2, s2 = gpu_recurrent(ri2)
+    assert np.array_equal(y_bits, y2) and np.array_equal(s, s2)
+
+
+def test_recurrent_T0_copies_state():
+    say("recurrent T=0")
+    ri = rec_inputs(2, 0, 1, 2, 128, 16, 111)
+    y_bits, s = gpu_recurrent(ri)
+    assert y_bits.size == 0 and np.array_equal(s, ri["state"])
+    ri["state"] = None
+    _, s = gpu_recurrent(ri)
+    assert np.array_equal(s, np.zeros_like(s))
+
+
+def test_recurrent_in_place_state():
+    say("recurrent in place")
+    ri = rec_inputs(2, 45, 2, 4, 128, 32, 112)
+    y_ref_bits, s_ref = gpu_recurrent(ri)
+    d = {k: H.to_dev(ri[k]) for k in ("q", "k", "v", "g", "beta")}
+    st = H.to_dev(ri["state"])
+    y = torch.empty(2, 45, 4, 32, dtype=torch.int16, device=H.DEV)
+    binding.recurrent(d["q"], d["k"], d["v"], d["g"], d["beta"], st, st, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(H.bits(y), y_ref_bits) and np.array_equal(H.f32(st), s_ref)
+
+
+def test_recurrent_gqa_is_bit_exact_against_repeated_heads():
+    say("recurrent GQA")
+    ri = rec_inputs(2, 40, 2, 8, 64, 32, 113)
+    y1, s1 = gpu_recurrent(ri)
+    rep = dict(ri, q=np.repeat(ri["q"], 4, axis=2), k=np.repeat(ri["k"], 4, axis=2))
+    y2, s2 = gpu_recurrent(rep)
+    assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
+
+
+def test_recurrent_time_split_is_bit_exact():
+    say("recurrent T split")
+    ri = rec_inputs(1, 90, 1, 2, 128, 32, 114)
+    y, s = gpu_recurrent(ri)
+    for T1 in (1, 3, 32, 50):
+        a = {k: np.ascontiguousarray(ri[k][:, :T1]) for k in ("q", "k", "v", "g", "beta")}
+        b = {k: np.ascontiguousarray(ri[k][:, T1:]) for k in ("q", "k", "v", "g", "beta")}
+        ya, sa = gpu_recurrent(dict(a, state=ri["state"]))
+        yb, sb = gpu_recurrent(dict(b, state=sa))
+        assert np.array_equal(np.concatenate([ya, yb], axis=1), y), T1
+        assert np.array_equal(sb, s), T1
+
+
+def test_recurrent_batch_head_permutation_is_bit_exact():
+    say("recurrent permutation")
+    ri = rec_inputs(3, 20, 2, 4, 64, 16, 115)
+    y, s = gpu_recurrent(ri)
+    pb, phk, phv = np.array([2, 0, 1]), np.array([1, 0]), np.array([2, 3, 0, 1])
+    perm = dict(q=ri["q"][pb][:, :, phk], k=ri["k"][pb][:, :, phk], v=ri["v"][pb][:, :, phv],
+                g=ri["g"][pb][:, :, phv], beta=ri["beta"][pb][:, :, phv], state=ri["state"][pb][:, phv])
+    y2, s2 = gpu_recurrent({k: np.ascontiguousarray(v) for k, v in perm.items()})
+    assert np.array_equal(y2, y[pb][:, :, phv]) and np.array_equal(s2, s[pb][:, phv])
+
+
+def test_recurrent_repeat_runs_are_bitwise_identical():
+    say("recurrent determinism")
+    ri = rec_inputs(4, 77, 2, 4, 128, 64, 116)
+    y1, s1 = gpu_recurrent(ri)
+    y2, s2 = gpu_recurrent(ri)
+    assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
+
+
+def test_recurrent_invariants_on_gpu():
+    # beta = 0, g = 1: the state is carried unchanged (exactly)
+    say("recurrent invariants")
+    ri = rec_inputs(1, 10, 1, 2, 64, 16, 117)
+    ri["g"][:] = 1.0
+    ri["beta"][:] = 0.0
+    _, s = gpu_recurrent(ri)
+    assert np.array_equal(s, ri["state"])
+    # g = 0 at the last step: S = beta v k^T regardless of the history
+    ri = rec_inputs(1, 10, 1, 2, 64, 16, 118)
+    ri["g"][:, -1] = 0.0
+    _, s = gpu_recurrent(ri)
+    f = oracle.bf16_to_f64
+    for h in range(2):
+        ref = np.outer(f(ri["v"][0, -1, h]) * ri["beta"][0, -1, h], f(ri["k"][0, -1, 0]))
+        np.testing.assert_allclose(s[0, h], ref, rtol=2 ** -22, atol=0)
+
+
+# --------------------------------------------------------------- prologue
+
+def layer_inputs(B, T, Hk, Hv, Dk, Dv, K, wid, state=True, conv_state=True):
+    return inputs.layer_raw(B=B, T=T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, K=K, workload_id=wid,
+                            state=state, conv_state=conv_state)
+
+
+def gpu_prep(raw, Hk, Hv, Dk, Dv, qs, ks, eps=1e-6, in_place=False, write_cs=True):
+    B, T, C = raw["qkv"].shape
+    K = raw["conv_w"].shape[1]
+    d = {k: H.to_dev(raw[k]) for k in ("qkv", "conv_w", "conv_state", "a", "b", "A_log", "dt_bias")}
+    q = torch.empty(B, T, Hk, Dk, dtype=torch.int16, device=H.DEV)
+    k = torch.empty_like(q)
+    v = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=H.DEV)
+    g = torch.empty(B, T, Hv, dtype=torch.float32, device=H.DEV)
+    beta = torch.empty_like(g)
+    if in_place:
+        cs_out = d["conv_state"]
+    else:
+        cs_out = torch.full((B, K - 1, C), NAN_BF16, dtype=torch.int16, device=H.DEV) if write_cs else None
+    binding.prep(d["qkv"], d["conv_w"], d["conv_state"], cs_out, d["a"], d["b"], d["A_log"],
+                 d["dt_bias"], q, k, v, g, beta, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs,
+                 k_scale=ks, eps=eps)
+    torch.cuda.synchronize()
+    return dict(q=H.bits(q), k=H.bits(k), v=H.bits(v), g=H.f32(g), beta=H.f32(beta),
+                conv_state=None if cs_out is None else H.bits(cs_out))
+
+
+PREP_CASES = [
+    # B, T, Hk, Hv, Dk, Dv, K, conv_state, wid
+    (1, 64, 2, 4, 32, 32, 4, False, 200),
+    (2, 37, 2, 4, 64, 24, 4, True, 201),
+    (1, 50, 4, 8, 128, 128, 3, True, 202),
+    (3, 17, 1, 2, 256, 48, 2, True, 203),
+    (2, 2, 16, 32, 128, 128, 4, True, 204),      # T < K - 1
+    (1, 300, 16, 32, 128, 128, 4, False, 205),   # full-width channels, several token chunks
+]
+
+
+@pytest.mark.parametrize("case", PREP_CASES, ids=lambda c: "B%dT%dHk%dHv%dDk%dDv%dK%d" % c[:7])
+def test_prep_matches_oracle(case):
+    B, T, Hk, Hv, Dk, Dv, K, cs, wid = case
+    say("prep", case)
+    raw = layer_inputs(B, T, Hk, Hv, Dk, Dv, K, wid, conv_state=cs)
+    qs, ks = 1.0 / Dk, Dk ** -0.5
+    out = gpu_prep(raw, Hk, Hv, Dk, Dv, qs, ks)
+    ref = oracle.prep(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"], raw["A_log"],
+                      raw["dt_bias"], Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs, k_scale=ks)
+    flips = sum(H.check_bf16_within_ulp(out[n], ref[n], n) for n in ("q", "k", "v"))
+    n_el = out["q"].size * 2 + out["v"].size
+    assert flips <= max(4, n_el // 1000), f"{flips} of {n_el} roundings differ from nearest-even"
+    H.check_gates(out["g"], out["beta"], ref["g"], ref["beta"])
+    assert np.array_equal(out["conv_state"], ref["conv_state"])
+
+
+def test_prep_conv_state_in_place_and_T0():
+    say("prep in-place conv state / T=0")
+    raw = layer_inputs(2, 9, 2, 4, 64, 16, 4, 210)
+    ref = gpu_prep(raw, 2, 4, 64, 16, 0.1, 0.2)
+    ip = gpu_prep(raw, 2, 4, 64, 16, 0.1, 0.2, in_place=True)
+    for n in ("q", "k", "v", "g", "beta", "conv_state"):
+        assert np.array_equal(ip[n], ref[n]), n
+    raw0 = layer_inputs(2, 0, 2, 4, 64, 16, 4, 211)
+    out0 = gpu_prep(raw0, 2, 4, 64, 16, 0.1, 0.2)
+    assert np.array_equal(out0["conv_state"], raw0["conv_state"])
+    raw0["conv_state"] = None
+    out0 = gpu_prep(raw0, 2, 4, 64, 16, 0.1, 0.2)
+    assert not out0["conv_state"].any()
+
+
+# ------------------------------------------------------------- layer core
+
+def gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks, eps=1e-6):
+    B, T, C = raw["qkv"].shape
+    K = raw["conv_w"].shape[1]
+    d = {k: H.to_dev(raw[k]) for k in ("qkv", "conv_w", "conv_state", "a", "b", "A_log", "dt_bias",
+                                       "state")}
+    y = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=H.DEV)
+    s_out = torch.empty(B, Hv, Dv, Dk, dtype=torch.float32, device=H.DEV)
+    cs_out = torch.empty(B, K - 1, C, dtype=torch.int16, device=H.DEV)
+    nws = binding.layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=H.DEV)
+    binding.layer_core(d["qkv"], d["conv_w"], d["conv_state"], cs_out, d["a"], d["b"], d["A_log"],
+                       d["dt_bias"], d["state"], s_out, y, ws, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv,
+                       q_scale=qs, k_scale=ks, eps=eps)
+    torch.cuda.synchronize()
+    return H.bits(y), H.f32(s_out), H.bits(cs_out)
+
+
+# The end-to-end state tolerance: the prologue rounds q, k, v to bf16 from
+# f32 (GPU) and from fp64 (oracle); near-ties round differently (the prep
+# tests bound these flips), and one flipped k or v input moves the affected
+# state terms by up to one bf16 ulp, 2^-8 relative.  The recurrence alone is
+# held to the 1e-4 bound above; end to end the bound is 2^-8 normwise.
+CORE_STATE_TOL = 2.0 ** -8
+
+CORE_CASES = [
+    # B, T, Hk, Hv, Dk, Dv, K, wid
+    (1, 64, 2, 4, 32, 32, 4, 300),
+    (2, 45, 2, 4, 64, 24, 3, 301),
+    (1, 130, 4, 8, 128, 128, 4, 302),
+]
+
+
+@pytest.mark.parametrize("case", CORE_CASES, ids=lambda c: "B%dT%dHk%dHv%dDk%dDv%dK%d" % c[:7])
+def test_layer_core_matches_oracle(case):
+    B, T, Hk, Hv, Dk, Dv, K, wid = case
+    say("layer_core", case)
+    raw = layer_inputs(B, T, Hk, Hv, Dk, Dv, K, wid)
+    qs, ks = 1.0 / Dk, Dk ** -0.5
+    y, s, cs = gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks)
+    y_ref, s_ref, cs_ref = oracle.layer_core(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"],
+                                             raw["b"], raw["A_log"], raw["dt_bias"], raw["state"],
+                                             Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs, k_scale=ks)
+    H.check_y(y, y_ref, str(case))
+    e = H.check_state(s, s_ref, CORE_STATE_TOL, str(case))
+    say("layer_core state normwise err", e)
+    assert np.array_equal(cs, cs_ref)
+
+
+def test_layer_core_equals_prep_then_recurrent():
+    say("layer_core composition")
+    Hk, Hv, Dk, Dv, K = 2, 4, 128, 64, 4
+    raw = layer_inputs(2, 70, Hk, Hv, Dk, Dv, K, 310)
+    y, s, cs = gpu_layer_core(raw, Hk, Hv, Dk, Dv, 0.01, 0.09)
+    p = gpu_prep(raw, Hk, Hv, Dk, Dv, 0.01, 0.09)
+    y2, s2 = gpu_recurrent(dict(q=p["q"], k=p["k"], v=p["v"], g=p["g"], beta=p["beta"],
+                                state=raw["state"]))
+    assert np.array_equal(y, y2) and np.array_equal(s, s2) and np.array_equal(cs, p["conv_state"])
+
+
+def test_prefill_workload_full_size_sampled():
+    """The T=4096 prefill workload at full size; four v-heads recomputed by the
+    oracle end to end (all rows), plus the whole prologue output."""
+    say("prefill workload full size")
+    w = inputs.WORKLOADS["prefill"]
+    Hk, Hv, Dk, Dv = w["Hk"], w["Hv"], w["Dk"], w["Dv"]
+    raw = inputs.workload("prefill")
+    qs, ks = inputs.scales(Dk)
+    y, s, cs = gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks)
+    assert not np.isnan(s).any()
+    worst = 0.0
+    for hv in (0, 5, 17, 31):
+        sub = H.layer_sub(raw, 0, hv, list(range(Dv)), Hk, Hv, Dk, Dv)
+        y_ref, s_ref, _ = oracle.layer_core(sub["qkv"], sub["conv_w"], sub["conv_state"], sub["a"],
+                                            sub["b"], sub["A_log"], sub["dt_bias"], sub["state"],
+                                            Hk=1, Hv=1, Dk=Dk, Dv=Dv, q_scale=qs, k_scale=ks)
+        H.check_y(y[:, :, hv:hv + 1], y_ref, f"hv={hv}")
+        worst = max(worst, H.check_state(s[:, hv:hv + 1], s_ref, CORE_STATE_TOL, f"hv={hv}"))
+    say("prefill state normwise err", worst)
+    assert np.array_equal(cs, raw["qkv"][:, -(w["K"] - 1):])
+
+
+def test_prefill_workload_recurrence_strict():
+    """Recurrence at the prefill workload's size on oracle-prepared inputs
+    (the oracle's own prologue, rounded to the stored dtypes), sampled heads,
+    strict 1e-4 state bound."""
+    say("prefill recurrence strict")
+    w = inputs.WORKLOADS["prefill"]
+    Hk, Hv, Dk, Dv, T = w["Hk"], w["Hv"], w["Dk"], w["Dv"], w["T"]
+    raw = inputs.workload("prefill")
+    qs, ks = inputs.scales(Dk)
+    p = oracle.prep(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"], raw["A_log"],
+                    raw["dt_bias"], Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs, k_scale=ks)
+    ri = dict(q=oracle.round_bf16(p["q"]), k=oracle.round_bf16(p["k"]), v=oracle.round_bf16(p["v"]),
+              g=oracle.round_f32(p["g"]), beta=oracle.round_f32(p["beta"]), state=None)
+    y, s = gpu_recurrent(ri)
+    for hv in (1, 12, 30):
+        args = H.recurrence_sub(ri, 0, hv, list(range(Dv)), Hk, Hv)
+        y_ref, s_ref = oracle.recurrent(*args)
+        H.check_y(y[:, :, hv:hv + 1], y_ref, f"hv={hv}")
+        H.check_state(s[:, hv:hv + 1], s_ref, 1e-4, f"hv={hv}")
+
+
+def test_long_workload_full_size_sampled():
+    """B=4, T=32768 with random initial state: the full layer core on the GPU;
+    the oracle recomputes 8 rows of 3 (b, hv) heads over the whole sequence
+    (drift check, 1e-3 state bound on the recurrence-dominated rows)."""
+    say("long workload full size")
+    w = inputs.WORKLOADS["long"]
+    Hk, Hv, Dk, Dv = w["Hk"], w["Hv"], w["Dk"], w["Dv"]
+    raw = inputs.workload("long")
+    qs, ks = inputs.scales(Dk)
+    y, s, cs = gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks)
+    assert not np.isnan(s).any()
+    rows = [0, 9, 31, 64, 77, 100, 126, 127]
+    for b, hv in ((0, 0), (1, 13), (3, 31)):
+        sub = H.layer_sub(raw, b, hv, rows, Hk, Hv, Dk, Dv)
+        y_ref, s_ref, _ = oracle.layer_core(sub["qkv"], sub["conv_w"], sub["conv_state"], sub["a"],
+                                            sub["b"], sub["A_log"], sub["dt_bias"], sub["state"],
+                                            Hk=1, Hv=1, Dk=Dk, Dv=len(rows), q_scale=qs, k_scale=ks)
+        H.check_y(y[b:b + 1, :, hv:hv + 1][..., rows], y_ref, f"b={b} hv={hv}")
+        e = H.check_state(s[b:b + 1, hv:hv + 1][:, :, rows], s_ref, CORE_STATE_TOL, f"b={b} hv={hv}")
+        say("long", b, hv, "state err", e)
