@@ -158,7 +158,7 @@ def main():
         "data": "synthetic (seeded)",
         "config": {"workload": "prefill B=1 T=4096 Hk=16 Hv=32 Dk=Dv=128 K=4, zero conv/recurrent state",
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "alu", "kernel": "recurrent_kernel<128,32>",
+        "roofline": {"bound": "alu", "kernel": "recurrent_chunk_kernel<128,32>",
                      "achieved": achieved_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
                      "flops_per_launch": flops, "avg_launch_us": rec_us},
@@ -247,7 +247,7 @@ def bench_decode(args, torch, dev, up, inputs, binding, np):
         "unit": "token*head/s",
         "us_per_step": out["layer_core"],
         "layer_core_GBs": core_bytes / out["layer_core"] / 1e3,
-        "roofline": {"bound": "hbm", "kernel": "recurrent_kernel<128,1>", "achieved": gbs,
+        "roofline": {"bound": "hbm", "kernel": "recurrent_step_kernel<128>", "achieved": gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                      "bytes_per_launch": rec_bytes, "avg_launch_us": out["recurrent"]},
     }

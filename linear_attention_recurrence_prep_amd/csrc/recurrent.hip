@@ -7,20 +7,19 @@
 //  recurrence loop; "mlx-bun 0.4.0 -> 1.0.0, qwen3-delta.ts",
 //  gated_delta_step, which runs the same order per row).
 //
-// Mapping (CDNA4, 64-wide wavefronts):
-//   * one state row per group of L = Dk/8 lanes; each lane keeps 8 floats
-//     of its row in VGPRs for the whole T loop (elements 4j..4j+3 and
-//     Dk/2+4j..Dk/2+4j+3 for lane j of the group, so a 16-lane group reads
-//     k/q rows from LDS as contiguous 256-byte ds_read_b128 runs);
-//   * a workgroup of 4 waves owns ROWS = 4*64/L consecutive rows of one
-//     (b, hv); the two Dk-long dot products are DPP butterflies inside the
-//     lane group (plus one ds_swizzle step when L = 32);
-//   * k, q (converted to f32 once), v, g and beta for the next TC steps are
-//     loaded from HBM into registers while the current TC steps run, then
-//     written to LDS between two barriers; y for TC steps is buffered in LDS
-//     and flushed as contiguous bf16 runs;
-//   * block -> (b, hv) mapping keeps all row blocks of a head, and the
-//     v-heads sharing a k-head, on the same XCD (shared L2 for k/q).
+// Both kernels evaluate one step in the factored form
+//   a = S k,  c = S q           (old state, one pass, two interleaved sums)
+//   delta = (v - g a) beta       (= (v - (gS) k) beta)
+//   y     = g c + delta (k.q)    (= (gS + delta k^T) q)
+//   S     = g S + delta k^T
+// which is the same arithmetic up to rounding order, needs one pass over the
+// row for both dot products, and lets the two cross-lane sums overlap.
+//
+// Mapping (CDNA4, 64-wide wavefronts): one state row per group of L = Dk/8
+// lanes; lane j of a group keeps elements 4j..4j+3 and Dk/2+4j..Dk/2+4j+3
+// of the row in VGPRs for the whole sequence, so a group reads a k or q row
+// as two contiguous 256-byte runs (Dk = 128).  The cross-lane sums are DPP
+// butterflies inside the group (plus one ds_swizzle step when L = 32).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -32,186 +31,196 @@ struct RecCfg {
     static constexpr int L = DK / 8;             // lanes per state row
     static constexpr int RPW = 64 / L;           // rows per wave
     static constexpr int ROWS = 4 * RPW;         // rows per block
-    static constexpr int V4 = DK / 4;            // float4 per k/q row
+};
+
+// XCD-aware block order: the hardware deals consecutive block ids out
+// round-robin over the 8 XCDs; remap so consecutive logical blocks (the row
+// blocks of one head, then the next head, so also the v-heads sharing a
+// k-head) land on the same XCD and share its L2.
+__device__ __forceinline__ int xcd_block(int n_blocks) {
+    int lb = blockIdx.x;
+    if ((n_blocks & 7) == 0) lb = (lb & 7) * (n_blocks >> 3) + (lb >> 3);
+    return lb;
+}
+
+// ============================================================ long sequences
+//
+// Sequences are processed in chunks of TC steps.  While chunk c runs out of
+// LDS buffer c&1, the block's threads hold chunk c+1 (k, q, v, g, beta
+// loaded from HBM at the start of chunk c) in registers; after the steps they
+// convert it to f32, add the per-step k.q, and write it to buffer (c+1)&1:
+// one barrier per chunk.  Steps past T are padded with g = 1, beta = 0,
+// which leaves every state element bit-for-bit unchanged, so the step loop
+// is fully unrolled with no tail case.  y is kept in lane registers during a
+// chunk (lane j of a row group holds the steps t = j mod L), then stored to
+// an LDS buffer as bf16 and written to HBM only when that buffer is full or
+// the sequence ends.
+
+template <int DK, int TC>
+struct ChunkBuf {
+    float4 k[TC][DK / 4];
+    float4 q[TC][DK / 4];
+    float4 sc[TC];                           // g, beta, k.q, 0
+    float4 v4[TC / 4][RecCfg<DK>::ROWS];     // v of steps 4i..4i+3, per row
 };
 
 template <int DK, int TC>
-struct RecShared {
-    float4 ks[TC][DK / 4];
-    float4 qs[TC][DK / 4];
-    float vs[TC][RecCfg<DK>::ROWS];
-    float ys[TC][RecCfg<DK>::ROWS];
-    float gs[TC];
-    float bs[TC];
-};
-
-// Global -> register staging of one chunk of TC steps.  Indices past T or Dv
-// are clamped to the last valid token / row: those staged values are never
-// consumed (steps >= T are not run, rows >= Dv are not stored), and clamping
-// keeps every load unconditional, so the compiler never has to assume a
-// pending load into the staging registers.
-template <int DK, int TC>
-struct RecStage {
+struct ChunkCfg {
     using C = RecCfg<DK>;
-    static constexpr int KQ_VEC = 2 * TC * DK / 8;            // uint4 of k and q
-    static constexpr int KQ_PER_T = (KQ_VEC + C::NT - 1) / C::NT;
-    static constexpr int V_VEC = TC * C::ROWS / 8;            // uint4 of v
-    static constexpr int V_PER_T = (V_VEC + C::NT - 1) / C::NT;
-    uint4 kq[KQ_PER_T];
-    uint4 vv[V_PER_T];
+    static constexpr int YBYTES = 64 * 1024;                         // y buffer
+    static constexpr int YSTEPS = YBYTES / (C::ROWS * 2) / TC * TC;  // whole chunks
+    static constexpr int PAIRS = TC * DK / 8;                        // (step, 8 cols)
+    static constexpr int PPT = PAIRS / C::NT;                        // per thread
+    static constexpr int VVEC = TC * C::ROWS / 8;                    // uint4 of v
+    static constexpr int VPT = (VVEC + C::NT - 1) / C::NT;
+    static_assert(PAIRS % C::NT == 0, "chunk must give every thread whole pairs");
+    static_assert(TC % 4 == 0 && 2 * TC <= C::NT, "chunk length");
+};
+
+template <int DK, int TC>
+struct ChunkSmem {
+    ChunkBuf<DK, TC> buf[2];
+    uint16_t y[ChunkCfg<DK, TC>::YSTEPS][RecCfg<DK>::ROWS];
+};
+
+template <int DK, int TC>
+struct ChunkStage {
+    using C = RecCfg<DK>;
+    using CC = ChunkCfg<DK, TC>;
+    uint4 kr[CC::PPT];
+    uint4 qr[CC::PPT];
+    uint4 vr[CC::VPT];
     float gb;
 
     __device__ __forceinline__ void load(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                          const uint16_t* __restrict__ v, const float* __restrict__ g,
                                          const float* __restrict__ beta, int b, int hk, int hv, int dv0,
                                          int t0, int T, int Hk, int Hv, int Dv, int tid) {
+        // indices past T / Dv are clamped; those values are never consumed
 #pragma unroll
-        for (int i = 0; i < KQ_PER_T; ++i) {
-            const int idx = min(tid + i * C::NT, KQ_VEC - 1);
-            const int which = idx / (TC * DK / 8);
-            const int rem = idx % (TC * DK / 8);
-            const int t = min(t0 + rem / (DK / 8), T - 1);
-            const int c8 = rem % (DK / 8);
-            const uint16_t* src = which ? q : k;
-            kq[i] = *reinterpret_cast<const uint4*>(src + (((int64_t)b * T + t) * Hk + hk) * DK + c8 * 8);
+        for (int i = 0; i < CC::PPT; ++i) {
+            const int p = tid + i * C::NT;
+            const int t = min(t0 + p / (DK / 8), T - 1);
+            const int64_t off = (((int64_t)b * T + t) * Hk + hk) * DK + (p % (DK / 8)) * 8;
+            kr[i] = *reinterpret_cast<const uint4*>(k + off);
+            qr[i] = *reinterpret_cast<const uint4*>(q + off);
         }
 #pragma unroll
-        for (int i = 0; i < V_PER_T; ++i) {
-            const int idx = min(tid + i * C::NT, V_VEC - 1);
+        for (int i = 0; i < CC::VPT; ++i) {
+            const int idx = min(tid + i * C::NT, CC::VVEC - 1);
             const int t = min(t0 + idx / (C::ROWS / 8), T - 1);
             const int row = min(dv0 + (idx % (C::ROWS / 8)) * 8, Dv - 8);
-            vv[i] = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t) * Hv + hv) * Dv + row);
+            vr[i] = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t) * Hv + hv) * Dv + row);
         }
         {
-            const int t = min(t0 + tid % TC, T - 1);
-            const int64_t i = ((int64_t)b * T + t) * Hv + hv;
-            gb = (tid % (2 * TC)) < TC ? g[i] : beta[i];
+            const int t = t0 + tid % TC;
+            const int64_t i = ((int64_t)b * T + min(t, T - 1)) * Hv + hv;
+            const bool is_g = (tid % (2 * TC)) < TC;
+            const float x = is_g ? g[i] : beta[i];
+            gb = t < T ? x : (is_g ? 1.f : 0.f);   // padding steps: g = 1, beta = 0
         }
     }
 
-    __device__ __forceinline__ void store(RecShared<DK, TC>& sh, int tid) const {
+    __device__ __forceinline__ void store(ChunkBuf<DK, TC>& sb, int tid) const {
 #pragma unroll
-        for (int i = 0; i < KQ_PER_T; ++i) {
-            const int idx = tid + i * C::NT;
-            if (KQ_VEC % C::NT == 0 || idx < KQ_VEC) {
-                const int which = idx / (TC * DK / 8);
-                const int rem = idx % (TC * DK / 8);
-                const int step = rem / (DK / 8);
-                const int c8 = rem % (DK / 8);
-                float f[8];
-                unpack8(kq[i], f);
-                float4* dst = which ? sh.qs[step] : sh.ks[step];
-                dst[2 * c8] = make_float4(f[0], f[1], f[2], f[3]);
-                dst[2 * c8 + 1] = make_float4(f[4], f[5], f[6], f[7]);
-            }
+        for (int i = 0; i < CC::PPT; ++i) {
+            const int p = tid + i * C::NT;
+            const int step = p / (DK / 8);
+            const int c8 = p % (DK / 8);
+            float kf[8], qf[8];
+            unpack8(kr[i], kf);
+            unpack8(qr[i], qf);
+            sb.k[step][2 * c8] = make_float4(kf[0], kf[1], kf[2], kf[3]);
+            sb.k[step][2 * c8 + 1] = make_float4(kf[4], kf[5], kf[6], kf[7]);
+            sb.q[step][2 * c8] = make_float4(qf[0], qf[1], qf[2], qf[3]);
+            sb.q[step][2 * c8 + 1] = make_float4(qf[4], qf[5], qf[6], qf[7]);
+            float kq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kq = fmaf(kf[e], qf[e], kq);
+            kq = group_sum<DK / 8>(kq);       // the DK/8 lanes of this step
+            if (c8 == 0) sb.sc[step].z = kq;
         }
 #pragma unroll
-        for (int i = 0; i < V_PER_T; ++i) {
+        for (int i = 0; i < CC::VPT; ++i) {
             const int idx = tid + i * C::NT;
-            if (V_VEC % C::NT == 0 || idx < V_VEC) {
+            if (CC::VVEC % C::NT == 0 || idx < CC::VVEC) {
                 const int step = idx / (C::ROWS / 8);
                 const int part = idx % (C::ROWS / 8);
                 float f[8];
-                unpack8(vv[i], f);
-                float4* dst = reinterpret_cast<float4*>(&sh.vs[step][part * 8]);
-                dst[0] = make_float4(f[0], f[1], f[2], f[3]);
-                dst[1] = make_float4(f[4], f[5], f[6], f[7]);
+                unpack8(vr[i], f);
+                float* dst = reinterpret_cast<float*>(&sb.v4[step / 4][part * 8]) + (step % 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dst[4 * e] = f[e];
             }
         }
-        if (tid < 2 * TC) {
-            if (tid < TC) sh.gs[tid] = gb;
-            else sh.bs[tid - TC] = gb;
-        }
+        if (tid < TC) sb.sc[tid].x = gb;
+        else if (tid < 2 * TC) sb.sc[tid - TC].y = gb;
     }
 };
 
-// Operands of one step, read from LDS one step ahead of their use.
-template <int DK>
-struct StepIn {
-    float4 k0, k1, q0, q1;
-    float g, beta, v;
-};
-
-template <int DK, int TC>
-__device__ __forceinline__ StepIn<DK> read_step(const RecShared<DK, TC>& sh, int t, int j, int rloc) {
-    using C = RecCfg<DK>;
-    StepIn<DK> r;
-    r.k0 = sh.ks[t][j];
-    r.k1 = sh.ks[t][C::L + j];
-    r.q0 = sh.qs[t][j];
-    r.q1 = sh.qs[t][C::L + j];
-    r.g = sh.gs[t];
-    r.beta = sh.bs[t];
-    r.v = sh.vs[t][rloc];
-    return r;
+__device__ __forceinline__ float pick(const float4& x, int i) {
+    return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
 }
 
-// Runs `steps` (1..TC) steps of the staged chunk on this lane's 8 state
-// elements; y of each step goes to sh.ys (one lane per row writes).
+// TC steps of one chunk on this lane's 8 state elements.
 template <int DK, int TC>
-__device__ __forceinline__ void run_chunk(RecShared<DK, TC>& sh, float (&s)[8], int steps, int j, int rloc) {
-    using C = RecCfg<DK>;
-    StepIn<DK> nx = read_step<DK, TC>(sh, 0, j, rloc);
-    for (int t = 0; t < steps; ++t) {
-        const StepIn<DK> cu = nx;
-        nx = read_step<DK, TC>(sh, min(t + 1, TC - 1), j, rloc);
-        const float kk[8] = {cu.k0.x, cu.k0.y, cu.k0.z, cu.k0.w, cu.k1.x, cu.k1.y, cu.k1.z, cu.k1.w};
-        const float qq[8] = {cu.q0.x, cu.q0.y, cu.q0.z, cu.q0.w, cu.q1.x, cu.q1.y, cu.q1.z, cu.q1.w};
-        // decay, then read-out with the decayed state
-        float kv = 0.f;
+__device__ __forceinline__ void run_chunk(const ChunkBuf<DK, TC>& sb, float (&s)[8],
+                                          float (&yr)[(TC + DK / 8 - 1) / (DK / 8)], int j, int rloc) {
+    constexpr int L = DK / 8;
+    float4 vv;
+#pragma unroll
+    for (int t = 0; t < TC; ++t) {
+        if (t % 4 == 0) vv = sb.v4[t / 4][rloc];
+        const float4 k0 = sb.k[t][j], k1 = sb.k[t][L + j];
+        const float4 q0 = sb.q[t][j], q1 = sb.q[t][L + j];
+        const float4 sc = sb.sc[t];
+        const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+        const float qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        float a = 0.f, c = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            s[i] *= cu.g;
-            kv = fmaf(s[i], kk[i], kv);
+            a = fmaf(s[i], kk[i], a);
+            c = fmaf(s[i], qq[i], c);
         }
-        kv = group_sum<C::L>(kv);
-        const float delta = (cu.v - kv) * cu.beta;
-        // rank-1 update, then output with the updated state
-        float yo = 0.f;
+        group_sum2<L>(a, c);
+        const float gt = sc.x, bt = sc.y, kq = sc.z;
+        const float delta = fmaf(-gt, a, pick(vv, t % 4)) * bt;
+        const float yo = fmaf(gt, c, delta * kq);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            s[i] = fmaf(kk[i], delta, s[i]);
-            yo = fmaf(s[i], qq[i], yo);
-        }
-        yo = group_sum<C::L>(yo);
-        if (j == 0) sh.ys[t][rloc] = yo;
+        for (int i = 0; i < 8; ++i) s[i] = fmaf(delta, kk[i], gt * s[i]);
+        if (j == t % L) yr[t / L] = yo;
     }
 }
 
-// y of one chunk: per step ROWS contiguous bf16 values of (b, t, hv, dv0..).
 template <int DK, int TC>
-__device__ __forceinline__ void flush_y(const RecShared<DK, TC>& sh, uint16_t* __restrict__ y, int b, int hv,
-                                        int dv0, int t0, int T, int Hv, int Dv, int tid) {
+__device__ __forceinline__ void flush_y(const ChunkSmem<DK, TC>& sh, uint16_t* __restrict__ y, int b, int hv,
+                                        int dv0, int tbase, int nsteps, int T, int Hv, int Dv, int tid) {
     using C = RecCfg<DK>;
-    constexpr int YV = TC * C::ROWS / 8;
-    for (int idx = tid; idx < YV; idx += C::NT) {
+    const int nvec = nsteps * (C::ROWS / 8);
+    for (int idx = tid; idx < nvec; idx += C::NT) {
         const int step = idx / (C::ROWS / 8);
         const int part = idx % (C::ROWS / 8);
-        const int t = t0 + step;
+        const int t = tbase + step;
         const int r = dv0 + part * 8;
-        if (t < T && r < Dv) {
-            const float4* src = reinterpret_cast<const float4*>(&sh.ys[step][part * 8]);
-            const float4 lo = src[0], hi = src[1];
-            const float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            *reinterpret_cast<uint4*>(y + (((int64_t)b * T + t) * Hv + hv) * Dv + r) = pack8(f);
-        }
+        if (t < T && r < Dv)
+            *reinterpret_cast<uint4*>(y + (((int64_t)b * T + t) * Hv + hv) * Dv + r) =
+                *reinterpret_cast<const uint4*>(&sh.y[step][part * 8]);
     }
 }
 
 template <int DK, int TC>
-__global__ __launch_bounds__(256) void recurrent_kernel(
+__global__ __launch_bounds__(256) void recurrent_chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta,
     const float* state_in, float* state_out, uint16_t* __restrict__ y,
     int T, int Hk, int Hv, int Dv, int row_blocks, int n_blocks) {
     using C = RecCfg<DK>;
-    __shared__ RecShared<DK, TC> sh;
+    using CC = ChunkCfg<DK, TC>;
+    constexpr int L = C::L;
+    constexpr int NY = (TC + L - 1) / L;
+    __shared__ ChunkSmem<DK, TC> sh;
 
-    // XCD-aware block order: hardware dispatches consecutive block ids
-    // round-robin over 8 XCDs; remap so consecutive logical blocks (row blocks
-    // of one head, then the next head) share an XCD.
-    int lb = blockIdx.x;
-    if ((n_blocks & 7) == 0) lb = (lb & 7) * (n_blocks >> 3) + (lb >> 3);
+    const int lb = xcd_block(n_blocks);
     const int n = lb / row_blocks;          // b * Hv + hv
     const int rb = lb % row_blocks;
     const int b = n / Hv;
@@ -220,14 +229,12 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
     const int dv0 = rb * C::ROWS;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int j = lane % C::L;              // position inside the row group
-    const int rloc = wave * C::RPW + lane / C::L;   // row inside the block
+    const int j = lane % L;
+    const int rloc = (tid >> 6) * C::RPW + lane / L;
     const int row = dv0 + rloc;
     const bool row_ok = row < Dv;
 
-    // state row -> registers
     float s[8];
     const int64_t srow = ((int64_t)n * Dv + row) * DK;
     if (state_in != nullptr && row_ok) {
@@ -239,31 +246,35 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) s[i] = 0.f;
     }
-    // the state must be resident before the step loop; waiting here keeps the
-    // loop free of waits on the next chunk's in-flight prefetch
-    __builtin_amdgcn_s_waitcnt(0);
 
-    const int nchunks = (T + TC - 1) / TC;
-    if (nchunks > 0) {   // uniform over the block
-        RecStage<DK, TC> st;
-        st.load(q, k, v, g, beta, b, hk, hv, dv0, 0, T, Hk, Hv, Dv, tid);
-        st.store(sh, tid);
-        __syncthreads();
-        // every chunk but the last: the next chunk's HBM loads are in flight
-        // while this chunk's steps run
-        for (int c = 0; c + 1 < nchunks; ++c) {
-            const int t0 = c * TC;
-            st.load(q, k, v, g, beta, b, hk, hv, dv0, t0 + TC, T, Hk, Hv, Dv, tid);
-            run_chunk<DK, TC>(sh, s, TC, j, rloc);
-            __syncthreads();
-            st.store(sh, tid);   // staged chunk consumed: install the next one
-            flush_y<DK, TC>(sh, y, b, hv, dv0, t0, T, Hv, Dv, tid);
-            __syncthreads();
+    const int nchunks = (T + TC - 1) / TC;   // >= 1 (this kernel runs for T > 0)
+    ChunkStage<DK, TC> st;
+    st.load(q, k, v, g, beta, b, hk, hv, dv0, 0, T, Hk, Hv, Dv, tid);
+    __builtin_amdgcn_s_waitcnt(0);           // state and chunk 0 resident
+    st.store(sh.buf[0], tid);
+    __syncthreads();
+
+    int ybase = 0;                           // first step held in sh.y
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * TC;
+        if (c + 1 < nchunks) st.load(q, k, v, g, beta, b, hk, hv, dv0, t0 + TC, T, Hk, Hv, Dv, tid);
+        float yr[NY];
+        run_chunk<DK, TC>(sh.buf[c & 1], s, yr, j, rloc);
+        // y of this chunk -> LDS (bf16); each lane holds steps t = i*L + j
+        const int yoff = t0 - ybase;
+#pragma unroll
+        for (int i = 0; i < NY; ++i) {
+            const int t = i * L + j;
+            if (t < TC) sh.y[yoff + t][rloc] = (uint16_t)f32_to_bf16(yr[i]);
         }
-        const int t0 = (nchunks - 1) * TC;
-        run_chunk<DK, TC>(sh, s, T - t0, j, rloc);
+        if (c + 1 < nchunks) st.store(sh.buf[(c + 1) & 1], tid);
         __syncthreads();
-        flush_y<DK, TC>(sh, y, b, hv, dv0, t0, T, Hv, Dv, tid);
+        const bool last = c + 1 == nchunks;
+        if (last || yoff + TC == CC::YSTEPS) {
+            flush_y<DK, TC>(sh, y, b, hv, dv0, ybase, yoff + TC, T, Hv, Dv, tid);
+            ybase = t0 + TC;
+            if (!last) __syncthreads();      // sh.y is rewritten by the next chunk
+        }
     }
 
     if (row_ok) {
@@ -272,32 +283,120 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
     }
 }
 
-template <int DK, int TC>
-static hipError_t launch_rec(const RecurrentArgs& a, hipStream_t stream) {
+// =========================================================== short sequences
+//
+// Decode-sized T: no staging.  Each lane loads the 8 k and q values of its
+// columns straight from HBM/L2 for every step (bf16, 2 x 8 bytes each), the
+// state is streamed in and out once (non-temporal: it is not reused), and y
+// leaves from lane 0 of each row group.
+
+template <int DK>
+__global__ __launch_bounds__(256) void recurrent_step_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta,
+    const float* state_in, float* state_out, uint16_t* __restrict__ y,
+    int T, int Hk, int Hv, int Dv, int row_blocks, int n_blocks) {
     using C = RecCfg<DK>;
-    const int row_blocks = (a.Dv + C::ROWS - 1) / C::ROWS;
-    const int64_t blocks = (int64_t)a.B * a.Hv * row_blocks;
-    if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((recurrent_kernel<DK, TC>), dim3((unsigned)blocks), dim3(C::NT), 0, stream,
-                       a.q, a.k, a.v, a.g, a.beta, a.state_in, a.state_out, a.y,
-                       a.T, a.Hk, a.Hv, a.Dv, row_blocks, (int)blocks);
-    return hipGetLastError();
+    constexpr int L = C::L;
+    const int lb = xcd_block(n_blocks);
+    const int n = lb / row_blocks;
+    const int rb = lb % row_blocks;
+    const int b = n / Hv;
+    const int hv = n % Hv;
+    const int hk = hv / (Hv / Hk);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int j = lane % L;
+    const int row = rb * C::ROWS + (tid >> 6) * C::RPW + lane / L;
+    const bool row_ok = row < Dv;
+    const int rowc = min(row, Dv - 1);
+
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    float s[8];
+    const int64_t srow = ((int64_t)n * Dv + row) * DK;
+    if (state_in != nullptr && row_ok) {
+        const f4v a0 = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(state_in + srow + 4 * j));
+        const f4v a1 = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(state_in + srow + DK / 2 + 4 * j));
+        s[0] = a0.x; s[1] = a0.y; s[2] = a0.z; s[3] = a0.w;
+        s[4] = a1.x; s[5] = a1.y; s[6] = a1.z; s[7] = a1.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] = 0.f;
+    }
+
+    for (int t = 0; t < T; ++t) {
+        const int64_t tok = (int64_t)b * T + t;
+        const uint16_t* kp = k + (tok * Hk + hk) * DK;
+        const uint16_t* qp = q + (tok * Hk + hk) * DK;
+        const uint2 kw0 = *reinterpret_cast<const uint2*>(kp + 4 * j);
+        const uint2 kw1 = *reinterpret_cast<const uint2*>(kp + DK / 2 + 4 * j);
+        const uint2 qw0 = *reinterpret_cast<const uint2*>(qp + 4 * j);
+        const uint2 qw1 = *reinterpret_cast<const uint2*>(qp + DK / 2 + 4 * j);
+        const float vt = bf16lo(v[(tok * Hv + hv) * Dv + rowc]);
+        const float gt = g[tok * Hv + hv];
+        const float bt = beta[tok * Hv + hv];
+        const float kk[8] = {bf16lo(kw0.x), bf16hi(kw0.x), bf16lo(kw0.y), bf16hi(kw0.y),
+                             bf16lo(kw1.x), bf16hi(kw1.x), bf16lo(kw1.y), bf16hi(kw1.y)};
+        const float qq[8] = {bf16lo(qw0.x), bf16hi(qw0.x), bf16lo(qw0.y), bf16hi(qw0.y),
+                             bf16lo(qw1.x), bf16hi(qw1.x), bf16lo(qw1.y), bf16hi(qw1.y)};
+        float a = 0.f, c = 0.f, kq = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a = fmaf(s[i], kk[i], a);
+            c = fmaf(s[i], qq[i], c);
+            kq = fmaf(kk[i], qq[i], kq);
+        }
+        group_sum2<L>(a, c);
+        kq = group_sum<L>(kq);
+        const float delta = fmaf(-gt, a, vt) * bt;
+        const float yo = fmaf(gt, c, delta * kq);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] = fmaf(delta, kk[i], gt * s[i]);
+        if (j == 0 && row_ok) y[(tok * Hv + hv) * Dv + row] = (uint16_t)f32_to_bf16(yo);
+    }
+
+    if (row_ok) {
+        const f4v o0 = {s[0], s[1], s[2], s[3]};
+        const f4v o1 = {s[4], s[5], s[6], s[7]};
+        __builtin_nontemporal_store(o0, reinterpret_cast<f4v*>(state_out + srow + 4 * j));
+        __builtin_nontemporal_store(o1, reinterpret_cast<f4v*>(state_out + srow + DK / 2 + 4 * j));
+    }
 }
+
+// ================================================================== launch
 
 int64_t recurrent_blocks(int B, int Hv, int Dk, int Dv) {
     const int rows = 4 * 64 / (Dk / 8);
     return (int64_t)B * Hv * ((Dv + rows - 1) / rows);
 }
 
+template <int DK, int TC>
+static hipError_t launch_rec(const RecurrentArgs& a, hipStream_t stream, bool chunked) {
+    using C = RecCfg<DK>;
+    const int row_blocks = (a.Dv + C::ROWS - 1) / C::ROWS;
+    const int64_t blocks = (int64_t)a.B * a.Hv * row_blocks;
+    if (blocks <= 0) return hipSuccess;
+    if (chunked)
+        hipLaunchKernelGGL((recurrent_chunk_kernel<DK, TC>), dim3((unsigned)blocks), dim3(C::NT), 0, stream,
+                           a.q, a.k, a.v, a.g, a.beta, a.state_in, a.state_out, a.y, a.T, a.Hk, a.Hv, a.Dv,
+                           row_blocks, (int)blocks);
+    else
+        hipLaunchKernelGGL((recurrent_step_kernel<DK>), dim3((unsigned)blocks), dim3(C::NT), 0, stream,
+                           a.q, a.k, a.v, a.g, a.beta, a.state_in, a.state_out, a.y, a.T, a.Hk, a.Hv, a.Dv,
+                           row_blocks, (int)blocks);
+    return hipGetLastError();
+}
+
+// Sequences shorter than this run the staging-free kernel.
+constexpr int kChunkedMinT = 8;
+
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream) {
-    // short sequences (decode) use one-step chunks: no idle LDS, more blocks
-    // per CU; longer ones stage TC = 4096/Dk steps (16 KiB of f32 k or q).
-    const bool small = a.T <= 4;
+    const bool chunked = a.T >= kChunkedMinT;
     switch (a.Dk) {
-        case 32: return small ? launch_rec<32, 1>(a, stream) : launch_rec<32, 64>(a, stream);
-        case 64: return small ? launch_rec<64, 1>(a, stream) : launch_rec<64, 64>(a, stream);
-        case 128: return small ? launch_rec<128, 1>(a, stream) : launch_rec<128, 32>(a, stream);
-        case 256: return small ? launch_rec<256, 1>(a, stream) : launch_rec<256, 16>(a, stream);
+        case 32: return launch_rec<32, 64>(a, stream, chunked);
+        case 64: return launch_rec<64, 32>(a, stream, chunked);
+        case 128: return launch_rec<128, 32>(a, stream, chunked);
+        case 256: return launch_rec<256, 16>(a, stream, chunked);
         default: return hipErrorInvalidValue;
     }
 }
