@@ -24,8 +24,43 @@ import platform
 import sys
 import time
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "linear_attention_recurrence_prep_amd", "csrc")
+KERNEL_SOURCES = {
+    "recurrent_chunk_kernel": ["recurrent.hip"],
+    "recurrent_step_kernel": ["recurrent.hip"],
+    "prep_kernel": ["prep.hip"],
+}
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CU x 4 SIMD x 16 lanes x 2 (packed) x 2 (FMA) x 2.4 GHz
+
+
+def source_digest(kernel):
+    """sha256 of a kernel's source file and the shared device headers."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel] + ["gdn_device.h", "gdn_launch.h"]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel's source changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            kv = dict(x.split("=", 1) for x in line.split())
+            if kv.get("kernel") == kernel and kv.get("workload") == workload:
+                if kv.get("source_sha256") != source_digest(kernel):
+                    return None
+                return int(kv["traffic_bytes"])
+    return None
 
 
 def parse():
@@ -160,10 +195,13 @@ def main():
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "alu", "kernel": "recurrent_chunk_kernel<128,32>",
                      "achieved": achieved_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
+                     "traffic": measured_traffic("recurrent_chunk_kernel", "prefill_T4096"),
+                     "traffic_algorithmic": rec_bytes,
                      "flops_per_launch": flops, "avg_launch_us": rec_us},
         "prologue": {"kernel": "prep_kernel<128,4>", "avg_launch_us": prep_us,
                      "bytes_per_launch": prep_bytes, "achieved_GBs": prep_bytes / prep_us / 1e3,
+                     "traffic": measured_traffic("prep_kernel", "prefill_T4096"),
                      "frac_hbm": prep_bytes / prep_us / 1e3 / HBM_PEAK_GBS},
         "decode_b64": decode,
         "cpu_baseline": cpu,
@@ -248,7 +286,8 @@ def bench_decode(args, torch, dev, up, inputs, binding, np):
         "us_per_step": out["layer_core"],
         "layer_core_GBs": core_bytes / out["layer_core"] / 1e3,
         "roofline": {"bound": "hbm", "kernel": "recurrent_step_kernel<128>", "achieved": gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("recurrent_step_kernel", "decode_B64"),
                      "bytes_per_launch": rec_bytes, "avg_launch_us": out["recurrent"]},
     }
 

@@ -122,7 +122,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int 
 #pragma unroll
             for (int j = 0; j < K - 1; ++j) u = fmaf(w[j][e], h[j][e], u);
             u = fmaf(w[K - 1][e], x[e], u);
-            act[e] = u / (1.f + expf(-u));
+            // SiLU with the hardware exp2 and reciprocal (about 2 ulp in f32,
+            // far below the half-ulp of the bf16 result)
+            act[e] = u * __builtin_amdgcn_rcpf(1.f + __expf(-u));
             ss = fmaf(act[e], act[e], ss);
         }
         ss = group_sum<DK / 8>(ss);
@@ -137,10 +139,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int 
         if (!valid) continue;
         const int64_t tok = (int64_t)b * T + t;
         if (region < 2) {
-            const float r = 1.f / sqrtf(ss / (float)DK + p.eps);
+            const float rs = scale / sqrtf(ss / (float)DK + p.eps);
             float o[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = act[e] * r * scale;
+            for (int e = 0; e < 8; ++e) o[e] = act[e] * rs;
             uint16_t* dst = region == 0 ? p.q + tok * HKDK + c0 : p.k + tok * HKDK + (c0 - HKDK);
             *reinterpret_cast<uint4*>(dst) = pack8(o);
         } else {

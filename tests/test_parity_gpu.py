@@ -375,3 +375,28 @@ def test_long_workload_full_size_sampled():
         H.check_y(y[b:b + 1, :, hv:hv + 1][..., rows], y_ref, f"b={b} hv={hv}")
         e = H.check_state(s[b:b + 1, hv:hv + 1][:, :, rows], s_ref, CORE_STATE_TOL, f"b={b} hv={hv}")
         say("long", b, hv, "state err", e)
+
+
+@pytest.mark.parametrize("T", [1, 8, 40], ids=["step_kernel", "chunk_kernel", "chunk_kernel_2chunks"])
+def test_y_bf16_rounding_ties_to_even(T):
+    """y = S q is rounded to bf16 on the device.  With a zero state, k = q = e_0
+    and g = 0 every step, y_t = v * beta_t exactly in f32 (powers of two times
+    beta), so the bf16 code is decided by the rounding alone; it must be the
+    nearest-even rounding of that exact value."""
+    say("y rounding ties", T)
+    Dk, Dv = 32, 8
+    one = 0x3F80
+    q = np.zeros((1, T, 1, Dk), np.uint16)
+    q[..., 0] = one
+    k = q.copy()
+    vals = np.array([1.0, -1.0, 2.0, 0.5, 4.0, -0.25, 1.0, -8.0])
+    v = np.tile(oracle.round_bf16(vals), (1, T, 1, 1)).reshape(1, T, 1, Dv)
+    betas = np.array([1 + 2 ** -8, 1 + 2 ** -7 + 2 ** -8, 1 + 2 ** -8 + 2 ** -20, 1 - 2 ** -9,
+                      1 + 3 * 2 ** -8, 0.5 + 2 ** -10, 1.0, 1 - 3 * 2 ** -10], np.float64)
+    beta = np.resize(betas, T).astype(np.float32).reshape(1, T, 1)
+    g = np.zeros((1, T, 1), np.float32)
+    y_bits, _ = gpu_recurrent(dict(q=q, k=k, v=v, g=g, beta=beta, state=None))
+    exact = vals[None, :] * beta.reshape(T, 1).astype(np.float64)    # exact in f32 and f64
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)
+    expect = oracle.round_bf16(exact)
+    assert np.array_equal(y_bits.reshape(T, Dv), expect)
