@@ -70,7 +70,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=200)
-    ap.add_argument("--kernel-only", default=None, choices=[None, "recurrent", "prep", "decode", "copy"],
+    ap.add_argument("--kernel-only", default=None, choices=[None, "recurrent", "prep", "decode", "copy", "chunked"],
                     help="launch only this kernel (for counter collection)")
     return ap.parse_args()
 
@@ -133,11 +133,17 @@ def main():
     def rec_only():
         binding.recurrent(pq, pk, pv, pg, pb, None, s_out, y)
 
+    cws = torch.empty(max(binding.recurrent_chunked_workspace_bytes(B, T, Hk, Hv, Dk, Dv), 1),
+                      dtype=torch.uint8, device=dev)
+
+    def chunked_only():
+        binding.recurrent_chunked(pq, pk, pv, pg, pb, None, s_out, y, cws)
+
     prep_only()
     torch.cuda.synchronize()
 
     if args.kernel_only:
-        return kernel_only(args, torch, dev, prep_only, rec_only, up, inputs, binding, np)
+        return kernel_only(args, torch, dev, prep_only, rec_only, up, inputs, binding, np, chunked_only)
 
     for _ in range(args.warmup):
         step()
@@ -326,11 +332,13 @@ def cpu_baseline(raw, Hk, Hv, Dk, Dv, qs, ks, eps):
             "host_cpus": os.cpu_count()}
 
 
-def kernel_only(args, torch, dev, prep_only, rec_only, up, inputs, binding, np):
+def kernel_only(args, torch, dev, prep_only, rec_only, up, inputs, binding, np, chunked_only):
     """Launch one kernel a few times (for rocprofv3 counter passes)."""
     n = max(args.steps, 1)
     if args.kernel_only == "recurrent":
         fn = rec_only
+    elif args.kernel_only == "chunked":
+        fn = chunked_only
     elif args.kernel_only == "prep":
         fn = prep_only
     elif args.kernel_only == "copy":

@@ -91,6 +91,29 @@ gdn_status gdn_recurrent(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_bf16 *v
                          int B, int T, int Hk, int Hv, int Dk, int Dv, void *stream);
 
 /*
+ * gdn_recurrent_chunked -- the same recurrence as gdn_recurrent, evaluated in
+ * chunks of 32 steps on the matrix cores (equal to the per-step loop up to
+ * rounding order): within a chunk the deltas of all steps solve one unit
+ * lower-triangular system built from k_t . k_s, beta and the decay ratios,
+ * and the state advances by one dense product per chunk.
+ * Arguments as gdn_recurrent plus a caller-owned device workspace of at least
+ * gdn_recurrent_chunked_workspace_bytes(...) bytes (256-byte aligned; not
+ * read before written; may be NULL when that size is 0).
+ * Supported sizes: Dk == 128 and Dv a multiple of 16 (else
+ * GDN_ERR_UNSUPPORTED).  Splitting a sequence at a multiple of 32 steps and
+ * carrying the state gives bit-identical results.
+ */
+gdn_status gdn_recurrent_chunked(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_bf16 *v,
+                                 const float *g, const float *beta,
+                                 const float *state_in, float *state_out, gdn_bf16 *y,
+                                 void *workspace, size_t workspace_bytes,
+                                 int B, int T, int Hk, int Hv, int Dk, int Dv, void *stream);
+
+/* Workspace bytes of gdn_recurrent_chunked (0 for unsupported sizes or
+ * B*T == 0). */
+size_t gdn_recurrent_chunked_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv);
+
+/*
  * gdn_prep -- the data-parallel prologue.
  * ("mlex ... gated_delta.rs", GatedDeltaNet::forward from the conv-state
  *  splice through g; "mlx-bun ... qwen3-delta.ts", compute_g.)
@@ -125,15 +148,17 @@ gdn_status gdn_prep(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
                     float q_scale, float k_scale, float eps, void *stream);
 
 /*
- * Bytes of device workspace gdn_layer_core needs for these sizes (the bf16
- * q, k, v and f32 g, beta of the prologue, each 256-byte aligned).  Returns 0
- * for invalid sizes (and when B*T == 0).
+ * Bytes of device workspace gdn_layer_core needs for these sizes: the bf16
+ * q, k, v and f32 g, beta of the prologue, plus the chunked recurrence's
+ * workspace when that form is used (Dk == 128, Dv % 16 == 0, T >= 64); each
+ * part 256-byte aligned.  Returns 0 for invalid sizes (and when B*T == 0).
  */
 size_t gdn_layer_core_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv);
 
 /*
- * gdn_layer_core -- gdn_prep followed by gdn_recurrent, defined as exactly
- * that composition (same roundings), on one stream.
+ * gdn_layer_core -- gdn_prep followed by the recurrence, on one stream:
+ * gdn_recurrent_chunked when Dk == 128, Dv % 16 == 0 and T >= 64, else
+ * gdn_recurrent; results are bit-identical to making those two calls.
  * ("mlex ... gated_delta.rs", GatedDeltaNet::forward between the input
  *  projections and the output normalisation.)
  *

@@ -51,6 +51,10 @@ def lib():
         L.gdn_recurrent.restype = _i
         L.gdn_prep.argtypes = [_p] * 13 + [_i] * 7 + [_f] * 3 + [_p]
         L.gdn_prep.restype = _i
+        L.gdn_recurrent_chunked.argtypes = [_p] * 9 + [ctypes.c_size_t] + [_i] * 6 + [_p]
+        L.gdn_recurrent_chunked.restype = _i
+        L.gdn_recurrent_chunked_workspace_bytes.argtypes = [_i] * 6
+        L.gdn_recurrent_chunked_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_layer_core_workspace_bytes.argtypes = [_i] * 6
         L.gdn_layer_core_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_layer_core.argtypes = [_p] * 12 + [ctypes.c_size_t] + [_i] * 7 + [_f] * 3 + [_p]
@@ -119,6 +123,41 @@ def recurrent(q, k, v, g, beta, state_in, state_out, y, *, stream=None):
     _check(lib().gdn_recurrent(*args, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream)))
 
 
+def recurrent_chunked_workspace_bytes(B, T, Hk, Hv, Dk, Dv) -> int:
+    return int(lib().gdn_recurrent_chunked_workspace_bytes(B, T, Hk, Hv, Dk, Dv))
+
+
+def _workspace(workspace, dev):
+    if workspace is None:
+        return None, 0
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    n = workspace.numel() * workspace.element_size()
+    return (workspace.data_ptr() if n else None), n
+
+
+def recurrent_chunked(q, k, v, g, beta, state_in, state_out, y, workspace, *, stream=None):
+    """The recurrence in 32-step chunks on the matrix cores
+    (gdn_recurrent_chunked).  Arguments as ``recurrent`` plus a device
+    ``workspace`` tensor of at least ``recurrent_chunked_workspace_bytes``
+    bytes."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dev = q.device
+    args = [
+        _ptr(q, "q", _BF16, (B, T, Hk, Dk), dev),
+        _ptr(k, "k", _BF16, (B, T, Hk, Dk), dev),
+        _ptr(v, "v", _BF16, (B, T, Hv, Dv), dev),
+        _ptr(g, "g", (torch.float32,), (B, T, Hv), dev),
+        _ptr(beta, "beta", (torch.float32,), (B, T, Hv), dev),
+        _ptr(state_in, "state_in", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(state_out, "state_out", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
+    ]
+    ws, nws = _workspace(workspace, dev)
+    _check(lib().gdn_recurrent_chunked(*args, ws, nws, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream)))
+
+
 def prep(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, q, k, v, g, beta, *,
          Hk, Hv, Dk, Dv, q_scale, k_scale, eps=1e-6, stream=None):
     """Prologue (gdn_prep).  qkv [B,T,C] bf16, conv_w [C,K] bf16,
@@ -160,13 +199,7 @@ def layer_core(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias,
     B, T, C = qkv.shape
     K = conv_w.shape[1]
     dev = qkv.device
-    ws_bytes = 0
-    ws_ptr = None
-    if workspace is not None:
-        if workspace.device != dev or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
-        ws_bytes = workspace.numel() * workspace.element_size()
-        ws_ptr = workspace.data_ptr() if ws_bytes else None
+    ws_ptr, ws_bytes = _workspace(workspace, dev)
     args = [
         _ptr(qkv, "qkv", _BF16, (B, T, C), dev),
         _ptr(conv_w, "conv_w", _BF16, (C, K), dev),

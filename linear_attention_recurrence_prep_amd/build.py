@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["gdn_api.cpp", "prep.hip", "recurrent.hip"]
+SOURCES = ["gdn_api.cpp", "prep.hip", "recurrent.hip", "chunked.hip"]
 
 ARCH = "gfx950"
 # Packed FP32 instructions are disabled for every HIP translation unit: the

@@ -183,10 +183,16 @@ gdn_status validate_prep(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_
 // -------------------------------------------------------------- workspace --
 
 struct Workspace {
-    uint64_t q, k, v, g, beta, total;
+    uint64_t q, k, v, g, beta, chunked, total;
+    bool use_chunked;
 };
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+// The layer core switches to the chunked recurrence from this length on.
+constexpr int kLayerChunkedMinT = 64;
+
+bool layer_uses_chunked(int T, int Dk, int Dv) { return T >= kLayerChunkedMinT && gdn::chunked_supported(Dk, Dv); }
 
 bool workspace_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, Workspace& w) {
     uint64_t nqk, nv, ng;
@@ -196,9 +202,16 @@ bool workspace_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, Workspace& w
     w.v = w.k + align256(nqk * 2);
     w.g = w.v + align256(nv * 2);
     w.beta = w.g + align256(ng * 4);
-    w.total = w.beta + align256(ng * 4);
+    w.chunked = w.beta + align256(ng * 4);
+    w.use_chunked = B > 0 && layer_uses_chunked(T, Dk, Dv);
+    w.total = w.chunked + (w.use_chunked ? gdn::chunked_layout(B, T, Hv, Dk).total : 0);
     if ((int64_t)B * T == 0) w.total = 0;
     return true;
+}
+
+uint64_t chunked_bytes(int B, int T, int Hv, int Dk, int Dv) {
+    if ((int64_t)B * T == 0 || !gdn::chunked_supported(Dk, Dv)) return 0;
+    return gdn::chunked_layout(B, T, Hv, Dk).total;
 }
 
 }  // namespace
@@ -232,6 +245,54 @@ gdn_status gdn_recurrent(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v
     if (B == 0) return ok();
     gdn::RecurrentArgs a{q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv};
     return hip_result(gdn::launch_recurrent(a, static_cast<hipStream_t>(stream)), "recurrent");
+}
+
+size_t gdn_recurrent_chunked_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv) {
+    if (check_dims(B, T, Hk, Hv, Dk, Dv) != GDN_OK) return 0;
+    uint64_t n;
+    if (!elems(n, {B, T, Hv, Dk})) return 0;
+    return (size_t)chunked_bytes(B, T, Hv, Dk, Dv);
+}
+
+gdn_status gdn_recurrent_chunked(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,
+                                 const float* beta, const float* state_in, float* state_out, gdn_bf16* y,
+                                 void* workspace, size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk,
+                                 int Dv, void* stream) {
+    gdn_status st = validate_recurrent(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv);
+    if (st != GDN_OK) return st;
+    if (!gdn::chunked_supported(Dk, Dv))
+        return fail(GDN_ERR_UNSUPPORTED, "chunked recurrence needs Dk == 128 and Dv %% 16 == 0 (Dk=%d, Dv=%d)", Dk,
+                    Dv);
+    if (gdn::chunked_blocks(B, T, Hv, Dv) > kMaxBlocks) return fail(GDN_ERR_BAD_DIMS, "grid too large");
+    const uint64_t need = chunked_bytes(B, T, Hv, Dk, Dv);
+    if (need > 0) {
+        if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL but %llu bytes are needed",
+                                    (unsigned long long)need);
+        if (workspace_bytes < need)
+            return fail(GDN_ERR_WORKSPACE, "workspace has %zu bytes, %llu needed", workspace_bytes,
+                        (unsigned long long)need);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(GDN_ERR_MISALIGNED, "workspace is not 256-byte aligned");
+        uint64_t nqk, nv, ng, ns;
+        elems(nqk, {B, T, Hk, Dk});
+        elems(nv, {B, T, Hv, Dv});
+        elems(ng, {B, T, Hv});
+        elems(ns, {B, Hv, Dv, Dk});
+        std::vector<Span> s = {
+            {"q", q, nqk * 2, false},      {"k", k, nqk * 2, false},
+            {"v", v, nv * 2, false},       {"g", g, ng * 4, false},
+            {"beta", beta, ng * 4, false}, {"state_in", state_in, ns * 4, false},
+            {"state_out", state_out, ns * 4, true}, {"y", y, nv * 2, true},
+            {"workspace", workspace, need, true},
+        };
+        st = check_spans(s, {{5, 6}});
+        if (st != GDN_OK) return st;
+    }
+    if (B == 0) return ok();
+    gdn::RecurrentArgs a{q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (T == 0) return hip_result(gdn::launch_recurrent(a, s), "recurrent");
+    return hip_result(gdn::launch_recurrent_chunked(a, workspace, s), "chunked recurrent");
 }
 
 gdn_status gdn_prep(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_bf16* conv_state_in,
@@ -288,6 +349,7 @@ gdn_status gdn_layer_core(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn
     if (st != GDN_OK) return st;
     st = validate_recurrent(wq, wk, wv, wg, wb, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, false);
     if (st != GDN_OK) return st;
+    if (w.use_chunked && gdn::chunked_blocks(B, T, Hv, Dv) > kMaxBlocks) return fail(GDN_ERR_BAD_DIMS, "grid too large");
     {
         const int64_t C = 2LL * Hk * Dk + (int64_t)Hv * Dv;
         uint64_t nx, nw, ncs, ng, nv, ns;
@@ -323,6 +385,7 @@ gdn_status gdn_layer_core(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn
         if (st != GDN_OK) return st;
     }
     gdn::RecurrentArgs r{wq, wk, wv, wg, wb, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv};
+    if (w.use_chunked) return hip_result(gdn::launch_recurrent_chunked(r, ws + w.chunked, s), "chunked recurrent");
     return hip_result(gdn::launch_recurrent(r, s), "recurrent");
 }
 

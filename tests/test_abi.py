@@ -123,12 +123,26 @@ def test_prep_allows_in_place_conv_state_and_empty_batch(L):
     assert call_prep(L, B=0, cs_in=None, cs_out=None) == OK
 
 
+def chunked_expect(B, T, Hv, Dk):
+    up = lambda x: (x + 255) // 256 * 256
+    units = B * Hv * ((T + 31) // 32)
+    return up(units * 32 * Dk * 4) + 2 * up(units * 32 * 32 * 4) + 2 * up(units * 32 * 4)
+
+
 def test_workspace_bytes(L):
     f = L.gdn_layer_core_workspace_bytes
     up = lambda x: (x + 255) // 256 * 256
     B, T, Hk, Hv, Dk, Dv = 1, 4096, 16, 32, 128, 128
-    expect = 2 * up(B * T * Hk * Dk * 2) + up(B * T * Hv * Dv * 2) + 2 * up(B * T * Hv * 4)
-    assert f(B, T, Hk, Hv, Dk, Dv) == expect
+    prep_part = 2 * up(B * T * Hk * Dk * 2) + up(B * T * Hv * Dv * 2) + 2 * up(B * T * Hv * 4)
+    # Dk = 128, Dv % 16 == 0, T >= 64: the layer core adds the chunked recurrence's part
+    assert f(B, T, Hk, Hv, Dk, Dv) == prep_part + chunked_expect(B, T, Hv, Dk)
+    assert L.gdn_recurrent_chunked_workspace_bytes(B, T, Hk, Hv, Dk, Dv) == chunked_expect(B, T, Hv, Dk)
+    # short sequences and other head sizes use the per-step kernels: prologue part only
+    T2 = 63
+    assert f(B, T2, Hk, Hv, Dk, Dv) == 2 * up(T2 * Hk * Dk * 2) + up(T2 * Hv * Dv * 2) + 2 * up(T2 * Hv * 4)
+    assert f(2, 100, 2, 4, 64, 32) == 2 * up(200 * 2 * 64 * 2) + up(200 * 4 * 32 * 2) + 2 * up(200 * 4 * 4)
+    assert L.gdn_recurrent_chunked_workspace_bytes(1, 100, 2, 4, 64, 32) == 0     # unsupported Dk
+    assert L.gdn_recurrent_chunked_workspace_bytes(1, 100, 2, 4, 128, 24) == 0    # Dv % 16 != 0
     assert f(1, 0, 16, 32, 128, 128) == 0
     assert f(0, 10, 16, 32, 128, 128) == 0
     assert f(1, 10, 3, 32, 128, 128) == 0     # invalid dims
@@ -169,3 +183,21 @@ def test_binding_argument_checks_on_cpu():
         binding._ptr(q, "q", binding._BF16, (1, 2, 1, 64), q.device)
     with pytest.raises(ValueError):
         binding._ptr(q.transpose(1, 3), "q", binding._BF16, (1, 32, 1, 2), q.device)
+
+
+def call_chunked(L, ws=addr(20), ws_bytes=1 << 32, **over):
+    p, d = rec_args(**over)
+    return L.gdn_recurrent_chunked(p["q"], p["k"], p["v"], p["g"], p["beta"], p["state_in"], p["state_out"],
+                                   p["y"], ws, ctypes.c_size_t(ws_bytes), d["B"], d["T"], d["Hk"], d["Hv"],
+                                   d["Dk"], d["Dv"], None)
+
+
+def test_recurrent_chunked_rejects(L):
+    assert call_chunked(L, Dk=64) == UNSUP
+    assert call_chunked(L, Dk=128, Dv=24) == UNSUP
+    assert call_chunked(L, Dk=128, ws=None) == WS
+    assert call_chunked(L, Dk=128, ws_bytes=1000) == WS
+    assert call_chunked(L, Dk=128, ws=addr(20) + 128) == ALIGN
+    assert call_chunked(L, Dk=128, ws=addr(7)) == OVERLAP          # workspace over y
+    assert call_chunked(L, Dk=128, q=None) == NULLP
+    assert call_chunked(L, Dk=128, B=0) == OK

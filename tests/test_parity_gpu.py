@@ -53,6 +53,27 @@ def gpu_recurrent(ri, state_dev="copy", y_guard=True):
     return H.bits(y), H.f32(s_out)
 
 
+def gpu_recurrent_chunked(ri, in_place=False):
+    """Run gdn_recurrent_chunked on device copies of ri; returns (y bits, state)."""
+    B, T, Hk, Dk = ri["q"].shape
+    Hv, Dv = ri["v"].shape[2:]
+    d = {k: H.to_dev(ri[k]) for k in ("q", "k", "v", "g", "beta")}
+    s_in = H.to_dev(ri["state"]) if ri["state"] is not None else None
+    yfull, y = H.guarded((B, T, Hv, Dv), torch.int16, NAN_BF16)
+    if in_place:
+        sfull, s_out = None, s_in
+    else:
+        sfull, s_out = H.guarded((B, Hv, Dv, Dk), torch.float32, float("nan"))
+    nws = binding.recurrent_chunked_workspace_bytes(B, T, Hk, Hv, Dk, Dv)
+    wfull, ws = H.guarded((max(nws, 1),), torch.uint8, 0xA5)
+    binding.recurrent_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], s_in, s_out, y, ws)
+    torch.cuda.synchronize()
+    assert H.guards_intact(yfull, NAN_BF16), "y guard band written"
+    assert sfull is None or H.guards_intact(sfull, float("nan")), "state guard band written"
+    assert H.guards_intact(wfull, 0xA5), "workspace guard band written"
+    return H.bits(y), H.f32(s_out)
+
+
 def oracle_recurrent(ri):
     f = oracle.bf16_to_f64
     s0 = None if ri["state"] is None else ri["state"].astype(np.float64)
@@ -301,14 +322,19 @@ def test_layer_core_matches_oracle(case):
     assert np.array_equal(cs, cs_ref)
 
 
-def test_layer_core_equals_prep_then_recurrent():
-    say("layer_core composition")
-    Hk, Hv, Dk, Dv, K = 2, 4, 128, 64, 4
-    raw = layer_inputs(2, 70, Hk, Hv, Dk, Dv, K, 310)
+@pytest.mark.parametrize("shape", [(2, 70, 2, 4, 128, 64), (2, 40, 2, 4, 128, 64), (1, 90, 1, 2, 64, 32)],
+                         ids=["chunked", "short", "Dk64"])
+def test_layer_core_equals_prep_then_recurrent(shape):
+    """The layer core is the prologue followed by the chunked recurrence
+    (Dk = 128, Dv % 16 == 0, T >= 64) or else the per-step one, bit for bit."""
+    B, T, Hk, Hv, Dk, Dv = shape
+    say("layer_core composition", shape)
+    raw = layer_inputs(B, T, Hk, Hv, Dk, Dv, 4, 310)
     y, s, cs = gpu_layer_core(raw, Hk, Hv, Dk, Dv, 0.01, 0.09)
     p = gpu_prep(raw, Hk, Hv, Dk, Dv, 0.01, 0.09)
-    y2, s2 = gpu_recurrent(dict(q=p["q"], k=p["k"], v=p["v"], g=p["g"], beta=p["beta"],
-                                state=raw["state"]))
+    ri = dict(q=p["q"], k=p["k"], v=p["v"], g=p["g"], beta=p["beta"], state=raw["state"])
+    chunked = Dk == 128 and Dv % 16 == 0 and T >= 64
+    y2, s2 = gpu_recurrent_chunked(ri) if chunked else gpu_recurrent(ri)
     assert np.array_equal(y, y2) and np.array_equal(s, s2) and np.array_equal(cs, p["conv_state"])
 
 
@@ -400,3 +426,107 @@ def test_y_bf16_rounding_ties_to_even(T):
     assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)
     expect = oracle.round_bf16(exact)
     assert np.array_equal(y_bits.reshape(T, Dv), expect)
+
+
+# ------------------------------------------------- chunked (matrix-core) form
+
+CHUNK_CASES = [
+    # B, T, Hk, Hv, Dk, Dv, wid
+    (1, 64, 2, 4, 128, 32, 400),           # two whole chunks
+    (2, 33, 1, 2, 128, 16, 401),           # one step past a chunk
+    (1, 100, 2, 2, 128, 48, 402),          # ragged tail
+    (3, 5, 2, 4, 128, 128, 403),           # shorter than a chunk
+    (64, 1, 16, 32, 128, 128, 2),          # decode-sized batch, one step
+    (1, 257, 4, 8, 128, 64, 404),          # GQA 2, nine chunks
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: "B%dT%dHk%dHv%dDk%dDv%d" % c[:6])
+def test_recurrent_chunked_matches_oracle(case):
+    B, T, Hk, Hv, Dk, Dv, wid = case
+    say("recurrent_chunked", case)
+    ri = rec_inputs(B, T, Hk, Hv, Dk, Dv, wid)
+    y_bits, s = gpu_recurrent_chunked(ri)
+    y_ref, s_ref = oracle_recurrent(ri)
+    H.check_y(y_bits, y_ref, str(case))
+    e = H.check_state(s, s_ref, 1e-4, str(case))
+    say("chunked state err", e)
+
+
+def test_recurrent_chunked_properties():
+    say("recurrent_chunked properties")
+    ri = rec_inputs(2, 96, 2, 8, 128, 32, 410)
+    y, s = gpu_recurrent_chunked(ri)
+    # repeat run: bitwise identical
+    y2, s2 = gpu_recurrent_chunked(ri)
+    assert np.array_equal(y, y2) and np.array_equal(s, s2)
+    # GQA against explicitly repeated k-heads: bitwise identical
+    rep = dict(ri, q=np.repeat(ri["q"], 4, axis=2), k=np.repeat(ri["k"], 4, axis=2))
+    y3, s3 = gpu_recurrent_chunked(rep)
+    assert np.array_equal(y, y3) and np.array_equal(s, s3)
+    # in place
+    y4, s4 = gpu_recurrent_chunked(ri, in_place=True)
+    assert np.array_equal(y, y4) and np.array_equal(s, s4)
+    # split at a chunk boundary, state carried: bitwise identical
+    for T1 in (32, 64):
+        a = {k: np.ascontiguousarray(ri[k][:, :T1]) for k in ("q", "k", "v", "g", "beta")}
+        b = {k: np.ascontiguousarray(ri[k][:, T1:]) for k in ("q", "k", "v", "g", "beta")}
+        ya, sa = gpu_recurrent_chunked(dict(a, state=ri["state"]))
+        yb, sb = gpu_recurrent_chunked(dict(b, state=sa))
+        assert np.array_equal(np.concatenate([ya, yb], axis=1), y), T1
+        assert np.array_equal(sb, s), T1
+    # NULL state equals an explicit zero state
+    z = dict(ri, state=None)
+    y5, s5 = gpu_recurrent_chunked(z)
+    y6, s6 = gpu_recurrent_chunked(dict(ri, state=np.zeros_like(ri["state"])))
+    assert np.array_equal(y5, y6) and np.array_equal(s5, s6)
+    # T = 0 copies the state
+    e = {k: np.ascontiguousarray(ri[k][:, :0]) for k in ("q", "k", "v", "g", "beta")}
+    _, s7 = gpu_recurrent_chunked(dict(e, state=ri["state"]))
+    assert np.array_equal(s7, ri["state"])
+
+
+def test_recurrent_chunked_invariants():
+    say("recurrent_chunked invariants")
+    # beta = 0, g = 1: the state is carried unchanged
+    ri = rec_inputs(1, 40, 1, 2, 128, 16, 411)
+    ri["g"][:] = 1.0
+    ri["beta"][:] = 0.0
+    _, s = gpu_recurrent_chunked(ri)
+    np.testing.assert_allclose(s, ri["state"], rtol=0, atol=0)
+    # g = 0 at the last step: S = beta v k^T regardless of the history
+    ri = rec_inputs(1, 40, 1, 2, 128, 16, 412)
+    ri["g"][:, -1] = 0.0
+    _, s = gpu_recurrent_chunked(ri)
+    f = oracle.bf16_to_f64
+    for h in range(2):
+        ref = np.outer(f(ri["v"][0, -1, h]) * ri["beta"][0, -1, h], f(ri["k"][0, -1, 0]))
+        np.testing.assert_allclose(s[0, h], ref, rtol=1e-6, atol=1e-7 * np.abs(ref).max())
+
+
+def test_recurrent_chunked_rejects_unsupported_sizes():
+    ri = rec_inputs(1, 10, 1, 1, 64, 16, 413)
+    with pytest.raises(binding.GdnError):
+        gpu_recurrent_chunked(ri)
+
+
+def test_recurrent_chunked_long_head_drift():
+    """One head of the long workload over all 32768 steps, 16 rows: the
+    oracle's prologue prepares the inputs (from the head's channels only), the
+    chunked recurrence runs on them, and the state stays within 1e-3."""
+    say("chunked long head")
+    w = inputs.WORKLOADS["long"]
+    Hk, Hv, Dk, Dv = w["Hk"], w["Hv"], w["Dk"], w["Dv"]
+    raw = inputs.workload("long")
+    qs, ks = inputs.scales(Dk)
+    b, hv, rows = 2, 21, list(range(48, 64))
+    sub = H.layer_sub(raw, b, hv, rows, Hk, Hv, Dk, Dv)
+    p = oracle.prep(sub["qkv"], sub["conv_w"], sub["conv_state"], sub["a"], sub["b"], sub["A_log"],
+                    sub["dt_bias"], Hk=1, Hv=1, Dk=Dk, Dv=len(rows), q_scale=qs, k_scale=ks)
+    ri = dict(q=oracle.round_bf16(p["q"]), k=oracle.round_bf16(p["k"]), v=oracle.round_bf16(p["v"]),
+              g=oracle.round_f32(p["g"]), beta=oracle.round_f32(p["beta"]), state=sub["state"])
+    y, s = gpu_recurrent_chunked(ri)
+    y_ref, s_ref = oracle_recurrent(ri)
+    H.check_y(y, y_ref, "long head")
+    e = H.check_state(s, s_ref, 1e-3, "long head")
+    say("long head state err", e)
