@@ -99,7 +99,7 @@ gdn_status gdn_recurrent(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_bf16 *v
  * Arguments as gdn_recurrent plus a caller-owned device workspace of at least
  * gdn_recurrent_chunked_workspace_bytes(...) bytes (256-byte aligned; not
  * read before written; may be NULL when that size is 0).
- * Supported sizes: Dk == 128 and Dv a multiple of 16 (else
+ * Supported sizes: Dk == 128, Dv a multiple of 16 and Hv * Dv <= 2^25 (else
  * GDN_ERR_UNSUPPORTED).  Splitting a sequence at a multiple of 32 steps and
  * carrying the state gives bit-identical results.
  */
@@ -150,14 +150,14 @@ gdn_status gdn_prep(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
 /*
  * Bytes of device workspace gdn_layer_core needs for these sizes: the bf16
  * q, k, v and f32 g, beta of the prologue, plus the chunked recurrence's
- * workspace when that form is used (Dk == 128, Dv % 16 == 0, T >= 64); each
- * part 256-byte aligned.  Returns 0 for invalid sizes (and when B*T == 0).
+ * workspace when that form is used (T >= 64 and sizes gdn_recurrent_chunked
+ * supports); each part 256-byte aligned.  Returns 0 for invalid sizes (and when B*T == 0).
  */
 size_t gdn_layer_core_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv);
 
 /*
  * gdn_layer_core -- gdn_prep followed by the recurrence, on one stream:
- * gdn_recurrent_chunked when Dk == 128, Dv % 16 == 0 and T >= 64, else
+ * gdn_recurrent_chunked when T >= 64 and it supports the sizes, else
  * gdn_recurrent; results are bit-identical to making those two calls.
  * ("mlex ... gated_delta.rs", GatedDeltaNet::forward between the input
  *  projections and the output normalisation.)

@@ -17,6 +17,9 @@ OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
 SOURCES = ["gdn_api.cpp", "prep.hip", "recurrent.hip", "chunked.hip"]
+# Matrix-core accumulators in ordinary VGPRs (no AGPR copies around the
+# element-wise work on them).
+SOURCE_FLAGS = {"chunked.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 ARCH = "gfx950"
 # Packed FP32 instructions are disabled for every HIP translation unit: the
@@ -39,7 +42,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     for src in SOURCES:
         obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

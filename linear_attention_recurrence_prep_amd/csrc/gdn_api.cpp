@@ -192,7 +192,9 @@ uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 // The layer core switches to the chunked recurrence from this length on.
 constexpr int kLayerChunkedMinT = 64;
 
-bool layer_uses_chunked(int T, int Dk, int Dv) { return T >= kLayerChunkedMinT && gdn::chunked_supported(Dk, Dv); }
+bool layer_uses_chunked(int T, int Hv, int Dk, int Dv) {
+    return T >= kLayerChunkedMinT && gdn::chunked_supported(Hv, Dk, Dv);
+}
 
 bool workspace_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, Workspace& w) {
     uint64_t nqk, nv, ng;
@@ -203,15 +205,15 @@ bool workspace_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, Workspace& w
     w.g = w.v + align256(nv * 2);
     w.beta = w.g + align256(ng * 4);
     w.chunked = w.beta + align256(ng * 4);
-    w.use_chunked = B > 0 && layer_uses_chunked(T, Dk, Dv);
-    w.total = w.chunked + (w.use_chunked ? gdn::chunked_layout(B, T, Hv, Dk).total : 0);
+    w.use_chunked = B > 0 && layer_uses_chunked(T, Hv, Dk, Dv);
+    w.total = w.chunked + (w.use_chunked ? gdn::chunked_layout(B, T, Hk, Hv, Dk).total : 0);
     if ((int64_t)B * T == 0) w.total = 0;
     return true;
 }
 
-uint64_t chunked_bytes(int B, int T, int Hv, int Dk, int Dv) {
-    if ((int64_t)B * T == 0 || !gdn::chunked_supported(Dk, Dv)) return 0;
-    return gdn::chunked_layout(B, T, Hv, Dk).total;
+uint64_t chunked_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv) {
+    if ((int64_t)B * T == 0 || !gdn::chunked_supported(Hv, Dk, Dv)) return 0;
+    return gdn::chunked_layout(B, T, Hk, Hv, Dk).total;
 }
 
 }  // namespace
@@ -251,7 +253,7 @@ size_t gdn_recurrent_chunked_workspace_bytes(int B, int T, int Hk, int Hv, int D
     if (check_dims(B, T, Hk, Hv, Dk, Dv) != GDN_OK) return 0;
     uint64_t n;
     if (!elems(n, {B, T, Hv, Dk})) return 0;
-    return (size_t)chunked_bytes(B, T, Hv, Dk, Dv);
+    return (size_t)chunked_bytes(B, T, Hk, Hv, Dk, Dv);
 }
 
 gdn_status gdn_recurrent_chunked(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,
@@ -260,11 +262,12 @@ gdn_status gdn_recurrent_chunked(const gdn_bf16* q, const gdn_bf16* k, const gdn
                                  int Dv, void* stream) {
     gdn_status st = validate_recurrent(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
-    if (!gdn::chunked_supported(Dk, Dv))
-        return fail(GDN_ERR_UNSUPPORTED, "chunked recurrence needs Dk == 128 and Dv %% 16 == 0 (Dk=%d, Dv=%d)", Dk,
-                    Dv);
+    if (!gdn::chunked_supported(Hv, Dk, Dv))
+        return fail(GDN_ERR_UNSUPPORTED,
+                    "chunked recurrence needs Dk == 128, Dv %% 16 == 0 and Hv * Dv <= 2^25 (Dk=%d, Dv=%d, Hv=%d)", Dk,
+                    Dv, Hv);
     if (gdn::chunked_blocks(B, T, Hv, Dv) > kMaxBlocks) return fail(GDN_ERR_BAD_DIMS, "grid too large");
-    const uint64_t need = chunked_bytes(B, T, Hv, Dk, Dv);
+    const uint64_t need = chunked_bytes(B, T, Hk, Hv, Dk, Dv);
     if (need > 0) {
         if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL but %llu bytes are needed",
                                     (unsigned long long)need);
