@@ -20,8 +20,8 @@
 // products replace the per-step dot products.
 //
 // fp32 products on bf16 matrix cores.  Every f32 operand x is cut into three
-// bf16 planes x = h + m + l exactly (h is x truncated to bf16, m and l the
-// same on the remainders), so that a product of an f32 matrix with an exact
+// bf16 planes x = h + m + l exactly (h is x rounded to bf16, m the remainder
+// rounded, l what is left), so that a product of an f32 matrix with an exact
 // bf16 matrix (q, k, v) is three bf16 MFMAs with f32 accumulation, and a
 // product of two f32 matrices is the six plane products down to 2^-16 of the
 // leading one (the three dropped terms are below 2^-24 relative).
@@ -67,8 +67,8 @@ constexpr int DKC = 128;      // key head size of the chunked form
 constexpr int NW = DKC / 32;  // waves per sequential block (32 state columns each)
 
 // Per-unit sizes of the workspace arrays, in 16-byte vectors (one per lane).
-constexpr int kWVec = NW * 2 * 3 * 64;    // W planes       [NW][t-tile][plane][lane]
-constexpr int kTVec = 2 * 3 * 64;         // -Tb, -P planes [t-tile][plane][lane]
+constexpr int kWVec = NW * 2 * 2 * 64;    // W in f32       [NW][t-tile][half][lane]
+constexpr int kPVec = 2 * 2 * 64;         // -P planes (two) [t-tile][plane][lane]
 constexpr int kQVec = NW * 2 * 64;        // q, k per k-unit [NW][tile][lane]
 
 // ------------------------------------------------------------ bf16 planes
@@ -77,29 +77,65 @@ struct Planes {
     u4_t h, m, l;
 };
 
-// upper halves of a and b packed (a in the low half)
-__device__ __forceinline__ uint32_t top16x2(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+typedef float f2_t __attribute__((ext_vector_type(2)));
 
-// x minus x truncated to bf16 (exact)
-__device__ __forceinline__ float rest16(float x) { return x - __uint_as_float(__float_as_uint(x) & 0xFFFF0000u); }
+// (a, b) rounded to bf16 (nearest even), a in the low half
+__device__ __forceinline__ bf2_t rne2(float a, float b) { return __builtin_convertvector(f2_t{a, b}, bf2_t); }
+
+// The bf16 pairs (-1, 0) and (0, -1) as 32-bit words.  The first is handed
+// to the dot-product instruction from a scalar register set by s_mov: as a
+// compile-time constant it is encoded as the inline constant -1.0, which the
+// hardware does not read as that pair.
+struct NegOnes {
+    bf2_t lo, hi;
+};
+__device__ __forceinline__ NegOnes neg_ones() {
+    uint32_t lo;
+    asm volatile("s_mov_b32 %0, 0xbf80" : "=s"(lo));
+    return NegOnes{__builtin_bit_cast(bf2_t, lo), __builtin_bit_cast(bf2_t, 0xBF800000u)};
+}
+
+// a - h.lo and b - h.hi, each one dot-product instruction: the bf16 products
+// are exact and the remainder of a rounding is exactly representable, so the
+// results are exact
+__device__ __forceinline__ float rem_lo(const NegOnes& n, bf2_t h, float a) {
+    return __builtin_amdgcn_fdot2_f32_bf16(h, n.lo, a, false);
+}
+__device__ __forceinline__ float rem_hi(const NegOnes& n, bf2_t h, float b) {
+    return __builtin_amdgcn_fdot2_f32_bf16(h, n.hi, b, false);
+}
 
 struct Split2 {
     uint32_t h, m, l;    // bf16 pairs of each plane
 };
 
-__device__ __forceinline__ Split2 split2(float a, float b) {
-    Split2 r;
-    r.h = top16x2(__float_as_uint(a), __float_as_uint(b));
-    const float a1 = rest16(a), b1 = rest16(b);
-    r.m = top16x2(__float_as_uint(a1), __float_as_uint(b1));
-    r.l = top16x2(__float_as_uint(rest16(a1)), __float_as_uint(rest16(b1)));
-    return r;
+// x = h + m + l exactly for x = a, b: h = bf16(x), m = bf16(x - h),
+// l = x - h - m (at most 8 significant bits, so a bf16 exactly)
+__device__ __forceinline__ Split2 split2(const NegOnes& n, float a, float b) {
+    const bf2_t h = rne2(a, b);
+    const float a1 = rem_lo(n, h, a), b1 = rem_hi(n, h, b);
+    const bf2_t m = rne2(a1, b1);
+    const bf2_t l = rne2(rem_lo(n, m, a1), rem_hi(n, m, b1));
+    return Split2{__builtin_bit_cast(uint32_t, h), __builtin_bit_cast(uint32_t, m), __builtin_bit_cast(uint32_t, l)};
+}
+
+// eight f32 (x0 then x1) -> the two leading bf16 planes (x = h + m to 2^-17)
+__device__ __forceinline__ void split8hm(const NegOnes& n, const f4_t x0, const f4_t x1, u4_t& h, u4_t& m) {
+    const float xs[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float a = xs[2 * p], b = xs[2 * p + 1];
+        const bf2_t hp = rne2(a, b);
+        h[p] = __builtin_bit_cast(uint32_t, hp);
+        m[p] = __builtin_bit_cast(uint32_t, rne2(rem_lo(n, hp, a), rem_hi(n, hp, b)));
+    }
 }
 
 // eight f32 (x0 then x1) -> three bf16 planes
-__device__ __forceinline__ Planes split8(const f4_t x0, const f4_t x1) {
-    const Split2 s0 = split2(x0[0], x0[1]), s1 = split2(x0[2], x0[3]);
-    const Split2 s2 = split2(x1[0], x1[1]), s3 = split2(x1[2], x1[3]);
+__device__ __forceinline__ Planes split8(const NegOnes& n, const f4_t x0, const f4_t x1) {
+    const Split2 s0 = split2(n, x0[0], x0[1]), s1 = split2(n, x0[2], x0[3]);
+    const Split2 s2 = split2(n, x1[0], x1[1]), s3 = split2(n, x1[2], x1[3]);
     Planes p;
     p.h = u4_t{s0.h, s1.h, s2.h, s3.h};
     p.m = u4_t{s0.m, s1.m, s2.m, s3.m};
@@ -134,19 +170,26 @@ struct PrepSmem {
             float kk[CK][CK + 1];
             float qk[CK][CK + 1];
         } in;
-        float w[CK][DKC + 4];    // solved W (the inputs above are dead by then)
+        struct {                 // written once the inputs above are dead
+            uint16_t tw[3][CK][CK + 8];    // planes of T diag(beta gamma)
+            uint16_t tb[3][CK][CK + 8];    // planes of -T diag(beta)
+        } pl;
     } u;
-    float a[CK][CK + 4];         // strictly lower A (row-major, 16-byte rows)
-    float tn[CK][CK + 4];        // -T diag(beta)
+    union {
+        struct {
+            float a[CK][CK + 4];     // strictly lower A (row-major, 16-byte rows)
+            float tm[CK][CK + 4];    // T = (I + A)^-1
+        } s;
+        uint16_t vs[CK][128 + 8];    // a 128-column slice of the chunk's v rows
+    } w;
     float gs[CK], bs[CK], gm[CK];
 };
 
 struct ChunkPtrs {
-    u4_t* wsw;      // W planes
-    u4_t* tbn;      // -Tb planes
-    u4_t* pn;       // -P planes
-    float* gm;      // gamma_t
-    float* rhon;    // -rho in kperm order
+    u4_t* wsw;      // W (f32)
+    u4_t* u;        // -Tb V (f32 accumulator tiles)
+    u4_t* pn;       // -P planes (two)
+    float* rg;      // per unit: -rho in kperm order [32], then gamma_t [32]
     u4_t* qsw;      // q rows
     u4_t* ksw;      // k columns
 };
@@ -154,8 +197,9 @@ struct ChunkPtrs {
 __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const float* __restrict__ g,
-                                                            const float* __restrict__ beta, ChunkPtrs o, int T,
-                                                            int Hk, int Hv, int NC) {
+                                                            const float* __restrict__ beta,
+                                                            const uint16_t* __restrict__ v, ChunkPtrs o, int T,
+                                                            int Hk, int Hv, int Dv, int NC) {
     __shared__ PrepSmem sh;
     const int64_t unit = blockIdx.x;          // (b * Hv + hv) * NC + c
     const int c = (int)(unit % NC);
@@ -165,7 +209,10 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
     const int hk = hv / G;
     const int64_t kunit = ((int64_t)b * Hk + hk) * NC + c;
     const int t0 = c * CK;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lq = lane >> 4;
+    const NegOnes no = neg_ones();
 
     // 1. k, q rows of the chunk (zero past T), g and beta (1 and 0 past T)
     for (int idx = tid; idx < CK * DKC / 8; idx += 256) {
@@ -188,52 +235,55 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
     }
     __syncthreads();
 
-    // 2a. q and k in operand layout, once per k-head (the first v-head of
-    //     each group writes them): q rows 16j + r at columns 32w + kperm(q, e);
-    //     k rows kperm(q, e) at column 32w + 16tt + r
+    // 2a. k^T in operand layout for this wave's columns (rows kperm(q, e),
+    //     column 32w + 16tt + r); the first v-head of each group also stores
+    //     it and q (rows 16j + r, columns 32w + kperm(q, e)) for the
+    //     sequential pass
+    u4_t kt[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const int d = 32 * wv + 16 * tt + lr;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int s0 = p < 2 ? 4 * lq + 2 * p : 16 + 4 * lq + 2 * (p - 2);
+            kt[tt][p] = (uint32_t)sh.kb[s0][d] | ((uint32_t)sh.kb[s0 + 1][d] << 16);
+        }
+    }
     if (hv % G == 0) {
+        u4_t* kd = o.ksw + kunit * kQVec + wv * 2 * 64 + lane;
+        u4_t* qd = o.qsw + kunit * kQVec + wv * 2 * 64 + lane;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int slot = tid + 256 * i;
-            const int w = slot >> 7, jt = (slot >> 6) & 1, l = slot & 63;
-            const int r = l & 15, q4 = l >> 4;
-            const u2_t lo = *reinterpret_cast<const u2_t*>(&sh.u.in.qb[16 * jt + r][32 * w + 4 * q4]);
-            const u2_t hi = *reinterpret_cast<const u2_t*>(&sh.u.in.qb[16 * jt + r][32 * w + 16 + 4 * q4]);
-            o.qsw[kunit * kQVec + slot] = u4_t{lo[0], lo[1], hi[0], hi[1]};
-            const int d = 32 * w + 16 * jt + r;
-            u4_t kv;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int s0 = p < 2 ? 4 * q4 + 2 * p : 16 + 4 * q4 + 2 * (p - 2);
-                kv[p] = (uint32_t)sh.kb[s0][d] | ((uint32_t)sh.kb[s0 + 1][d] << 16);
-            }
-            o.ksw[kunit * kQVec + slot] = kv;
+        for (int jt = 0; jt < 2; ++jt) {
+            kd[jt * 64] = kt[jt];
+            const u2_t lo = *reinterpret_cast<const u2_t*>(&sh.u.in.qb[16 * jt + lr][32 * wv + 4 * lq]);
+            const u2_t hi = *reinterpret_cast<const u2_t*>(&sh.u.in.qb[16 * jt + lr][32 * wv + 16 + 4 * lq]);
+            qd[jt * 64] = u4_t{lo[0], lo[1], hi[0], hi[1]};
         }
     }
 
     // 2b. k k^T and q k^T, 32 x 32 each: wave w owns output tile (w / 2, w % 2)
     {
-        const int mi = wave >> 1, ni = wave & 1;
+        const int mi = wv >> 1, ni = wv & 1;
         f4_t ckk = {0.f, 0.f, 0.f, 0.f}, cqk = ckk;
 #pragma unroll
         for (int ks = 0; ks < DKC / 32; ++ks) {
-            const int col = ks * 32 + 8 * (lane >> 4);
-            const u4_t ka = *reinterpret_cast<const u4_t*>(&sh.kb[16 * mi + (lane & 15)][col]);
-            const u4_t qa = *reinterpret_cast<const u4_t*>(&sh.u.in.qb[16 * mi + (lane & 15)][col]);
-            const u4_t kb = *reinterpret_cast<const u4_t*>(&sh.kb[16 * ni + (lane & 15)][col]);
+            const int col = ks * 32 + 8 * lq;
+            const u4_t ka = *reinterpret_cast<const u4_t*>(&sh.kb[16 * mi + lr][col]);
+            const u4_t qa = *reinterpret_cast<const u4_t*>(&sh.u.in.qb[16 * mi + lr][col]);
+            const u4_t kb = *reinterpret_cast<const u4_t*>(&sh.kb[16 * ni + lr][col]);
             ckk = mma(ka, kb, ckk);
             cqk = mma(qa, kb, cqk);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sh.u.in.kk[16 * mi + 4 * (lane >> 4) + i][16 * ni + (lane & 15)] = ckk[i];
-            sh.u.in.qk[16 * mi + 4 * (lane >> 4) + i][16 * ni + (lane & 15)] = cqk[i];
+            sh.u.in.kk[16 * mi + 4 * lq + i][16 * ni + lr] = ckk[i];
+            sh.u.in.qk[16 * mi + 4 * lq + i][16 * ni + lr] = cqk[i];
         }
     }
     __syncthreads();
 
     // 3. decay ratios R[t][s] = g_{s+1}...g_t (s <= t) for s in this thread's
-    //    four columns, then A, -P (planes), gamma, -rho
+    //    four columns, then A, -P (two planes), gamma, -rho
     {
         const int t = tid >> 3, s0 = (tid & 7) * 4;
         float r[4];
@@ -252,80 +302,129 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
             av[e] = s < t ? sh.bs[t] * r[e] * sh.u.in.kk[t][s] : 0.f;
             pv[e] = s <= t ? -(r[e] * sh.u.in.qk[t][s]) : 0.f;
         }
-        *reinterpret_cast<float4*>(&sh.a[t][s0]) = make_float4(av[0], av[1], av[2], av[3]);
+        *reinterpret_cast<float4*>(&sh.w.s.a[t][s0]) = make_float4(av[0], av[1], av[2], av[3]);
         // these four columns are elements 4 half .. 4 half + 3 of quarter q4
         const int half = s0 >> 4, q4 = (s0 & 15) >> 2;
         const int l = 16 * q4 + (t & 15), jt = t >> 4;
-        const Split2 p0 = split2(pv[0], pv[1]), p1 = split2(pv[2], pv[3]);
-        u2_t* pdst = reinterpret_cast<u2_t*>(o.pn + unit * kTVec + (jt * 3) * 64 + l) + half;
+        const Split2 p0 = split2(no, pv[0], pv[1]), p1 = split2(no, pv[2], pv[3]);
+        u2_t* pdst = reinterpret_cast<u2_t*>(o.pn + unit * kPVec + (jt * 2) * 64 + l) + half;
         pdst[0] = u2_t{p0.h, p1.h};
         pdst[2 * 64] = u2_t{p0.m, p1.m};
-        pdst[4 * 64] = u2_t{p0.l, p1.l};
         if (s0 == 0) {
             const float gm = sh.gs[0] * r[0];     // gamma_t = g_0 R[t][0]
             sh.gm[t] = gm;
-            o.gm[unit * CK + t] = gm;
+            o.rg[unit * 2 * CK + CK + t] = gm;
         }
         if (t == CK - 1)
-            *reinterpret_cast<float4*>(o.rhon + unit * CK + 8 * q4 + 4 * half) = make_float4(-r[0], -r[1], -r[2], -r[3]);
+            *reinterpret_cast<float4*>(o.rg + unit * 2 * CK + 8 * q4 + 4 * half) = make_float4(-r[0], -r[1], -r[2], -r[3]);
     }
     __syncthreads();
 
-    // 4. forward substitution (I + A) X = RHS, one column per thread:
-    //    columns 0..DK-1: RHS = beta gamma k (-> W); DK..DK+CK-1: RHS = e_j (-> T).
-    //    Each row goes to LDS as soon as it is known; the scheduling barrier
-    //    per row keeps the row's operands from being hoisted (the live set
-    //    stays at the 32 solved values).
-    if (tid < DKC + CK) {
+    // 4. T = (I + A)^-1 by forward substitution, one column per thread.  Each
+    //    row goes to LDS as soon as it is known; the scheduling barrier per
+    //    row keeps the row's operands from being hoisted.
+    if (tid < CK) {
         const int j = tid;
-        const bool wcol = j < DKC;
-        const float nbj = wcol ? 0.f : -sh.bs[j - DKC];
         float x[CK];
 #pragma unroll
         for (int t = 0; t < CK; ++t) {
-            const float rhs = wcol ? sh.bs[t] * sh.gm[t] * bf16lo(sh.kb[t][j]) : (t == j - DKC ? 1.f : 0.f);
             float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
             for (int s4 = 0; s4 < t; s4 += 4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(&sh.a[t][s4]);
+                const float4 a4 = *reinterpret_cast<const float4*>(&sh.w.s.a[t][s4]);
                 acc0 = fmaf(a4.x, x[s4], acc0);
                 if (s4 + 1 < t) acc1 = fmaf(a4.y, x[s4 + 1], acc1);
                 if (s4 + 2 < t) acc0 = fmaf(a4.z, x[s4 + 2], acc0);
                 if (s4 + 3 < t) acc1 = fmaf(a4.w, x[s4 + 3], acc1);
             }
-            x[t] = rhs - (acc0 + acc1);
-            if (wcol) sh.u.w[t][j] = x[t];
-            else sh.tn[t][j - DKC] = x[t] * nbj;
+            x[t] = (t == j ? 1.f : 0.f) - (acc0 + acc1);
+            sh.w.s.tm[t][j] = x[t];
             __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads();
 
-    // 5. W planes (rows 16j + r, columns 32w + kperm(q, e)) and -Tb planes
-    //    (rows 16j + r, columns 8q + e)
+    // 5. planes of T diag(beta gamma) and of -T diag(beta), four entries per thread
+    {
+        const int t = tid >> 3, s0 = (tid & 7) * 4;
+        const float4 tv = *reinterpret_cast<const float4*>(&sh.w.s.tm[t][s0]);
+        const float x[4] = {tv.x, tv.y, tv.z, tv.w};
+        float w4[4], b4[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int slot = tid + 256 * i;
-        const int w = slot >> 7, jt = (slot >> 6) & 1, l = slot & 63;
-        const int row = 16 * jt + (l & 15), q4 = l >> 4;
-        const f4_t x0 = *reinterpret_cast<const f4_t*>(&sh.u.w[row][32 * w + 4 * q4]);
-        const f4_t x1 = *reinterpret_cast<const f4_t*>(&sh.u.w[row][32 * w + 16 + 4 * q4]);
-        const Planes p = split8(x0, x1);
-        u4_t* dst = o.wsw + unit * kWVec + ((w * 2 + jt) * 3) * 64 + l;
-        dst[0] = p.h;
-        dst[64] = p.m;
-        dst[128] = p.l;
+        for (int e = 0; e < 4; ++e) {
+            const float bs = sh.bs[s0 + e];
+            w4[e] = x[e] * (bs * sh.gm[s0 + e]);
+            b4[e] = -(x[e] * bs);
+        }
+        const Split2 w0 = split2(no, w4[0], w4[1]), w1 = split2(no, w4[2], w4[3]);
+        const Split2 b0 = split2(no, b4[0], b4[1]), b1 = split2(no, b4[2], b4[3]);
+        *reinterpret_cast<u2_t*>(&sh.u.pl.tw[0][t][s0]) = u2_t{w0.h, w1.h};
+        *reinterpret_cast<u2_t*>(&sh.u.pl.tw[1][t][s0]) = u2_t{w0.m, w1.m};
+        *reinterpret_cast<u2_t*>(&sh.u.pl.tw[2][t][s0]) = u2_t{w0.l, w1.l};
+        *reinterpret_cast<u2_t*>(&sh.u.pl.tb[0][t][s0]) = u2_t{b0.h, b1.h};
+        *reinterpret_cast<u2_t*>(&sh.u.pl.tb[1][t][s0]) = u2_t{b0.m, b1.m};
+        *reinterpret_cast<u2_t*>(&sh.u.pl.tb[2][t][s0]) = u2_t{b0.l, b1.l};
     }
-    if (tid < 128) {
-        const int jt = tid >> 6, l = tid & 63;
-        const int row = 16 * jt + (l & 15), q4 = l >> 4;
-        const f4_t x0 = *reinterpret_cast<const f4_t*>(&sh.tn[row][8 * q4]);
-        const f4_t x1 = *reinterpret_cast<const f4_t*>(&sh.tn[row][8 * q4 + 4]);
-        const Planes p = split8(x0, x1);
-        u4_t* dst = o.tbn + unit * kTVec + (jt * 3) * 64 + l;
-        dst[0] = p.h;
-        dst[64] = p.m;
-        dst[128] = p.l;
+    __syncthreads();
+
+    // 6. W^T = K^T (T diag(beta gamma))^T on the matrix cores: wave w forms
+    //    column tiles 2w, 2w+1 of W^T for both t-tiles; its accumulators are
+    //    W rows 16j + r at columns 32w + kperm(q, e), the layout of the
+    //    sequential pass (stored in f32; that pass cuts them into planes).
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+        Planes tw;
+        const int row = 16 * jt + lr;
+        const u2_t h0 = *reinterpret_cast<const u2_t*>(&sh.u.pl.tw[0][row][4 * lq]);
+        const u2_t h1 = *reinterpret_cast<const u2_t*>(&sh.u.pl.tw[0][row][16 + 4 * lq]);
+        const u2_t m0 = *reinterpret_cast<const u2_t*>(&sh.u.pl.tw[1][row][4 * lq]);
+        const u2_t m1 = *reinterpret_cast<const u2_t*>(&sh.u.pl.tw[1][row][16 + 4 * lq]);
+        const u2_t l0 = *reinterpret_cast<const u2_t*>(&sh.u.pl.tw[2][row][4 * lq]);
+        const u2_t l1 = *reinterpret_cast<const u2_t*>(&sh.u.pl.tw[2][row][16 + 4 * lq]);
+        tw.h = u4_t{h0[0], h0[1], h1[0], h1[1]};
+        tw.m = u4_t{m0[0], m0[1], m1[0], m1[1]};
+        tw.l = u4_t{l0[0], l0[1], l1[0], l1[1]};
+        const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+        const f4_t w0 = mma3b(kt[0], tw, zero);
+        const f4_t w1 = mma3b(kt[1], tw, zero);
+        u4_t* dst = o.wsw + unit * kWVec + ((wv * 2 + jt) * 2) * 64 + lane;
+        dst[0] = __builtin_bit_cast(u4_t, w0);
+        dst[64] = __builtin_bit_cast(u4_t, w1);
+    }
+
+    // 7. U = -Tb V for every 16 value columns rb and t-tile j, in the
+    //    accumulator layout of the sequential pass (lane holds rows
+    //    16j + 4q .. 16j + 4q + 3 of column 16 rb + r); v is staged through
+    //    LDS 128 columns at a time (rows past T are zero)
+    Planes tb[2];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+        const int row = 16 * jt + lr;
+        tb[jt].h = *reinterpret_cast<const u4_t*>(&sh.u.pl.tb[0][row][8 * lq]);
+        tb[jt].m = *reinterpret_cast<const u4_t*>(&sh.u.pl.tb[1][row][8 * lq]);
+        tb[jt].l = *reinterpret_cast<const u4_t*>(&sh.u.pl.tb[2][row][8 * lq]);
+    }
+    for (int c0 = 0; c0 < Dv; c0 += 128) {
+        const int wdt = min(128, Dv - c0);
+        for (int idx = tid; idx < CK * (wdt / 8); idx += 256) {
+            const int t = idx / (wdt / 8), c8 = idx % (wdt / 8);
+            uint4 vv = make_uint4(0, 0, 0, 0);
+            if (t0 + t < T) vv = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t0 + t) * Hv + hv) * Dv + c0 + c8 * 8);
+            *reinterpret_cast<uint4*>(&sh.w.vs[t][c8 * 8]) = vv;
+        }
+        __syncthreads();
+        for (int rb = wv; rb < wdt / 16; rb += 4) {
+            const int col = 16 * rb + lr;
+            u4_t vb;
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                vb[p] = (uint32_t)sh.w.vs[8 * lq + 2 * p][col] | ((uint32_t)sh.w.vs[8 * lq + 2 * p + 1][col] << 16);
+            const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+            u4_t* dst = o.u + (unit * (Dv / 16) + c0 / 16 + rb) * 2 * 64 + lane;
+            dst[0] = __builtin_bit_cast(u4_t, mma3a(tb[0], vb, zero));
+            dst[64] = __builtin_bit_cast(u4_t, mma3a(tb[1], vb, zero));
+        }
+        __syncthreads();
     }
 }
 
@@ -333,82 +432,104 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
 
 struct SeqIn {
     const u4_t* wsw;
-    const u4_t* tbn;
+    const u4_t* u;
     const u4_t* pn;
-    const float* gm;
-    const float* rhon;
+    const float* rg;
     const u4_t* qsw;
     const u4_t* ksw;
-    const uint16_t* v;
 };
 
 // Per-block constants of the sequential pass.  `wv` is the wave index held
 // in a scalar register, so role branches and address arithmetic stay scalar.
 struct SeqCtx {
     int64_t unit0, kunit0;      // first chunk of this (b, hv) and of its (b, hk)
-    const uint16_t* v0;         // &v[b][0][hv][r0]
-    int64_t vstride;            // Hv * Dv (one step of v and y)
-    uint32_t voff;              // lane offset of V[8q][r] from a chunk's first row
-    int T, wv, lane;
+    int rblk, row_blocks;       // this block's 16 state rows, Dv / 16
+    int wv, lane;
 };
 
-// One chunk's operands in registers (two sets alternate: one chunk ahead).
+// A wave-uniform pointer moved to scalar registers, so that loads through it
+// take the scalar-base form (the per-lane part is one fixed 32-bit offset)
+// and no address registers are rewritten while earlier loads are in flight.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* uniform_ptr(const T* p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return (const __attribute__((address_space(1))) T*)(((uint64_t)hi << 32) | lo);
+}
+
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* uniform_ptr_w(T* p) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return (__attribute__((address_space(1))) T*)(((uint64_t)hi << 32) | lo);
+}
+
+// One chunk's operands in registers.
 struct SeqOps {
-    Planes w[2];      // W, t-tiles 0 and 1
+    f4_t wf[2][2];    // W of t-tiles 0 and 1 (f32, elements 0..3 and 4..7)
+    Planes w[2];      // the same as bf16 planes (cut one step before use)
     u4_t q[2];        // q, t-tiles 0 and 1
     u4_t k[2];        // k^T, this wave's two column tiles
-    Planes tp;        // waves 0, 1: -Tb of t-tile `wave`; waves 2, 3: -P of t-tile `wave - 2`
-    uint32_t vr[8];   // waves 0, 1: V[8q + e][r] (bf16 bits, packed where used)
-    f4_t rho[2];      // -rho[kperm(q, e)]
-    float gt;         // gamma_t, t = 16 (wave & 1) + r
-    float gc;         // gamma_{C-1}
+    u4_t a0, a1;      // waves 0, 1: -Tb V of t-tile `wave` (f32 bits) and a repeat of it;
+                      // waves 2, 3: -P planes h, m of t-tile `wave - 2` of the previous chunk
+    float rg;         // -rho[lane] (lanes 0..31), gamma[lane - 32] (lanes 32..63)
 
+    // Loads of one chunk in four parts, so that the sequential pass can
+    // spread them over the step it overlaps (part 0: W tile 0, 1: W tile 1,
+    // 2: q and k, 3: the rest).  Every wave issues the same number of loads
+    // (role-independent counts keep the memory waits exact).
+    template <int PART>
     __device__ __forceinline__ void load(const SeqIn& in, const SeqCtx& x, int c) {
         const int64_t unit = x.unit0 + c, kunit = x.kunit0 + c;
         const int wv = x.wv, lane = x.lane;
-        const u4_t* ws = in.wsw + unit * kWVec + wv * 6 * 64;
-        w[0].h = ws[lane];
-        w[0].m = ws[64 + lane];
-        w[0].l = ws[128 + lane];
-        w[1].h = ws[192 + lane];
-        w[1].m = ws[256 + lane];
-        w[1].l = ws[320 + lane];
-        const u4_t* qs = in.qsw + kunit * kQVec + wv * 2 * 64;
-        const u4_t* ks = in.ksw + kunit * kQVec + wv * 2 * 64;
-        q[0] = qs[lane];
-        q[1] = qs[64 + lane];
-        k[0] = ks[lane];
-        k[1] = ks[64 + lane];
-        const u4_t* ts = (wv < 2 ? in.tbn : in.pn) + unit * kTVec + (wv & 1) * 3 * 64;
-        tp.h = ts[lane];
-        tp.m = ts[64 + lane];
-        tp.l = ts[128 + lane];
-        const f4_t* rs = reinterpret_cast<const f4_t*>(in.rhon + unit * CK) + 2 * (lane >> 4);
-        rho[0] = rs[0];
-        rho[1] = rs[1];
-        gt = in.gm[unit * CK + 16 * (wv & 1) + (lane & 15)];
-        gc = in.gm[unit * CK + CK - 1];
-        if (wv < 2) {
-            // V[t0 + 8q + e][r]; in the last chunk steps past T read step
-            // T-1 instead (their column of Tb is zero)
-            const int t0 = c * CK;
-            const uint16_t* vb = x.v0 + (int64_t)t0 * x.vstride;
-            if (t0 + CK <= x.T) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vr[e] = vb[e * x.vstride + x.voff];
-            } else {
-                const int lim = x.T - 1 - t0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    vr[e] = vb[(int64_t)min(8 * (lane >> 4) + e, lim) * x.vstride + (lane & 15)];
-            }
+        if constexpr (PART <= 1) {
+            const auto ws = uniform_ptr(in.wsw + unit * kWVec + wv * 4 * 64 + PART * 2 * 64);
+            wf[PART][0] = __builtin_bit_cast(f4_t, ws[lane]);
+            wf[PART][1] = __builtin_bit_cast(f4_t, ws[64 + lane]);
+        } else if constexpr (PART == 2) {
+            const auto qs = uniform_ptr(in.qsw + kunit * kQVec + wv * 2 * 64);
+            const auto ks = uniform_ptr(in.ksw + kunit * kQVec + wv * 2 * 64);
+            q[0] = qs[lane];
+            q[1] = qs[64 + lane];
+            k[0] = ks[lane];
+            k[1] = ks[64 + lane];
+        } else {
+            const int64_t punit = x.unit0 + max(c - 1, 0);   // -P is used one chunk later
+            const u4_t* ab = wv < 2 ? in.u + ((unit * x.row_blocks + x.rblk) * 2 + wv) * 64
+                                    : in.pn + punit * kPVec + (wv & 1) * 2 * 64;
+            a0 = uniform_ptr(ab)[lane];
+            a1 = uniform_ptr(ab + (wv < 2 ? 0 : 64))[lane];
+            rg = uniform_ptr(in.rg + unit * 2 * CK)[lane];
         }
     }
+
+    __device__ __forceinline__ void split_w(const NegOnes& no) {
+        w[0] = split8(no, wf[0][0], wf[0][1]);
+        w[1] = split8(no, wf[1][0], wf[1][1]);
+    }
+
+    __device__ __forceinline__ void load_all(const SeqIn& in, const SeqCtx& x, int c) {
+        load<0>(in, x, c);
+        load<1>(in, x, c);
+        load<2>(in, x, c);
+        load<3>(in, x, c);
+    }
 };
+
+// keeps the instructions of the enclosed part where they are written
+#define SEQ_PIN(stmt)                          \
+    do {                                       \
+        __builtin_amdgcn_sched_barrier(0);     \
+        stmt;                                  \
+        __builtin_amdgcn_sched_barrier(0);     \
+    } while (0)
 
 struct SeqSmem {
     f4_t x[2][NW * 2 * 64];   // per-wave shares of W S^T - Tb V, double-buffered by chunk parity
     f4_t y[2][NW * 2 * 64];   // per-wave shares of S Q^T (transposed Y')
+    float rg[2][2 * CK];      // -rho (kperm order) and gamma of the chunk
 };
 
 __global__ __launch_bounds__(256) void chunk_seq_kernel(SeqIn in, const float* state_in, float* state_out,
@@ -427,16 +548,16 @@ __global__ __launch_bounds__(256) void chunk_seq_kernel(SeqIn in, const float* s
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, lq = lane >> 4;
     const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+    const NegOnes no = neg_ones();
 
     SeqCtx x;
     x.unit0 = (int64_t)n * NC;
     x.kunit0 = ((int64_t)b * Hk + hk) * NC;
-    x.vstride = (int64_t)Hv * Dv;
-    x.v0 = in.v + ((int64_t)b * T * Hv + hv) * Dv + r0;
-    x.voff = (uint32_t)(8 * lq * x.vstride + lr);
-    x.T = T;
+    x.rblk = rblk;
+    x.row_blocks = row_blocks;
     x.wv = wv;
     x.lane = lane;
+    const int64_t vstride = (int64_t)Hv * Dv;     // one step of y
 
     // state tile tt, register i: S[r0 + lr][32 wv + 16 tt + 4 lq + i]
     f4_t S[2];
@@ -454,20 +575,43 @@ __global__ __launch_bounds__(256) void chunk_seq_kernel(SeqIn in, const float* s
     // y rows of waves 2, 3: step 16 (wv & 1) + lr of the chunk, columns r0 + 4 lq ..
     uint16_t* y0 = y + ((int64_t)b * T * Hv + hv) * Dv + r0;
     const int yt = 16 * (wv & 1) + lr;
-    const uint32_t yoff = (uint32_t)(yt * x.vstride + 4 * lq);
+    const uint32_t yoff = (uint32_t)(yt * vstride + 4 * lq);
 
-    auto step = [&](int c, const SeqOps& o) {
+    // D of the previous chunk: waves 2, 3 finish that chunk's y during the
+    // matrix-core phase of the next one, when their vector unit is free
+    f4_t dp0 = zero, dp1 = zero;
+
+    // y rows of chunk cp, t-tile (wv & 1): Y^T = gamma_t (S Q^T) + D^T (-P)^T
+    // (leading planes of D and P: 2^-16 relative, below y's rounding)
+    auto finish_y = [&](int cp, const u4_t pnh, const u4_t pnm) {
+        const int jt = wv & 1;
+        const f4_t* yb = sh.y[cp & 1];
+        const float* rg = sh.rg[cp & 1];
+        const f4_t q0 = yb[jt * 64 + lane], q1 = yb[(2 + jt) * 64 + lane];
+        const f4_t q2 = yb[(4 + jt) * 64 + lane], q3 = yb[(6 + jt) * 64 + lane];
+        f4_t ys = ((q0 + q1) + q2) + q3;
+        ys = ys * rg[CK + yt];
+        u4_t dh, dm;
+        split8hm(no, dp0, dp1, dh, dm);
+        ys = mma(dm, pnh, ys);
+        ys = mma(dh, pnm, ys);
+        ys = mma(dh, pnh, ys);
+        if (cp * CK + yt < T)
+            *reinterpret_cast<__attribute__((address_space(1))) u2_t*>(uniform_ptr_w(y0 + (int64_t)cp * CK * vstride) + yoff) =
+                u2_t{pack_bf16x2(ys[0], ys[1]), pack_bf16x2(ys[2], ys[3])};
+    };
+
+    // one chunk with o; W of the next chunk (n1) is cut into planes and the
+    // loads of chunk cn into n2 are spread over it
+    auto step = [&](int c, const SeqOps& o, SeqOps& n1, SeqOps& nx, int cn) {
         // state planes: element e of quarter lq is column kperm(lq, e)
-        const Planes s = split8(S[0], S[1]);
+        const Planes s = split8(no, S[0], S[1]);
+        SEQ_PIN(nx.load<0>(in, x, cn));
 
         // this wave's share of W S^T - Tb V (rows t, columns r), two t-tiles
         f4_t x0 = zero, x1 = zero;
-        if (wv < 2) {
-            const u4_t v = {o.vr[0] | (o.vr[1] << 16), o.vr[2] | (o.vr[3] << 16), o.vr[4] | (o.vr[5] << 16),
-                            o.vr[6] | (o.vr[7] << 16)};
-            if (wv == 0) x0 = mma3a(o.tp, v, x0);
-            else x1 = mma3a(o.tp, v, x1);
-        }
+        if (wv == 0) x0 = __builtin_bit_cast(f4_t, o.a0);
+        else if (wv == 1) x1 = __builtin_bit_cast(f4_t, o.a0);
         x0 = mma(o.w[0].l, s.h, x0);
         x1 = mma(o.w[1].l, s.h, x1);
         x0 = mma(o.w[0].h, s.l, x0);
@@ -481,13 +625,16 @@ __global__ __launch_bounds__(256) void chunk_seq_kernel(SeqIn in, const float* s
         x0 = mma(o.w[0].h, s.h, x0);
         x1 = mma(o.w[1].h, s.h, x1);
 
-        // this wave's share of S Q^T (rows r, columns t)
-        f4_t y0v = mma(s.l, o.q[0], zero);
-        f4_t y1v = mma(s.l, o.q[1], zero);
-        y0v = mma(s.m, o.q[0], y0v);
-        y1v = mma(s.m, o.q[1], y1v);
+        // this wave's share of S Q^T (rows r, columns t); y is rounded to
+        // bf16, so the state's two leading planes suffice (2^-16)
+        f4_t y0v = mma(s.m, o.q[0], zero);
+        f4_t y1v = mma(s.m, o.q[1], zero);
         y0v = mma(s.h, o.q[0], y0v);
         y1v = mma(s.h, o.q[1], y1v);
+
+        SEQ_PIN(nx.load<1>(in, x, cn));
+        n1.split_w(no);
+        if (wv >= 2 && c > 0) finish_y(c - 1, o.a0, o.a1);
 
         f4_t* xb = sh.x[c & 1];
         f4_t* yb = sh.y[c & 1];
@@ -495,8 +642,11 @@ __global__ __launch_bounds__(256) void chunk_seq_kernel(SeqIn in, const float* s
         xb[(2 * wv + 1) * 64 + lane] = x1;
         yb[(2 * wv) * 64 + lane] = y0v;
         yb[(2 * wv + 1) * 64 + lane] = y1v;
+        float* rg = sh.rg[c & 1];
+        if (wv == 0) rg[lane] = o.rg;
         __syncthreads();
 
+        SEQ_PIN(nx.load<2>(in, x, cn));
         // D = W S^T - Tb V = -Delta, summed in wave order (identical in every wave)
         const f4_t p00 = xb[0 * 64 + lane], p10 = xb[2 * 64 + lane], p20 = xb[4 * 64 + lane], p30 = xb[6 * 64 + lane];
         const f4_t p01 = xb[1 * 64 + lane], p11 = xb[3 * 64 + lane], p21 = xb[5 * 64 + lane], p31 = xb[7 * 64 + lane];
@@ -504,40 +654,36 @@ __global__ __launch_bounds__(256) void chunk_seq_kernel(SeqIn in, const float* s
         const f4_t d1 = ((p01 + p11) + p21) + p31;
 
         // S = gamma_{C-1} S + K^T (diag(rho) Delta)
-        const Planes bs = split8(o.rho[0] * d0, o.rho[1] * d1);
-        S[0] = S[0] * o.gc;
-        S[1] = S[1] * o.gc;
+        const f4_t rh0 = *reinterpret_cast<const f4_t*>(rg + 8 * lq);
+        const f4_t rh1 = *reinterpret_cast<const f4_t*>(rg + 8 * lq + 4);
+        const float gc = rg[2 * CK - 1];
+        const Planes bs = split8(no, rh0 * d0, rh1 * d1);
+        S[0] = S[0] * gc;
+        S[1] = S[1] * gc;
         S[0] = mma3b(o.k[0], bs, S[0]);
         S[1] = mma3b(o.k[1], bs, S[1]);
-
-        if (wv >= 2) {
-            // Y^T = gamma_t (S Q^T) + D^T (-P)^T for t-tile wv - 2
-            const int jt = wv & 1;
-            const f4_t q0 = yb[jt * 64 + lane], q1 = yb[(2 + jt) * 64 + lane];
-            const f4_t q2 = yb[(4 + jt) * 64 + lane], q3 = yb[(6 + jt) * 64 + lane];
-            f4_t ys = ((q0 + q1) + q2) + q3;
-            ys = ys * o.gt;
-            const Planes ds = split8(d0, d1);
-            ys = mma(ds.l, o.tp.h, ys);
-            ys = mma(ds.h, o.tp.l, ys);
-            ys = mma(ds.m, o.tp.m, ys);
-            ys = mma(ds.m, o.tp.h, ys);
-            ys = mma(ds.h, o.tp.m, ys);
-            ys = mma(ds.h, o.tp.h, ys);
-            if (c * CK + yt < T)
-                *reinterpret_cast<u2_t*>(y0 + (int64_t)c * CK * x.vstride + yoff) =
-                    u2_t{pack_bf16x2(ys[0], ys[1]), pack_bf16x2(ys[2], ys[3])};
-        }
+        dp0 = d0;
+        dp1 = d1;
+        SEQ_PIN(nx.load<3>(in, x, cn));
     };
 
-    SeqOps oa, ob;
-    oa.load(in, x, 0);
-    for (int c = 0; c < NC; c += 2) {
-        ob.load(in, x, min(c + 1, NC - 1));
-        step(c, oa);
-        if (c + 1 >= NC) break;
-        oa.load(in, x, min(c + 2, NC - 1));
-        step(c + 1, ob);
+    // three operand sets: chunk c + 2 loads while chunk c runs
+    SeqOps o0, o1, o2;
+    o0.load_all(in, x, 0);
+    o1.load_all(in, x, min(1, NC - 1));
+    o0.split_w(no);
+    int c = 0;
+    for (; c + 3 <= NC; c += 3) {     // one exit: the sets rotate through whole rounds
+        step(c, o0, o1, o2, min(c + 2, NC - 1));
+        step(c + 1, o1, o2, o0, min(c + 3, NC - 1));
+        step(c + 2, o2, o0, o1, min(c + 4, NC - 1));
+    }
+    if (c < NC) step(c, o0, o1, o2, min(c + 2, NC - 1));
+    if (c + 1 < NC) step(c + 1, o1, o2, o0, min(c + 3, NC - 1));
+    // y of the last chunk (its -P, its shares of S Q^T and gamma are in place)
+    if (wv >= 2) {
+        const auto ps = uniform_ptr(in.pn + (x.unit0 + NC - 1) * kPVec + (wv & 1) * 2 * 64);
+        finish_y(NC - 1, ps[lane], ps[64 + lane]);
     }
 
     *reinterpret_cast<f4_t*>(sp_out + soff) = S[0];
@@ -551,7 +697,7 @@ bool chunked_supported(int Hv, int Dk, int Dv) {
     return Dk == DKC && Dv % RB == 0 && (int64_t)Hv * Dv <= (int64_t(1) << 25);
 }
 
-ChunkedLayout chunked_layout(int B, int T, int Hk, int Hv, int Dk) {
+ChunkedLayout chunked_layout(int B, int T, int Hk, int Hv, int Dk, int Dv) {
     (void)Dk;
     ChunkedLayout L;
     const int64_t NC = (T + CK - 1) / CK;
@@ -560,11 +706,10 @@ ChunkedLayout chunked_layout(int B, int T, int Hk, int Hv, int Dk) {
     auto a256 = [](uint64_t x) { return (x + 255) & ~uint64_t(255); };
     L.nc = (int)NC;
     L.wsw = 0;
-    L.tbn = L.wsw + a256(units * kWVec * 16);
-    L.pn = L.tbn + a256(units * kTVec * 16);
-    L.gm = L.pn + a256(units * kTVec * 16);
-    L.rhon = L.gm + a256(units * CK * 4);
-    L.qsw = L.rhon + a256(units * CK * 4);
+    L.u = L.wsw + a256(units * kWVec * 16);
+    L.pn = L.u + a256(units * CK * (uint64_t)Dv * 4);
+    L.rg = L.pn + a256(units * kPVec * 16);
+    L.qsw = L.rg + a256(units * 2 * CK * 4);
     L.ksw = L.qsw + a256(kunits * kQVec * 16);
     L.total = L.ksw + a256(kunits * kQVec * 16);
     return L;
@@ -577,30 +722,27 @@ int64_t chunked_blocks(int B, int T, int Hv, int Dv) {
 
 hipError_t launch_recurrent_chunked(const RecurrentArgs& a, void* ws, hipStream_t stream) {
     if (!chunked_supported(a.Hv, a.Dk, a.Dv) || a.T <= 0 || a.B <= 0) return hipErrorInvalidValue;
-    const ChunkedLayout L = chunked_layout(a.B, a.T, a.Hk, a.Hv, a.Dk);
+    const ChunkedLayout L = chunked_layout(a.B, a.T, a.Hk, a.Hv, a.Dk, a.Dv);
     char* base = static_cast<char*>(ws);
     ChunkPtrs o;
     o.wsw = reinterpret_cast<u4_t*>(base + L.wsw);
-    o.tbn = reinterpret_cast<u4_t*>(base + L.tbn);
+    o.u = reinterpret_cast<u4_t*>(base + L.u);
     o.pn = reinterpret_cast<u4_t*>(base + L.pn);
-    o.gm = reinterpret_cast<float*>(base + L.gm);
-    o.rhon = reinterpret_cast<float*>(base + L.rhon);
+    o.rg = reinterpret_cast<float*>(base + L.rg);
     o.qsw = reinterpret_cast<u4_t*>(base + L.qsw);
     o.ksw = reinterpret_cast<u4_t*>(base + L.ksw);
     const int64_t units = (int64_t)a.B * a.Hv * L.nc;
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g, a.beta, o,
-                       a.T, a.Hk, a.Hv, L.nc);
+    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g, a.beta, a.v,
+                       o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     SeqIn in;
     in.wsw = o.wsw;
-    in.tbn = o.tbn;
+    in.u = o.u;
     in.pn = o.pn;
-    in.gm = o.gm;
-    in.rhon = o.rhon;
+    in.rg = o.rg;
     in.qsw = o.qsw;
     in.ksw = o.ksw;
-    in.v = a.v;
     const int row_blocks = a.Dv / RB;
     const int64_t blocks = (int64_t)a.B * a.Hv * row_blocks;
     hipLaunchKernelGGL(chunk_seq_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, a.state_in, a.state_out,

@@ -206,14 +206,14 @@ bool workspace_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, Workspace& w
     w.beta = w.g + align256(ng * 4);
     w.chunked = w.beta + align256(ng * 4);
     w.use_chunked = B > 0 && layer_uses_chunked(T, Hv, Dk, Dv);
-    w.total = w.chunked + (w.use_chunked ? gdn::chunked_layout(B, T, Hk, Hv, Dk).total : 0);
+    w.total = w.chunked + (w.use_chunked ? gdn::chunked_layout(B, T, Hk, Hv, Dk, Dv).total : 0);
     if ((int64_t)B * T == 0) w.total = 0;
     return true;
 }
 
 uint64_t chunked_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv) {
     if ((int64_t)B * T == 0 || !gdn::chunked_supported(Hv, Dk, Dv)) return 0;
-    return gdn::chunked_layout(B, T, Hk, Hv, Dk).total;
+    return gdn::chunked_layout(B, T, Hk, Hv, Dk, Dv).total;
 }
 
 }  // namespace

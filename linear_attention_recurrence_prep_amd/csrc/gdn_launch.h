@@ -44,18 +44,17 @@ int64_t prep_blocks(int B, int T, int Hk, int Hv, int Dk, int Dv);
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream);
 
 // Chunked (matrix-core) recurrence: Dk == 128, Dv a multiple of 16,
-// Hv * Dv <= 2^25.  Its
-// workspace holds, per (b, hv, 32-step chunk), W [32 x Dk], -T diag(beta)
-// [32 x 32] and -P [32 x 32] as three bf16 planes each, gamma [32] and -rho
-// [32] in f32, and per (b, hk, chunk) q and k [32 x Dk] in bf16, all in the
-// register layout of the sequential kernel (byte offsets below, each
-// 256-byte aligned).
+// Hv * Dv <= 2^25.  Its workspace holds, per (b, hv, 32-step chunk), W
+// [32 x Dk] and -T diag(beta) V [32 x Dv] in f32, -P
+// [32 x 32] as two bf16 planes, -rho and gamma [32 each] in f32, and per
+// (b, hk, chunk) q and k [32 x Dk] in bf16, all in the register layout of the
+// sequential kernel (byte offsets below, each 256-byte aligned).
 struct ChunkedLayout {
     int nc;                 // chunks per sequence
-    uint64_t wsw, tbn, pn, gm, rhon, qsw, ksw, total;
+    uint64_t wsw, u, pn, rg, qsw, ksw, total;
 };
 bool chunked_supported(int Hv, int Dk, int Dv);
-ChunkedLayout chunked_layout(int B, int T, int Hk, int Hv, int Dk);
+ChunkedLayout chunked_layout(int B, int T, int Hk, int Hv, int Dk, int Dv);
 int64_t chunked_blocks(int B, int T, int Hv, int Dv);
 hipError_t launch_recurrent_chunked(const RecurrentArgs& a, void* workspace, hipStream_t stream);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);

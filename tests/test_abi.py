@@ -123,14 +123,14 @@ def test_prep_allows_in_place_conv_state_and_empty_batch(L):
     assert call_prep(L, B=0, cs_in=None, cs_out=None) == OK
 
 
-def chunked_expect(B, T, Hk, Hv, Dk):
-    # per (b, hv, chunk): W as three bf16 planes, -Tb and -P as three planes,
-    # gamma and -rho in f32; per (b, hk, chunk): q and k in bf16
+def chunked_expect(B, T, Hk, Hv, Dk, Dv):
+    # per (b, hv, chunk): W and -Tb V in f32, -P as two bf16 planes, -rho
+    # and gamma in f32; per (b, hk, chunk): q and k in bf16
     up = lambda x: (x + 255) // 256 * 256
     nc = (T + 31) // 32
     units, kunits = B * Hv * nc, B * Hk * nc
-    return (up(units * 32 * Dk * 2 * 3) + 2 * up(units * 32 * 32 * 2 * 3) + 2 * up(units * 32 * 4)
-            + 2 * up(kunits * 32 * Dk * 2))
+    return (up(units * 32 * Dk * 4) + up(units * 32 * Dv * 4) + up(units * 32 * 32 * 2 * 2)
+            + up(units * 64 * 4) + 2 * up(kunits * 32 * Dk * 2))
 
 
 def test_workspace_bytes(L):
@@ -139,8 +139,8 @@ def test_workspace_bytes(L):
     B, T, Hk, Hv, Dk, Dv = 1, 4096, 16, 32, 128, 128
     prep_part = 2 * up(B * T * Hk * Dk * 2) + up(B * T * Hv * Dv * 2) + 2 * up(B * T * Hv * 4)
     # Dk = 128, Dv % 16 == 0, T >= 64: the layer core adds the chunked recurrence's part
-    assert f(B, T, Hk, Hv, Dk, Dv) == prep_part + chunked_expect(B, T, Hk, Hv, Dk)
-    assert L.gdn_recurrent_chunked_workspace_bytes(B, T, Hk, Hv, Dk, Dv) == chunked_expect(B, T, Hk, Hv, Dk)
+    assert f(B, T, Hk, Hv, Dk, Dv) == prep_part + chunked_expect(B, T, Hk, Hv, Dk, Dv)
+    assert L.gdn_recurrent_chunked_workspace_bytes(B, T, Hk, Hv, Dk, Dv) == chunked_expect(B, T, Hk, Hv, Dk, Dv)
     # short sequences and other head sizes use the per-step kernels: prologue part only
     T2 = 63
     assert f(B, T2, Hk, Hv, Dk, Dv) == 2 * up(T2 * Hk * Dk * 2) + up(T2 * Hv * Dv * 2) + 2 * up(T2 * Hv * 4)
