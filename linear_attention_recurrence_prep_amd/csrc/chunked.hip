@@ -472,8 +472,7 @@ struct SeqOps {
     Planes w[2];      // the same as bf16 planes (cut one step before use)
     u4_t q[2];        // q, t-tiles 0 and 1
     u4_t k[2];        // k^T, this wave's two column tiles
-    u4_t a0, a1;      // waves 0, 1: -Tb V of t-tile `wave` (f32 bits) and a repeat of it;
-                      // waves 2, 3: -P planes h, m of t-tile `wave - 2` of the previous chunk
+    u4_t a0;          // -Tb V of t-tile (wave & 1) (f32 bits; waves 0, 1 use it)
     float rg;         // -rho[lane] (lanes 0..31), gamma[lane - 32] (lanes 32..63)
 
     // Loads of one chunk in four parts, so that the sequential pass can
@@ -496,11 +495,9 @@ struct SeqOps {
             k[0] = ks[lane];
             k[1] = ks[64 + lane];
         } else {
-            const int64_t punit = x.unit0 + max(c - 1, 0);   // -P is used one chunk later
-            const u4_t* ab = wv < 2 ? in.u + ((unit * x.row_blocks + x.rblk) * 2 + wv) * 64
-                                    : in.pn + punit * kPVec + (wv & 1) * 2 * 64;
-            a0 = uniform_ptr(ab)[lane];
-            a1 = uniform_ptr(ab + (wv < 2 ? 0 : 64))[lane];
+            // every state wave loads a -Tb V tile (waves 0, 1 add theirs; equal
+            // load counts keep the memory waits exact) and rho/gamma
+            a0 = uniform_ptr(in.u + ((unit * x.row_blocks + x.rblk) * 2 + (wv & 1)) * 64)[lane];
             rg = uniform_ptr(in.rg + unit * 2 * CK)[lane];
         }
     }
@@ -526,15 +523,24 @@ struct SeqOps {
         __builtin_amdgcn_sched_barrier(0);     \
     } while (0)
 
+// Six waves per block: waves 0..3 hold the state (32 columns each) and run
+// the chunk chain; waves 4, 5 finish y of the previous chunk (one t-tile
+// each) off that chain.  Buffers the output waves read one chunk late are
+// kept three deep.
+constexpr int NWY = 2;
+constexpr int SEQ_THREADS = 64 * (NW + NWY);
+
 struct SeqSmem {
-    f4_t x[2][NW * 2 * 64];   // per-wave shares of W S^T - Tb V, double-buffered by chunk parity
-    f4_t y[2][NW * 2 * 64];   // per-wave shares of S Q^T (transposed Y')
-    float rg[2][2 * CK];      // -rho (kperm order) and gamma of the chunk
+    f4_t x[2][NW * 2 * 64];   // per-wave shares of W S^T - Tb V, by chunk parity
+    f4_t y[3][NW * 2 * 64];   // per-wave shares of S Q^T (transposed Y'), chunk mod 3
+    float rg[3][2 * CK];      // -rho (kperm order) and gamma of the chunk, chunk mod 3
+    f4_t d[2][2][64];         // D of the chunk (B-operand layout), by chunk parity
 };
 
-__global__ __launch_bounds__(256) void chunk_seq_kernel(SeqIn in, const float* state_in, float* state_out,
-                                                        uint16_t* __restrict__ y, int T, int Hk, int Hv, int Dv,
-                                                        int NC, int row_blocks, int n_blocks) {
+__global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const float* state_in,
+                                                                float* state_out, uint16_t* __restrict__ y,
+                                                                int T, int Hk, int Hv, int Dv, int NC,
+                                                                int row_blocks, int n_blocks) {
     __shared__ SeqSmem sh;
 
     int lb = blockIdx.x;
@@ -549,15 +555,55 @@ __global__ __launch_bounds__(256) void chunk_seq_kernel(SeqIn in, const float* s
     const int lr = lane & 15, lq = lane >> 4;
     const f4_t zero = {0.f, 0.f, 0.f, 0.f};
     const NegOnes no = neg_ones();
+    const int64_t vstride = (int64_t)Hv * Dv;     // one step of y
+    const int64_t unit0 = (int64_t)n * NC;
 
+    if (wv >= NW) {
+        // ------------------------------------------------ output waves
+        // y rows of t-tile jt: Y^T = gamma_t (S Q^T) + D^T (-P)^T, with the
+        // leading planes of D and P (2^-16 relative, below y's rounding)
+        const int jt = wv - NW;
+        const int yt = 16 * jt + lr;
+        uint16_t* y0 = y + ((int64_t)b * T * Hv + hv) * Dv + r0;
+        const uint32_t yoff = (uint32_t)(yt * vstride + 4 * lq);
+        u4_t ch = {0, 0, 0, 0}, cm = ch;              // -P planes of the chunk finished next
+        int b3 = 0;                                   // (c - 1) mod 3
+        for (int c = 0; c <= NC; ++c) {
+            const auto ps = uniform_ptr(in.pn + (unit0 + min(c, NC - 1)) * kPVec + jt * 2 * 64);
+            const u4_t nh = ps[lane], nm = ps[64 + lane];
+            __syncthreads();                          // chunk c's barrier (c == NC: the final one)
+            if (c > 0) {
+                const int cp = c - 1;
+                const f4_t* yb = sh.y[b3];
+                const f4_t q0 = yb[jt * 64 + lane], q1 = yb[(2 + jt) * 64 + lane];
+                const f4_t q2 = yb[(4 + jt) * 64 + lane], q3 = yb[(6 + jt) * 64 + lane];
+                f4_t ys = ((q0 + q1) + q2) + q3;
+                ys = ys * sh.rg[b3][CK + yt];
+                u4_t dh, dm;
+                split8hm(no, sh.d[cp & 1][0][lane], sh.d[cp & 1][1][lane], dh, dm);
+                ys = mma(dm, ch, ys);
+                ys = mma(dh, cm, ys);
+                ys = mma(dh, ch, ys);
+                if (cp * CK + yt < T)
+                    *reinterpret_cast<__attribute__((address_space(1))) u2_t*>(
+                        uniform_ptr_w(y0 + (int64_t)cp * CK * vstride) + yoff) =
+                        u2_t{pack_bf16x2(ys[0], ys[1]), pack_bf16x2(ys[2], ys[3])};
+                b3 = b3 == 2 ? 0 : b3 + 1;
+            }
+            ch = nh;
+            cm = nm;
+        }
+        return;
+    }
+
+    // ---------------------------------------------------- state waves
     SeqCtx x;
-    x.unit0 = (int64_t)n * NC;
+    x.unit0 = unit0;
     x.kunit0 = ((int64_t)b * Hk + hk) * NC;
     x.rblk = rblk;
     x.row_blocks = row_blocks;
     x.wv = wv;
     x.lane = lane;
-    const int64_t vstride = (int64_t)Hv * Dv;     // one step of y
 
     // state tile tt, register i: S[r0 + lr][32 wv + 16 tt + 4 lq + i]
     f4_t S[2];
@@ -572,38 +618,9 @@ __global__ __launch_bounds__(256) void chunk_seq_kernel(SeqIn in, const float* s
         S[1] = zero;
     }
 
-    // y rows of waves 2, 3: step 16 (wv & 1) + lr of the chunk, columns r0 + 4 lq ..
-    uint16_t* y0 = y + ((int64_t)b * T * Hv + hv) * Dv + r0;
-    const int yt = 16 * (wv & 1) + lr;
-    const uint32_t yoff = (uint32_t)(yt * vstride + 4 * lq);
-
-    // D of the previous chunk: waves 2, 3 finish that chunk's y during the
-    // matrix-core phase of the next one, when their vector unit is free
-    f4_t dp0 = zero, dp1 = zero;
-
-    // y rows of chunk cp, t-tile (wv & 1): Y^T = gamma_t (S Q^T) + D^T (-P)^T
-    // (leading planes of D and P: 2^-16 relative, below y's rounding)
-    auto finish_y = [&](int cp, const u4_t pnh, const u4_t pnm) {
-        const int jt = wv & 1;
-        const f4_t* yb = sh.y[cp & 1];
-        const float* rg = sh.rg[cp & 1];
-        const f4_t q0 = yb[jt * 64 + lane], q1 = yb[(2 + jt) * 64 + lane];
-        const f4_t q2 = yb[(4 + jt) * 64 + lane], q3 = yb[(6 + jt) * 64 + lane];
-        f4_t ys = ((q0 + q1) + q2) + q3;
-        ys = ys * rg[CK + yt];
-        u4_t dh, dm;
-        split8hm(no, dp0, dp1, dh, dm);
-        ys = mma(dm, pnh, ys);
-        ys = mma(dh, pnm, ys);
-        ys = mma(dh, pnh, ys);
-        if (cp * CK + yt < T)
-            *reinterpret_cast<__attribute__((address_space(1))) u2_t*>(uniform_ptr_w(y0 + (int64_t)cp * CK * vstride) + yoff) =
-                u2_t{pack_bf16x2(ys[0], ys[1]), pack_bf16x2(ys[2], ys[3])};
-    };
-
-    // one chunk with o; W of the next chunk (n1) is cut into planes and the
-    // loads of chunk cn into n2 are spread over it
-    auto step = [&](int c, const SeqOps& o, SeqOps& n1, SeqOps& nx, int cn) {
+    // one chunk c (b3 = c mod 3) with o; W of the next chunk (n1) is cut into
+    // planes and the loads of chunk cn into nx are spread over it
+    auto step = [&](int c, int b3, const SeqOps& o, SeqOps& n1, SeqOps& nx, int cn) {
         // state planes: element e of quarter lq is column kperm(lq, e)
         const Planes s = split8(no, S[0], S[1]);
         SEQ_PIN(nx.load<0>(in, x, cn));
@@ -634,15 +651,14 @@ __global__ __launch_bounds__(256) void chunk_seq_kernel(SeqIn in, const float* s
 
         SEQ_PIN(nx.load<1>(in, x, cn));
         n1.split_w(no);
-        if (wv >= 2 && c > 0) finish_y(c - 1, o.a0, o.a1);
 
         f4_t* xb = sh.x[c & 1];
-        f4_t* yb = sh.y[c & 1];
+        f4_t* yb = sh.y[b3];
         xb[(2 * wv) * 64 + lane] = x0;
         xb[(2 * wv + 1) * 64 + lane] = x1;
         yb[(2 * wv) * 64 + lane] = y0v;
         yb[(2 * wv + 1) * 64 + lane] = y1v;
-        float* rg = sh.rg[c & 1];
+        float* rg = sh.rg[b3];
         if (wv == 0) rg[lane] = o.rg;
         __syncthreads();
 
@@ -662,8 +678,10 @@ __global__ __launch_bounds__(256) void chunk_seq_kernel(SeqIn in, const float* s
         S[1] = S[1] * gc;
         S[0] = mma3b(o.k[0], bs, S[0]);
         S[1] = mma3b(o.k[1], bs, S[1]);
-        dp0 = d0;
-        dp1 = d1;
+        if (wv == 0) {
+            sh.d[c & 1][0][lane] = d0;
+            sh.d[c & 1][1][lane] = d1;
+        }
         SEQ_PIN(nx.load<3>(in, x, cn));
     };
 
@@ -674,17 +692,13 @@ __global__ __launch_bounds__(256) void chunk_seq_kernel(SeqIn in, const float* s
     o0.split_w(no);
     int c = 0;
     for (; c + 3 <= NC; c += 3) {     // one exit: the sets rotate through whole rounds
-        step(c, o0, o1, o2, min(c + 2, NC - 1));
-        step(c + 1, o1, o2, o0, min(c + 3, NC - 1));
-        step(c + 2, o2, o0, o1, min(c + 4, NC - 1));
+        step(c, 0, o0, o1, o2, min(c + 2, NC - 1));
+        step(c + 1, 1, o1, o2, o0, min(c + 3, NC - 1));
+        step(c + 2, 2, o2, o0, o1, min(c + 4, NC - 1));
     }
-    if (c < NC) step(c, o0, o1, o2, min(c + 2, NC - 1));
-    if (c + 1 < NC) step(c + 1, o1, o2, o0, min(c + 3, NC - 1));
-    // y of the last chunk (its -P, its shares of S Q^T and gamma are in place)
-    if (wv >= 2) {
-        const auto ps = uniform_ptr(in.pn + (x.unit0 + NC - 1) * kPVec + (wv & 1) * 2 * 64);
-        finish_y(NC - 1, ps[lane], ps[64 + lane]);
-    }
+    if (c < NC) step(c, 0, o0, o1, o2, min(c + 2, NC - 1));
+    if (c + 1 < NC) step(c + 1, 1, o1, o2, o0, min(c + 3, NC - 1));
+    __syncthreads();                  // the output waves' last chunk
 
     *reinterpret_cast<f4_t*>(sp_out + soff) = S[0];
     *reinterpret_cast<f4_t*>(sp_out + soff + 16) = S[1];
@@ -745,7 +759,8 @@ hipError_t launch_recurrent_chunked(const RecurrentArgs& a, void* ws, hipStream_
     in.ksw = o.ksw;
     const int row_blocks = a.Dv / RB;
     const int64_t blocks = (int64_t)a.B * a.Hv * row_blocks;
-    hipLaunchKernelGGL(chunk_seq_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, a.state_in, a.state_out,
+    hipLaunchKernelGGL(chunk_seq_kernel, dim3((unsigned)blocks), dim3(SEQ_THREADS), 0, stream, in, a.state_in,
+                       a.state_out,
                        a.y, a.T, a.Hk, a.Hv, a.Dv, L.nc, row_blocks, (int)blocks);
     return hipGetLastError();
 }
