@@ -6,8 +6,10 @@ conv K=4, zero conv and recurrent state, seeded synthetic inputs resident in
 HBM before timing.  Metric: recurrence tokens/s*head = B*T*Hv / step time.
 
 Also measured in the same run (same JSON line):
-  * the dominant kernel (the recurrence) timed alone with HIP events on the
-    stream it is launched on -> roofline against the FP32 vector peak;
+  * the dominant work, the chunked recurrence (its two launches, chunk
+    preparation and the sequential pass, one gdn_recurrent_chunked call),
+    timed alone with HIP events on the stream it is launched on -> roofline
+    of its algorithmic fp32 flops against the fp32 peak;
   * batched decode, B=64, T=1 (layer core, 8 rotating sets of state and conv
     state, 1 GiB, so the 256 MB last-level cache cannot hold them) -> HBM
     roofline of its recurrence kernel;
@@ -27,12 +29,13 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_prep_amd", "csrc")
 KERNEL_SOURCES = {
+    "chunked_recurrence": ["chunked.hip"],
     "recurrent_chunk_kernel": ["recurrent.hip"],
     "recurrent_step_kernel": ["recurrent.hip"],
     "prep_kernel": ["prep.hip"],
 }
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CU x 4 SIMD x 16 lanes x 2 (packed) x 2 (FMA) x 2.4 GHz
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector alike)
 
 
 def source_digest(kernel):
@@ -164,16 +167,20 @@ def main():
     value = B * T * Hv / (ms_step * 1e-3)
     print(f"[bench] prefill layer core {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
-    # dominant kernel alone, events on the stream it runs on
-    rec_us = time_kernel(torch, stream, rec_only, args.steps)
+    # dominant work alone, events on the stream it runs on: the chunked
+    # recurrence (chunk_prep_kernel + chunk_seq_kernel), then for reference
+    # the per-step form the layer core uses for short sequences, and the prologue
+    chunk_us = time_kernel(torch, stream, chunked_only, args.steps)
+    step_form_us = time_kernel(torch, stream, rec_only, max(3, args.steps // 4))
     prep_us = time_kernel(torch, stream, prep_only, args.steps)
     flops = 7 * B * T * Hv * Dk * Dv
-    achieved_tflops = flops / (rec_us * 1e-6) / 1e12
+    achieved_tflops = flops / (chunk_us * 1e-6) / 1e12
     rec_bytes = (2 * B * T * Hk * Dk * 2 + B * T * Hv * Dv * 2 + 2 * B * T * Hv * 4 + B * T * Hv * Dv * 2
                  + B * Hv * Dv * Dk * 4)
     prep_bytes = (B * T * C * 2 + C * K * 2 + 2 * B * T * Hv * 2 + 2 * Hv * 4 + 2 * B * T * Hk * Dk * 2
                   + B * T * Hv * Dv * 2 + 2 * B * T * Hv * 4 + B * (K - 1) * C * 2)
-    print(f"[bench] recurrent kernel {rec_us:.1f} us ({achieved_tflops:.1f} TFLOP/s), "
+    print(f"[bench] chunked recurrence {chunk_us:.1f} us ({achieved_tflops:.1f} TFLOP/s, "
+          f"{achieved_tflops / FP32_PEAK_TFLOPS:.1%} of fp32 peak); per-step form {step_form_us:.1f} us; "
           f"prep kernel {prep_us:.1f} us ({prep_bytes / prep_us / 1e3:.0f} GB/s)", file=sys.stderr, flush=True)
 
     # ------------------------------------------------------------- decode
@@ -199,12 +206,15 @@ def main():
         "data": "synthetic (seeded)",
         "config": {"workload": "prefill B=1 T=4096 Hk=16 Hv=32 Dk=Dv=128 K=4, zero conv/recurrent state",
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "alu", "kernel": "recurrent_chunk_kernel<128,32>",
-                     "achieved": achieved_tflops, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tflops / FP32_VECTOR_PEAK_TFLOPS,
-                     "traffic": measured_traffic("recurrent_chunk_kernel", "prefill_T4096"),
+        "roofline": {"bound": "mfma", "kernel": "chunk_prep_kernel + chunk_seq_kernel (gdn_recurrent_chunked)",
+                     "achieved": achieved_tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tflops / FP32_PEAK_TFLOPS,
+                     "traffic": measured_traffic("chunked_recurrence", "prefill_T4096"),
                      "traffic_algorithmic": rec_bytes,
-                     "flops_per_launch": flops, "avg_launch_us": rec_us},
+                     "flops_per_launch": flops, "avg_launch_us": chunk_us,
+                     "arithmetic": "fp32, on bf16 matrix cores through exact three-plane splits"},
+        "recurrence_per_step_form": {"kernel": "recurrent_chunk_kernel<128,32>", "avg_launch_us": step_form_us,
+                                     "achieved_TFLOPs": flops / (step_form_us * 1e-6) / 1e12},
         "prologue": {"kernel": "prep_kernel<128,4>", "avg_launch_us": prep_us,
                      "bytes_per_launch": prep_bytes, "achieved_GBs": prep_bytes / prep_us / 1e3,
                      "traffic": measured_traffic("prep_kernel", "prefill_T4096"),

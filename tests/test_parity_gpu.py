@@ -381,6 +381,29 @@ def test_prefill_workload_recurrence_strict():
         H.check_state(s[:, hv:hv + 1], s_ref, 1e-4, f"hv={hv}")
 
 
+def test_prefill_workload_chunked_recurrence_strict():
+    """The chunked recurrence at the prefill workload's full size (the form the
+    layer core runs there), on oracle-prepared inputs: sampled heads, all
+    rows, strict 1e-4 state bound."""
+    say("prefill chunked recurrence strict")
+    w = inputs.WORKLOADS["prefill"]
+    Hk, Hv, Dk, Dv = w["Hk"], w["Hv"], w["Dk"], w["Dv"]
+    raw = inputs.workload("prefill")
+    qs, ks = inputs.scales(Dk)
+    p = oracle.prep(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"], raw["A_log"],
+                    raw["dt_bias"], Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs, k_scale=ks)
+    ri = dict(q=oracle.round_bf16(p["q"]), k=oracle.round_bf16(p["k"]), v=oracle.round_bf16(p["v"]),
+              g=oracle.round_f32(p["g"]), beta=oracle.round_f32(p["beta"]), state=None)
+    y, s = gpu_recurrent_chunked(ri)
+    worst = 0.0
+    for hv in (2, 15, 29):
+        args = H.recurrence_sub(ri, 0, hv, list(range(Dv)), Hk, Hv)
+        y_ref, s_ref = oracle.recurrent(*args)
+        H.check_y(y[:, :, hv:hv + 1], y_ref, f"hv={hv}")
+        worst = max(worst, H.check_state(s[:, hv:hv + 1], s_ref, 1e-4, f"hv={hv}"))
+    say("prefill chunked state normwise err", worst)
+
+
 def test_long_workload_full_size_sampled():
     """B=4, T=32768 with random initial state: the full layer core on the GPU;
     the oracle recomputes 8 rows of 3 (b, hv) heads over the whole sequence
