@@ -31,6 +31,7 @@ _lib = None
 _dp = ctypes.POINTER(ctypes.c_double)
 _fp = ctypes.POINTER(ctypes.c_float)
 _hp = ctypes.POINTER(ctypes.c_uint16)
+_bp = ctypes.POINTER(ctypes.c_uint8)
 _i = ctypes.c_int
 _d = ctypes.c_double
 
@@ -52,10 +53,10 @@ def lib():
                                   _dp, _dp, _dp, _dp, _dp,
                                   _i, _i, _i, _i, _i, _i, _i, _d, _d, _d]
         L.oracle_prep.restype = _i
-        L.oracle_recurrent.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+        L.oracle_recurrent.argtypes = [_dp, _dp, _dp, _dp, _dp, _bp, _dp, _dp, _dp,
                                        _i, _i, _i, _i, _i, _i]
         L.oracle_recurrent.restype = _i
-        L.oracle_layer_core.argtypes = [_hp, _hp, _hp, _hp, _hp, _hp, _fp, _fp,
+        L.oracle_layer_core.argtypes = [_hp, _hp, _hp, _hp, _hp, _hp, _fp, _fp, _bp,
                                         _dp, _dp, _dp,
                                         _i, _i, _i, _i, _i, _i, _i, _d, _d, _d]
         L.oracle_layer_core.restype = _i
@@ -92,6 +93,13 @@ def _f64(a):
     if a is None:
         return None
     return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _mask(a):
+    """Step mask as contiguous bytes (nonzero = active), or None."""
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a) != 0, dtype=np.uint8)
 
 
 # ------------------------------------------------------------------ formats
@@ -151,11 +159,13 @@ def prep(qkv, conv_w, conv_state_in, a, b, A_log, dt_bias, *, Hk, Hv, Dk, Dv,
     return dict(q=q, k=k, v=v, g=g, beta=beta, conv_state=cs)
 
 
-def recurrent(q, k, v, g, beta, state_in=None):
+def recurrent(q, k, v, g, beta, state_in=None, mask=None):
     """Gated delta rule in fp64.  q,k [B,T,Hk,Dk]; v [B,T,Hv,Dv]; g,beta
-    [B,T,Hv]; state_in [B,Hv,Dv,Dk] or None.  Inputs are taken as exact
-    values (widened to float64).  Returns (y [B,T,Hv,Dv], state_out)."""
+    [B,T,Hv]; state_in [B,Hv,Dv,Dk] or None; mask [B,T] (nonzero = active
+    step) or None.  Inputs are taken as exact values (widened to float64).
+    Returns (y [B,T,Hv,Dv], state_out)."""
     q, k, v, g, beta, state_in = map(_f64, (q, k, v, g, beta, state_in))
+    mask = _mask(mask)
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     assert k.shape == q.shape and v.shape[:2] == (B, T)
@@ -164,8 +174,10 @@ def recurrent(q, k, v, g, beta, state_in=None):
         assert state_in.shape == (B, Hv, Dv, Dk)
     y = np.empty((B, T, Hv, Dv))
     s = np.empty((B, Hv, Dv, Dk))
+    if mask is not None:
+        assert mask.shape == (B, T)
     rc = lib().oracle_recurrent(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(g, _dp),
-                                _ptr(beta, _dp), _ptr(state_in, _dp), _ptr(s, _dp),
+                                _ptr(beta, _dp), _ptr(mask, _bp), _ptr(state_in, _dp), _ptr(s, _dp),
                                 _ptr(y, _dp), B, T, Hk, Hv, Dk, Dv)
     if rc != 0:
         raise RuntimeError("oracle_recurrent failed")
@@ -173,11 +185,13 @@ def recurrent(q, k, v, g, beta, state_in=None):
 
 
 def layer_core(qkv, conv_w, conv_state_in, a, b, A_log, dt_bias, state_in=None, *,
-               Hk, Hv, Dk, Dv, q_scale, k_scale, eps=1e-6):
+               Hk, Hv, Dk, Dv, q_scale, k_scale, eps=1e-6, mask=None):
     """Prologue, stored-dtype roundings (q,k,v -> bf16; g,beta -> f32), then
-    the recurrence.  Returns (y float64 [B,T,Hv,Dv], state_out float64,
-    conv_state_out bf16 bits)."""
+    the recurrence (mask [B,T] masks recurrence steps, None = all active).
+    Returns (y float64 [B,T,Hv,Dv], state_out float64, conv_state_out bf16
+    bits)."""
     qkv, conv_w, conv_state_in, a, b = map(_h, (qkv, conv_w, conv_state_in, a, b))
+    mask = _mask(mask)
     A_log, dt_bias = _f32(A_log), _f32(dt_bias)
     state_in = _f64(state_in)
     B, T, C = qkv.shape
@@ -190,7 +204,7 @@ def layer_core(qkv, conv_w, conv_state_in, a, b, A_log, dt_bias, state_in=None, 
     cs = np.empty((B, K - 1, C), dtype=np.uint16)
     rc = lib().oracle_layer_core(_ptr(qkv, _hp), _ptr(conv_w, _hp), _ptr(conv_state_in, _hp),
                                  _ptr(cs, _hp), _ptr(a, _hp), _ptr(b, _hp),
-                                 _ptr(A_log, _fp), _ptr(dt_bias, _fp),
+                                 _ptr(A_log, _fp), _ptr(dt_bias, _fp), _ptr(mask, _bp),
                                  _ptr(state_in, _dp), _ptr(s, _dp), _ptr(y, _dp),
                                  B, T, Hk, Hv, Dk, Dv, K,
                                  float(q_scale), float(k_scale), float(eps))

@@ -257,12 +257,17 @@ int oracle_prep(const uint16_t *qkv, const uint16_t *conv_w,
  *   S[i,j] <- S[i,j] + delta_i k_t[j]   (rank-1 update)
  *   y_t[i] = sum_j S[i,j] q_t[j]         (output with the updated state)
  *
+ * Masked steps ([bun] qwen3-delta.ts, the masked variant of the step
+ * kernel, selected for padded prefill): mask [B,T] (NULL = every step
+ * active); a step whose mask byte is 0 leaves S untouched (no decay, no
+ * update) and writes y_t = 0.
+ *
  * Layouts: q,k [B,T,Hk,Dk]; v,y [B,T,Hv,Dv]; g,beta [B,T,Hv];
  * state_in/state_out [B,Hv,Dv,Dk] (state_in NULL = zeros; may alias out).
  * All double.  Returns 0, or -1 on bad sizes / allocation failure.
  */
 int oracle_recurrent(const double *q, const double *k, const double *v,
-                     const double *g, const double *beta,
+                     const double *g, const double *beta, const unsigned char *mask,
                      const double *state_in, double *state_out, double *y,
                      int B, int T, int Hk, int Hv, int Dk, int Dv)
 {
@@ -291,6 +296,11 @@ int oracle_recurrent(const double *q, const double *k, const double *v,
                 const double gt = g[(bb * T + t) * Hv + hv];
                 const double bt = beta[(bb * T + t) * Hv + hv];
                 double *yt = y + ((bb * T + t) * Hv + hv) * Dv;
+                if (mask && !mask[bb * T + t]) {
+                    for (long i = 0; i < Dv; ++i)
+                        yt[i] = 0.0;
+                    continue;
+                }
                 for (long i = 0; i < (long)Dv * Dk; ++i)
                     S[i] = S[i] * gt;
                 for (long i = 0; i < Dv; ++i) {
@@ -330,12 +340,13 @@ int oracle_recurrent(const double *q, const double *k, const double *v,
  *   q, k, v  -> bf16 (round to nearest, ties to even)
  *   g, beta  -> f32  (C conversion, round to nearest even)
  * y_out is the recurrence output in double (callers round to bf16 for
- * storage); state_out is double.
+ * storage); state_out is double.  mask [B,T] (NULL = all active) masks
+ * recurrence steps only, as in the pages (the conv runs over every token).
  */
 int oracle_layer_core(const uint16_t *qkv, const uint16_t *conv_w,
                       const uint16_t *conv_state_in, uint16_t *conv_state_out,
                       const uint16_t *a, const uint16_t *b,
-                      const float *A_log, const float *dt_bias,
+                      const float *A_log, const float *dt_bias, const unsigned char *mask,
                       const double *state_in, double *state_out, double *y_out,
                       int B, int T, int Hk, int Hv, int Dk, int Dv, int K,
                       double q_scale, double k_scale, double eps)
@@ -365,7 +376,7 @@ int oracle_layer_core(const uint16_t *qkv, const uint16_t *conv_w,
         g[i] = (double)(float)g[i];
         be[i] = (double)(float)be[i];
     }
-    rc = oracle_recurrent(q, k, v, g, be, state_in, state_out, y_out, B, T, Hk, Hv, Dk, Dv);
+    rc = oracle_recurrent(q, k, v, g, be, mask, state_in, state_out, y_out, B, T, Hk, Hv, Dk, Dv);
 done:
     free(q);
     free(k);

@@ -62,6 +62,29 @@ def matrix_form(q, k, v, g, beta, s0):
     return y, sT
 
 
+def matrix_form_masked(q, k, v, g, beta, s0, mask):
+    """The matrix form with masked steps: an inactive step maps S to itself
+    (A = I, B = 0) and outputs zero."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    rep = Hv // Hk
+    y = np.zeros((B, T, Hv, Dv))
+    sT = np.zeros((B, Hv, Dv, Dk))
+    for b in range(B):
+        for h in range(Hv):
+            hk = h // rep
+            S = np.zeros((Dv, Dk)) if s0 is None else s0[b, h].copy()
+            for t in range(T):
+                if not mask[b, t]:
+                    continue
+                kt = k[b, t, hk][:, None]
+                A = g[b, t, h] * (np.eye(Dk) - beta[b, t, h] * (kt @ kt.T))
+                S = S @ A + beta[b, t, h] * (v[b, t, h][:, None] @ kt.T)
+                y[b, t, h] = S @ q[b, t, hk]
+            sT[b, h] = S
+    return y, sT
+
+
 def relerr(a, b):
     return np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
 
@@ -151,6 +174,62 @@ def test_recurrence_matrix_form_on_tiny_workload():
     assert y.shape == (1, 64, w["Hv"], w["Dv"])
     assert relerr(y, y2) < 1e-12
     assert relerr(s, s2) < 1e-12
+
+
+# ------------------------------------------------------------ masked steps
+
+def test_masked_recurrence_matches_masked_matrix_form():
+    q, k, v, g, beta, s0 = rand_recurrence(40, 2, 9, 1, 2, 6, 4)
+    mask = rnd(41).random((2, 9)) < 0.6
+    mask[0, 0] = False
+    mask[1, -1] = False
+    y, s = oracle.recurrent(q, k, v, g, beta, s0, mask=mask)
+    y2, s2 = matrix_form_masked(q, k, v, g, beta, s0, mask)
+    assert relerr(y, y2) < 1e-12 and relerr(s, s2) < 1e-12
+    assert not np.any(y[~mask])
+
+
+def test_masked_run_equals_run_over_active_steps():
+    """Masking steps out equals dropping them from the sequence (per row):
+    same final state, and the active steps' outputs, bit for bit."""
+    q, k, v, g, beta, s0 = rand_recurrence(42, 3, 11, 2, 4, 5, 3)
+    mask = rnd(43).random((3, 11)) < 0.5
+    y, s = oracle.recurrent(q, k, v, g, beta, s0, mask=mask)
+    for b in range(3):
+        idx = np.flatnonzero(mask[b])
+        sl = lambda x: np.ascontiguousarray(x[b:b + 1, idx])
+        yc, sc = oracle.recurrent(sl(q), sl(k), sl(v), sl(g), sl(beta), s0[b:b + 1])
+        assert np.array_equal(sc[0], s[b])
+        assert np.array_equal(yc[0], y[b, idx])
+        assert np.array_equal(y[b, ~mask[b]], np.zeros_like(y[b, ~mask[b]]))
+
+
+def test_mask_all_on_and_all_off():
+    q, k, v, g, beta, s0 = rand_recurrence(44, 2, 6, 1, 2, 4, 4)
+    y, s = oracle.recurrent(q, k, v, g, beta, s0)
+    y1, s1 = oracle.recurrent(q, k, v, g, beta, s0, mask=np.ones((2, 6), bool))
+    assert np.array_equal(y, y1) and np.array_equal(s, s1)
+    y0, s0b = oracle.recurrent(q, k, v, g, beta, s0, mask=np.zeros((2, 6), bool))
+    assert np.array_equal(s0b, s0) and not np.any(y0)
+
+
+def test_layer_core_mask_touches_only_the_recurrence():
+    Hk, Hv, Dk, Dv = 2, 4, 8, 4
+    raw = small_layer(10, T=9, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv)
+    kw = dict(Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=0.125, k_scale=0.35)
+    B, T = raw["qkv"].shape[:2]
+    mask = rnd(45).random((B, T)) < 0.6
+    y, s, cs = oracle.layer_core(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
+                                 raw["A_log"], raw["dt_bias"], raw["state"], mask=mask, **kw)
+    _, _, cs_full = oracle.layer_core(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
+                                      raw["A_log"], raw["dt_bias"], raw["state"], **kw)
+    assert np.array_equal(cs, cs_full)       # the conv runs over every token
+    p = oracle.prep(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
+                    raw["A_log"], raw["dt_bias"], **kw)
+    r = lambda x: oracle.bf16_to_f64(oracle.round_bf16(x))
+    y2, s2 = oracle.recurrent(r(p["q"]), r(p["k"]), r(p["v"]), oracle.round_f32(p["g"]),
+                              oracle.round_f32(p["beta"]), raw["state"], mask=mask)
+    assert np.array_equal(y, y2) and np.array_equal(s, s2)
 
 
 def test_I1_beta0_g1_leaves_state():
