@@ -57,7 +57,7 @@ typedef enum gdn_status {
     GDN_ERR_HIP = -8           /* a kernel launch failed */
 } gdn_status;
 
-/* Library ABI version (incremented on any signature change). */
+/* Library ABI version (incremented when entry points are added or changed). */
 int gdn_version(void);
 
 /* Static name of a status code. */
@@ -91,6 +91,22 @@ gdn_status gdn_recurrent(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_bf16 *v
                          int B, int T, int Hk, int Hv, int Dk, int Dv, void *stream);
 
 /*
+ * gdn_recurrent_masked -- gdn_recurrent with a step mask.
+ * ("mlx-bun ... qwen3-delta.ts", the masked variant of the step kernel that
+ *  padded prefill selects: the whole step runs only where the mask is set.)
+ *
+ *   mask  [B,T] uint8, nonzero = active step; NULL = every step active
+ *         (then identical to gdn_recurrent).  Any alignment; read only.
+ * An inactive step leaves the state untouched (no decay, no update) and
+ * writes y_t = 0 (+0.0 in bf16).  Masking steps out equals dropping them from
+ * the sequence, row by row.  Other arguments as gdn_recurrent.
+ */
+gdn_status gdn_recurrent_masked(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_bf16 *v,
+                                const float *g, const float *beta, const uint8_t *mask,
+                                const float *state_in, float *state_out, gdn_bf16 *y,
+                                int B, int T, int Hk, int Hv, int Dk, int Dv, void *stream);
+
+/*
  * gdn_recurrent_chunked -- the same recurrence as gdn_recurrent, evaluated in
  * chunks of 32 steps on the matrix cores (equal to the per-step loop up to
  * rounding order): within a chunk the deltas of all steps solve one unit
@@ -108,6 +124,14 @@ gdn_status gdn_recurrent_chunked(const gdn_bf16 *q, const gdn_bf16 *k, const gdn
                                  const float *state_in, float *state_out, gdn_bf16 *y,
                                  void *workspace, size_t workspace_bytes,
                                  int B, int T, int Hk, int Hv, int Dk, int Dv, void *stream);
+
+/* gdn_recurrent_chunked with a step mask (semantics of gdn_recurrent_masked;
+ * NULL = every step active). */
+gdn_status gdn_recurrent_chunked_masked(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_bf16 *v,
+                                        const float *g, const float *beta, const uint8_t *mask,
+                                        const float *state_in, float *state_out, gdn_bf16 *y,
+                                        void *workspace, size_t workspace_bytes,
+                                        int B, int T, int Hk, int Hv, int Dk, int Dv, void *stream);
 
 /* Workspace bytes of gdn_recurrent_chunked (0 for unsupported sizes or
  * B*T == 0). */
@@ -175,6 +199,23 @@ gdn_status gdn_layer_core(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
                           void *workspace, size_t workspace_bytes,
                           int B, int T, int Hk, int Hv, int Dk, int Dv, int K,
                           float q_scale, float k_scale, float eps, void *stream);
+
+/*
+ * gdn_layer_core_masked -- gdn_layer_core with a step mask on the recurrence
+ * (semantics of gdn_recurrent_masked; NULL = every step active).  As on the
+ * pages, the mask applies to the recurrence only: the prologue (conv, norms,
+ * gates, conv_state_out) runs over every token.  Bit-identical to gdn_prep
+ * followed by gdn_recurrent_chunked_masked / gdn_recurrent_masked under the
+ * same rule as gdn_layer_core.
+ */
+gdn_status gdn_layer_core_masked(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
+                                 const gdn_bf16 *conv_state_in, gdn_bf16 *conv_state_out,
+                                 const gdn_bf16 *a, const gdn_bf16 *b,
+                                 const float *A_log, const float *dt_bias, const uint8_t *mask,
+                                 const float *state_in, float *state_out, gdn_bf16 *y,
+                                 void *workspace, size_t workspace_bytes,
+                                 int B, int T, int Hk, int Hv, int Dk, int Dv, int K,
+                                 float q_scale, float k_scale, float eps, void *stream);
 
 #ifdef __cplusplus
 }

@@ -49,6 +49,12 @@ def lib():
         L.gdn_last_error.restype = ctypes.c_char_p
         L.gdn_recurrent.argtypes = [_p] * 8 + [_i] * 6 + [_p]
         L.gdn_recurrent.restype = _i
+        L.gdn_recurrent_masked.argtypes = [_p] * 9 + [_i] * 6 + [_p]
+        L.gdn_recurrent_masked.restype = _i
+        L.gdn_recurrent_chunked_masked.argtypes = [_p] * 10 + [ctypes.c_size_t] + [_i] * 6 + [_p]
+        L.gdn_recurrent_chunked_masked.restype = _i
+        L.gdn_layer_core_masked.argtypes = [_p] * 13 + [ctypes.c_size_t] + [_i] * 7 + [_f] * 3 + [_p]
+        L.gdn_layer_core_masked.restype = _i
         L.gdn_prep.argtypes = [_p] * 13 + [_i] * 7 + [_f] * 3 + [_p]
         L.gdn_prep.restype = _i
         L.gdn_recurrent_chunked.argtypes = [_p] * 9 + [ctypes.c_size_t] + [_i] * 6 + [_p]
@@ -78,6 +84,7 @@ def _check(status: int):
 
 
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_MASK = (torch.uint8, torch.bool)
 
 
 def _ptr(t, name, dtypes, shape, device):
@@ -102,11 +109,11 @@ def _stream(device, stream):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def recurrent(q, k, v, g, beta, state_in, state_out, y, *, stream=None):
-    """Gated delta rule over T steps (gdn_recurrent).  q,k [B,T,Hk,Dk] bf16;
-    v [B,T,Hv,Dv] bf16; g,beta [B,T,Hv] f32; state_in [B,Hv,Dv,Dk] f32 or
-    None; state_out like state_in (may be the same tensor); y [B,T,Hv,Dv]
-    bf16 (written)."""
+def recurrent(q, k, v, g, beta, state_in, state_out, y, *, mask=None, stream=None):
+    """Gated delta rule over T steps (gdn_recurrent_masked).  q,k [B,T,Hk,Dk]
+    bf16; v [B,T,Hv,Dv] bf16; g,beta [B,T,Hv] f32; state_in [B,Hv,Dv,Dk] f32
+    or None; state_out like state_in (may be the same tensor); y [B,T,Hv,Dv]
+    bf16 (written); mask [B,T] uint8/bool or None (every step active)."""
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     dev = q.device
@@ -120,7 +127,8 @@ def recurrent(q, k, v, g, beta, state_in, state_out, y, *, stream=None):
         _ptr(state_out, "state_out", (torch.float32,), (B, Hv, Dv, Dk), dev),
         _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
     ]
-    _check(lib().gdn_recurrent(*args, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream)))
+    m = _ptr(mask, "mask", _MASK, (B, T), dev)
+    _check(lib().gdn_recurrent_masked(*args[:5], m, *args[5:], B, T, Hk, Hv, Dk, Dv, _stream(dev, stream)))
 
 
 def recurrent_chunked_workspace_bytes(B, T, Hk, Hv, Dk, Dv) -> int:
@@ -136,9 +144,9 @@ def _workspace(workspace, dev):
     return (workspace.data_ptr() if n else None), n
 
 
-def recurrent_chunked(q, k, v, g, beta, state_in, state_out, y, workspace, *, stream=None):
+def recurrent_chunked(q, k, v, g, beta, state_in, state_out, y, workspace, *, mask=None, stream=None):
     """The recurrence in 32-step chunks on the matrix cores
-    (gdn_recurrent_chunked).  Arguments as ``recurrent`` plus a device
+    (gdn_recurrent_chunked_masked).  Arguments as ``recurrent`` plus a device
     ``workspace`` tensor of at least ``recurrent_chunked_workspace_bytes``
     bytes."""
     B, T, Hk, Dk = q.shape
@@ -155,7 +163,9 @@ def recurrent_chunked(q, k, v, g, beta, state_in, state_out, y, workspace, *, st
         _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
     ]
     ws, nws = _workspace(workspace, dev)
-    _check(lib().gdn_recurrent_chunked(*args, ws, nws, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream)))
+    m = _ptr(mask, "mask", _MASK, (B, T), dev)
+    _check(lib().gdn_recurrent_chunked_masked(*args[:5], m, *args[5:], ws, nws, B, T, Hk, Hv, Dk, Dv,
+                                              _stream(dev, stream)))
 
 
 def prep(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, q, k, v, g, beta, *,
@@ -192,10 +202,11 @@ def layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv) -> int:
 
 def layer_core(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias,
                state_in, state_out, y, workspace, *, Hk, Hv, Dk, Dv, q_scale, k_scale,
-               eps=1e-6, stream=None):
-    """Prologue then recurrence (gdn_layer_core).  Arguments as ``prep`` and
-    ``recurrent``; ``workspace`` is a uint8/int8 device tensor of at least
-    ``layer_core_workspace_bytes(...)`` bytes (or None when that is 0)."""
+               eps=1e-6, mask=None, stream=None):
+    """Prologue then recurrence (gdn_layer_core_masked).  Arguments as
+    ``prep`` and ``recurrent``; ``workspace`` is a uint8/int8 device tensor of
+    at least ``layer_core_workspace_bytes(...)`` bytes (or None when that is
+    0); ``mask`` [B,T] masks recurrence steps (None = all active)."""
     B, T, C = qkv.shape
     K = conv_w.shape[1]
     dev = qkv.device
@@ -214,5 +225,6 @@ def layer_core(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias,
         _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
         ws_ptr,
     ]
-    _check(lib().gdn_layer_core(*args, ws_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps,
-                                _stream(dev, stream)))
+    m = _ptr(mask, "mask", _MASK, (B, T), dev)
+    _check(lib().gdn_layer_core_masked(*args[:8], m, *args[8:], ws_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale,
+                                       k_scale, eps, _stream(dev, stream)))

@@ -47,8 +47,8 @@
 //    W S_0^T - Tb V and of Q S_0^T over its columns, the four shares are summed
 //    through LDS (the only exchange, one barrier per chunk), and every wave
 //    then updates its state columns; two waves finish Y.
-// Padding steps past T carry g = 1, beta = 0 and zero k, q: their Delta is 0
-// and they leave S unchanged.
+// Padding steps past T and masked steps carry g = 1, beta = 0: their Delta is
+// 0 and they leave S unchanged (a masked step's y is written as zero).
 #include <algorithm>
 
 #include "gdn_device.h"
@@ -198,6 +198,7 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
                                                             const uint16_t* __restrict__ k,
                                                             const float* __restrict__ g,
                                                             const float* __restrict__ beta,
+                                                            const uint8_t* __restrict__ mask,
                                                             const uint16_t* __restrict__ v, ChunkPtrs o, int T,
                                                             int Hk, int Hv, int Dv, int NC) {
     __shared__ PrepSmem sh;
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
     const int lr = lane & 15, lq = lane >> 4;
     const NegOnes no = neg_ones();
 
-    // 1. k, q rows of the chunk (zero past T), g and beta (1 and 0 past T)
+    // 1. k, q rows of the chunk (zero past T), g and beta
     for (int idx = tid; idx < CK * DKC / 8; idx += 256) {
         const int t = idx / (DKC / 8), c8 = idx % (DKC / 8);
         uint4 kv = make_uint4(0, 0, 0, 0), qv = kv;
@@ -227,11 +228,14 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
         *reinterpret_cast<uint4*>(&sh.u.in.qb[t][c8 * 8]) = qv;
     }
     if (tid < CK) {
+        // steps past T and masked steps: g = 1, beta = 0 (no decay, no write)
         const int t = t0 + tid;
-        const int64_t i = ((int64_t)b * T + min(t, T - 1)) * Hv + hv;
+        const int64_t bt = (int64_t)b * T + min(t, T - 1);
+        const int64_t i = bt * Hv + hv;
         const float gv = g[i], bv = beta[i];
-        sh.gs[tid] = t < T ? gv : 1.f;
-        sh.bs[tid] = t < T ? bv : 0.f;
+        const bool on = t < T && (mask == nullptr || mask[bt] != 0);
+        sh.gs[tid] = on ? gv : 1.f;
+        sh.bs[tid] = on ? bv : 0.f;
     }
     __syncthreads();
 
@@ -539,8 +543,9 @@ struct SeqSmem {
 
 __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const float* state_in,
                                                                 float* state_out, uint16_t* __restrict__ y,
-                                                                int T, int Hk, int Hv, int Dv, int NC,
-                                                                int row_blocks, int n_blocks) {
+                                                                const uint8_t* __restrict__ mask, int T, int Hk,
+                                                                int Hv, int Dv, int NC, int row_blocks,
+                                                                int n_blocks) {
     __shared__ SeqSmem sh;
 
     int lb = blockIdx.x;
@@ -584,10 +589,13 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
                 ys = mma(dm, ch, ys);
                 ys = mma(dh, cm, ys);
                 ys = mma(dh, ch, ys);
-                if (cp * CK + yt < T)
+                const int t = cp * CK + yt;
+                if (t < T) {
+                    u2_t w = {pack_bf16x2(ys[0], ys[1]), pack_bf16x2(ys[2], ys[3])};
+                    if (mask != nullptr && mask[(int64_t)b * T + t] == 0) w = u2_t{0, 0};   // masked step
                     *reinterpret_cast<__attribute__((address_space(1))) u2_t*>(
-                        uniform_ptr_w(y0 + (int64_t)cp * CK * vstride) + yoff) =
-                        u2_t{pack_bf16x2(ys[0], ys[1]), pack_bf16x2(ys[2], ys[3])};
+                        uniform_ptr_w(y0 + (int64_t)cp * CK * vstride) + yoff) = w;
+                }
                 b3 = b3 == 2 ? 0 : b3 + 1;
             }
             ch = nh;
@@ -746,8 +754,8 @@ hipError_t launch_recurrent_chunked(const RecurrentArgs& a, void* ws, hipStream_
     o.qsw = reinterpret_cast<u4_t*>(base + L.qsw);
     o.ksw = reinterpret_cast<u4_t*>(base + L.ksw);
     const int64_t units = (int64_t)a.B * a.Hv * L.nc;
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g, a.beta, a.v,
-                       o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
+    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g, a.beta,
+                       a.mask, a.v, o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     SeqIn in;
@@ -760,8 +768,7 @@ hipError_t launch_recurrent_chunked(const RecurrentArgs& a, void* ws, hipStream_
     const int row_blocks = a.Dv / RB;
     const int64_t blocks = (int64_t)a.B * a.Hv * row_blocks;
     hipLaunchKernelGGL(chunk_seq_kernel, dim3((unsigned)blocks), dim3(SEQ_THREADS), 0, stream, in, a.state_in,
-                       a.state_out,
-                       a.y, a.T, a.Hk, a.Hv, a.Dv, L.nc, row_blocks, (int)blocks);
+                       a.state_out, a.y, a.mask, a.T, a.Hk, a.Hv, a.Dv, L.nc, row_blocks, (int)blocks);
     return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kVersion = 1;
+constexpr int kVersion = 2;
 constexpr int64_t kMaxBlocks = (1LL << 31) - 1;
 
 thread_local char g_err[512] = "";
@@ -38,6 +38,7 @@ struct Span {
     const void* p;
     uint64_t bytes;
     bool output;
+    unsigned align = 16;    // required alignment of p in bytes
 };
 
 // Element-count product with overflow detection (all factors >= 0).
@@ -71,8 +72,8 @@ gdn_status check_dims(int B, int T, int Hk, int Hv, int Dk, int Dv) {
 
 gdn_status check_spans(const std::vector<Span>& s, const std::vector<std::pair<int, int>>& alias_ok) {
     for (const Span& x : s) {
-        if (x.p && (reinterpret_cast<uintptr_t>(x.p) & 15u))
-            return fail(GDN_ERR_MISALIGNED, "%s is not 16-byte aligned", x.name);
+        if (x.p && (reinterpret_cast<uintptr_t>(x.p) & (x.align - 1u)))
+            return fail(GDN_ERR_MISALIGNED, "%s is not %u-byte aligned", x.name, x.align);
     }
     for (size_t i = 0; i < s.size(); ++i) {
         for (size_t j = i + 1; j < s.size(); ++j) {
@@ -100,8 +101,9 @@ gdn_status hip_result(hipError_t e, const char* what) {
 // ------------------------------------------------------------ recurrent --
 
 gdn_status validate_recurrent(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,
-                              const float* beta, const float* state_in, float* state_out, gdn_bf16* y,
-                              int B, int T, int Hk, int Hv, int Dk, int Dv, bool check_overlap = true) {
+                              const float* beta, const uint8_t* mask, const float* state_in, float* state_out,
+                              gdn_bf16* y, int B, int T, int Hk, int Hv, int Dk, int Dv,
+                              bool check_overlap = true) {
     gdn_status st = check_dims(B, T, Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
     uint64_t nqk, nv, ng, ns;
@@ -124,6 +126,7 @@ gdn_status validate_recurrent(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf
         {"v", v, nv * 2, false},         {"g", g, ng * 4, false},
         {"beta", beta, ng * 4, false},   {"state_in", state_in, ns * 4, false},
         {"state_out", state_out, ns * 4, true}, {"y", y, nv * 2, true},
+        {"mask", mask, (uint64_t)B * T, false, 1},
     };
     return check_spans(s, {{5, 6}});
 }
@@ -239,14 +242,20 @@ const char* gdn_status_string(int status) {
 
 const char* gdn_last_error(void) { return g_err; }
 
+gdn_status gdn_recurrent_masked(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,
+                                const float* beta, const uint8_t* mask, const float* state_in, float* state_out,
+                                gdn_bf16* y, int B, int T, int Hk, int Hv, int Dk, int Dv, void* stream) {
+    gdn_status st = validate_recurrent(q, k, v, g, beta, mask, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv);
+    if (st != GDN_OK) return st;
+    if (B == 0) return ok();
+    gdn::RecurrentArgs a{q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, mask};
+    return hip_result(gdn::launch_recurrent(a, static_cast<hipStream_t>(stream)), "recurrent");
+}
+
 gdn_status gdn_recurrent(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,
                          const float* beta, const float* state_in, float* state_out, gdn_bf16* y, int B,
                          int T, int Hk, int Hv, int Dk, int Dv, void* stream) {
-    gdn_status st = validate_recurrent(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv);
-    if (st != GDN_OK) return st;
-    if (B == 0) return ok();
-    gdn::RecurrentArgs a{q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv};
-    return hip_result(gdn::launch_recurrent(a, static_cast<hipStream_t>(stream)), "recurrent");
+    return gdn_recurrent_masked(q, k, v, g, beta, nullptr, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, stream);
 }
 
 size_t gdn_recurrent_chunked_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv) {
@@ -256,11 +265,12 @@ size_t gdn_recurrent_chunked_workspace_bytes(int B, int T, int Hk, int Hv, int D
     return (size_t)chunked_bytes(B, T, Hk, Hv, Dk, Dv);
 }
 
-gdn_status gdn_recurrent_chunked(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,
-                                 const float* beta, const float* state_in, float* state_out, gdn_bf16* y,
-                                 void* workspace, size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk,
-                                 int Dv, void* stream) {
-    gdn_status st = validate_recurrent(q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv);
+gdn_status gdn_recurrent_chunked_masked(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v,
+                                        const float* g, const float* beta, const uint8_t* mask,
+                                        const float* state_in, float* state_out, gdn_bf16* y, void* workspace,
+                                        size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk, int Dv,
+                                        void* stream) {
+    gdn_status st = validate_recurrent(q, k, v, g, beta, mask, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
     if (!gdn::chunked_supported(Hv, Dk, Dv))
         return fail(GDN_ERR_UNSUPPORTED,
@@ -286,16 +296,24 @@ gdn_status gdn_recurrent_chunked(const gdn_bf16* q, const gdn_bf16* k, const gdn
             {"v", v, nv * 2, false},       {"g", g, ng * 4, false},
             {"beta", beta, ng * 4, false}, {"state_in", state_in, ns * 4, false},
             {"state_out", state_out, ns * 4, true}, {"y", y, nv * 2, true},
-            {"workspace", workspace, need, true},
+            {"workspace", workspace, need, true}, {"mask", mask, (uint64_t)B * T, false, 1},
         };
         st = check_spans(s, {{5, 6}});
         if (st != GDN_OK) return st;
     }
     if (B == 0) return ok();
-    gdn::RecurrentArgs a{q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv};
+    gdn::RecurrentArgs a{q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, mask};
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (T == 0) return hip_result(gdn::launch_recurrent(a, s), "recurrent");
     return hip_result(gdn::launch_recurrent_chunked(a, workspace, s), "chunked recurrent");
+}
+
+gdn_status gdn_recurrent_chunked(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,
+                                 const float* beta, const float* state_in, float* state_out, gdn_bf16* y,
+                                 void* workspace, size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk,
+                                 int Dv, void* stream) {
+    return gdn_recurrent_chunked_masked(q, k, v, g, beta, nullptr, state_in, state_out, y, workspace,
+                                        workspace_bytes, B, T, Hk, Hv, Dk, Dv, stream);
 }
 
 gdn_status gdn_prep(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_bf16* conv_state_in,
@@ -320,11 +338,12 @@ size_t gdn_layer_core_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int 
     return (size_t)w.total;
 }
 
-gdn_status gdn_layer_core(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_bf16* conv_state_in,
-                          gdn_bf16* conv_state_out, const gdn_bf16* a, const gdn_bf16* b, const float* A_log,
-                          const float* dt_bias, const float* state_in, float* state_out, gdn_bf16* y,
-                          void* workspace, size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk,
-                          int Dv, int K, float q_scale, float k_scale, float eps, void* stream) {
+gdn_status gdn_layer_core_masked(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_bf16* conv_state_in,
+                                 gdn_bf16* conv_state_out, const gdn_bf16* a, const gdn_bf16* b,
+                                 const float* A_log, const float* dt_bias, const uint8_t* mask,
+                                 const float* state_in, float* state_out, gdn_bf16* y, void* workspace,
+                                 size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk, int Dv, int K,
+                                 float q_scale, float k_scale, float eps, void* stream) {
     gdn_status st = check_dims(B, T, Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
     Workspace w;
@@ -350,7 +369,7 @@ gdn_status gdn_layer_core(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn
     st = validate_prep(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, wq, wk, wv, wg, wb, B, T,
                        Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps, false);
     if (st != GDN_OK) return st;
-    st = validate_recurrent(wq, wk, wv, wg, wb, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, false);
+    st = validate_recurrent(wq, wk, wv, wg, wb, mask, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, false);
     if (st != GDN_OK) return st;
     if (w.use_chunked && gdn::chunked_blocks(B, T, Hv, Dv) > kMaxBlocks) return fail(GDN_ERR_BAD_DIMS, "grid too large");
     {
@@ -375,6 +394,7 @@ gdn_status gdn_layer_core(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn
             {"state_out", state_out, ns * 4, true},
             {"y", y, nv * 2, true},
             {"workspace", workspace, w.total, true},
+            {"mask", mask, (uint64_t)B * T, false, 1},
         };
         st = check_spans(s, {{2, 3}, {8, 9}});
         if (st != GDN_OK) return st;
@@ -387,9 +407,19 @@ gdn_status gdn_layer_core(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn
         st = hip_result(gdn::launch_prep(p, s), "prep");
         if (st != GDN_OK) return st;
     }
-    gdn::RecurrentArgs r{wq, wk, wv, wg, wb, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv};
+    gdn::RecurrentArgs r{wq, wk, wv, wg, wb, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, mask};
     if (w.use_chunked) return hip_result(gdn::launch_recurrent_chunked(r, ws + w.chunked, s), "chunked recurrent");
     return hip_result(gdn::launch_recurrent(r, s), "recurrent");
+}
+
+gdn_status gdn_layer_core(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_bf16* conv_state_in,
+                          gdn_bf16* conv_state_out, const gdn_bf16* a, const gdn_bf16* b, const float* A_log,
+                          const float* dt_bias, const float* state_in, float* state_out, gdn_bf16* y,
+                          void* workspace, size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk,
+                          int Dv, int K, float q_scale, float k_scale, float eps, void* stream) {
+    return gdn_layer_core_masked(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, nullptr,
+                                 state_in, state_out, y, workspace, workspace_bytes, B, T, Hk, Hv, Dk, Dv, K,
+                                 q_scale, k_scale, eps, stream);
 }
 
 }  // extern "C"

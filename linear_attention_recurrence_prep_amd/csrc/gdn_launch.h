@@ -17,6 +17,7 @@ struct RecurrentArgs {
     float* state_out;
     uint16_t* y;
     int B, T, Hk, Hv, Dk, Dv;
+    const uint8_t* mask = nullptr;   // [B, T] step mask (0 = inactive), may be null
 };
 
 struct PrepArgs {

@@ -94,8 +94,9 @@ struct ChunkStage {
 
     __device__ __forceinline__ void load(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                          const uint16_t* __restrict__ v, const float* __restrict__ g,
-                                         const float* __restrict__ beta, int b, int hk, int hv, int dv0,
-                                         int t0, int T, int Hk, int Hv, int Dv, int tid) {
+                                         const float* __restrict__ beta, const uint8_t* __restrict__ mask,
+                                         int b, int hk, int hv, int dv0, int t0, int T, int Hk, int Hv, int Dv,
+                                         int tid) {
         // indices past T / Dv are clamped; those values are never consumed
 #pragma unroll
         for (int i = 0; i < CC::PPT; ++i) {
@@ -113,11 +114,15 @@ struct ChunkStage {
             vr[i] = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t) * Hv + hv) * Dv + row);
         }
         {
+            // padding steps past T and masked steps: g = 1, beta = 0 (the state
+            // stays as it is; a masked step's y is written as zero at the flush)
             const int t = t0 + tid % TC;
-            const int64_t i = ((int64_t)b * T + min(t, T - 1)) * Hv + hv;
+            const int64_t bt = (int64_t)b * T + min(t, T - 1);
+            const int64_t i = bt * Hv + hv;
             const bool is_g = (tid % (2 * TC)) < TC;
             const float x = is_g ? g[i] : beta[i];
-            gb = t < T ? x : (is_g ? 1.f : 0.f);   // padding steps: g = 1, beta = 0
+            const bool on = t < T && (mask == nullptr || mask[bt] != 0);
+            gb = on ? x : (is_g ? 1.f : 0.f);
         }
     }
 
@@ -193,8 +198,9 @@ __device__ __forceinline__ void run_chunk(const ChunkBuf<DK, TC>& sb, float (&s)
 }
 
 template <int DK, int TC>
-__device__ __forceinline__ void flush_y(const ChunkSmem<DK, TC>& sh, uint16_t* __restrict__ y, int b, int hv,
-                                        int dv0, int tbase, int nsteps, int T, int Hv, int Dv, int tid) {
+__device__ __forceinline__ void flush_y(const ChunkSmem<DK, TC>& sh, uint16_t* __restrict__ y,
+                                        const uint8_t* __restrict__ mask, int b, int hv, int dv0, int tbase,
+                                        int nsteps, int T, int Hv, int Dv, int tid) {
     using C = RecCfg<DK>;
     const int nvec = nsteps * (C::ROWS / 8);
     for (int idx = tid; idx < nvec; idx += C::NT) {
@@ -202,16 +208,18 @@ __device__ __forceinline__ void flush_y(const ChunkSmem<DK, TC>& sh, uint16_t* _
         const int part = idx % (C::ROWS / 8);
         const int t = tbase + step;
         const int r = dv0 + part * 8;
-        if (t < T && r < Dv)
-            *reinterpret_cast<uint4*>(y + (((int64_t)b * T + t) * Hv + hv) * Dv + r) =
-                *reinterpret_cast<const uint4*>(&sh.y[step][part * 8]);
+        if (t < T && r < Dv) {
+            uint4 w = *reinterpret_cast<const uint4*>(&sh.y[step][part * 8]);
+            if (mask != nullptr && mask[(int64_t)b * T + t] == 0) w = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(y + (((int64_t)b * T + t) * Hv + hv) * Dv + r) = w;
+        }
     }
 }
 
 template <int DK, int TC>
 __global__ __launch_bounds__(256) void recurrent_chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta,
+    const float* __restrict__ g, const float* __restrict__ beta, const uint8_t* __restrict__ mask,
     const float* state_in, float* state_out, uint16_t* __restrict__ y,
     int T, int Hk, int Hv, int Dv, int row_blocks, int n_blocks) {
     using C = RecCfg<DK>;
@@ -249,7 +257,7 @@ __global__ __launch_bounds__(256) void recurrent_chunk_kernel(
 
     const int nchunks = (T + TC - 1) / TC;   // >= 1 (this kernel runs for T > 0)
     ChunkStage<DK, TC> st;
-    st.load(q, k, v, g, beta, b, hk, hv, dv0, 0, T, Hk, Hv, Dv, tid);
+    st.load(q, k, v, g, beta, mask, b, hk, hv, dv0, 0, T, Hk, Hv, Dv, tid);
     __builtin_amdgcn_s_waitcnt(0);           // state and chunk 0 resident
     st.store(sh.buf[0], tid);
     __syncthreads();
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(256) void recurrent_chunk_kernel(
     int ybase = 0;                           // first step held in sh.y
     for (int c = 0; c < nchunks; ++c) {
         const int t0 = c * TC;
-        if (c + 1 < nchunks) st.load(q, k, v, g, beta, b, hk, hv, dv0, t0 + TC, T, Hk, Hv, Dv, tid);
+        if (c + 1 < nchunks) st.load(q, k, v, g, beta, mask, b, hk, hv, dv0, t0 + TC, T, Hk, Hv, Dv, tid);
         float yr[NY];
         run_chunk<DK, TC>(sh.buf[c & 1], s, yr, j, rloc);
         // y of this chunk -> LDS (bf16); each lane holds steps t = i*L + j
@@ -271,7 +279,7 @@ __global__ __launch_bounds__(256) void recurrent_chunk_kernel(
         __syncthreads();
         const bool last = c + 1 == nchunks;
         if (last || yoff + TC == CC::YSTEPS) {
-            flush_y<DK, TC>(sh, y, b, hv, dv0, ybase, yoff + TC, T, Hv, Dv, tid);
+            flush_y<DK, TC>(sh, y, mask, b, hv, dv0, ybase, yoff + TC, T, Hv, Dv, tid);
             ybase = t0 + TC;
             if (!last) __syncthreads();      // sh.y is rewritten by the next chunk
         }
@@ -293,7 +301,7 @@ __global__ __launch_bounds__(256) void recurrent_chunk_kernel(
 template <int DK>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta,
+    const float* __restrict__ g, const float* __restrict__ beta, const uint8_t* __restrict__ mask,
     const float* state_in, float* state_out, uint16_t* __restrict__ y,
     int T, int Hk, int Hv, int Dv, int row_blocks, int n_blocks) {
     using C = RecCfg<DK>;
@@ -326,6 +334,10 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
 
     for (int t = 0; t < T; ++t) {
         const int64_t tok = (int64_t)b * T + t;
+        if (mask != nullptr && mask[tok] == 0) {      // masked step: state kept, y = 0
+            if (j == 0 && row_ok) y[(tok * Hv + hv) * Dv + row] = 0;
+            continue;
+        }
         const uint16_t* kp = k + (tok * Hk + hk) * DK;
         const uint16_t* qp = q + (tok * Hk + hk) * DK;
         const uint2 kw0 = *reinterpret_cast<const uint2*>(kp + 4 * j);
@@ -378,12 +390,12 @@ static hipError_t launch_rec(const RecurrentArgs& a, hipStream_t stream, bool ch
     if (blocks <= 0) return hipSuccess;
     if (chunked)
         hipLaunchKernelGGL((recurrent_chunk_kernel<DK, TC>), dim3((unsigned)blocks), dim3(C::NT), 0, stream,
-                           a.q, a.k, a.v, a.g, a.beta, a.state_in, a.state_out, a.y, a.T, a.Hk, a.Hv, a.Dv,
-                           row_blocks, (int)blocks);
+                           a.q, a.k, a.v, a.g, a.beta, a.mask, a.state_in, a.state_out, a.y, a.T, a.Hk, a.Hv,
+                           a.Dv, row_blocks, (int)blocks);
     else
         hipLaunchKernelGGL((recurrent_step_kernel<DK>), dim3((unsigned)blocks), dim3(C::NT), 0, stream,
-                           a.q, a.k, a.v, a.g, a.beta, a.state_in, a.state_out, a.y, a.T, a.Hk, a.Hv, a.Dv,
-                           row_blocks, (int)blocks);
+                           a.q, a.k, a.v, a.g, a.beta, a.mask, a.state_in, a.state_out, a.y, a.T, a.Hk, a.Hv,
+                           a.Dv, row_blocks, (int)blocks);
     return hipGetLastError();
 }
 

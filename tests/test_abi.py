@@ -205,3 +205,40 @@ def test_recurrent_chunked_rejects(L):
     assert call_chunked(L, Dk=128, ws=addr(7)) == OVERLAP          # workspace over y
     assert call_chunked(L, Dk=128, q=None) == NULLP
     assert call_chunked(L, Dk=128, B=0) == OK
+
+
+def call_rec_masked(L, mask, **over):
+    p, d = rec_args(**over)
+    return L.gdn_recurrent_masked(p["q"], p["k"], p["v"], p["g"], p["beta"], mask, p["state_in"],
+                                  p["state_out"], p["y"], d["B"], d["T"], d["Hk"], d["Hv"], d["Dk"], d["Dv"], None)
+
+
+def call_chunked_masked(L, mask, ws=addr(20), ws_bytes=1 << 32, **over):
+    p, d = rec_args(**over)
+    return L.gdn_recurrent_chunked_masked(p["q"], p["k"], p["v"], p["g"], p["beta"], mask, p["state_in"],
+                                          p["state_out"], p["y"], ws, ctypes.c_size_t(ws_bytes), d["B"], d["T"],
+                                          d["Hk"], d["Hv"], d["Dk"], d["Dv"], None)
+
+
+def test_masked_entry_points_validate_the_mask(L):
+    # a mask byte array may sit at any address: validation gets past it and stops at the
+    # (too small) workspace, which is checked later
+    assert call_chunked_masked(L, addr(9) + 3, Dk=128, ws_bytes=1000) == WS
+    # ... but it must not overlap an output
+    assert call_rec_masked(L, addr(7) + 1) == OVERLAP               # inside y
+    assert call_rec_masked(L, addr(6) + 5) == OVERLAP               # inside state_out
+    assert call_chunked_masked(L, addr(20) + 7, Dk=128) == OVERLAP  # inside the workspace
+    assert call_rec_masked(L, addr(9) + 1, Dk=48) == UNSUP
+    assert call_rec_masked(L, addr(9), B=0) == OK
+    assert call_chunked_masked(L, None, Dk=128, B=0) == OK
+
+
+def test_masked_layer_core_rejects(L):
+    p, d = prep_args()
+    f = lambda mask, y=addr(15): L.gdn_layer_core_masked(
+        p["qkv"], p["conv_w"], p["cs_in"], p["cs_out"], p["a"], p["b"], p["A_log"], p["dt_bias"], mask,
+        addr(13), addr(14), y, addr(20), ctypes.c_size_t(1 << 30), d["B"], d["T"], d["Hk"], d["Hv"],
+        d["Dk"], d["Dv"], d["K"], d["q_scale"], d["k_scale"], d["eps"], None)
+    assert f(addr(15) + 1) == OVERLAP      # mask inside y
+    assert f(addr(20) + 3) == OVERLAP      # mask inside the workspace
+    assert f(addr(9), y=addr(14)) == OVERLAP

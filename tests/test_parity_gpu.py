@@ -39,21 +39,22 @@ def rec_inputs(B, T, Hk, Hv, Dk, Dv, wid, state=True):
     return ri
 
 
-def gpu_recurrent(ri, state_dev="copy", y_guard=True):
-    """Run gdn_recurrent on device copies of ri; returns (y bits, state f32)."""
+def gpu_recurrent(ri, state_dev="copy", y_guard=True, mask=None):
+    """Run gdn_recurrent(_masked) on device copies of ri; returns (y bits, state f32)."""
     B, T, Hk, Dk = ri["q"].shape
     Hv, Dv = ri["v"].shape[2:]
     d = {k: H.to_dev(ri[k]) for k in ("q", "k", "v", "g", "beta")}
     s_in = H.to_dev(ri["state"]) if ri["state"] is not None else None
     yfull, y = H.guarded((B, T, Hv, Dv), torch.int16, NAN_BF16)
     sfull, s_out = H.guarded((B, Hv, Dv, Dk), torch.float32, float("nan"))
-    binding.recurrent(d["q"], d["k"], d["v"], d["g"], d["beta"], s_in, s_out, y)
+    m = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).to(H.DEV)
+    binding.recurrent(d["q"], d["k"], d["v"], d["g"], d["beta"], s_in, s_out, y, mask=m)
     torch.cuda.synchronize()
     assert H.guards_intact(yfull, NAN_BF16) and H.guards_intact(sfull, float("nan")), "guard band written"
     return H.bits(y), H.f32(s_out)
 
 
-def gpu_recurrent_chunked(ri, in_place=False):
+def gpu_recurrent_chunked(ri, in_place=False, mask=None):
     """Run gdn_recurrent_chunked on device copies of ri; returns (y bits, state)."""
     B, T, Hk, Dk = ri["q"].shape
     Hv, Dv = ri["v"].shape[2:]
@@ -66,7 +67,8 @@ def gpu_recurrent_chunked(ri, in_place=False):
         sfull, s_out = H.guarded((B, Hv, Dv, Dk), torch.float32, float("nan"))
     nws = binding.recurrent_chunked_workspace_bytes(B, T, Hk, Hv, Dk, Dv)
     wfull, ws = H.guarded((max(nws, 1),), torch.uint8, 0xA5)
-    binding.recurrent_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], s_in, s_out, y, ws)
+    m = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).to(H.DEV)
+    binding.recurrent_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], s_in, s_out, y, ws, mask=m)
     torch.cuda.synchronize()
     assert H.guards_intact(yfull, NAN_BF16), "y guard band written"
     assert sfull is None or H.guards_intact(sfull, float("nan")), "state guard band written"
@@ -274,7 +276,7 @@ def test_prep_conv_state_in_place_and_T0():
 
 # ------------------------------------------------------------- layer core
 
-def gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks, eps=1e-6):
+def gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks, eps=1e-6, mask=None):
     B, T, C = raw["qkv"].shape
     K = raw["conv_w"].shape[1]
     d = {k: H.to_dev(raw[k]) for k in ("qkv", "conv_w", "conv_state", "a", "b", "A_log", "dt_bias",
@@ -284,9 +286,10 @@ def gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks, eps=1e-6):
     cs_out = torch.empty(B, K - 1, C, dtype=torch.int16, device=H.DEV)
     nws = binding.layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=H.DEV)
+    m = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).to(H.DEV)
     binding.layer_core(d["qkv"], d["conv_w"], d["conv_state"], cs_out, d["a"], d["b"], d["A_log"],
                        d["dt_bias"], d["state"], s_out, y, ws, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv,
-                       q_scale=qs, k_scale=ks, eps=eps)
+                       q_scale=qs, k_scale=ks, eps=eps, mask=m)
     torch.cuda.synchronize()
     return H.bits(y), H.f32(s_out), H.bits(cs_out)
 
@@ -553,3 +556,87 @@ def test_recurrent_chunked_long_head_drift():
     H.check_y(y, y_ref, "long head")
     e = H.check_state(s, s_ref, 1e-3, "long head")
     say("long head state err", e)
+
+
+# ------------------------------------------------------------ masked steps
+
+def step_mask(seed, B, T, p=0.7):
+    """A random step mask with runs of inactive steps (left padding on row 0)."""
+    r = np.random.default_rng(seed)
+    m = r.random((B, T)) < p
+    m[0, : max(1, T // 5)] = False
+    return m.astype(np.uint8)
+
+
+MASK_CASES = [
+    # B, T, Hk, Hv, Dk, Dv, wid, form
+    (2, 5, 2, 4, 64, 32, 500, "per-step"),        # staging-free kernel (T < 8)
+    (2, 77, 1, 2, 32, 16, 501, "per-step"),       # staged kernel, ragged chunks
+    (1, 150, 2, 4, 128, 64, 502, "per-step"),
+    (2, 150, 2, 4, 128, 64, 503, "chunked"),
+    (3, 40, 1, 2, 128, 16, 504, "chunked"),
+]
+
+
+def run_form(form, ri, mask):
+    return gpu_recurrent_chunked(ri, mask=mask) if form == "chunked" else gpu_recurrent(ri, mask=mask)
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=lambda c: "B%dT%dHk%dHv%dDk%dDv%d-%s" % (c[:6] + (c[7],)))
+def test_masked_recurrence_matches_oracle(case):
+    B, T, Hk, Hv, Dk, Dv, wid, form = case
+    say("masked", case)
+    ri = rec_inputs(B, T, Hk, Hv, Dk, Dv, wid)
+    mask = step_mask(wid, B, T)
+    y, s = run_form(form, ri, mask)
+    f = oracle.bf16_to_f64
+    y_ref, s_ref = oracle.recurrent(f(ri["q"]), f(ri["k"]), f(ri["v"]), ri["g"].astype(np.float64),
+                                    ri["beta"].astype(np.float64), ri["state"].astype(np.float64), mask=mask)
+    H.check_y(y, y_ref, str(case))
+    assert not y[mask == 0].any(), "masked steps must write +0"
+    e = H.check_state(s, s_ref, 1e-4, str(case))
+    say("masked state err", e)
+
+
+@pytest.mark.parametrize("form", ["per-step", "chunked"])
+def test_mask_all_on_equals_no_mask_and_all_off_keeps_state(form):
+    ri = rec_inputs(2, 70, 2, 4, 128, 32, 505)
+    y, s = run_form(form, ri, None)
+    y1, s1 = run_form(form, ri, np.ones((2, 70), np.uint8))
+    assert np.array_equal(y, y1) and np.array_equal(s, s1)
+    y0, s0 = run_form(form, ri, np.zeros((2, 70), np.uint8))
+    assert not y0.any()
+    assert np.array_equal(s0, ri["state"])
+
+
+def test_per_step_masked_equals_run_over_active_steps():
+    """Per-step form: masking steps out is bit-identical to dropping them."""
+    ri = rec_inputs(2, 60, 2, 4, 64, 32, 506)
+    mask = step_mask(506, 2, 60)
+    y, s = gpu_recurrent(ri, mask=mask)
+    for b in range(2):
+        idx = np.flatnonzero(mask[b])
+        assert len(idx) >= 8           # both runs take the same (staged) kernel
+        sub = {k: np.ascontiguousarray(ri[k][b:b + 1, idx]) for k in ("q", "k", "v", "g", "beta")}
+        yc, sc = gpu_recurrent(dict(sub, state=ri["state"][b:b + 1]))
+        assert np.array_equal(yc[0], y[b, idx])
+        assert np.array_equal(sc[0], s[b])
+
+
+@pytest.mark.parametrize("T", [40, 96], ids=["per-step", "chunked"])
+def test_masked_layer_core_matches_oracle_and_composition(T):
+    B, Hk, Hv, Dk, Dv, K = 2, 2, 4, 128, 32, 4
+    raw = layer_inputs(B, T, Hk, Hv, Dk, Dv, K, 507)
+    qs, ks = 1.0 / Dk, Dk ** -0.5
+    mask = step_mask(507, B, T)
+    y, s, cs = gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks, mask=mask)
+    y_ref, s_ref, cs_ref = oracle.layer_core(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
+                                             raw["A_log"], raw["dt_bias"], raw["state"], Hk=Hk, Hv=Hv, Dk=Dk,
+                                             Dv=Dv, q_scale=qs, k_scale=ks, mask=mask)
+    H.check_y(y, y_ref, f"T={T}")
+    H.check_state(s, s_ref, CORE_STATE_TOL, f"T={T}")
+    assert np.array_equal(cs, cs_ref) and not y[mask == 0].any()
+    p = gpu_prep(raw, Hk, Hv, Dk, Dv, qs, ks)
+    ri = dict(q=p["q"], k=p["k"], v=p["v"], g=p["g"], beta=p["beta"], state=raw["state"])
+    y2, s2 = run_form("chunked" if T >= 64 else "per-step", ri, mask)
+    assert np.array_equal(y, y2) and np.array_equal(s, s2)
