@@ -60,6 +60,8 @@ def lib():
                                         _dp, _dp, _dp,
                                         _i, _i, _i, _i, _i, _i, _i, _d, _d, _d]
         L.oracle_layer_core.restype = _i
+        L.oracle_gated_rmsnorm.argtypes = [_hp, _hp, _hp, _dp, ctypes.c_long, _i, _d]
+        L.oracle_gated_rmsnorm.restype = _i
         L.oracle_rms_scale.argtypes = [_dp, _dp, ctypes.c_long, _i, _d, _d]
         L.oracle_rms_scale.restype = None
         L.oracle_gates.argtypes = [_hp, _hp, _fp, _fp, _dp, _dp, ctypes.c_long, _i]
@@ -211,6 +213,21 @@ def layer_core(qkv, conv_w, conv_state_in, a, b, A_log, dt_bias, state_in=None, 
     if rc != 0:
         raise RuntimeError("oracle_layer_core failed")
     return y, s, cs
+
+
+def gated_rmsnorm(y, z, norm_weight, eps=1e-6):
+    """Output epilogue in fp64: silu(z) * rms_norm(y) * norm_weight per row of
+    Dv values, from stored bf16 bits y, z [..., Dv] and norm_weight [Dv].
+    Returns float64 of y's shape (round_bf16 gives the stored result)."""
+    y, z, w = _h(y), _h(z), _h(norm_weight)
+    Dv = y.shape[-1]
+    assert z.shape == y.shape and w.shape == (Dv,)
+    out = np.empty(y.shape)
+    rc = lib().oracle_gated_rmsnorm(_ptr(y, _hp), _ptr(z, _hp), _ptr(w, _hp), _ptr(out, _dp),
+                                    y.size // Dv, Dv, float(eps))
+    if rc != 0:
+        raise RuntimeError("oracle_gated_rmsnorm failed")
+    return out
 
 
 def rms_scale(x, scale, eps=1e-6):

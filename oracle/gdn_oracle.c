@@ -385,3 +385,36 @@ done:
     free(be);
     return rc;
 }
+
+/* ------------------------------------------------------- output epilogue */
+
+/*
+ * Gated RMS normalisation of the recurrence output ([mlex]
+ * GatedDeltaNet::forward, the step after the recurrence loop): the stored
+ * bf16 y is widened, each row of Dv values (one token of one v-head) is
+ * normalised with no weight inside the norm, scaled by the per-channel
+ * norm_weight (shared by all heads), and gated by silu(z):
+ *   out[r][d] = silu(z[r][d]) * (y[r][d] / sqrt(mean_d y[r][d]^2 + eps) * w[d])
+ * y, z are [rows, Dv] bf16, w is [Dv] bf16; out is double (callers round to
+ * bf16 for storage, as the page casts the f32 result to the input dtype).
+ */
+int oracle_gated_rmsnorm(const uint16_t *y, const uint16_t *z, const uint16_t *w,
+                         double *out, long rows, int Dv, double eps)
+{
+    if (rows < 0 || Dv < 1)
+        return -1;
+    for (long r = 0; r < rows; ++r) {
+        const uint16_t *yr = y + r * Dv, *zr = z + r * Dv;
+        double ss = 0.0;
+        for (int d = 0; d < Dv; ++d) {
+            double u = bf16_bits_to_f64(yr[d]);
+            ss += u * u;
+        }
+        double rinv = 1.0 / sqrt(ss / (double)Dv + eps);
+        for (int d = 0; d < Dv; ++d) {
+            double normed = bf16_bits_to_f64(yr[d]) * rinv * bf16_bits_to_f64(w[d]);
+            out[r * Dv + d] = silu(bf16_bits_to_f64(zr[d])) * normed;
+        }
+    }
+    return 0;
+}

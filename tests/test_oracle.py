@@ -559,3 +559,102 @@ def test_mutations_are_caught_by_the_pins():
     assert relerr(variant("ok"), y_ref[0, :, 0]) < 1e-12
     for kind in ("readout_before_decay", "no_decay", "output_before_update"):
         assert relerr(variant(kind), y_ref[0, :, 0]) > 1e-3, kind
+
+
+# ---------------------------------------------------------- output epilogue
+
+def read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            key, rest = line.split(":")
+            vals[key] = np.array([float(x) for x in rest.split()])
+    return vals
+
+
+def bf16_of(x):
+    """Exact bf16 bits of values that bf16 represents (checked)."""
+    h = oracle.round_bf16(np.asarray(x, dtype=np.float64))
+    assert np.array_equal(oracle.bf16_to_f64(h), x)
+    return h
+
+
+def test_golden_gated_rmsnorm():
+    v = read_golden("gated_rmsnorm_8.txt")
+    w = bf16_of(v["w"])
+    for call in ("1", "2"):
+        y = bf16_of(v["y" + call].reshape(-1, 8))
+        z = bf16_of(v["z" + call].reshape(-1, 8))
+        out = oracle.gated_rmsnorm(y, z, w, eps=v["eps" + call][0])
+        assert np.array_equal(out.ravel(), v["out" + call])
+        assert np.array_equal(np.signbit(out.ravel()), np.signbit(v["out" + call]))
+        assert np.array_equal(oracle.bf16_to_f64(oracle.round_bf16(out)).ravel(), v["out" + call])
+
+
+def rand_epilogue(seed, rows, Dv, yscale=1.0):
+    r = rnd(seed)
+    y = oracle.round_bf16(r.standard_normal((rows, Dv)) * yscale)
+    z = oracle.round_bf16(r.standard_normal((rows, Dv)) * 2.0)
+    w = oracle.round_bf16(1.0 + 0.3 * r.standard_normal(Dv))
+    return y, z, w
+
+
+@pytest.mark.parametrize("Dv", [8, 24, 128, 520])
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 0.5])
+def test_gated_rmsnorm_matches_torch_library(Dv, eps):
+    y, z, w = rand_epilogue(40 + Dv, 37, Dv)
+    out = oracle.gated_rmsnorm(y, z, w, eps=eps)
+    f = lambda a: torch.from_numpy(oracle.bf16_to_f64(a))
+    ref = torch.nn.functional.rms_norm(f(y), (Dv,), eps=eps) * f(w) * torch.nn.functional.silu(f(z))
+    assert relerr(out, ref.numpy()) < 1e-14
+
+
+def test_gated_rmsnorm_invariants():
+    y, z, w = rand_epilogue(50, 16, 64)
+    f = oracle.bf16_to_f64
+    base = oracle.gated_rmsnorm(y, z, w, eps=0.0)
+    # the norm is scale invariant (powers of two are exact) and odd in y
+    assert np.array_equal(oracle.gated_rmsnorm(oracle.round_bf16(4.0 * f(y)), z, w, eps=0.0), base)
+    assert np.array_equal(oracle.gated_rmsnorm(oracle.round_bf16(-f(y)), z, w, eps=0.0), -base)
+    # the weight is per channel and linear
+    w2 = oracle.round_bf16(f(w) * np.where(np.arange(64) % 2 == 0, 2.0, 1.0))
+    ratio = oracle.gated_rmsnorm(y, z, w2, eps=0.0) / base
+    np.testing.assert_array_equal(ratio[:, 0::2], 2.0)
+    np.testing.assert_array_equal(ratio[:, 1::2], 1.0)
+    # z = 0 closes the gate; a row of y is normalised over itself only
+    assert not oracle.gated_rmsnorm(y, np.zeros_like(z), w, eps=0.0).any()
+    assert np.array_equal(oracle.gated_rmsnorm(y[3:5], z[3:5], w, eps=0.0), base[3:5])
+    # mean square of the normalised row is 1 (eps = 0): silu(z) = z for large z
+    big = oracle.round_bf16(np.full_like(f(z), 64.0))
+    one = oracle.round_bf16(np.ones(64))
+    n = oracle.gated_rmsnorm(y, big, one, eps=0.0) / 64.0
+    np.testing.assert_allclose(np.mean(n * n, axis=-1), 1.0, rtol=1e-14)
+    # eps dominates tiny rows: out -> y w silu(z) / sqrt(eps)
+    ys = oracle.round_bf16(f(y) * 2.0 ** -20)
+    out = oracle.gated_rmsnorm(ys, z, w, eps=1.0)
+    silu = f(z) / (1.0 + np.exp(-f(z)))
+    np.testing.assert_allclose(out, f(ys) * f(w) * silu, rtol=1e-11, atol=0)
+
+
+def test_epilogue_slips_are_caught_by_the_golden_example():
+    """Plausible slips in a transcription of the epilogue (sum instead of
+    mean, eps outside the root, sigmoid instead of silu, weight not applied)
+    each miss the hand-worked values that the oracle reproduces exactly."""
+    v = read_golden("gated_rmsnorm_8.txt")
+
+    def variant(kind, y, z, w, eps):
+        ss = (y * y).sum(-1, keepdims=True)
+        ms = ss if kind == "sum" else ss / y.shape[-1]
+        r = 1.0 / (np.sqrt(ms) + eps) if kind == "eps_outside" else 1.0 / np.sqrt(ms + eps)
+        gate = 1.0 / (1.0 + np.exp(-z)) if kind == "sigmoid" else z / (1.0 + np.exp(-z))
+        return gate * y * r * (1.0 if kind == "no_weight" else w)
+
+    for kind in ("ok", "sum", "eps_outside", "sigmoid", "no_weight"):
+        miss = False
+        for call in ("1", "2"):
+            out = variant(kind, v["y" + call].reshape(-1, 8), v["z" + call].reshape(-1, 8), v["w"],
+                          v["eps" + call][0])
+            miss |= not np.array_equal(out.ravel(), v["out" + call])
+        assert miss == (kind != "ok"), kind
