@@ -13,6 +13,10 @@ Also measured in the same run (same JSON line):
   * batched decode, B=64, T=1 (layer core, 8 rotating sets of state and conv
     state, 1 GiB, so the 256 MB last-level cache cannot hold them) -> HBM
     roofline of its recurrence kernel;
+  * the prologue kernel and the output epilogue (gated RMS normalisation of
+    y, gdn_gated_rmsnorm) on the prefill workload, each over 4 rotating
+    buffer sets larger together than the last-level cache -> HBM roofline;
+    and the gated layer core (gdn_layer_core_gated) step time;
   * the CPU oracle on a bounded sample of the prefill workload, one thread.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
@@ -33,9 +37,11 @@ KERNEL_SOURCES = {
     "recurrent_chunk_kernel": ["recurrent.hip"],
     "recurrent_step_kernel": ["recurrent.hip"],
     "prep_kernel": ["prep.hip"],
+    "gated_rmsnorm_kernel": ["epilogue.hip"],
 }
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector alike)
+R_HBM = 4                      # rotating buffer sets for the HBM-bound kernels
 
 
 def source_digest(kernel):
@@ -73,7 +79,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=200)
-    ap.add_argument("--kernel-only", default=None, choices=[None, "recurrent", "prep", "decode", "copy", "chunked"],
+    ap.add_argument("--kernel-only", default=None, choices=[None, "recurrent", "prep", "decode", "copy", "chunked",
+                                                         "epilogue"],
                     help="launch only this kernel (for counter collection)")
     return ap.parse_args()
 
@@ -142,11 +149,41 @@ def main():
     def chunked_only():
         binding.recurrent_chunked(pq, pk, pv, pg, pb, None, s_out, y, cws)
 
+    # the output epilogue (gated RMS normalisation of y) on the same workload
+    gate = inputs.epilogue_raw(B=B, T=T, Hv=Hv, Dv=Dv, workload_id=w["id"], with_y=False)
+    gz, gw = up(gate["z"]), up(gate["norm_weight"])
+    out = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+
+    # The HBM-bound kernels are timed over R_HBM rotating buffer sets (each
+    # >= 100 MB, together more than the 256 MB last-level cache), so every
+    # launch streams its operands from HBM rather than from that cache.
+    prep_sets = [dict(qkv=d["qkv"].clone(), q=torch.empty_like(pq), k=torch.empty_like(pk),
+                      v=torch.empty_like(pv), g=torch.empty_like(pg), b=torch.empty_like(pb))
+                 for _ in range(R_HBM)]
+
+    def prep_rot(i):
+        p_ = prep_sets[i % R_HBM]
+        binding.prep(p_["qkv"], d["conv_w"], d["conv_state"], cs_out, d["a"], d["b"], d["A_log"],
+                     d["dt_bias"], p_["q"], p_["k"], p_["v"], p_["g"], p_["b"], Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv,
+                     q_scale=qs, k_scale=ks, eps=eps)
+
+    epi_sets = [dict(y=torch.empty_like(y), z=gz.clone(), out=torch.empty_like(out)) for _ in range(R_HBM)]
+
+    def epilogue_rot(i):
+        e_ = epi_sets[i % R_HBM]
+        binding.gated_rmsnorm(e_["y"], e_["z"], gw, e_["out"], eps=eps)
+
+    def step_gated():
+        binding.layer_core_gated(d["qkv"], d["conv_w"], d["conv_state"], cs_out, d["a"], d["b"], d["A_log"],
+                                 d["dt_bias"], gz, gw, d["state"], s_out, out, ws, Hk=Hk, Hv=Hv, Dk=Dk,
+                                 Dv=Dv, q_scale=qs, k_scale=ks, eps=eps, norm_eps=eps)
+
     prep_only()
     torch.cuda.synchronize()
 
     if args.kernel_only:
-        return kernel_only(args, torch, dev, prep_only, rec_only, up, inputs, binding, np, chunked_only)
+        return kernel_only(args, torch, dev, prep_rot, rec_only, up, inputs, binding, np, chunked_only,
+                           epilogue_rot, epi_sets, y)
 
     for _ in range(args.warmup):
         step()
@@ -172,7 +209,12 @@ def main():
     # the per-step form the layer core uses for short sequences, and the prologue
     chunk_us = time_kernel(torch, stream, chunked_only, args.steps)
     step_form_us = time_kernel(torch, stream, rec_only, max(3, args.steps // 4))
-    prep_us = time_kernel(torch, stream, prep_only, args.steps)
+    prep_us = time_rotating(torch, stream, prep_rot, max(args.steps, 2 * R_HBM))
+    for e_ in epi_sets:
+        e_["y"].copy_(y)            # the layer core's y as the epilogue's input
+    epi_us = time_rotating(torch, stream, epilogue_rot, max(args.steps, 2 * R_HBM))
+    gated_us = time_kernel(torch, stream, step_gated, args.steps)
+    epi_bytes = 3 * B * T * Hv * Dv * 2 + Dv * 2
     flops = 7 * B * T * Hv * Dk * Dv
     achieved_tflops = flops / (chunk_us * 1e-6) / 1e12
     rec_bytes = (2 * B * T * Hk * Dk * 2 + B * T * Hv * Dv * 2 + 2 * B * T * Hv * 4 + B * T * Hv * Dv * 2
@@ -182,6 +224,8 @@ def main():
     print(f"[bench] chunked recurrence {chunk_us:.1f} us ({achieved_tflops:.1f} TFLOP/s, "
           f"{achieved_tflops / FP32_PEAK_TFLOPS:.1%} of fp32 peak); per-step form {step_form_us:.1f} us; "
           f"prep kernel {prep_us:.1f} us ({prep_bytes / prep_us / 1e3:.0f} GB/s)", file=sys.stderr, flush=True)
+    print(f"[bench] epilogue {epi_us:.1f} us ({epi_bytes / epi_us / 1e3:.0f} GB/s); "
+          f"gated layer core {gated_us:.1f} us/step", file=sys.stderr, flush=True)
 
     # ------------------------------------------------------------- decode
     decode = bench_decode(args, torch, dev, up, inputs, binding, np)
@@ -216,14 +260,35 @@ def main():
         "recurrence_per_step_form": {"kernel": "recurrent_chunk_kernel<128,32>", "avg_launch_us": step_form_us,
                                      "achieved_TFLOPs": flops / (step_form_us * 1e-6) / 1e12},
         "prologue": {"kernel": "prep_kernel<128,4>", "avg_launch_us": prep_us,
+                     "buffers": f"{R_HBM} rotating sets (inputs and outputs exceed the last-level cache)",
                      "bytes_per_launch": prep_bytes, "achieved_GBs": prep_bytes / prep_us / 1e3,
                      "traffic": measured_traffic("prep_kernel", "prefill_T4096"),
                      "frac_hbm": prep_bytes / prep_us / 1e3 / HBM_PEAK_GBS},
+        "epilogue": {"kernel": "gated_rmsnorm_kernel<16,1>", "avg_launch_us": epi_us,
+                     "buffers": f"{R_HBM} rotating sets (inputs and outputs exceed the last-level cache)",
+                     "bytes_per_launch": epi_bytes, "achieved_GBs": epi_bytes / epi_us / 1e3,
+                     "traffic": measured_traffic("gated_rmsnorm_kernel", "prefill_T4096"),
+                     "frac_hbm": epi_bytes / epi_us / 1e3 / HBM_PEAK_GBS,
+                     "layer_core_gated_us": gated_us},
         "decode_b64": decode,
         "cpu_baseline": cpu,
         "wall_s_timed": t_wall,
     }
     print(json.dumps(line), flush=True)
+
+
+def time_rotating(torch, stream, fn, n):
+    """Average launch time of fn(i), i = 0..n-1 (fn rotates buffer sets)."""
+    for i in range(R_HBM):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
 
 
 def time_kernel(torch, stream, fn, n):
@@ -342,15 +407,26 @@ def cpu_baseline(raw, Hk, Hv, Dk, Dv, qs, ks, eps):
             "host_cpus": os.cpu_count()}
 
 
-def kernel_only(args, torch, dev, prep_only, rec_only, up, inputs, binding, np, chunked_only):
-    """Launch one kernel a few times (for rocprofv3 counter passes)."""
+def kernel_only(args, torch, dev, prep_rot, rec_only, up, inputs, binding, np, chunked_only, epilogue_rot,
+                epi_sets, y):
+    """Launch one kernel a few times (for rocprofv3 counter passes), in the
+    configuration the benchmark times (rotating sets for prep and epilogue)."""
     n = max(args.steps, 1)
+    ctr = iter(range(1 << 30))
     if args.kernel_only == "recurrent":
         fn = rec_only
     elif args.kernel_only == "chunked":
         fn = chunked_only
     elif args.kernel_only == "prep":
-        fn = prep_only
+        def fn():
+            prep_rot(next(ctr))
+    elif args.kernel_only == "epilogue":
+        rec_only()
+        for e_ in epi_sets:
+            e_["y"].copy_(y)
+
+        def fn():
+            epilogue_rot(next(ctr))
     elif args.kernel_only == "copy":
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)   # 256 MiB
         dst = torch.empty_like(src)

@@ -217,6 +217,54 @@ gdn_status gdn_layer_core_masked(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
                                  int B, int T, int Hk, int Hv, int Dk, int Dv, int K,
                                  float q_scale, float k_scale, float eps, void *stream);
 
+/*
+ * gdn_gated_rmsnorm -- output epilogue of the layer: gated RMS normalisation
+ * of the recurrence output ("mlex 0.1.2 -- src/models/gated_delta.rs",
+ * GatedDeltaNet::forward, the step after the recurrence loop).  Per row of Dv
+ * values (one token b, t of one v-head hv), computed in f32:
+ *
+ *   out[b,t,hv,:] = bf16( silu(z) * y / sqrt(mean(y^2) + eps) * norm_weight )
+ *
+ * silu(u) = u / (1 + e^-u); the result is rounded to nearest even.
+ *
+ *   y            [B, T, Hv, Dv] bf16  the recurrence output as stored
+ *   z            [B, T, Hv, Dv] bf16  the gate (the layer's z projection)
+ *   norm_weight  [Dv] bf16            per-channel weight, shared by all heads
+ *   out          [B, T, Hv, Dv] bf16  (= [B, T, Hv*Dv], the layer's output
+ *                                      before its output projection)
+ *   eps          finite, >= 0 (with eps = 0 an all-zero row gives NaN, as the
+ *                formula does; the arithmetic is f32, as on the page, so with
+ *                eps = 0 a row whose mean square lies below the f32 normal
+ *                range, 2^-126, is outside the stated accuracy)
+ *
+ * Dv is a multiple of 8 in [8, 4096].  Device pointers, caller-owned, each
+ * 16-byte aligned; norm_weight may be NULL only when B*T == 0.  out may be
+ * exactly y or exactly z (in place); any other overlap of out with an input is
+ * an error.  Only enqueues on `stream`; every check runs before the launch.
+ */
+gdn_status gdn_gated_rmsnorm(const gdn_bf16 *y, const gdn_bf16 *z, const gdn_bf16 *norm_weight,
+                             gdn_bf16 *out, int B, int T, int Hv, int Dv, float eps, void *stream);
+
+/*
+ * gdn_layer_core_gated -- gdn_layer_core_masked followed by the output
+ * epilogue: the recurrence writes y into `out`, then gdn_gated_rmsnorm turns
+ * it, in place, into silu(z)·rms_norm(y)·norm_weight (bit-identical to those
+ * two calls).  z and norm_weight are as in gdn_gated_rmsnorm and must not
+ * overlap any output (out, state_out, conv_state_out, workspace); norm_eps is
+ * the epilogue's eps, eps the prologue's.  Workspace: as gdn_layer_core
+ * (gdn_layer_core_workspace_bytes).
+ */
+gdn_status gdn_layer_core_gated(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
+                                const gdn_bf16 *conv_state_in, gdn_bf16 *conv_state_out,
+                                const gdn_bf16 *a, const gdn_bf16 *b,
+                                const float *A_log, const float *dt_bias,
+                                const gdn_bf16 *z, const gdn_bf16 *norm_weight, const uint8_t *mask,
+                                const float *state_in, float *state_out, gdn_bf16 *out,
+                                void *workspace, size_t workspace_bytes,
+                                int B, int T, int Hk, int Hv, int Dk, int Dv, int K,
+                                float q_scale, float k_scale, float eps, float norm_eps,
+                                void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,6 +65,10 @@ def lib():
         L.gdn_layer_core_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_layer_core.argtypes = [_p] * 12 + [ctypes.c_size_t] + [_i] * 7 + [_f] * 3 + [_p]
         L.gdn_layer_core.restype = _i
+        L.gdn_gated_rmsnorm.argtypes = [_p] * 4 + [_i] * 4 + [_f, _p]
+        L.gdn_gated_rmsnorm.restype = _i
+        L.gdn_layer_core_gated.argtypes = [_p] * 15 + [ctypes.c_size_t] + [_i] * 7 + [_f] * 4 + [_p]
+        L.gdn_layer_core_gated.restype = _i
         _lib = L
     return _lib
 
@@ -228,3 +232,50 @@ def layer_core(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias,
     m = _ptr(mask, "mask", _MASK, (B, T), dev)
     _check(lib().gdn_layer_core_masked(*args[:8], m, *args[8:], ws_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale,
                                        k_scale, eps, _stream(dev, stream)))
+
+
+def gated_rmsnorm(y, z, norm_weight, out, *, eps=1e-6, stream=None):
+    """Output epilogue (gdn_gated_rmsnorm): out = bf16(silu(z) * rms_norm(y)
+    * norm_weight) per row of Dv.  y, z, out [B,T,Hv,Dv] bf16 (out may be y
+    or z itself); norm_weight [Dv] bf16."""
+    B, T, Hv, Dv = y.shape
+    dev = y.device
+    args = [
+        _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
+        _ptr(z, "z", _BF16, (B, T, Hv, Dv), dev),
+        _ptr(norm_weight, "norm_weight", _BF16, (Dv,), dev),
+        _ptr(out, "out", _BF16, (B, T, Hv, Dv), dev),
+    ]
+    _check(lib().gdn_gated_rmsnorm(*args, B, T, Hv, Dv, eps, _stream(dev, stream)))
+
+
+def layer_core_gated(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, z, norm_weight,
+                     state_in, state_out, out, workspace, *, Hk, Hv, Dk, Dv, q_scale, k_scale,
+                     eps=1e-6, norm_eps=1e-6, mask=None, stream=None):
+    """Layer core then the output epilogue (gdn_layer_core_gated).  Arguments
+    as ``layer_core`` plus z [B,T,Hv,Dv] and norm_weight [Dv] (bf16); ``out``
+    [B,T,Hv,Dv] bf16 receives silu(z)·rms_norm(y)·norm_weight."""
+    B, T, C = qkv.shape
+    K = conv_w.shape[1]
+    dev = qkv.device
+    ws_ptr, ws_bytes = _workspace(workspace, dev)
+    args = [
+        _ptr(qkv, "qkv", _BF16, (B, T, C), dev),
+        _ptr(conv_w, "conv_w", _BF16, (C, K), dev),
+        _ptr(conv_state_in, "conv_state_in", _BF16, (B, K - 1, C), dev),
+        _ptr(conv_state_out, "conv_state_out", _BF16, (B, K - 1, C), dev),
+        _ptr(a, "a", _BF16, (B, T, Hv), dev),
+        _ptr(b, "b", _BF16, (B, T, Hv), dev),
+        _ptr(A_log, "A_log", (torch.float32,), (Hv,), dev),
+        _ptr(dt_bias, "dt_bias", (torch.float32,), (Hv,), dev),
+        _ptr(z, "z", _BF16, (B, T, Hv, Dv), dev),
+        _ptr(norm_weight, "norm_weight", _BF16, (Dv,), dev),
+        _ptr(mask, "mask", _MASK, (B, T), dev),
+        _ptr(state_in, "state_in", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(state_out, "state_out", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(out, "out", _BF16, (B, T, Hv, Dv), dev),
+        ws_ptr,
+    ]
+    _check(lib().gdn_layer_core_gated(*args, ws_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps,
+                                      norm_eps, _stream(dev, stream)))
+

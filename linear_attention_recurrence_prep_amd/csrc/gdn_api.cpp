@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kVersion = 2;
+constexpr int kVersion = 3;
 constexpr int64_t kMaxBlocks = (1LL << 31) - 1;
 
 thread_local char g_err[512] = "";
@@ -129,6 +129,32 @@ gdn_status validate_recurrent(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf
         {"mask", mask, (uint64_t)B * T, false, 1},
     };
     return check_spans(s, {{5, 6}});
+}
+
+// ------------------------------------------------------------- epilogue --
+
+gdn_status validate_gated(const gdn_bf16* y, const gdn_bf16* z, const gdn_bf16* w, const gdn_bf16* out, int B,
+                          int T, int Hv, int Dv, float eps, bool check_overlap = true) {
+    if (B < 0 || T < 0) return fail(GDN_ERR_BAD_DIMS, "B=%d and T=%d must be >= 0", B, T);
+    if (Hv < 1) return fail(GDN_ERR_BAD_DIMS, "Hv=%d must be >= 1", Hv);
+    if (Dv < 8 || Dv > 4096 || Dv % 8 != 0)
+        return fail(GDN_ERR_UNSUPPORTED, "Dv=%d must be a multiple of 8 in [8, 4096]", Dv);
+    if (!std::isfinite(eps) || eps < 0.f) return fail(GDN_ERR_BAD_VALUE, "norm eps must be finite and >= 0");
+    uint64_t rows, n;
+    if (!elems(rows, {B, T, Hv}) || !elems(n, {B, T, Hv, Dv})) return fail(GDN_ERR_BAD_DIMS, "tensor sizes overflow");
+    if (gdn::gated_norm_blocks((int64_t)rows, Dv) > kMaxBlocks) return fail(GDN_ERR_BAD_DIMS, "grid too large");
+    if (rows > 0) {
+        if (!y) return fail(GDN_ERR_NULL_POINTER, "y is NULL");
+        if (!z) return fail(GDN_ERR_NULL_POINTER, "z is NULL");
+        if (!w) return fail(GDN_ERR_NULL_POINTER, "norm_weight is NULL");
+        if (!out) return fail(GDN_ERR_NULL_POINTER, "out is NULL");
+    }
+    if (!check_overlap) return GDN_OK;
+    std::vector<Span> s = {
+        {"y", y, n * 2, false}, {"z", z, n * 2, false}, {"norm_weight", w, (uint64_t)Dv * 2, false},
+        {"out", out, n * 2, true},
+    };
+    return check_spans(s, {{0, 3}, {1, 3}});
 }
 
 // ----------------------------------------------------------------- prep --
@@ -338,12 +364,15 @@ size_t gdn_layer_core_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int 
     return (size_t)w.total;
 }
 
-gdn_status gdn_layer_core_masked(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_bf16* conv_state_in,
-                                 gdn_bf16* conv_state_out, const gdn_bf16* a, const gdn_bf16* b,
-                                 const float* A_log, const float* dt_bias, const uint8_t* mask,
-                                 const float* state_in, float* state_out, gdn_bf16* y, void* workspace,
-                                 size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk, int Dv, int K,
-                                 float q_scale, float k_scale, float eps, void* stream) {
+// The layer core, optionally followed by the output epilogue (gated: z and
+// norm_weight given), which then runs in place on y.
+static gdn_status layer_core_impl(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_bf16* conv_state_in,
+                                  gdn_bf16* conv_state_out, const gdn_bf16* a, const gdn_bf16* b,
+                                  const float* A_log, const float* dt_bias, const uint8_t* mask,
+                                  const float* state_in, float* state_out, gdn_bf16* y, void* workspace,
+                                  size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk, int Dv, int K,
+                                  float q_scale, float k_scale, float eps, bool gated, const gdn_bf16* z,
+                                  const gdn_bf16* norm_weight, float norm_eps, void* stream) {
     gdn_status st = check_dims(B, T, Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
     Workspace w;
@@ -371,6 +400,10 @@ gdn_status gdn_layer_core_masked(const gdn_bf16* qkv, const gdn_bf16* conv_w, co
     if (st != GDN_OK) return st;
     st = validate_recurrent(wq, wk, wv, wg, wb, mask, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, false);
     if (st != GDN_OK) return st;
+    if (gated) {
+        st = validate_gated(y, z, norm_weight, y, B, T, Hv, Dv, norm_eps, false);
+        if (st != GDN_OK) return st;
+    }
     if (w.use_chunked && gdn::chunked_blocks(B, T, Hv, Dv) > kMaxBlocks) return fail(GDN_ERR_BAD_DIMS, "grid too large");
     {
         const int64_t C = 2LL * Hk * Dk + (int64_t)Hv * Dv;
@@ -395,6 +428,8 @@ gdn_status gdn_layer_core_masked(const gdn_bf16* qkv, const gdn_bf16* conv_w, co
             {"y", y, nv * 2, true},
             {"workspace", workspace, w.total, true},
             {"mask", mask, (uint64_t)B * T, false, 1},
+            {"z", gated ? z : nullptr, nv * 2, false},
+            {"norm_weight", gated ? norm_weight : nullptr, (uint64_t)Dv * 2, false},
         };
         st = check_spans(s, {{2, 3}, {8, 9}});
         if (st != GDN_OK) return st;
@@ -408,8 +443,44 @@ gdn_status gdn_layer_core_masked(const gdn_bf16* qkv, const gdn_bf16* conv_w, co
         if (st != GDN_OK) return st;
     }
     gdn::RecurrentArgs r{wq, wk, wv, wg, wb, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, mask};
-    if (w.use_chunked) return hip_result(gdn::launch_recurrent_chunked(r, ws + w.chunked, s), "chunked recurrent");
-    return hip_result(gdn::launch_recurrent(r, s), "recurrent");
+    st = w.use_chunked ? hip_result(gdn::launch_recurrent_chunked(r, ws + w.chunked, s), "chunked recurrent")
+                       : hip_result(gdn::launch_recurrent(r, s), "recurrent");
+    if (st != GDN_OK || !gated) return st;
+    gdn::GatedNormArgs e{y, z, norm_weight, y, (int64_t)B * T * Hv, Dv, norm_eps};
+    return hip_result(gdn::launch_gated_rmsnorm(e, s), "gated rmsnorm");
+}
+
+gdn_status gdn_layer_core_masked(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_bf16* conv_state_in,
+                                 gdn_bf16* conv_state_out, const gdn_bf16* a, const gdn_bf16* b,
+                                 const float* A_log, const float* dt_bias, const uint8_t* mask,
+                                 const float* state_in, float* state_out, gdn_bf16* y, void* workspace,
+                                 size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk, int Dv, int K,
+                                 float q_scale, float k_scale, float eps, void* stream) {
+    return layer_core_impl(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, mask, state_in,
+                           state_out, y, workspace, workspace_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale,
+                           eps, false, nullptr, nullptr, 0.f, stream);
+}
+
+gdn_status gdn_layer_core_gated(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_bf16* conv_state_in,
+                                gdn_bf16* conv_state_out, const gdn_bf16* a, const gdn_bf16* b,
+                                const float* A_log, const float* dt_bias, const gdn_bf16* z,
+                                const gdn_bf16* norm_weight, const uint8_t* mask, const float* state_in,
+                                float* state_out, gdn_bf16* out, void* workspace, size_t workspace_bytes, int B,
+                                int T, int Hk, int Hv, int Dk, int Dv, int K, float q_scale, float k_scale,
+                                float eps, float norm_eps, void* stream) {
+    return layer_core_impl(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, mask, state_in,
+                           state_out, out, workspace, workspace_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale,
+                           eps, true, z, norm_weight, norm_eps, stream);
+}
+
+gdn_status gdn_gated_rmsnorm(const gdn_bf16* y, const gdn_bf16* z, const gdn_bf16* norm_weight, gdn_bf16* out,
+                             int B, int T, int Hv, int Dv, float eps, void* stream) {
+    gdn_status st = validate_gated(y, z, norm_weight, out, B, T, Hv, Dv, eps);
+    if (st != GDN_OK) return st;
+    const int64_t rows = (int64_t)B * T * Hv;
+    if (rows == 0) return ok();
+    gdn::GatedNormArgs e{y, z, norm_weight, out, rows, Dv, eps};
+    return hip_result(gdn::launch_gated_rmsnorm(e, static_cast<hipStream_t>(stream)), "gated rmsnorm");
 }
 
 gdn_status gdn_layer_core(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_bf16* conv_state_in,

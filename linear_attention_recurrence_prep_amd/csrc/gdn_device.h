@@ -38,6 +38,29 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
                       pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
 }
 
+// ------------------------------------------------------------ activations ----
+
+// e^-|u| with subnormal results: the hardware exp2 does not return
+// subnormals, so the exponent is halved (exactly) and the result squared:
+// h = 2^(-|u| log2(e) / 2) stays normal for |u| < 174, and h·h rounds once,
+// correctly, into the subnormal range (about 2 f32 ulp overall).
+__device__ __forceinline__ float exp_neg_abs(float u) {
+    const float h = __builtin_amdgcn_exp2f(fabsf(u) * -0.72134752044448170f);
+    return h * h;
+}
+
+// silu(u) = u · sigmoid(u) in the form that cannot overflow, for values that
+// are rounded to bf16 afterwards: with e = e^-|u| in (0, 1],
+// silu(u) = (u >= 0 ? u : u·e) / (1 + e), so large negative u gives the tiny
+// true value rather than u / inf.  Hardware exp2 and reciprocal, each within
+// about one f32 ulp; the exp argument's rounding adds |u|·2^-24 relative, far
+// below a bf16 rounding.  NaN stays NaN.
+__device__ __forceinline__ float silu_fast(float u) {
+    const float e = exp_neg_abs(u);
+    const float s = __builtin_amdgcn_rcpf(1.0f + e);
+    return (u >= 0.0f ? u : u * e) * s;
+}
+
 // ------------------------------------------------------------ cross-lane ----
 
 // DPP controls (GCN/CDNA encoding): quad permutations, mirrors inside a

@@ -60,4 +60,19 @@ int64_t chunked_blocks(int B, int T, int Hv, int Dv);
 hipError_t launch_recurrent_chunked(const RecurrentArgs& a, void* workspace, hipStream_t stream);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 
+// Output epilogue: out = bf16(silu(z) * rms_norm(y) * w) per row of Dv
+// values (Dv a multiple of 8); out may alias y or z exactly.
+struct GatedNormArgs {
+    const uint16_t* y;
+    const uint16_t* z;
+    const uint16_t* w;
+    uint16_t* out;
+    int64_t rows;
+    int Dv;
+    float eps;
+};
+int gated_norm_lanes(int Dv);
+int64_t gated_norm_blocks(int64_t rows, int Dv);
+hipError_t launch_gated_rmsnorm(const GatedNormArgs& a, hipStream_t stream);
+
 }  // namespace gdn

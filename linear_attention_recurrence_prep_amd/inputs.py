@@ -36,6 +36,7 @@ SEED = 1234
 TENSOR_IDS = {
     "qkv": 0, "conv_w": 1, "conv_state": 2, "a": 3, "b": 4, "A_log": 5,
     "dt_bias": 6, "state": 7, "q_raw": 8, "k_raw": 9, "v": 10,
+    "z": 11, "norm_weight": 12, "y": 13, "row_scale": 14,
 }
 
 WORKLOADS = {
@@ -129,6 +130,23 @@ def layer_raw(*, B, T, Hk, Hv, Dk, Dv, K=4, workload_id=3, state=False, conv_sta
         dt_bias=normal_f32(generator(w, "dt_bias", seed), (Hv,), 0.1),
         state=normal_f32(generator(w, "state", seed), (B, Hv, Dv, Dk), 0.02) if state else None,
     )
+
+
+def epilogue_raw(*, B, T, Hv, Dv, workload_id=5, with_y=True, seed=SEED):
+    """Raw draws for the output epilogue: z [B,T,Hv,Dv] bf16 N(0,1) (the
+    layer's gate projection); norm_weight [Dv] bf16 1 + N(0, 0.1^2); and, for
+    a standalone call, y [B,T,Hv,Dv] bf16: N(0,1) rows each scaled by
+    2^U[-24, 4], so that some rows are small enough for eps to matter."""
+    w = workload_id
+    out = dict(
+        z=normal_bf16(generator(w, "z", seed), (B, T, Hv, Dv)),
+        norm_weight=f32_to_bf16_bits(
+            np.float32(1.0) + normal_f32(generator(w, "norm_weight", seed), (Dv,), 0.1)),
+    )
+    if with_y:
+        scale = np.exp2(generator(w, "row_scale", seed).uniform(-24.0, 4.0, (B, T, Hv, 1))).astype(np.float32)
+        out["y"] = f32_to_bf16_bits(normal_f32(generator(w, "y", seed), (B, T, Hv, Dv)) * scale)
+    return out
 
 
 def workload(name: str, seed: int = SEED):

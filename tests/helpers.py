@@ -142,3 +142,21 @@ def guards_intact(full, fill, pad=4096):
     if full.dtype.is_floating_point and math.isnan(fill):
         return bool(torch.isnan(head).all() and torch.isnan(tail).all())
     return bool((head == fill).all() and (tail == fill).all())
+
+
+def check_epilogue(out_bits, ref, label=""):
+    """Output epilogue: every value within one bf16 ulp of the fp64 value (the
+    f32 arithmetic is good to about 2^-20 relative, so only values that close
+    to a rounding boundary may round the other way: at least 99% of the
+    values must carry the bits of the correctly rounded result).  NaN where
+    and only where the fp64 value is NaN.  Returns the count of flipped
+    roundings."""
+    x = oracle.bf16_to_f64(out_bits)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(np.isnan(x), nan_ref), f"{label}: NaN pattern differs"
+    err = np.abs(x - ref)[~nan_ref]
+    bad = err > bf16_ulp(ref[~nan_ref])
+    assert not bad.any(), f"{label}: {bad.sum()} values beyond 1 bf16 ulp (worst {err.max():.3e})"
+    flips = int(np.count_nonzero((out_bits != oracle.round_bf16(np.nan_to_num(ref)))[~nan_ref]))
+    assert flips <= max(2, 0.01 * out_bits.size), f"{label}: {flips} of {out_bits.size} roundings differ"
+    return flips

@@ -242,3 +242,44 @@ def test_masked_layer_core_rejects(L):
     assert f(addr(15) + 1) == OVERLAP      # mask inside y
     assert f(addr(20) + 3) == OVERLAP      # mask inside the workspace
     assert f(addr(9), y=addr(14)) == OVERLAP
+
+
+def call_gated(L, **over):
+    p = dict(y=addr(0), z=addr(1), w=addr(2), out=addr(3))
+    d = dict(B=2, T=5, Hv=4, Dv=64, eps=1e-6)
+    for k_, v_ in over.items():
+        (p if k_ in p else d)[k_] = v_
+    return L.gdn_gated_rmsnorm(p["y"], p["z"], p["w"], p["out"], d["B"], d["T"], d["Hv"], d["Dv"],
+                               ctypes.c_float(d["eps"]), None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(B=-1), DIMS), (dict(Hv=0), DIMS), (dict(Dv=12), UNSUP), (dict(Dv=0), UNSUP), (dict(Dv=4104), UNSUP),
+    (dict(eps=-1.0), VALUE), (dict(eps=float("nan")), VALUE), (dict(eps=float("inf")), VALUE),
+    (dict(y=None), NULLP), (dict(z=None), NULLP), (dict(w=None), NULLP), (dict(out=None), NULLP),
+    (dict(y=addr(0) + 8), ALIGN), (dict(out=addr(3) + 2), ALIGN),
+    (dict(out=addr(0) + 16), OVERLAP), (dict(out=addr(1) + 32), OVERLAP), (dict(out=addr(2)), OVERLAP),
+    (dict(B=1 << 30, T=1 << 30), DIMS),
+    (dict(B=0), OK), (dict(T=0, y=None, z=None, w=None, out=None), OK),
+])
+def test_gated_rmsnorm_rejects(L, over, code):
+    assert call_gated(L, **over) == code
+
+
+def test_layer_core_gated_rejects(L):
+    p, d = prep_args()
+
+    def f(z=addr(16), w=addr(17), out=addr(15), ws=addr(20), norm_eps=1e-6, B=d["B"]):
+        return L.gdn_layer_core_gated(
+            p["qkv"], p["conv_w"], p["cs_in"], p["cs_out"], p["a"], p["b"], p["A_log"], p["dt_bias"], z, w,
+            None, addr(13), addr(14), out, ws, ctypes.c_size_t(1 << 30), B, d["T"], d["Hk"], d["Hv"], d["Dk"],
+            d["Dv"], d["K"], d["q_scale"], d["k_scale"], d["eps"], ctypes.c_float(norm_eps), None)
+
+    assert f(z=None) == NULLP
+    assert f(w=None) == NULLP
+    assert f(norm_eps=-1.0) == VALUE
+    assert f(z=addr(15)) == OVERLAP            # z is read after out is written
+    assert f(w=addr(14) + 64) == OVERLAP       # norm_weight inside state_out
+    assert f(z=addr(20) + 256) == OVERLAP      # z inside the workspace
+    assert f(z=addr(3)) == OVERLAP             # z over conv_state_out
+    assert f(B=0) == OK

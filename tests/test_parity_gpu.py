@@ -259,6 +259,34 @@ def test_prep_matches_oracle(case):
     assert np.array_equal(out["conv_state"], ref["conv_state"])
 
 
+def test_prep_extreme_activations_and_gates():
+    """Conv outputs deep in SiLU's negative tail (where e^-u overflows f32 and
+    the true value is a tiny normal or subnormal number) and gate inputs far
+    out on both sides, against the oracle."""
+    B, T, Hk, Hv, Dk, Dv, K = 1, 24, 1, 2, 32, 32, 4
+    say("prep extremes")
+    raw = layer_inputs(B, T, Hk, Hv, Dk, Dv, K, 215)
+    f = oracle.bf16_to_f64
+    tail = np.array([-87.0, -88.0, -89.0, -92.0, -95.0, -100.0, -103.0, -110.0, -200.0, -1e4, 88.0, 100.0,
+                     -20.0, 20.0, 0.0, -0.0, -87.5, -96.0, -101.0, -104.0, -3.0, 3.0, -88.5, -150.0])
+    cw = f(raw["conv_w"])
+    x = f(raw["qkv"])
+    for c in (5, Dk + 7, 2 * Dk + 3, 2 * Dk + Dv + 11):    # a q, a k and two v channels
+        cw[c] = [0.0, 0.0, 0.0, 1.0]                          # the newest tap only: u = x
+        x[0, :, c] = tail
+    raw["conv_w"], raw["qkv"] = oracle.round_bf16(cw), oracle.round_bf16(x)
+    raw["b"] = oracle.round_bf16(np.resize(tail, (B, T, Hv)) * np.array([1.0, -1.0]))
+    raw["a"] = oracle.round_bf16(np.resize(tail[::-1], (B, T, Hv)))
+    qs, ks = 1.0 / Dk, Dk ** -0.5
+    out = gpu_prep(raw, Hk, Hv, Dk, Dv, qs, ks)
+    ref = oracle.prep(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"], raw["A_log"],
+                      raw["dt_bias"], Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs, k_scale=ks)
+    for n in ("q", "k", "v"):
+        H.check_bf16_within_ulp(out[n], ref[n], n)
+    H.check_gates(out["g"], out["beta"], ref["g"], ref["beta"])
+    assert oracle.bf16_to_f64(out["v"][0, 2, 0, 3]) < 0     # silu(-89) is a normal bf16 number
+
+
 def test_prep_conv_state_in_place_and_T0():
     say("prep in-place conv state / T=0")
     raw = layer_inputs(2, 9, 2, 4, 64, 16, 4, 210)
