@@ -56,6 +56,8 @@ def lib():
         L.oracle_recurrent.argtypes = [_dp, _dp, _dp, _dp, _dp, _bp, _dp, _dp, _dp,
                                        _i, _i, _i, _i, _i, _i]
         L.oracle_recurrent.restype = _i
+        L.oracle_recurrent_per_key.argtypes = L.oracle_recurrent.argtypes
+        L.oracle_recurrent_per_key.restype = _i
         L.oracle_layer_core.argtypes = [_hp, _hp, _hp, _hp, _hp, _hp, _fp, _fp, _bp,
                                         _dp, _dp, _dp,
                                         _i, _i, _i, _i, _i, _i, _i, _d, _d, _d]
@@ -162,28 +164,43 @@ def prep(qkv, conv_w, conv_state_in, a, b, A_log, dt_bias, *, Hk, Hv, Dk, Dv,
 
 
 def recurrent(q, k, v, g, beta, state_in=None, mask=None):
-    """Gated delta rule in fp64.  q,k [B,T,Hk,Dk]; v [B,T,Hv,Dv]; g,beta
-    [B,T,Hv]; state_in [B,Hv,Dv,Dk] or None; mask [B,T] (nonzero = active
-    step) or None.  Inputs are taken as exact values (widened to float64).
-    Returns (y [B,T,Hv,Dv], state_out)."""
+    """Gated delta rule in fp64.  q,k [B,T,Hk,Dk]; v [B,T,Hv,Dv]; g [B,T,Hv]
+    (per-head decay) or [B,T,Hv,Dk] (per-key decay); beta [B,T,Hv];
+    state_in [B,Hv,Dv,Dk] or None; mask [B,T] (nonzero = active step) or
+    None.  Inputs are taken as exact values (widened to float64).  Returns
+    (y [B,T,Hv,Dv], state_out)."""
     q, k, v, g, beta, state_in = map(_f64, (q, k, v, g, beta, state_in))
     mask = _mask(mask)
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     assert k.shape == q.shape and v.shape[:2] == (B, T)
-    assert g.shape == (B, T, Hv) and beta.shape == (B, T, Hv)
+    per_key = g.ndim == 4
+    assert g.shape == ((B, T, Hv, Dk) if per_key else (B, T, Hv)) and beta.shape == (B, T, Hv)
     if state_in is not None:
         assert state_in.shape == (B, Hv, Dv, Dk)
     y = np.empty((B, T, Hv, Dv))
     s = np.empty((B, Hv, Dv, Dk))
     if mask is not None:
         assert mask.shape == (B, T)
-    rc = lib().oracle_recurrent(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(g, _dp),
+    fn = lib().oracle_recurrent_per_key if per_key else lib().oracle_recurrent
+    rc = fn(_ptr(q, _dp), _ptr(k, _dp), _ptr(v, _dp), _ptr(g, _dp),
                                 _ptr(beta, _dp), _ptr(mask, _bp), _ptr(state_in, _dp), _ptr(s, _dp),
                                 _ptr(y, _dp), B, T, Hk, Hv, Dk, Dv)
     if rc != 0:
         raise RuntimeError("oracle_recurrent failed")
     return y, s
+
+
+def recurrent_snapshots(q, k, v, g, beta, steps, state_in=None, mask=None):
+    """States after the first n steps, for each n in ``steps``: the
+    recurrence run over each prefix of the inputs.  Returns
+    [len(steps), B, Hv, Dv, Dk] float64."""
+    out = []
+    for n in steps:
+        sl = lambda a: None if a is None else np.ascontiguousarray(np.asarray(a)[:, :n])
+        _, s = recurrent(sl(q), sl(k), sl(v), sl(g), sl(beta), state_in, sl(mask))
+        out.append(s)
+    return np.stack(out)
 
 
 def layer_core(qkv, conv_w, conv_state_in, a, b, A_log, dt_bias, state_in=None, *,

@@ -262,14 +262,20 @@ int oracle_prep(const uint16_t *qkv, const uint16_t *conv_w,
  * active); a step whose mask byte is 0 leaves S untouched (no decay, no
  * update) and writes y_t = 0.
  *
- * Layouts: q,k [B,T,Hk,Dk]; v,y [B,T,Hv,Dv]; g,beta [B,T,Hv];
- * state_in/state_out [B,Hv,Dv,Dk] (state_in NULL = zeros; may alias out).
- * All double.  Returns 0, or -1 on bad sizes / allocation failure.
+ * Per-key decay (the "vectorized" gate, g of shape [B,T,Hv,Dk], that
+ * [bun] names beside the per-head gate it ports): the decay step scales each
+ * state column by its own factor, S[i,j] <- g_t[j] * S[i,j]; every other
+ * step is unchanged.  g_per_key selects this form.
+ *
+ * Layouts: q,k [B,T,Hk,Dk]; v,y [B,T,Hv,Dv]; g,beta [B,T,Hv] (g [B,T,Hv,Dk]
+ * with g_per_key); state_in/state_out [B,Hv,Dv,Dk] (state_in NULL = zeros;
+ * may alias out).  All double.  Returns 0, or -1 on bad sizes / allocation
+ * failure.
  */
-int oracle_recurrent(const double *q, const double *k, const double *v,
-                     const double *g, const double *beta, const unsigned char *mask,
-                     const double *state_in, double *state_out, double *y,
-                     int B, int T, int Hk, int Hv, int Dk, int Dv)
+static int recurrence(const double *q, const double *k, const double *v,
+                      const double *g, int g_per_key, const double *beta,
+                      const unsigned char *mask, const double *state_in, double *state_out,
+                      double *y, int B, int T, int Hk, int Hv, int Dk, int Dv)
 {
     if (B < 0 || T < 0 || Hk < 1 || Hv < 1 || Dk < 1 || Dv < 1 || Hv % Hk != 0)
         return -1;
@@ -293,7 +299,8 @@ int oracle_recurrent(const double *q, const double *k, const double *v,
                 const double *kt = k + ((bb * T + t) * Hk + hk) * Dk;
                 const double *qt = q + ((bb * T + t) * Hk + hk) * Dk;
                 const double *vt = v + ((bb * T + t) * Hv + hv) * Dv;
-                const double gt = g[(bb * T + t) * Hv + hv];
+                const double *gt = g_per_key ? g + ((bb * T + t) * Hv + hv) * Dk
+                                             : g + (bb * T + t) * Hv + hv;
                 const double bt = beta[(bb * T + t) * Hv + hv];
                 double *yt = y + ((bb * T + t) * Hv + hv) * Dv;
                 if (mask && !mask[bb * T + t]) {
@@ -301,8 +308,9 @@ int oracle_recurrent(const double *q, const double *k, const double *v,
                         yt[i] = 0.0;
                     continue;
                 }
-                for (long i = 0; i < (long)Dv * Dk; ++i)
-                    S[i] = S[i] * gt;
+                for (long i = 0; i < Dv; ++i)
+                    for (long j = 0; j < Dk; ++j)
+                        S[i * Dk + j] = S[i * Dk + j] * (g_per_key ? gt[j] : gt[0]);
                 for (long i = 0; i < Dv; ++i) {
                     double acc = 0.0;
                     for (long j = 0; j < Dk; ++j)
@@ -329,6 +337,24 @@ int oracle_recurrent(const double *q, const double *k, const double *v,
     free(kv);
     free(delta);
     return 0;
+}
+
+/* The recurrence with the per-head gate g [B,T,Hv]. */
+int oracle_recurrent(const double *q, const double *k, const double *v,
+                     const double *g, const double *beta, const unsigned char *mask,
+                     const double *state_in, double *state_out, double *y,
+                     int B, int T, int Hk, int Hv, int Dk, int Dv)
+{
+    return recurrence(q, k, v, g, 0, beta, mask, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv);
+}
+
+/* The recurrence with the per-key gate g [B,T,Hv,Dk]. */
+int oracle_recurrent_per_key(const double *q, const double *k, const double *v,
+                             const double *g, const double *beta, const unsigned char *mask,
+                             const double *state_in, double *state_out, double *y,
+                             int B, int T, int Hk, int Hv, int Dk, int Dv)
+{
+    return recurrence(q, k, v, g, 1, beta, mask, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv);
 }
 
 /* ------------------------------------------------------------ layer core */

@@ -658,3 +658,83 @@ def test_epilogue_slips_are_caught_by_the_golden_example():
                           v["eps" + call][0])
             miss |= not np.array_equal(out.ravel(), v["out" + call])
         assert miss == (kind != "ok"), kind
+
+
+# ---------------------------------------------------- per-key decay (vectorized g)
+
+def matrix_form_per_key(q, k, v, g, beta, s0):
+    """Independent formulation with a per-key gate g [B,T,Hv,Dk]:
+    S_t = S_{t-1} diag(g_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    rep = Hv // Hk
+    y = np.zeros((B, T, Hv, Dv))
+    sT = np.zeros((B, Hv, Dv, Dk))
+    for b in range(B):
+        for h in range(Hv):
+            S = np.zeros((Dv, Dk)) if s0 is None else s0[b, h].copy()
+            for t in range(T):
+                kt = k[b, t, h // rep][:, None]
+                A = np.diag(g[b, t, h]) @ (np.eye(Dk) - beta[b, t, h] * (kt @ kt.T))
+                S = S @ A + beta[b, t, h] * (v[b, t, h][:, None] @ kt.T)
+                y[b, t, h] = S @ q[b, t, h // rep]
+            sT[b, h] = S
+    return y, sT
+
+
+def rand_per_key_gate(seed, B, T, Hv, Dk):
+    return rnd(seed).uniform(0.0, 1.0, (B, T, Hv, Dk))
+
+
+def test_per_key_gate_constant_over_keys_equals_per_head_gate():
+    q, k, v, g, beta, s0 = rand_recurrence(60, 2, 9, 1, 2, 6, 5)
+    gv = np.repeat(g[..., None], 6, axis=-1)
+    y1, s1 = oracle.recurrent(q, k, v, g, beta, s0)
+    y2, s2 = oracle.recurrent(q, k, v, gv, beta, s0)
+    assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
+
+
+@pytest.mark.parametrize("shape", [(1, 7, 1, 1, 4, 3), (2, 6, 1, 2, 5, 5), (1, 5, 2, 4, 6, 4)])
+def test_per_key_gate_matches_matrix_form(shape):
+    B, T, Hk, Hv, Dk, Dv = shape
+    q, k, v, _, beta, s0 = rand_recurrence(61 + Dk, B, T, Hk, Hv, Dk, Dv)
+    g = rand_per_key_gate(62 + Dk, B, T, Hv, Dk)
+    y, s = oracle.recurrent(q, k, v, g, beta, s0)
+    y_ref, s_ref = matrix_form_per_key(q, k, v, g, beta, s0)
+    assert relerr(y, y_ref) < 1e-12 and relerr(s, s_ref) < 1e-12
+    # the orientation matters: scaling the rows of S (the value index)
+    # instead of its columns (the key index) is a different recurrence
+    if Dk == Dv:
+        y_rows = np.zeros_like(y_ref)
+        for bb in range(B):
+            for h in range(Hv):
+                S = s0[bb, h].copy()
+                for t in range(T):
+                    kt = k[bb, t, h // (Hv // Hk)][:, None]
+                    S = np.diag(g[bb, t, h]) @ S @ (np.eye(Dk) - beta[bb, t, h] * (kt @ kt.T)) \
+                        + beta[bb, t, h] * (v[bb, t, h][:, None] @ kt.T)
+                    y_rows[bb, t, h] = S @ q[bb, t, h // (Hv // Hk)]
+        assert relerr(y_rows, y_ref) > 1e-3
+
+
+def test_per_key_gate_with_beta0_is_columnwise_decay():
+    B, T, Hk, Hv, Dk, Dv = 1, 6, 1, 2, 5, 3
+    q, k, v, _, _, s0 = rand_recurrence(63, B, T, Hk, Hv, Dk, Dv)
+    g = rand_per_key_gate(64, B, T, Hv, Dk)
+    y, s = oracle.recurrent(q, k, v, g, np.zeros((B, T, Hv)), s0)
+    cum = np.cumprod(g, axis=1)                        # [B,T,Hv,Dk]
+    np.testing.assert_allclose(s, s0 * cum[:, -1][:, :, None, :], rtol=1e-14)
+    for t in range(T):
+        St = s0 * cum[:, t][:, :, None, :]
+        np.testing.assert_allclose(y[:, t], np.einsum("bhij,bhj->bhi", St, np.repeat(q[:, t], 2, axis=1)),
+                                   rtol=1e-12)
+
+
+def test_snapshots_are_prefix_states():
+    q, k, v, g, beta, s0 = rand_recurrence(65, 2, 8, 1, 2, 4, 3)
+    snaps = oracle.recurrent_snapshots(q, k, v, g, beta, [0, 3, 8], s0)
+    _, s_full = oracle.recurrent(q, k, v, g, beta, s0)
+    assert np.array_equal(snaps[0], s0) and np.array_equal(snaps[2], s_full)
+    # the state after 3 steps, carried into the remaining 5, reproduces the run
+    _, s_rest = oracle.recurrent(q[:, 3:], k[:, 3:], v[:, 3:], g[:, 3:], beta[:, 3:], snaps[1])
+    assert np.array_equal(s_rest, s_full)
