@@ -17,6 +17,8 @@ Also measured in the same run (same JSON line):
     y, gdn_gated_rmsnorm) on the prefill workload, each over 4 rotating
     buffer sets larger together than the last-level cache -> HBM roofline;
     and the gated layer core (gdn_layer_core_gated) step time;
+  * a speculative-verify window (B=64, T=4, state emitted after 1..4 steps)
+    and per-key-gate decode (B=64, T=1), both HBM-bound, rotating state sets;
   * the CPU oracle on a bounded sample of the prefill workload, one thread.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
@@ -229,6 +231,7 @@ def main():
 
     # ------------------------------------------------------------- decode
     decode = bench_decode(args, torch, dev, up, inputs, binding, np)
+    serving = bench_verify_and_per_key(args, torch, dev, up, inputs, binding, np)
 
     # -------------------------------------------------------- CPU baseline
     cpu = None
@@ -271,6 +274,8 @@ def main():
                      "frac_hbm": epi_bytes / epi_us / 1e3 / HBM_PEAK_GBS,
                      "layer_core_gated_us": gated_us},
         "decode_b64": decode,
+        "verify_window_b64": serving["verify_window"],
+        "per_key_decode_b64": serving["per_key_decode"],
         "cpu_baseline": cpu,
         "wall_s_timed": t_wall,
     }
@@ -366,11 +371,66 @@ def bench_decode(args, torch, dev, up, inputs, binding, np):
         "unit": "token*head/s",
         "us_per_step": out["layer_core"],
         "layer_core_GBs": core_bytes / out["layer_core"] / 1e3,
-        "roofline": {"bound": "hbm", "kernel": "recurrent_step_kernel<128>", "achieved": gbs,
+        "roofline": {"bound": "hbm", "kernel": "recurrent_step_kernel<128, false, false>", "achieved": gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic("recurrent_step_kernel", "decode_B64"),
                      "bytes_per_launch": rec_bytes, "avg_launch_us": out["recurrent"]},
     }
+
+
+def bench_verify_and_per_key(args, torch, dev, up, inputs, binding, np):
+    """Two serving-side uses of the per-step form, B=64 Hk=16 Hv=32
+    Dk=Dv=128, over rotating state sets: a speculative-verify window (T=4,
+    the state emitted after 1, 2, 3 and 4 steps) and decode (T=1) with the
+    per-key decay gate g [B,T,Hv,Dk]."""
+    B, Hk, Hv, Dk, Dv = 64, 16, 32, 128, 128
+    stream = torch.cuda.current_stream(dev)
+    sb = B * Hv * Dv * Dk * 4                      # one state set, bytes
+    res = {}
+    for name, T, R, per_key, steps in (("verify_window", 4, 2, False, [1, 2, 3, 4]),
+                                       ("per_key_decode", 1, 8, True, [])):
+        raw = inputs.recurrence_raw(B=B, T=T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, workload_id=7, state=True)
+        # unit-scale keys keep the state bounded over the repeated in-place steps
+        q = (up(raw["q_raw"]).view(torch.bfloat16).float() / Dk ** 0.5).to(torch.bfloat16)
+        k = (up(raw["k_raw"]).view(torch.bfloat16).float() / Dk ** 0.5).to(torch.bfloat16)
+        v = up(raw["v"])
+        g = (torch.full((B, T, Hv, Dk), 0.9, device=dev) if per_key
+             else torch.full((B, T, Hv), 0.9, device=dev))
+        beta = torch.full((B, T, Hv), 0.5, device=dev)
+        y = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+        sets = [dict(st=up(raw["state"]).clone(),
+                     snaps=torch.empty(len(steps), B, Hv, Dv, Dk, device=dev) if steps else None)
+                for _ in range(R)]
+
+        def fn(i, steps=steps, sets=sets, q=q, k=k, v=v, g=g, beta=beta, y=y, per_key=per_key):
+            s_ = sets[i % len(sets)]
+            if steps:
+                binding.recurrent_snapshots(q, k, v, g, beta, s_["st"], s_["st"], y, steps, s_["snaps"])
+            else:
+                binding.recurrent_per_key(q, k, v, g, beta, s_["st"], s_["st"], y)
+
+        for i in range(2 * R):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = max(args.decode_steps // 2, 10)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / n
+        nbytes = (2 + len(steps)) * sb + 2 * B * T * Hk * Dk * 2 + 2 * B * T * Hv * Dv * 2 + B * T * Hv * 4 \
+            + B * T * Hv * (Dk if per_key else 1) * 4
+        gbs = nbytes / us / 1e3
+        kern = "recurrent_step_kernel<128, %s, %s>" % ("true" if per_key else "false", "true" if steps else "false")
+        res[name] = {"workload": f"B={B} T={T} Hk={Hk} Hv={Hv} Dk=Dv={Dk}, {R} rotating state sets"
+                                 + (f", snapshots after {steps} steps" if steps else ", per-key gate"),
+                     "kernel": kern, "avg_launch_us": us, "bytes_per_launch": nbytes, "achieved_GBs": gbs,
+                     "frac_hbm": gbs / HBM_PEAK_GBS}
+        print(f"[bench] {name}: {us:.1f} us ({gbs:.0f} GB/s, {gbs / HBM_PEAK_GBS:.0%} of HBM)", file=sys.stderr,
+              flush=True)
+    return res
 
 
 def cpu_baseline(raw, Hk, Hv, Dk, Dv, qs, ks, eps):

@@ -218,6 +218,49 @@ gdn_status gdn_layer_core_masked(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
                                  float q_scale, float k_scale, float eps, void *stream);
 
 /*
+ * gdn_recurrent_snapshots -- the recurrence (per-step form) that also emits
+ * the state after chosen numbers of steps, so that a speculative-verify
+ * rollback to the first `keep` tokens of a window needs a copy, not a replay
+ * ("mlx-bun 0.4.0 -> 1.0.0, qwen3-delta.ts", the recurrent cache's verify
+ * round: it restores the pre-round state and replays the first `keep` window
+ * tokens, relying on the state after `keep` steps being the same arithmetic
+ * prefix whether or not the rest was processed).
+ *
+ *   snap_steps  HOST array of n_snap step counts, strictly increasing, each
+ *               in [0, T]; n_snap in [0, 32].  Count n means "after the first
+ *               n steps" (0 = state_in, T = state_out); masked steps count.
+ *   snapshots   device f32 [n_snap, B, Hv, Dv, Dk], written (NULL allowed
+ *               when n_snap == 0 or B == 0); must not overlap anything else.
+ *   g_per_key   0: g is [B, T, Hv] (per-head decay, as gdn_recurrent_masked);
+ *               1: g is [B, T, Hv, Dk], the per-key ("vectorized") decay that
+ *               the same page names beside the per-head gate it ports:
+ *               S[i][j] <- g_t[j] * S[i][j] at the decay step, all else as
+ *               gdn_recurrent.
+ *
+ * The other arguments and rules are those of gdn_recurrent_masked.  The
+ * state (state_out and every snapshot) is bit-identical to the state_out of
+ * gdn_recurrent_masked run over the same prefix (per-head gate); y agrees
+ * within the recurrence tolerance (y may differ in the last bit for T >= 8,
+ * where gdn_recurrent stages the steps through a different kernel).
+ */
+gdn_status gdn_recurrent_snapshots(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_bf16 *v,
+                                   const float *g, int g_per_key, const float *beta,
+                                   const uint8_t *mask, const float *state_in, float *state_out,
+                                   gdn_bf16 *y, const int32_t *snap_steps, int n_snap,
+                                   float *snapshots, int B, int T, int Hk, int Hv, int Dk, int Dv,
+                                   void *stream);
+
+/*
+ * gdn_recurrent_per_key -- the recurrence with the per-key decay gate g
+ * [B, T, Hv, Dk] f32 (gdn_recurrent_snapshots with g_per_key = 1 and no
+ * snapshots).  Per-step form for every T.
+ */
+gdn_status gdn_recurrent_per_key(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_bf16 *v,
+                                 const float *g, const float *beta, const uint8_t *mask,
+                                 const float *state_in, float *state_out, gdn_bf16 *y,
+                                 int B, int T, int Hk, int Hv, int Dk, int Dv, void *stream);
+
+/*
  * gdn_gated_rmsnorm -- output epilogue of the layer: gated RMS normalisation
  * of the recurrence output ("mlex 0.1.2 -- src/models/gated_delta.rs",
  * GatedDeltaNet::forward, the step after the recurrence loop).  Per row of Dv

@@ -65,6 +65,10 @@ def lib():
         L.gdn_layer_core_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_layer_core.argtypes = [_p] * 12 + [ctypes.c_size_t] + [_i] * 7 + [_f] * 3 + [_p]
         L.gdn_layer_core.restype = _i
+        L.gdn_recurrent_snapshots.argtypes = [_p] * 4 + [_i] + [_p] * 6 + [_i, _p] + [_i] * 6 + [_p]
+        L.gdn_recurrent_snapshots.restype = _i
+        L.gdn_recurrent_per_key.argtypes = [_p] * 9 + [_i] * 6 + [_p]
+        L.gdn_recurrent_per_key.restype = _i
         L.gdn_gated_rmsnorm.argtypes = [_p] * 4 + [_i] * 4 + [_f, _p]
         L.gdn_gated_rmsnorm.restype = _i
         L.gdn_layer_core_gated.argtypes = [_p] * 15 + [ctypes.c_size_t] + [_i] * 7 + [_f] * 4 + [_p]
@@ -278,4 +282,55 @@ def layer_core_gated(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt
     ]
     _check(lib().gdn_layer_core_gated(*args, ws_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps,
                                       norm_eps, _stream(dev, stream)))
+
+
+def recurrent_snapshots(q, k, v, g, beta, state_in, state_out, y, snap_steps, snapshots, *, mask=None,
+                        stream=None):
+    """The recurrence (per-step form) that also writes the state after each
+    step count in ``snap_steps`` (a list of strictly increasing ints in
+    [0, T], at most 32) into ``snapshots`` [n, B, Hv, Dv, Dk] f32
+    (gdn_recurrent_snapshots).  ``g`` is [B,T,Hv] (per-head decay) or
+    [B,T,Hv,Dk] (per-key decay); other arguments as ``recurrent``."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dev = q.device
+    per_key = g is not None and g.dim() == 4
+    steps = [int(s_) for s_ in snap_steps]
+    arr = (ctypes.c_int32 * max(len(steps), 1))(*steps)
+    args = [
+        _ptr(q, "q", _BF16, (B, T, Hk, Dk), dev),
+        _ptr(k, "k", _BF16, (B, T, Hk, Dk), dev),
+        _ptr(v, "v", _BF16, (B, T, Hv, Dv), dev),
+        _ptr(g, "g", (torch.float32,), (B, T, Hv, Dk) if per_key else (B, T, Hv), dev),
+    ]
+    rest = [
+        _ptr(beta, "beta", (torch.float32,), (B, T, Hv), dev),
+        _ptr(mask, "mask", _MASK, (B, T), dev),
+        _ptr(state_in, "state_in", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(state_out, "state_out", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
+    ]
+    snaps = _ptr(snapshots, "snapshots", (torch.float32,), (len(steps), B, Hv, Dv, Dk), dev)
+    _check(lib().gdn_recurrent_snapshots(*args, int(per_key), *rest, ctypes.cast(arr, ctypes.c_void_p),
+                                         len(steps), snaps, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream)))
+
+
+def recurrent_per_key(q, k, v, g, beta, state_in, state_out, y, *, mask=None, stream=None):
+    """The recurrence with the per-key decay gate g [B,T,Hv,Dk] f32
+    (gdn_recurrent_per_key); other arguments as ``recurrent``."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dev = q.device
+    args = [
+        _ptr(q, "q", _BF16, (B, T, Hk, Dk), dev),
+        _ptr(k, "k", _BF16, (B, T, Hk, Dk), dev),
+        _ptr(v, "v", _BF16, (B, T, Hv, Dv), dev),
+        _ptr(g, "g", (torch.float32,), (B, T, Hv, Dk), dev),
+        _ptr(beta, "beta", (torch.float32,), (B, T, Hv), dev),
+        _ptr(mask, "mask", _MASK, (B, T), dev),
+        _ptr(state_in, "state_in", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(state_out, "state_out", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
+    ]
+    _check(lib().gdn_recurrent_per_key(*args, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream)))
 

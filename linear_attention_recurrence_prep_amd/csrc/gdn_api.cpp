@@ -103,12 +103,13 @@ gdn_status hip_result(hipError_t e, const char* what) {
 gdn_status validate_recurrent(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,
                               const float* beta, const uint8_t* mask, const float* state_in, float* state_out,
                               gdn_bf16* y, int B, int T, int Hk, int Hv, int Dk, int Dv,
-                              bool check_overlap = true) {
+                              bool check_overlap = true, bool g_per_key = false,
+                              const float* snapshots = nullptr, uint64_t snapshot_bytes = 0) {
     gdn_status st = check_dims(B, T, Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
-    uint64_t nqk, nv, ng, ns;
+    uint64_t nqk, nv, ng, ns, ngate;
     if (!elems(nqk, {B, T, Hk, Dk}) || !elems(nv, {B, T, Hv, Dv}) || !elems(ng, {B, T, Hv}) ||
-        !elems(ns, {B, Hv, Dv, Dk}))
+        !elems(ns, {B, Hv, Dv, Dk}) || !elems(ngate, {B, T, Hv, g_per_key ? Dk : 1}))
         return fail(GDN_ERR_BAD_DIMS, "tensor sizes overflow");
     if (gdn::recurrent_blocks(B, Hv, Dk, Dv) > kMaxBlocks) return fail(GDN_ERR_BAD_DIMS, "grid too large");
     if (B > 0 && !state_out) return fail(GDN_ERR_NULL_POINTER, "state_out is NULL");
@@ -123,10 +124,11 @@ gdn_status validate_recurrent(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf
     if (!check_overlap) return GDN_OK;
     std::vector<Span> s = {
         {"q", q, nqk * 2, false},        {"k", k, nqk * 2, false},
-        {"v", v, nv * 2, false},         {"g", g, ng * 4, false},
+        {"v", v, nv * 2, false},         {"g", g, ngate * 4, false},
         {"beta", beta, ng * 4, false},   {"state_in", state_in, ns * 4, false},
         {"state_out", state_out, ns * 4, true}, {"y", y, nv * 2, true},
         {"mask", mask, (uint64_t)B * T, false, 1},
+        {"snapshots", snapshots, snapshot_bytes, true},
     };
     return check_spans(s, {{5, 6}});
 }
@@ -276,6 +278,47 @@ gdn_status gdn_recurrent_masked(const gdn_bf16* q, const gdn_bf16* k, const gdn_
     if (B == 0) return ok();
     gdn::RecurrentArgs a{q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, mask};
     return hip_result(gdn::launch_recurrent(a, static_cast<hipStream_t>(stream)), "recurrent");
+}
+
+gdn_status gdn_recurrent_snapshots(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,
+                                   int g_per_key, const float* beta, const uint8_t* mask, const float* state_in,
+                                   float* state_out, gdn_bf16* y, const int32_t* snap_steps, int n_snap,
+                                   float* snapshots, int B, int T, int Hk, int Hv, int Dk, int Dv, void* stream) {
+    if (n_snap < 0 || n_snap > gdn::kMaxSnapshots)
+        return fail(GDN_ERR_BAD_VALUE, "n_snap=%d not in [0, %d]", n_snap, gdn::kMaxSnapshots);
+    gdn::SnapList sl;
+    sl.n = n_snap;
+    if (n_snap > 0) {
+        if (!snap_steps) return fail(GDN_ERR_NULL_POINTER, "snap_steps is NULL");
+        for (int i = 0; i < n_snap; ++i) {
+            const int32_t t = snap_steps[i];
+            if (t < 0 || t > T) return fail(GDN_ERR_BAD_VALUE, "snap_steps[%d]=%d not in [0, T=%d]", i, t, T);
+            if (i > 0 && t <= snap_steps[i - 1])
+                return fail(GDN_ERR_BAD_VALUE, "snap_steps must be strictly increasing (entry %d)", i);
+            sl.steps[i] = t;
+        }
+    }
+    gdn_status st = check_dims(B, T, Hk, Hv, Dk, Dv);
+    if (st != GDN_OK) return st;
+    uint64_t ns;
+    if (!elems(ns, {n_snap, B, Hv, Dv, Dk})) return fail(GDN_ERR_BAD_DIMS, "snapshot size overflows");
+    if (n_snap > 0 && B > 0 && !snapshots) return fail(GDN_ERR_NULL_POINTER, "snapshots is NULL");
+    st = validate_recurrent(q, k, v, g, beta, mask, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, true,
+                            g_per_key != 0, n_snap > 0 ? snapshots : nullptr, ns * 4);
+    if (st != GDN_OK) return st;
+    if (B == 0) return ok();
+    sl.out = snapshots;
+    gdn::RecurrentArgs a{q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, mask};
+    a.g_per_key = g_per_key != 0;
+    a.snap = n_snap > 0 ? &sl : nullptr;
+    return hip_result(gdn::launch_recurrent(a, static_cast<hipStream_t>(stream)), "recurrent");
+}
+
+gdn_status gdn_recurrent_per_key(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,
+                                 const float* beta, const uint8_t* mask, const float* state_in, float* state_out,
+                                 gdn_bf16* y, int B, int T, int Hk, int Hv, int Dk, int Dv, void* stream) {
+    return gdn_recurrent_snapshots(q, k, v, g, 1, beta, mask, state_in, state_out, y, nullptr, 0, nullptr, B, T,
+                                   Hk, Hv, Dk, Dv, stream);
 }
 
 gdn_status gdn_recurrent(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,

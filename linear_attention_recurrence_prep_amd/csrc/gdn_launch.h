@@ -7,6 +7,14 @@
 
 namespace gdn {
 
+// States to emit after chosen step counts (the per-step kernels only).
+constexpr int kMaxSnapshots = 32;
+struct SnapList {
+    int n = 0;                      // number of snapshots (0 = none)
+    int steps[kMaxSnapshots] = {};  // strictly increasing step counts in [0, T]
+    float* out = nullptr;           // [n, B, Hv, Dv, Dk]
+};
+
 struct RecurrentArgs {
     const uint16_t* q;
     const uint16_t* k;
@@ -18,6 +26,8 @@ struct RecurrentArgs {
     uint16_t* y;
     int B, T, Hk, Hv, Dk, Dv;
     const uint8_t* mask = nullptr;   // [B, T] step mask (0 = inactive), may be null
+    bool g_per_key = false;          // g is [B, T, Hv, Dk] (per-key decay)
+    const SnapList* snap = nullptr;  // states after chosen step counts, may be null
 };
 
 struct PrepArgs {

@@ -297,13 +297,40 @@ __global__ __launch_bounds__(256) void recurrent_chunk_kernel(
 // columns straight from HBM/L2 for every step (bf16, 2 x 8 bytes each), the
 // state is streamed in and out once (non-temporal: it is not reused), and y
 // leaves from lane 0 of each row group.
+//
+// Two options (compile-time, so the plain kernel is unchanged):
+//   VG    per-key decay, g [B, T, Hv, Dk]: S <- S diag(g_t).  In the factored
+//         form a = S (g.k) and c = S (g.q) (elementwise products of the
+//         lane's 8 columns), delta = (v - a) beta, y = c + delta (k.q),
+//         S = g.S + delta k^T.
+//   SNAP  after every step count listed in the snapshot list (0 = before the
+//         first step), the row's state is also written to that snapshot.
+
+// Entry i of the snapshot list (i uniform; static indexing only, so the
+// by-value kernel argument is never copied to scratch).  -1 past the end.
+__device__ __forceinline__ int snap_step(const SnapList& sl, int i) {
+    int r = -1;
+#pragma unroll
+    for (int u = 0; u < kMaxSnapshots; ++u)
+        if (u == i && u < sl.n) r = sl.steps[u];
+    return r;
+}
 
 template <int DK>
+__device__ __forceinline__ void store_row(float* dst, const float (&s)[8], int j) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v o0 = {s[0], s[1], s[2], s[3]};
+    const f4v o1 = {s[4], s[5], s[6], s[7]};
+    __builtin_nontemporal_store(o0, reinterpret_cast<f4v*>(dst + 4 * j));
+    __builtin_nontemporal_store(o1, reinterpret_cast<f4v*>(dst + DK / 2 + 4 * j));
+}
+
+template <int DK, bool VG, bool SNAP>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const uint8_t* __restrict__ mask,
     const float* state_in, float* state_out, uint16_t* __restrict__ y,
-    int T, int Hk, int Hv, int Dv, int row_blocks, int n_blocks) {
+    int T, int Hk, int Hv, int Dv, int row_blocks, int n_blocks, SnapList snap, int64_t snap_stride) {
     using C = RecCfg<DK>;
     constexpr int L = C::L;
     const int lb = xcd_block(n_blocks);
@@ -332,12 +359,21 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
         for (int i = 0; i < 8; ++i) s[i] = 0.f;
     }
 
+    int snap_i = 0, snap_next = -1;
+    if constexpr (SNAP) {
+        snap_next = snap_step(snap, 0);
+        if (snap_next == 0) {
+            if (row_ok) store_row<DK>(snap.out + srow, s, j);
+            snap_i = 1;
+            snap_next = snap_step(snap, 1);
+        }
+    }
+
     for (int t = 0; t < T; ++t) {
         const int64_t tok = (int64_t)b * T + t;
         if (mask != nullptr && mask[tok] == 0) {      // masked step: state kept, y = 0
             if (j == 0 && row_ok) y[(tok * Hv + hv) * Dv + row] = 0;
-            continue;
-        }
+        } else {
         const uint16_t* kp = k + (tok * Hk + hk) * DK;
         const uint16_t* qp = q + (tok * Hk + hk) * DK;
         const uint2 kw0 = *reinterpret_cast<const uint2*>(kp + 4 * j);
@@ -345,34 +381,60 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
         const uint2 qw0 = *reinterpret_cast<const uint2*>(qp + 4 * j);
         const uint2 qw1 = *reinterpret_cast<const uint2*>(qp + DK / 2 + 4 * j);
         const float vt = bf16lo(v[(tok * Hv + hv) * Dv + rowc]);
-        const float gt = g[tok * Hv + hv];
         const float bt = beta[tok * Hv + hv];
         const float kk[8] = {bf16lo(kw0.x), bf16hi(kw0.x), bf16lo(kw0.y), bf16hi(kw0.y),
                              bf16lo(kw1.x), bf16hi(kw1.x), bf16lo(kw1.y), bf16hi(kw1.y)};
         const float qq[8] = {bf16lo(qw0.x), bf16hi(qw0.x), bf16lo(qw0.y), bf16hi(qw0.y),
                              bf16lo(qw1.x), bf16hi(qw1.x), bf16lo(qw1.y), bf16hi(qw1.y)};
-        float a = 0.f, c = 0.f, kq = 0.f;
+        if constexpr (VG) {
+            const float* gp = g + (tok * Hv + hv) * DK;
+            const float4 g0 = *reinterpret_cast<const float4*>(gp + 4 * j);
+            const float4 g1 = *reinterpret_cast<const float4*>(gp + DK / 2 + 4 * j);
+            const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            float a = 0.f, c = 0.f, kq = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            a = fmaf(s[i], kk[i], a);
-            c = fmaf(s[i], qq[i], c);
-            kq = fmaf(kk[i], qq[i], kq);
+            for (int i = 0; i < 8; ++i) {
+                const float gs = gg[i] * s[i];        // the decayed state element
+                a = fmaf(gs, kk[i], a);
+                c = fmaf(gs, qq[i], c);
+                kq = fmaf(kk[i], qq[i], kq);
+                s[i] = gs;
+            }
+            group_sum2<L>(a, c);
+            kq = group_sum<L>(kq);
+            const float delta = (vt - a) * bt;
+            const float yo = fmaf(delta, kq, c);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s[i] = fmaf(delta, kk[i], s[i]);
+            if (j == 0 && row_ok) y[(tok * Hv + hv) * Dv + row] = (uint16_t)f32_to_bf16(yo);
+        } else {
+            const float gt = g[tok * Hv + hv];
+            float a = 0.f, c = 0.f, kq = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                a = fmaf(s[i], kk[i], a);
+                c = fmaf(s[i], qq[i], c);
+                kq = fmaf(kk[i], qq[i], kq);
+            }
+            group_sum2<L>(a, c);
+            kq = group_sum<L>(kq);
+            const float delta = fmaf(-gt, a, vt) * bt;
+            const float yo = fmaf(gt, c, delta * kq);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s[i] = fmaf(delta, kk[i], gt * s[i]);
+            if (j == 0 && row_ok) y[(tok * Hv + hv) * Dv + row] = (uint16_t)f32_to_bf16(yo);
         }
-        group_sum2<L>(a, c);
-        kq = group_sum<L>(kq);
-        const float delta = fmaf(-gt, a, vt) * bt;
-        const float yo = fmaf(gt, c, delta * kq);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s[i] = fmaf(delta, kk[i], gt * s[i]);
-        if (j == 0 && row_ok) y[(tok * Hv + hv) * Dv + row] = (uint16_t)f32_to_bf16(yo);
+        }
+        if constexpr (SNAP) {
+            if (t + 1 == snap_next) {
+                if (row_ok) store_row<DK>(snap.out + snap_i * snap_stride + srow, s, j);
+                ++snap_i;
+                snap_next = snap_step(snap, snap_i);
+            }
+        }
     }
 
-    if (row_ok) {
-        const f4v o0 = {s[0], s[1], s[2], s[3]};
-        const f4v o1 = {s[4], s[5], s[6], s[7]};
-        __builtin_nontemporal_store(o0, reinterpret_cast<f4v*>(state_out + srow + 4 * j));
-        __builtin_nontemporal_store(o1, reinterpret_cast<f4v*>(state_out + srow + DK / 2 + 4 * j));
-    }
+    if (row_ok) store_row<DK>(state_out + srow, s, j);
 }
 
 // ================================================================== launch
@@ -393,16 +455,47 @@ static hipError_t launch_rec(const RecurrentArgs& a, hipStream_t stream, bool ch
                            a.q, a.k, a.v, a.g, a.beta, a.mask, a.state_in, a.state_out, a.y, a.T, a.Hk, a.Hv,
                            a.Dv, row_blocks, (int)blocks);
     else
-        hipLaunchKernelGGL((recurrent_step_kernel<DK>), dim3((unsigned)blocks), dim3(C::NT), 0, stream,
-                           a.q, a.k, a.v, a.g, a.beta, a.mask, a.state_in, a.state_out, a.y, a.T, a.Hk, a.Hv,
-                           a.Dv, row_blocks, (int)blocks);
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, false, false>), dim3((unsigned)blocks), dim3(C::NT), 0,
+                           stream, a.q, a.k, a.v, a.g, a.beta, a.mask, a.state_in, a.state_out, a.y, a.T, a.Hk,
+                           a.Hv, a.Dv, row_blocks, (int)blocks, SnapList{}, (int64_t)0);
     return hipGetLastError();
+}
+
+// The per-step kernel with its options: per-key decay and/or snapshots.
+template <int DK, bool VG, bool SNAP>
+static hipError_t launch_step_opt(const RecurrentArgs& a, hipStream_t stream) {
+    using C = RecCfg<DK>;
+    const int row_blocks = (a.Dv + C::ROWS - 1) / C::ROWS;
+    const int64_t blocks = (int64_t)a.B * a.Hv * row_blocks;
+    if (blocks <= 0) return hipSuccess;
+    const SnapList sl = SNAP ? *a.snap : SnapList{};
+    const int64_t stride = (int64_t)a.B * a.Hv * a.Dv * DK;
+    hipLaunchKernelGGL((recurrent_step_kernel<DK, VG, SNAP>), dim3((unsigned)blocks), dim3(C::NT), 0, stream,
+                       a.q, a.k, a.v, a.g, a.beta, a.mask, a.state_in, a.state_out, a.y, a.T, a.Hk, a.Hv, a.Dv,
+                       row_blocks, (int)blocks, sl, stride);
+    return hipGetLastError();
+}
+
+template <int DK>
+static hipError_t launch_opt(const RecurrentArgs& a, hipStream_t stream) {
+    const bool snap = a.snap != nullptr && a.snap->n > 0;
+    if (a.g_per_key) return snap ? launch_step_opt<DK, true, true>(a, stream) : launch_step_opt<DK, true, false>(a, stream);
+    return snap ? launch_step_opt<DK, false, true>(a, stream) : launch_step_opt<DK, false, false>(a, stream);
 }
 
 // Sequences shorter than this run the staging-free kernel.
 constexpr int kChunkedMinT = 8;
 
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream) {
+    if (a.g_per_key || (a.snap != nullptr && a.snap->n > 0)) {
+        switch (a.Dk) {
+            case 32: return launch_opt<32>(a, stream);
+            case 64: return launch_opt<64>(a, stream);
+            case 128: return launch_opt<128>(a, stream);
+            case 256: return launch_opt<256>(a, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     const bool chunked = a.T >= kChunkedMinT;
     switch (a.Dk) {
         case 32: return launch_rec<32, 64>(a, stream, chunked);

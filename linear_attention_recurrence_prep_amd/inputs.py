@@ -36,7 +36,7 @@ SEED = 1234
 TENSOR_IDS = {
     "qkv": 0, "conv_w": 1, "conv_state": 2, "a": 3, "b": 4, "A_log": 5,
     "dt_bias": 6, "state": 7, "q_raw": 8, "k_raw": 9, "v": 10,
-    "z": 11, "norm_weight": 12, "y": 13, "row_scale": 14,
+    "z": 11, "norm_weight": 12, "y": 13, "row_scale": 14, "g_key": 15,
 }
 
 WORKLOADS = {
@@ -147,6 +147,11 @@ def epilogue_raw(*, B, T, Hv, Dv, workload_id=5, with_y=True, seed=SEED):
         scale = np.exp2(generator(w, "row_scale", seed).uniform(-24.0, 4.0, (B, T, Hv, 1))).astype(np.float32)
         out["y"] = f32_to_bf16_bits(normal_f32(generator(w, "y", seed), (B, T, Hv, Dv)) * scale)
     return out
+
+
+def per_key_gate(*, B, T, Hv, Dk, workload_id=6, seed=SEED):
+    """A per-key decay gate g [B,T,Hv,Dk] f32 ~ U[0.3, 1)."""
+    return generator(workload_id, "g_key", seed).uniform(0.3, 1.0, (B, T, Hv, Dk)).astype(np.float32)
 
 
 def workload(name: str, seed: int = SEED):

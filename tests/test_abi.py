@@ -283,3 +283,45 @@ def test_layer_core_gated_rejects(L):
     assert f(z=addr(20) + 256) == OVERLAP      # z inside the workspace
     assert f(z=addr(3)) == OVERLAP             # z over conv_state_out
     assert f(B=0) == OK
+
+
+def call_snap(L, steps=(1, 3), n=None, snaps=addr(9), per_key=0, **over):
+    p, d = rec_args(**over)
+    arr = (ctypes.c_int32 * max(len(steps), 1))(*steps)
+    n = len(steps) if n is None else n
+    return L.gdn_recurrent_snapshots(p["q"], p["k"], p["v"], p["g"], per_key, p["beta"], None, p["state_in"],
+                                     p["state_out"], p["y"], ctypes.cast(arr, ctypes.c_void_p), n, snaps,
+                                     d["B"], d["T"], d["Hk"], d["Hv"], d["Dk"], d["Dv"], None)
+
+
+def test_snapshots_reject(L):
+    assert call_snap(L, n=33) == VALUE
+    assert call_snap(L, n=-1) == VALUE
+    assert call_snap(L, steps=(3, 3)) == VALUE          # not strictly increasing
+    assert call_snap(L, steps=(2, 1)) == VALUE
+    assert call_snap(L, steps=(0, 9)) == VALUE          # beyond T = 8
+    assert call_snap(L, steps=(-1,)) == VALUE
+    assert call_snap(L, snaps=None) == NULLP
+    assert call_snap(L, snaps=addr(9) + 8) == ALIGN
+    assert call_snap(L, snaps=addr(7) + 16) == OVERLAP  # inside y
+    assert call_snap(L, snaps=addr(0)) == OVERLAP       # over q
+    assert call_snap(L, Dk=48) == UNSUP
+    assert call_snap(L, B=0) == OK
+    assert call_snap(L, B=0, snaps=None) == OK
+    arr = (ctypes.c_int32 * 1)(1)
+    p, d = rec_args()
+    assert L.gdn_recurrent_snapshots(p["q"], p["k"], p["v"], p["g"], 0, p["beta"], None, p["state_in"],
+                                     p["state_out"], p["y"], None, 2, addr(9), d["B"], d["T"], d["Hk"],
+                                     d["Hv"], d["Dk"], d["Dv"], None) == NULLP
+
+
+def test_per_key_gate_span_is_checked(L):
+    # g [B,T,Hv,Dk] f32 spans B*T*Hv*Dk*4 bytes: an output just past the
+    # per-head extent but inside the per-key extent overlaps it
+    p, d = rec_args()
+    inside = addr(3) + d["B"] * d["T"] * d["Hv"] * 4 + 64
+    assert L.gdn_recurrent_per_key(p["q"], p["k"], p["v"], p["g"], p["beta"], None, p["state_in"], inside,
+                                   p["y"], d["B"], d["T"], d["Hk"], d["Hv"], d["Dk"], d["Dv"], None) == OVERLAP
+    assert call_snap(L, snaps=inside, per_key=1) == OVERLAP
+    assert L.gdn_recurrent_per_key(p["q"], p["k"], p["v"], None, p["beta"], None, p["state_in"], addr(6),
+                                   p["y"], d["B"], d["T"], d["Hk"], d["Hv"], d["Dk"], d["Dv"], None) == NULLP

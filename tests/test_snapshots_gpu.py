@@ -1,0 +1,190 @@
+"""GPU parity of the per-step recurrence's options, through the C ABI:
+state snapshots after chosen step counts (for speculative-verify rollback)
+and the per-key ("vectorized") decay gate g [B,T,Hv,Dk].  Snapshots are
+checked bit for bit against the state of prefix runs and within the
+recurrence tolerances against the oracle; the per-key gate against the
+oracle (y within 1 bf16 ulp + 1e-3, state normwise <= 1e-4)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_recurrence_prep_amd import binding, inputs
+from tests import helpers as H
+from tests.test_parity_gpu import gpu_recurrent, rec_inputs, step_mask
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = 0x7FC0
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    binding.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_snapshots(ri, steps, mask=None, g=None):
+    """Run gdn_recurrent_snapshots; returns (y bits, state_out, snapshots)."""
+    B, T, Hk, Dk = ri["q"].shape
+    Hv, Dv = ri["v"].shape[2], ri["v"].shape[3]
+    d = {n: H.to_dev(ri[n]) for n in ("q", "k", "v", "beta")}
+    gg = H.to_dev(np.ascontiguousarray(ri["g"] if g is None else g, dtype=np.float32))
+    s_in = H.to_dev(ri["state"]) if ri.get("state") is not None else None
+    s_out = torch.full((B, Hv, Dv, Dk), float("nan"), device=H.DEV)
+    yfull, y = H.guarded((B, T, Hv, Dv), torch.int16, NAN_BF16)
+    sfull, snaps = H.guarded((len(steps), B, Hv, Dv, Dk), torch.float32, float("nan"))
+    m = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).to(H.DEV)
+    binding.recurrent_snapshots(d["q"], d["k"], d["v"], gg, d["beta"], s_in, s_out, y, steps, snaps, mask=m)
+    torch.cuda.synchronize()
+    assert H.guards_intact(yfull, NAN_BF16) and H.guards_intact(sfull, float("nan"))
+    return H.bits(y), H.f32(s_out), H.f32(snaps)
+
+
+def prefix(ri, n):
+    return {k: (v if k == "state" or v is None else np.ascontiguousarray(v[:, :n])) for k, v in ri.items()}
+
+
+SNAP_CASES = [
+    # B, T, Hk, Hv, Dk, Dv, steps, wid
+    (2, 12, 2, 4, 64, 32, [0, 1, 5, 8, 12], 700),
+    (16, 4, 2, 4, 128, 128, [1, 2, 3, 4], 701),        # a verify window of 4 draft tokens
+    (1, 40, 1, 2, 32, 16, [3, 17, 33, 39], 702),
+    (2, 6, 1, 1, 256, 24, [2, 6], 703),
+]
+
+
+@pytest.mark.parametrize("case", SNAP_CASES, ids=lambda c: "B%dT%dDk%dDv%d" % (c[0], c[1], c[4], c[5]))
+def test_snapshots_equal_prefix_states(case):
+    B, T, Hk, Hv, Dk, Dv, steps, wid = case
+    say("snapshots", case)
+    ri = rec_inputs(B, T, Hk, Hv, Dk, Dv, wid)
+    y, s, snaps = gpu_snapshots(ri, steps)
+    # state_out and y of the plain call (bit for bit: the state arithmetic is
+    # the same in every per-step kernel; y too when both run the step kernel)
+    y0, s0 = gpu_recurrent(ri)
+    assert np.array_equal(s, s0)
+    if T < 8:
+        assert np.array_equal(y, y0)
+    # each snapshot is the state of the run over that prefix
+    for i, n in enumerate(steps):
+        if n == 0:
+            assert np.array_equal(snaps[i], ri["state"])
+        else:
+            _, sn = gpu_recurrent(prefix(ri, n))
+            assert np.array_equal(snaps[i], sn), f"snapshot after {n} steps"
+    # and against the oracle
+    f = oracle.bf16_to_f64
+    ref = oracle.recurrent_snapshots(f(ri["q"]), f(ri["k"]), f(ri["v"]), ri["g"], ri["beta"], steps, ri["state"])
+    for i in range(len(steps)):
+        H.check_state(snaps[i], ref[i], 1e-4, f"snapshot {steps[i]}")
+    y_ref, _ = oracle.recurrent(f(ri["q"]), f(ri["k"]), f(ri["v"]), ri["g"], ri["beta"], ri["state"])
+    H.check_y(y, y_ref, str(case))
+
+
+def test_snapshots_count_masked_steps():
+    B, T, Hk, Hv, Dk, Dv = 2, 10, 1, 2, 128, 32
+    ri = rec_inputs(B, T, Hk, Hv, Dk, Dv, 704)
+    mask = step_mask(704, B, T)
+    steps = [2, 5, 10]
+    y, s, snaps = gpu_snapshots(ri, steps, mask=mask)
+    f = oracle.bf16_to_f64
+    ref = oracle.recurrent_snapshots(f(ri["q"]), f(ri["k"]), f(ri["v"]), ri["g"], ri["beta"], steps, ri["state"],
+                                     mask=mask)
+    for i in range(len(steps)):
+        H.check_state(snaps[i], ref[i], 1e-4, f"masked snapshot {steps[i]}")
+    assert np.array_equal(snaps[-1], s) and not y[mask == 0].any()
+    _, s0 = gpu_recurrent(ri, mask=mask)
+    assert np.array_equal(s, s0)
+
+
+def test_snapshot_rollback_then_continue():
+    """A verify round: run the window with snapshots, roll back to `keep`
+    tokens by taking that snapshot, continue with the next tokens; the state
+    equals a run over the accepted tokens followed by the new ones."""
+    B, Hk, Hv, Dk, Dv = 4, 2, 4, 128, 64
+    ri = rec_inputs(B, 9, Hk, Hv, Dk, Dv, 705)
+    window = prefix(ri, 5)
+    _, _, snaps = gpu_snapshots(window, [1, 2, 3, 4, 5])
+    keep = 3
+    tail = {k: (None if k == "state" else np.ascontiguousarray(v[:, 5:])) for k, v in ri.items()}
+    tail["state"] = snaps[keep - 1]
+    _, s_roll = gpu_recurrent(tail)
+    direct = {k: (v if k == "state" else np.ascontiguousarray(np.concatenate([v[:, :keep], v[:, 5:]], axis=1)))
+              for k, v in ri.items()}
+    _, s_direct = gpu_recurrent(direct)
+    # accepted prefix + new tokens as one run (T = 7 here: step kernel both
+    # times; the split at `keep` is exact in the per-step form)
+    assert np.array_equal(s_roll, s_direct)
+
+
+PK_CASES = [
+    # B, T, Hk, Hv, Dk, Dv, wid
+    (2, 5, 2, 4, 64, 32, 710),
+    (1, 33, 1, 2, 32, 16, 711),
+    (4, 1, 2, 4, 128, 128, 712),      # decode
+    (1, 20, 2, 4, 128, 64, 713),
+    (1, 9, 1, 1, 256, 40, 714),
+]
+
+
+@pytest.mark.parametrize("case", PK_CASES, ids=lambda c: "B%dT%dDk%dDv%d" % (c[0], c[1], c[4], c[5]))
+def test_per_key_gate_matches_oracle(case):
+    B, T, Hk, Hv, Dk, Dv, wid = case
+    say("per-key gate", case)
+    ri = rec_inputs(B, T, Hk, Hv, Dk, Dv, wid)
+    gk = inputs.per_key_gate(B=B, T=T, Hv=Hv, Dk=Dk, workload_id=wid)
+    mask = step_mask(wid, B, T) if T > 4 else None
+    d = {n: H.to_dev(ri[n]) for n in ("q", "k", "v", "beta")}
+    s_out = torch.empty(B, Hv, Dv, Dk, device=H.DEV)
+    yfull, y = H.guarded((B, T, Hv, Dv), torch.int16, NAN_BF16)
+    m = None if mask is None else torch.from_numpy(mask).to(H.DEV)
+    binding.recurrent_per_key(d["q"], d["k"], d["v"], H.to_dev(gk), d["beta"], H.to_dev(ri["state"]), s_out, y,
+                              mask=m)
+    torch.cuda.synchronize()
+    assert H.guards_intact(yfull, NAN_BF16)
+    f = oracle.bf16_to_f64
+    y_ref, s_ref = oracle.recurrent(f(ri["q"]), f(ri["k"]), f(ri["v"]), gk.astype(np.float64), ri["beta"],
+                                    ri["state"], mask=mask)
+    H.check_y(H.bits(y), y_ref, str(case))
+    e = H.check_state(H.f32(s_out), s_ref, 1e-4, str(case))
+    say("per-key state err", e)
+    # the same through the snapshot entry point, with snapshots
+    steps = sorted({1, T // 2, T} - {0}) if T > 1 else [1]
+    y2, s2, snaps = gpu_snapshots(ri, steps, mask=mask, g=gk)
+    assert np.array_equal(y2, H.bits(y)) and np.array_equal(s2, H.f32(s_out))
+    ref = oracle.recurrent_snapshots(f(ri["q"]), f(ri["k"]), f(ri["v"]), gk.astype(np.float64), ri["beta"], steps,
+                                     ri["state"], mask=mask)
+    for i in range(len(steps)):
+        H.check_state(snaps[i], ref[i], 1e-4, f"per-key snapshot {steps[i]}")
+
+
+def test_per_key_gate_identities():
+    """g = 1 with beta = 0 keeps the state exactly; a gate constant over the
+    keys matches the per-head gate within the tolerances."""
+    B, T, Hk, Hv, Dk, Dv = 2, 6, 2, 4, 128, 32
+    ri = rec_inputs(B, T, Hk, Hv, Dk, Dv, 715)
+    d = {n: H.to_dev(ri[n]) for n in ("q", "k", "v")}
+    s_out = torch.empty(B, Hv, Dv, Dk, device=H.DEV)
+    y = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=H.DEV)
+    ones = torch.ones(B, T, Hv, Dk, device=H.DEV)
+    binding.recurrent_per_key(d["q"], d["k"], d["v"], ones, torch.zeros(B, T, Hv, device=H.DEV),
+                              H.to_dev(ri["state"]), s_out, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(H.f32(s_out), ri["state"])
+    gk = np.repeat(ri["g"][..., None], Dk, axis=-1)
+    binding.recurrent_per_key(d["q"], d["k"], d["v"], H.to_dev(gk), H.to_dev(ri["beta"]), H.to_dev(ri["state"]),
+                              s_out, y)
+    torch.cuda.synchronize()
+    f = oracle.bf16_to_f64
+    y_ref, s_ref = oracle.recurrent(f(ri["q"]), f(ri["k"]), f(ri["v"]), ri["g"], ri["beta"], ri["state"])
+    H.check_y(H.bits(y), y_ref)
+    H.check_state(H.f32(s_out), s_ref, 1e-4)
