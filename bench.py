@@ -17,6 +17,8 @@ Also measured in the same run (same JSON line):
     y, gdn_gated_rmsnorm) on the prefill workload, each over 4 rotating
     buffer sets larger together than the last-level cache -> HBM roofline;
     and the gated layer core (gdn_layer_core_gated) step time;
+  * single-token decode B=1 (per-call time, warm and cold) and the long
+    batched prefill B=4, T=32768 (layer core and chunked recurrence);
   * a speculative-verify window (B=64, T=4, state emitted after 1..4 steps)
     and per-key-gate decode (B=64, T=1), both HBM-bound, rotating state sets;
   * the CPU oracle on a bounded sample of the prefill workload, one thread.
@@ -81,6 +83,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-long", action="store_true", help="skip the B=4 T=32768 long-prefill leg")
     ap.add_argument("--kernel-only", default=None, choices=[None, "recurrent", "prep", "decode", "copy", "chunked",
                                                          "epilogue"],
                     help="launch only this kernel (for counter collection)")
@@ -232,6 +235,8 @@ def main():
     # ------------------------------------------------------------- decode
     decode = bench_decode(args, torch, dev, up, inputs, binding, np)
     serving = bench_verify_and_per_key(args, torch, dev, up, inputs, binding, np)
+    decode1 = bench_decode_b1(args, torch, dev, up, inputs, binding, np)
+    long_prefill = None if args.no_long else bench_long_prefill(args, torch, dev, up, inputs, binding, np)
 
     # -------------------------------------------------------- CPU baseline
     cpu = None
@@ -274,6 +279,8 @@ def main():
                      "frac_hbm": epi_bytes / epi_us / 1e3 / HBM_PEAK_GBS,
                      "layer_core_gated_us": gated_us},
         "decode_b64": decode,
+        "decode_b1": decode1,
+        "long_prefill_b4": long_prefill,
         "verify_window_b64": serving["verify_window"],
         "per_key_decode_b64": serving["per_key_decode"],
         "cpu_baseline": cpu,
@@ -431,6 +438,131 @@ def bench_verify_and_per_key(args, torch, dev, up, inputs, binding, np):
         print(f"[bench] {name}: {us:.1f} us ({gbs:.0f} GB/s, {gbs / HBM_PEAK_GBS:.0%} of HBM)", file=sys.stderr,
               flush=True)
     return res
+
+
+def bench_decode_b1(args, torch, dev, up, inputs, binding, np):
+    """Single-token decode B=1, T=1 (Hk=16 Hv=32 Dk=Dv=128): microseconds per
+    call over 1000 back-to-back calls, warm (one state, updated in place) and
+    cold (256 rotating states, 512 MiB, beyond the last-level cache); the
+    recurrence alone and the layer core."""
+    B, T, Hk, Hv, Dk, Dv, K = 1, 1, 16, 32, 128, 128, 4
+    qs, ks = inputs.scales(Dk)
+    raw = inputs.layer_raw(B=B, T=T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, K=K, workload_id=1, state=True, conv_state=True)
+    d = {k: up(raw[k]) for k in ("qkv", "conv_w", "conv_state", "a", "b", "A_log", "dt_bias")}
+    R = 256
+    states = [up(raw["state"]).clone() for _ in range(R)]
+    y = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+    ws = torch.empty(max(binding.layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv), 1), dtype=torch.uint8,
+                     device=dev)
+    pq = torch.empty(B, T, Hk, Dk, dtype=torch.int16, device=dev)
+    pk, pv = torch.empty_like(pq), torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+    pg = torch.empty(B, T, Hv, dtype=torch.float32, device=dev)
+    pb = torch.empty_like(pg)
+    binding.prep(d["qkv"], d["conv_w"], d["conv_state"], None, d["a"], d["b"], d["A_log"], d["dt_bias"], pq, pk,
+                 pv, pg, pb, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs, k_scale=ks)
+
+    def rec(st):
+        binding.recurrent(pq, pk, pv, pg, pb, st, st, y)
+
+    def core(st):
+        binding.layer_core(d["qkv"], d["conv_w"], d["conv_state"], d["conv_state"], d["a"], d["b"], d["A_log"],
+                           d["dt_bias"], st, st, y, ws, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs, k_scale=ks)
+
+    stream = torch.cuda.current_stream(dev)
+    n = 1000
+    out = {}
+    for name, fn in (("recurrent", rec), ("layer_core", core)):
+        for mode, pick in (("warm", lambda i: states[0]), ("cold", lambda i: states[i % R])):
+            for i in range(R):
+                fn(pick(i))
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(n):
+                fn(pick(i))
+            b.record(stream)
+            torch.cuda.synchronize()
+            out[f"{name}_{mode}_us"] = a.elapsed_time(b) * 1e3 / n
+    # the same calls captured in a HIP graph (a decode loop replayed without
+    # host launch cost): 100 calls per graph, rotating the cold state ring
+    side = torch.cuda.Stream()
+    for name, fn in (("recurrent", rec), ("layer_core", core)):
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            for i in range(100):
+                fn(states[i % R])
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for i in range(100):
+                fn(states[i % R])
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(10):
+            graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out[f"{name}_graph_us"] = a.elapsed_time(b) * 1e3 / 1000
+        del graph
+    print(f"[bench] decode B=1: recurrence {out['recurrent_warm_us']:.2f} us warm / {out['recurrent_cold_us']:.2f} us "
+          f"cold / {out['recurrent_graph_us']:.2f} us in a graph; layer core {out['layer_core_warm_us']:.2f} / "
+          f"{out['layer_core_cold_us']:.2f} / {out['layer_core_graph_us']:.2f} us per call",
+          file=sys.stderr, flush=True)
+    out["workload"] = ("decode B=1 T=1 Hk=16 Hv=32 Dk=Dv=128; 1000 back-to-back calls; warm = one state in place, "
+                       "cold = 256 rotating states (512 MiB)")
+    out["note"] = ("per-call time of back-to-back calls (device time plus any host launch gap); *_graph_us: the "
+                   "same calls captured in a HIP graph of 100 calls over the cold state ring and replayed")
+    return out
+
+
+def bench_long_prefill(args, torch, dev, up, inputs, binding, np):
+    """Long batched prefill B=4, T=32768 (Hk=16 Hv=32 Dk=Dv=128, random
+    recurrent state): the layer core per step, and its chunked recurrence
+    alone against the fp32 peak."""
+    w = inputs.WORKLOADS["long"]
+    B, T, Hk, Hv, Dk, Dv, K = (w[k] for k in ("B", "T", "Hk", "Hv", "Dk", "Dv", "K"))
+    C = 2 * Hk * Dk + Hv * Dv
+    qs, ks = inputs.scales(Dk)
+    raw = inputs.workload("long")
+    d = {k: up(raw[k]) for k in ("qkv", "conv_w", "conv_state", "a", "b", "A_log", "dt_bias", "state")}
+    del raw
+    y = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+    s_out = torch.empty(B, Hv, Dv, Dk, dtype=torch.float32, device=dev)
+    cs_out = torch.empty(B, K - 1, C, dtype=torch.int16, device=dev)
+    ws = torch.empty(binding.layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv), dtype=torch.uint8, device=dev)
+    pq = torch.empty(B, T, Hk, Dk, dtype=torch.int16, device=dev)
+    pk, pv = torch.empty_like(pq), torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+    pg = torch.empty(B, T, Hv, dtype=torch.float32, device=dev)
+    pb = torch.empty_like(pg)
+    cws = torch.empty(binding.recurrent_chunked_workspace_bytes(B, T, Hk, Hv, Dk, Dv), dtype=torch.uint8,
+                      device=dev)
+
+    def step():
+        binding.layer_core(d["qkv"], d["conv_w"], d["conv_state"], cs_out, d["a"], d["b"], d["A_log"],
+                           d["dt_bias"], d["state"], s_out, y, ws, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv,
+                           q_scale=qs, k_scale=ks)
+
+    def chunked():
+        binding.recurrent_chunked(pq, pk, pv, pg, pb, d["state"], s_out, y, cws)
+
+    binding.prep(d["qkv"], d["conv_w"], d["conv_state"], None, d["a"], d["b"], d["A_log"], d["dt_bias"], pq, pk,
+                 pv, pg, pb, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs, k_scale=ks)
+    stream = torch.cuda.current_stream(dev)
+    n = 3
+    step_us = time_kernel(torch, stream, step, n)
+    chunk_us = time_kernel(torch, stream, chunked, n)
+    flops = 7 * B * T * Hv * Dk * Dv
+    tf = flops / (chunk_us * 1e-6) / 1e12
+    print(f"[bench] long prefill B=4 T=32768: layer core {step_us / 1e3:.2f} ms/step; chunked recurrence "
+          f"{chunk_us / 1e3:.2f} ms ({tf:.1f} TFLOP/s, {tf / FP32_PEAK_TFLOPS:.1%} of fp32 peak)",
+          file=sys.stderr, flush=True)
+    return {"workload": "long prefill B=4 T=32768 Hk=16 Hv=32 Dk=Dv=128 K=4, random recurrent state",
+            "ms_per_step": step_us / 1e3, "value": B * T * Hv / (step_us * 1e-6), "unit": "token*head/s",
+            "chunked_recurrence_ms": chunk_us / 1e3, "chunked_TFLOPs": tf, "frac_fp32_peak": tf / FP32_PEAK_TFLOPS,
+            "steps_timed": n}
 
 
 def cpu_baseline(raw, Hk, Hv, Dk, Dv, qs, ks, eps):
