@@ -162,7 +162,7 @@ __device__ __forceinline__ f4_t mma3b(u4_t a, const Planes& b, f4_t c) {
 
 // ========================================================= chunk preparation
 
-struct PrepSmem {
+struct alignas(16) PrepSmem {
     uint16_t kb[CK][DKC + 8];    // bf16 rows, padded against bank conflicts
     union {
         struct {
@@ -226,6 +226,21 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
         }
         *reinterpret_cast<uint4*>(&sh.kb[t][c8 * 8]) = kv;
         *reinterpret_cast<uint4*>(&sh.u.in.qb[t][c8 * 8]) = qv;
+    }
+    // the first 128-column slice of this chunk's v rows, loaded now (its
+    // latency hides behind steps 2-6) and staged through LDS in step 7
+    constexpr int kVPre = CK * 128 / 8 / 256;      // 16-byte vectors per thread
+    uint4 vpre[kVPre];
+    {
+        const int wdt = min(128, Dv);
+#pragma unroll
+        for (int i = 0; i < kVPre; ++i) {
+            const int idx = tid + i * 256;
+            const int t = idx / (wdt / 8), c8 = idx % (wdt / 8);
+            vpre[i] = make_uint4(0, 0, 0, 0);
+            if (idx < CK * (wdt / 8) && t0 + t < T)
+                vpre[i] = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t0 + t) * Hv + hv) * Dv + c8 * 8);
+        }
     }
     if (tid < CK) {
         // steps past T and masked steps: g = 1, beta = 0 (no decay, no write)
@@ -324,27 +339,64 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
     }
     __syncthreads();
 
-    // 4. T = (I + A)^-1 by forward substitution, one column per thread.  Each
-    //    row goes to LDS as soon as it is known; the scheduling barrier per
-    //    row keeps the row's operands from being hoisted.
+    // 4. T = (I + A)^-1 in 16 x 16 blocks.  A is strictly lower, so with
+    //    A = [[A11, 0], [A21, A22]]:  T11 = (I + A11)^-1, T22 = (I + A22)^-1,
+    //    T12 = 0 and T21 = -T22 A21 T11.
+    //    4a. T11 and T22 at once by forward substitution, one column per lane
+    //        (lanes 0-15: T11, lanes 16-31: T22), rows to LDS as soon as they
+    //        are known; lanes 32-63 zero T12.  The scheduling barrier per row
+    //        keeps the row's operands from being hoisted.
+    constexpr int CH = CK / 2;
     if (tid < CK) {
-        const int j = tid;
-        float x[CK];
+        const int j = tid % CH, base = tid < CH ? 0 : CH;
+        float x[CH];
 #pragma unroll
-        for (int t = 0; t < CK; ++t) {
+        for (int t = 0; t < CH; ++t) {
             float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
             for (int s4 = 0; s4 < t; s4 += 4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(&sh.w.s.a[t][s4]);
+                const float4 a4 = *reinterpret_cast<const float4*>(&sh.w.s.a[base + t][base + s4]);
                 acc0 = fmaf(a4.x, x[s4], acc0);
                 if (s4 + 1 < t) acc1 = fmaf(a4.y, x[s4 + 1], acc1);
                 if (s4 + 2 < t) acc0 = fmaf(a4.z, x[s4 + 2], acc0);
                 if (s4 + 3 < t) acc1 = fmaf(a4.w, x[s4 + 3], acc1);
             }
             x[t] = (t == j ? 1.f : 0.f) - (acc0 + acc1);
-            sh.w.s.tm[t][j] = x[t];
+            sh.w.s.tm[base + t][base + j] = x[t];
             __builtin_amdgcn_sched_barrier(0);
         }
+    } else if (tid < 2 * CK) {
+        // T12 = 0: rows 0..15, columns 16..31, one row per lane pair
+        const int t = (tid - CK) >> 1, h = (tid - CK) & 1;
+        *reinterpret_cast<float4*>(&sh.w.s.tm[t][CH + 8 * h]) = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(&sh.w.s.tm[t][CH + 8 * h + 4]) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    //    4b. M = A21 T11 (16 x 16, one entry per thread) into the unused upper
+    //        right block of A, then T21 = -T22 M.
+    {
+        const int i = tid >> 4, j = tid & 15;
+        float m0 = 0.f, m1 = 0.f;
+#pragma unroll
+        for (int k4 = 0; k4 < CH; k4 += 4) {
+            const float4 a4 = *reinterpret_cast<const float4*>(&sh.w.s.a[CH + i][k4]);
+            m0 = fmaf(a4.x, sh.w.s.tm[k4][j], m0);
+            m1 = fmaf(a4.y, sh.w.s.tm[k4 + 1][j], m1);
+            m0 = fmaf(a4.z, sh.w.s.tm[k4 + 2][j], m0);
+            m1 = fmaf(a4.w, sh.w.s.tm[k4 + 3][j], m1);
+        }
+        sh.w.s.a[i][CH + j] = m0 + m1;
+        __syncthreads();
+        float u0 = 0.f, u1 = 0.f;
+#pragma unroll
+        for (int k4 = 0; k4 < CH; k4 += 4) {
+            const float4 t4 = *reinterpret_cast<const float4*>(&sh.w.s.tm[CH + i][CH + k4]);
+            u0 = fmaf(t4.x, sh.w.s.a[k4][CH + j], u0);
+            u1 = fmaf(t4.y, sh.w.s.a[k4 + 1][CH + j], u1);
+            u0 = fmaf(t4.z, sh.w.s.a[k4 + 2][CH + j], u0);
+            u1 = fmaf(t4.w, sh.w.s.a[k4 + 3][CH + j], u1);
+        }
+        sh.w.s.tm[CH + i][j] = -(u0 + u1);
     }
     __syncthreads();
 
@@ -410,11 +462,21 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
     }
     for (int c0 = 0; c0 < Dv; c0 += 128) {
         const int wdt = min(128, Dv - c0);
-        for (int idx = tid; idx < CK * (wdt / 8); idx += 256) {
-            const int t = idx / (wdt / 8), c8 = idx % (wdt / 8);
-            uint4 vv = make_uint4(0, 0, 0, 0);
-            if (t0 + t < T) vv = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t0 + t) * Hv + hv) * Dv + c0 + c8 * 8);
-            *reinterpret_cast<uint4*>(&sh.w.vs[t][c8 * 8]) = vv;
+        if (c0 == 0) {
+#pragma unroll
+            for (int i = 0; i < kVPre; ++i) {
+                const int idx = tid + i * 256;
+                const int t = idx / (wdt / 8), c8 = idx % (wdt / 8);
+                if (idx < CK * (wdt / 8)) *reinterpret_cast<uint4*>(&sh.w.vs[t][c8 * 8]) = vpre[i];
+            }
+        } else {
+            for (int idx = tid; idx < CK * (wdt / 8); idx += 256) {
+                const int t = idx / (wdt / 8), c8 = idx % (wdt / 8);
+                uint4 vv = make_uint4(0, 0, 0, 0);
+                if (t0 + t < T)
+                    vv = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t0 + t) * Hv + hv) * Dv + c0 + c8 * 8);
+                *reinterpret_cast<uint4*>(&sh.w.vs[t][c8 * 8]) = vv;
+            }
         }
         __syncthreads();
         for (int rb = wv; rb < wdt / 16; rb += 4) {
