@@ -194,13 +194,18 @@ struct ChunkPtrs {
     u4_t* ksw;      // k columns
 };
 
+// KF = 0: q, k, v, g, beta are inputs.  KF = 2..4: they are computed here,
+// from the mixed projection qkv, with the prologue's arithmetic (the same
+// device functions as the prologue kernel, so the same bits) and a conv of
+// width KF; then Dv <= 128.
+template <int KF>
 __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const float* __restrict__ g,
                                                             const float* __restrict__ beta,
                                                             const uint8_t* __restrict__ mask,
-                                                            const uint16_t* __restrict__ v, ChunkPtrs o, int T,
-                                                            int Hk, int Hv, int Dv, int NC) {
+                                                            const uint16_t* __restrict__ v, PrologueIn pin,
+                                                            ChunkPtrs o, int T, int Hk, int Hv, int Dv, int NC) {
     __shared__ PrepSmem sh;
     const int64_t unit = blockIdx.x;          // (b * Hv + hv) * NC + c
     const int c = (int)(unit % NC);
@@ -216,6 +221,81 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
     const NegOnes no = neg_ones();
 
     // 1. k, q rows of the chunk (zero past T), g and beta
+    constexpr int kVPre = CK * 128 / 8 / 256;      // 16-byte vectors per thread (first v slice)
+    uint4 vpre[kVPre];
+    uint4 vrow[KF > 0 ? CK / 4 : 1];              // fused: this lane's v rows (8 tokens)
+    if constexpr (KF > 0) {
+        // Wave w computes tokens t0 + 8w .. t0 + 8w + 7.  Lanes 0-15 hold the
+        // q head's 8-channel groups, 16-31 the k head's (aligned 16-lane
+        // groups, as in the prologue kernel, for the norm's cross-lane sum),
+        // 32 .. 32 + Dv/8 - 1 the v head's.
+        const int C = 2 * Hk * DKC + Hv * Dv;
+        int region = 3, c0 = 0;
+        if (lane < 16) { region = 0; c0 = hk * DKC + 8 * lane; }
+        else if (lane < 32) { region = 1; c0 = Hk * DKC + hk * DKC + 8 * (lane - 16); }
+        else if (lane < 32 + Dv / 8) { region = 2; c0 = 2 * Hk * DKC + hv * Dv + 8 * (lane - 32); }
+        const bool valid = region < 3;
+        const float scale = region == 0 ? pin.q_scale : pin.k_scale;
+        const uint16_t* xb = pin.qkv + (int64_t)b * T * C + c0;
+        const uint16_t* csb = pin.conv_state_in ? pin.conv_state_in + (int64_t)b * (KF - 1) * C + c0 : nullptr;
+        float w[KF][8];
+        if (valid) {
+            const uint4* wp = reinterpret_cast<const uint4*>(pin.conv_w + (int64_t)c0 * KF);
+            float f[8 * KF];
+#pragma unroll
+            for (int v4 = 0; v4 < KF; ++v4) unpack8(wp[v4], f + 8 * v4);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < KF; ++j) w[j][i] = f[i * KF + j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < KF; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w[j][i] = 0.f;
+        }
+        // spliced input row pr (conv state rows, then qkv rows; zero past T)
+        auto xpad_row = [&](int pr) -> uint4 {
+            if (!valid || pr - (KF - 1) >= T) return make_uint4(0, 0, 0, 0);
+            if (pr >= KF - 1) return *reinterpret_cast<const uint4*>(xb + (int64_t)(pr - (KF - 1)) * C);
+            if (csb) return *reinterpret_cast<const uint4*>(csb + (int64_t)pr * C);
+            return make_uint4(0, 0, 0, 0);
+        };
+        const int tw0 = t0 + 8 * wv;
+        float h[KF - 1][8];
+#pragma unroll
+        for (int j = 0; j < KF - 1; ++j) unpack8(xpad_row(tw0 + j), h[j]);
+        uint4 rows[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rows[i] = xpad_row(tw0 + i + KF - 1);
+        // the new conv state (chunk 0's blocks; q/k channels from the first
+        // v-head of the group): the last KF-1 rows of the spliced input
+        if (c == 0 && wv == 0 && valid && pin.conv_state_out && (region == 2 || hv % G == 0)) {
+            uint16_t* out = pin.conv_state_out + (int64_t)b * (KF - 1) * C + c0;
+#pragma unroll
+            for (int i = 0; i < KF - 1; ++i) *reinterpret_cast<uint4*>(out + (int64_t)i * C) = xpad_row(T + i);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int t = tw0 + i;
+            float x[8];
+            unpack8(rows[i], x);
+            float act[8];
+            conv_silu8<KF>(w, h, x, act);
+            uint4 qk = make_uint4(0, 0, 0, 0);
+            if (region < 2) qk = qk_norm8<DKC>(act, scale, pin.eps);
+#pragma unroll
+            for (int j = 0; j < KF - 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) h[j][e] = h[j + 1][e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[KF - 2][e] = x[e];
+            const bool live = t < T;      // rows past T are zero, as for stored inputs
+            if (region == 0) *reinterpret_cast<uint4*>(&sh.u.in.qb[t - t0][8 * lane]) = live ? qk : make_uint4(0, 0, 0, 0);
+            else if (region == 1) *reinterpret_cast<uint4*>(&sh.kb[t - t0][8 * (lane - 16)]) = live ? qk : make_uint4(0, 0, 0, 0);
+            vrow[i] = live ? pack8(act) : make_uint4(0, 0, 0, 0);
+        }
+    } else {
     for (int idx = tid; idx < CK * DKC / 8; idx += 256) {
         const int t = idx / (DKC / 8), c8 = idx % (DKC / 8);
         uint4 kv = make_uint4(0, 0, 0, 0), qv = kv;
@@ -229,8 +309,6 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
     }
     // the first 128-column slice of this chunk's v rows, loaded now (its
     // latency hides behind steps 2-6) and staged through LDS in step 7
-    constexpr int kVPre = CK * 128 / 8 / 256;      // 16-byte vectors per thread
-    uint4 vpre[kVPre];
     {
         const int wdt = min(128, Dv);
 #pragma unroll
@@ -242,12 +320,19 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
                 vpre[i] = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t0 + t) * Hv + hv) * Dv + c8 * 8);
         }
     }
+    }
     if (tid < CK) {
         // steps past T and masked steps: g = 1, beta = 0 (no decay, no write)
         const int t = t0 + tid;
         const int64_t bt = (int64_t)b * T + min(t, T - 1);
         const int64_t i = bt * Hv + hv;
-        const float gv = g[i], bv = beta[i];
+        float gv, bv;
+        if constexpr (KF > 0) {
+            gate_g_beta(pin.a[i], pin.b[i], pin.A_log[hv], pin.dt_bias[hv], gv, bv);
+        } else {
+            gv = g[i];
+            bv = beta[i];
+        }
         const bool on = t < T && (mask == nullptr || mask[bt] != 0);
         sh.gs[tid] = on ? gv : 1.f;
         sh.bs[tid] = on ? bv : 0.f;
@@ -462,7 +547,13 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
     }
     for (int c0 = 0; c0 < Dv; c0 += 128) {
         const int wdt = min(128, Dv - c0);
-        if (c0 == 0) {
+        if (KF > 0) {
+            // fused: lane 32 + j of wave w holds column group j of tokens 8w .. 8w + 7
+            if (lane >= 32 && lane < 32 + wdt / 8) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&sh.w.vs[8 * wv + i][8 * (lane - 32)]) = vrow[i];
+            }
+        } else if (c0 == 0) {
 #pragma unroll
             for (int i = 0; i < kVPre; ++i) {
                 const int idx = tid + i * 256;
@@ -804,7 +895,24 @@ int64_t chunked_blocks(int B, int T, int Hv, int Dv) {
     return std::max<int64_t>((int64_t)B * Hv * NC, (int64_t)B * Hv * (Dv / RB));
 }
 
+bool layer_chunked_fusable(int Dv, int K, const void* conv_state_in, const void* conv_state_out) {
+    return Dv <= 128 && K >= 2 && K <= 4 && (conv_state_out == nullptr || conv_state_out != conv_state_in);
+}
+
+static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, int K, void* ws,
+                                 hipStream_t stream);
+
 hipError_t launch_recurrent_chunked(const RecurrentArgs& a, void* ws, hipStream_t stream) {
+    return launch_chunked(a, nullptr, 0, ws, stream);
+}
+
+hipError_t launch_layer_chunked(const RecurrentArgs& a, const PrologueIn& p, int K, void* ws, hipStream_t stream) {
+    if (!layer_chunked_fusable(a.Dv, K, p.conv_state_in, p.conv_state_out)) return hipErrorInvalidValue;
+    return launch_chunked(a, &p, K, ws, stream);
+}
+
+static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, int K, void* ws,
+                                 hipStream_t stream) {
     if (!chunked_supported(a.Hv, a.Dk, a.Dv) || a.T <= 0 || a.B <= 0) return hipErrorInvalidValue;
     const ChunkedLayout L = chunked_layout(a.B, a.T, a.Hk, a.Hv, a.Dk, a.Dv);
     char* base = static_cast<char*>(ws);
@@ -816,8 +924,28 @@ hipError_t launch_recurrent_chunked(const RecurrentArgs& a, void* ws, hipStream_
     o.qsw = reinterpret_cast<u4_t*>(base + L.qsw);
     o.ksw = reinterpret_cast<u4_t*>(base + L.ksw);
     const int64_t units = (int64_t)a.B * a.Hv * L.nc;
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g, a.beta,
-                       a.mask, a.v, o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
+    const PrologueIn none{};
+    const PrologueIn& pi = pin ? *pin : none;
+    switch (K) {
+        case 0:
+            hipLaunchKernelGGL(chunk_prep_kernel<0>, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g,
+                               a.beta, a.mask, a.v, pi, o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
+            break;
+        case 2:
+            hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g,
+                               a.beta, a.mask, a.v, pi, o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
+            break;
+        case 3:
+            hipLaunchKernelGGL(chunk_prep_kernel<3>, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g,
+                               a.beta, a.mask, a.v, pi, o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
+            break;
+        case 4:
+            hipLaunchKernelGGL(chunk_prep_kernel<4>, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g,
+                               a.beta, a.mask, a.v, pi, o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     SeqIn in;

@@ -479,15 +479,22 @@ static gdn_status layer_core_impl(const gdn_bf16* qkv, const gdn_bf16* conv_w, c
     }
     if (B == 0) return ok();
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (T > 0 || conv_state_out) {
-        gdn::PrepArgs p{qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, wq, wk, wv, wg, wb,
-                        B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps};
-        st = hip_result(gdn::launch_prep(p, s), "prep");
-        if (st != GDN_OK) return st;
-    }
     gdn::RecurrentArgs r{wq, wk, wv, wg, wb, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, mask};
-    st = w.use_chunked ? hip_result(gdn::launch_recurrent_chunked(r, ws + w.chunked, s), "chunked recurrent")
-                       : hip_result(gdn::launch_recurrent(r, s), "recurrent");
+    if (w.use_chunked && gdn::layer_chunked_fusable(Dv, K, conv_state_in, conv_state_out)) {
+        // the prologue runs inside the chunk preparation (same arithmetic, same bits)
+        const gdn::PrologueIn p{qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias,
+                                q_scale, k_scale, eps};
+        st = hip_result(gdn::launch_layer_chunked(r, p, K, ws + w.chunked, s), "chunked layer core");
+    } else {
+        if (T > 0 || conv_state_out) {
+            gdn::PrepArgs p{qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, wq, wk, wv, wg, wb,
+                            B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps};
+            st = hip_result(gdn::launch_prep(p, s), "prep");
+            if (st != GDN_OK) return st;
+        }
+        st = w.use_chunked ? hip_result(gdn::launch_recurrent_chunked(r, ws + w.chunked, s), "chunked recurrent")
+                           : hip_result(gdn::launch_recurrent(r, s), "recurrent");
+    }
     if (st != GDN_OK || !gated) return st;
     gdn::GatedNormArgs e{y, z, norm_weight, y, (int64_t)B * T * Hv, Dv, norm_eps};
     return hip_result(gdn::launch_gated_rmsnorm(e, s), "gated rmsnorm");

@@ -61,6 +61,42 @@ __device__ __forceinline__ float silu_fast(float u) {
     return (u >= 0.0f ? u : u * e) * s;
 }
 
+// ------------------------------------------------------ prologue pieces ----
+// The per-element arithmetic of the prologue, shared by the prologue kernel
+// and the chunk preparation that fuses it, so both produce identical bits.
+
+// g = exp(-exp(A_log) softplus(a + dt_bias)), beta = sigmoid(b), from the
+// stored bf16 a, b and the f32 A_log, dt_bias of the head.  beta uses the
+// overflow-free form (e = e^-|b|: 1/(1+e), or e/(1+e) for b < 0) with the
+// library exp and a true division: beta is kept in f32, so it is held to a
+// few f32 ulps, not to a bf16 rounding.
+__device__ __forceinline__ void gate_g_beta(uint16_t a, uint16_t b, float A_log, float dt_bias, float& g,
+                                            float& beta) {
+    const float x = __uint_as_float((uint32_t)a << 16) + dt_bias;
+    const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+    g = expf(-expf(A_log) * sp);
+    const float bb = __uint_as_float((uint32_t)b << 16);
+    const float e = expf(-fabsf(bb));
+    const float s = 1.f / (1.f + e);
+    beta = bb >= 0.f ? s : e * s;
+}
+
+// One token of 8 channels: the depthwise conv over the K-1 window rows h and
+// the new row x (weights w[j][e] for tap j, w[K-1] on the newest row), then
+// SiLU (overflow-free, about 2 f32 ulp).
+template <int K>
+__device__ __forceinline__ void conv_silu8(const float (&w)[K][8], const float (&h)[K - 1][8], const float (&x)[8],
+                                           float (&act)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float u = 0.f;
+#pragma unroll
+        for (int j = 0; j < K - 1; ++j) u = fmaf(w[j][e], h[j][e], u);
+        u = fmaf(w[K - 1][e], x[e], u);
+        act[e] = silu_fast(u);
+    }
+}
+
 // ------------------------------------------------------------ cross-lane ----
 
 // DPP controls (GCN/CDNA encoding): quad permutations, mirrors inside a
@@ -115,6 +151,22 @@ __device__ __forceinline__ void group_sum2(float& x, float& y) {
         b = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(y), 0x401F));
         x += a; y += b;
     }
+}
+
+// The q/k head norm of 8 channels held by each of the head's DK/8 lanes (an
+// aligned lane group; every lane of it must execute this): sum of squares
+// across the group, then act * scale / sqrt(mean + eps), rounded to bf16.
+template <int DK>
+__device__ __forceinline__ uint4 qk_norm8(const float (&act)[8], float scale, float eps) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(act[e], act[e], ss);
+    ss = group_sum<DK / 8>(ss);
+    const float rs = scale * __builtin_amdgcn_rsqf(ss * (1.0f / DK) + eps);
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = act[e] * rs;
+    return pack8(o);
 }
 
 }  // namespace gdn

@@ -68,6 +68,29 @@ bool chunked_supported(int Hv, int Dk, int Dv);
 ChunkedLayout chunked_layout(int B, int T, int Hk, int Hv, int Dk, int Dv);
 int64_t chunked_blocks(int B, int T, int Hv, int Dv);
 hipError_t launch_recurrent_chunked(const RecurrentArgs& a, void* workspace, hipStream_t stream);
+
+// The prologue's inputs, for the chunk preparation that computes q, k, v,
+// g and beta itself (unused otherwise).
+struct PrologueIn {
+    const uint16_t* qkv;
+    const uint16_t* conv_w;
+    const uint16_t* conv_state_in;   // may be null (zeros)
+    uint16_t* conv_state_out;        // may be null; never conv_state_in itself
+    const uint16_t* a;
+    const uint16_t* b;
+    const float* A_log;
+    const float* dt_bias;
+    float q_scale, k_scale, eps;
+};
+
+// The layer core's chunked recurrence with the prologue fused into the chunk
+// preparation: q, k, v, g, beta of RecurrentArgs are not read (computed from
+// p), conv_state_out is written.  Needs Dv <= 128, K in {2, 3, 4} and
+// conv_state_out not aliasing conv_state_in; the result is bit-identical to
+// launch_prep followed by launch_recurrent_chunked.
+bool layer_chunked_fusable(int Dv, int K, const void* conv_state_in, const void* conv_state_out);
+hipError_t launch_layer_chunked(const RecurrentArgs& a, const PrologueIn& p, int K, void* workspace,
+                                hipStream_t stream);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 
 // Output epilogue: out = bf16(silu(z) * rms_norm(y) * w) per row of Dv

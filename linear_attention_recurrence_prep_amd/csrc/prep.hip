@@ -30,16 +30,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int 
         const int64_t i = (bid - conv_blocks) * PREP_NT + tid;
         if (i < (int64_t)p.B * T * Hv) {
             const int h = (int)(i % Hv);
-            const float x = bf16lo(p.a[i]) + p.dt_bias[h];
-            const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-            p.g[i] = expf(-expf(p.A_log[h]) * sp);
-            // sigmoid without overflow (e = e^-|b|: 1/(1+e), or e/(1+e) for
-            // b < 0), with the library exp and a true division: beta is kept
-            // in f32, so it is held to a few f32 ulps, not to a bf16 rounding
-            const float bb = bf16lo(p.b[i]);
-            const float e = expf(-fabsf(bb));
-            const float s = 1.f / (1.f + e);
-            p.beta[i] = bb >= 0.f ? s : e * s;
+            float g, beta;
+            gate_g_beta(p.a[i], p.b[i], p.A_log[h], p.dt_bias[h], g, beta);
+            p.g[i] = g;
+            p.beta[i] = beta;
         }
         return;
     }
@@ -121,25 +115,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int 
         float x[8];
         unpack8(rows[i], x);
         float act[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float u = 0.f;
-#pragma unroll
-            for (int j = 0; j < K - 1; ++j) u = fmaf(w[j][e], h[j][e], u);
-            u = fmaf(w[K - 1][e], x[e], u);
-            // SiLU with the hardware exp2 and reciprocal (about 2 ulp in f32,
-            // far below the half-ulp of the bf16 result), overflow-free
-            act[e] = silu_fast(u);
-        }
-        // q/k heads: sum of squares over the head's Dk/8 lanes.  Region
-        // boundaries are multiples of Dk, so every lane group is wholly inside
-        // or outside this branch (the cross-lane sum never reads an idle lane).
-        float ss = 0.f;
-        if (region < 2) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(act[e], act[e], ss);
-            ss = group_sum<DK / 8>(ss);
-        }
+        conv_silu8<K>(w, h, x, act);
+        // q/k heads: the norm over the head's Dk/8 lanes.  Region boundaries
+        // are multiples of Dk, so every lane group is wholly inside or outside
+        // this branch (the cross-lane sum never reads an idle lane).
+        uint4 qk = make_uint4(0, 0, 0, 0);
+        if (region < 2) qk = qk_norm8<DK>(act, scale, p.eps);
         // slide the window
 #pragma unroll
         for (int j = 0; j < K - 2; ++j)
@@ -151,12 +132,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int 
         if (!valid) continue;
         const int64_t tok = (int64_t)b * T + t;
         if (region < 2) {
-            const float rs = scale * __builtin_amdgcn_rsqf(ss * (1.0f / DK) + p.eps);
-            float o[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = act[e] * rs;
             uint16_t* dst = region == 0 ? p.q + tok * HKDK + c0 : p.k + tok * HKDK + (c0 - HKDK);
-            *reinterpret_cast<uint4*>(dst) = pack8(o);
+            *reinterpret_cast<uint4*>(dst) = qk;
         } else {
             *reinterpret_cast<uint4*>(p.v + tok * Hv * Dv + (c0 - 2 * HKDK)) = pack8(act);
         }
