@@ -600,7 +600,7 @@ struct SeqIn {
 // in a scalar register, so role branches and address arithmetic stay scalar.
 struct SeqCtx {
     int64_t unit0, kunit0;      // first chunk of this (b, hv) and of its (b, hk)
-    int rblk, row_blocks;       // this block's 16 state rows, Dv / 16
+    int tile0, row_tiles;       // this block's first 16-row tile, Dv / 16
     int wv, lane;
 };
 
@@ -623,13 +623,14 @@ __device__ __forceinline__ __attribute__((address_space(1))) T* uniform_ptr_w(T*
     return (__attribute__((address_space(1))) T*)(((uint64_t)hi << 32) | lo);
 }
 
-// One chunk's operands in registers.
+// One chunk's operands in registers (NR row tiles of 16 state rows).
+template <int NR>
 struct SeqOps {
     f4_t wf[2][2];    // W of t-tiles 0 and 1 (f32, elements 0..3 and 4..7)
     Planes w[2];      // the same as bf16 planes (cut one step before use)
     u4_t q[2];        // q, t-tiles 0 and 1
     u4_t k[2];        // k^T, this wave's two column tiles
-    u4_t a0;          // -Tb V of t-tile (wave & 1) (f32 bits; waves 0, 1 use it)
+    u4_t a0[NR];      // -Tb V of t-tile (wave & 1), per row tile (f32 bits; waves 0, 1 use it)
     float rg;         // -rho[lane] (lanes 0..31), gamma[lane - 32] (lanes 32..63)
 
     // Loads of one chunk in four parts, so that the sequential pass can
@@ -654,7 +655,9 @@ struct SeqOps {
         } else {
             // every state wave loads a -Tb V tile (waves 0, 1 add theirs; equal
             // load counts keep the memory waits exact) and rho/gamma
-            a0 = uniform_ptr(in.u + ((unit * x.row_blocks + x.rblk) * 2 + (wv & 1)) * 64)[lane];
+#pragma unroll
+            for (int rt = 0; rt < NR; ++rt)
+                a0[rt] = uniform_ptr(in.u + ((unit * x.row_tiles + x.tile0 + rt) * 2 + (wv & 1)) * 64)[lane];
             rg = uniform_ptr(in.rg + unit * 2 * CK)[lane];
         }
     }
@@ -680,26 +683,32 @@ struct SeqOps {
         __builtin_amdgcn_sched_barrier(0);     \
     } while (0)
 
-// Six waves per block: waves 0..3 hold the state (32 columns each) and run
-// the chunk chain; waves 4, 5 finish y of the previous chunk (one t-tile
-// each) off that chain.  Buffers the output waves read one chunk late are
-// kept three deep.
+// Six waves per block: waves 0..3 hold the state (32 columns each) of NR
+// tiles of 16 rows and run the chunk chain; waves 4, 5 finish y of the
+// previous chunk (one t-tile each, every row tile) off that chain.  Buffers
+// the output waves read one chunk late are kept three deep.  With NR = 2 a
+// block serves 32 rows: the chunk's W, q, k and -P are loaded once for both
+// tiles and the tiles' independent products interleave; the grid halves,
+// which pays once it would exceed one block per CU (a CU runs one block of
+// this kernel at a time).  Each tile's arithmetic is the same either way.
 constexpr int NWY = 2;
 constexpr int SEQ_THREADS = 64 * (NW + NWY);
 
+template <int NR>
 struct SeqSmem {
-    f4_t x[2][NW * 2 * 64];   // per-wave shares of W S^T - Tb V, by chunk parity
-    f4_t y[3][NW * 2 * 64];   // per-wave shares of S Q^T (transposed Y'), chunk mod 3
-    float rg[3][2 * CK];      // -rho (kperm order) and gamma of the chunk, chunk mod 3
-    f4_t d[2][2][64];         // D of the chunk (B-operand layout), by chunk parity
+    f4_t x[2][NR][NW * 2 * 64];   // per-wave shares of W S^T - Tb V, by chunk parity
+    f4_t y[3][NR][NW * 2 * 64];   // per-wave shares of S Q^T (transposed Y'), chunk mod 3
+    float rg[3][2 * CK];          // -rho (kperm order) and gamma of the chunk, chunk mod 3
+    f4_t d[2][NR][2][64];         // D of the chunk (B-operand layout), by chunk parity
 };
 
+template <int NR>
 __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const float* state_in,
                                                                 float* state_out, uint16_t* __restrict__ y,
                                                                 const uint8_t* __restrict__ mask, int T, int Hk,
                                                                 int Hv, int Dv, int NC, int row_blocks,
                                                                 int n_blocks) {
-    __shared__ SeqSmem sh;
+    __shared__ SeqSmem<NR> sh;
 
     int lb = blockIdx.x;
     if ((n_blocks & 7) == 0) lb = (lb & 7) * (n_blocks >> 3) + (lb >> 3);
@@ -707,7 +716,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
     const int rblk = lb % row_blocks;
     const int b = n / Hv, hv = n % Hv;
     const int hk = hv / (Hv / Hk);
-    const int r0 = rblk * RB;
+    const int r0 = rblk * RB * NR;
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, lq = lane >> 4;
@@ -732,22 +741,25 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
             __syncthreads();                          // chunk c's barrier (c == NC: the final one)
             if (c > 0) {
                 const int cp = c - 1;
-                const f4_t* yb = sh.y[b3];
-                const f4_t q0 = yb[jt * 64 + lane], q1 = yb[(2 + jt) * 64 + lane];
-                const f4_t q2 = yb[(4 + jt) * 64 + lane], q3 = yb[(6 + jt) * 64 + lane];
-                f4_t ys = ((q0 + q1) + q2) + q3;
-                ys = ys * sh.rg[b3][CK + yt];
-                u4_t dh, dm;
-                split8hm(no, sh.d[cp & 1][0][lane], sh.d[cp & 1][1][lane], dh, dm);
-                ys = mma(dm, ch, ys);
-                ys = mma(dh, cm, ys);
-                ys = mma(dh, ch, ys);
                 const int t = cp * CK + yt;
-                if (t < T) {
-                    u2_t w = {pack_bf16x2(ys[0], ys[1]), pack_bf16x2(ys[2], ys[3])};
-                    if (mask != nullptr && mask[(int64_t)b * T + t] == 0) w = u2_t{0, 0};   // masked step
-                    *reinterpret_cast<__attribute__((address_space(1))) u2_t*>(
-                        uniform_ptr_w(y0 + (int64_t)cp * CK * vstride) + yoff) = w;
+#pragma unroll
+                for (int rt = 0; rt < NR; ++rt) {
+                    const f4_t* yb = sh.y[b3][rt];
+                    const f4_t q0 = yb[jt * 64 + lane], q1 = yb[(2 + jt) * 64 + lane];
+                    const f4_t q2 = yb[(4 + jt) * 64 + lane], q3 = yb[(6 + jt) * 64 + lane];
+                    f4_t ys = ((q0 + q1) + q2) + q3;
+                    ys = ys * sh.rg[b3][CK + yt];
+                    u4_t dh, dm;
+                    split8hm(no, sh.d[cp & 1][rt][0][lane], sh.d[cp & 1][rt][1][lane], dh, dm);
+                    ys = mma(dm, ch, ys);
+                    ys = mma(dh, cm, ys);
+                    ys = mma(dh, ch, ys);
+                    if (t < T) {
+                        u2_t w = {pack_bf16x2(ys[0], ys[1]), pack_bf16x2(ys[2], ys[3])};
+                        if (mask != nullptr && mask[(int64_t)b * T + t] == 0) w = u2_t{0, 0};   // masked step
+                        *reinterpret_cast<__attribute__((address_space(1))) u2_t*>(
+                            uniform_ptr_w(y0 + (int64_t)cp * CK * vstride + RB * rt) + yoff) = w;
+                    }
                 }
                 b3 = b3 == 2 ? 0 : b3 + 1;
             }
@@ -761,93 +773,145 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
     SeqCtx x;
     x.unit0 = unit0;
     x.kunit0 = ((int64_t)b * Hk + hk) * NC;
-    x.rblk = rblk;
-    x.row_blocks = row_blocks;
+    x.tile0 = rblk * NR;
+    x.row_tiles = Dv / RB;
     x.wv = wv;
     x.lane = lane;
 
-    // state tile tt, register i: S[r0 + lr][32 wv + 16 tt + 4 lq + i]
-    f4_t S[2];
+    // row tile rt, state tile tt, register i: S[r0 + 16 rt + lr][32 wv + 16 tt + 4 lq + i]
+    f4_t S[NR][2];
     float* sp_out = state_out + ((int64_t)n * Dv + r0) * DKC + 32 * wv;
     const uint32_t soff = lr * DKC + 4 * lq;
-    if (state_in) {
-        const float* sp = state_in + ((int64_t)n * Dv + r0) * DKC + 32 * wv;
-        S[0] = *reinterpret_cast<const f4_t*>(sp + soff);
-        S[1] = *reinterpret_cast<const f4_t*>(sp + soff + 16);
-    } else {
-        S[0] = zero;
-        S[1] = zero;
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) {
+        if (state_in) {
+            const float* sp = state_in + ((int64_t)n * Dv + r0 + RB * rt) * DKC + 32 * wv;
+            S[rt][0] = *reinterpret_cast<const f4_t*>(sp + soff);
+            S[rt][1] = *reinterpret_cast<const f4_t*>(sp + soff + 16);
+        } else {
+            S[rt][0] = zero;
+            S[rt][1] = zero;
+        }
     }
 
     // one chunk c (b3 = c mod 3) with o; W of the next chunk (n1) is cut into
     // planes and the loads of chunk cn into nx are spread over it
-    auto step = [&](int c, int b3, const SeqOps& o, SeqOps& n1, SeqOps& nx, int cn) {
+    auto step = [&](int c, int b3, const SeqOps<NR>& o, SeqOps<NR>& n1, SeqOps<NR>& nx, int cn) {
         // state planes: element e of quarter lq is column kperm(lq, e)
-        const Planes s = split8(no, S[0], S[1]);
-        SEQ_PIN(nx.load<0>(in, x, cn));
+        Planes s[NR];
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) s[rt] = split8(no, S[rt][0], S[rt][1]);
+        SEQ_PIN(nx.template load<0>(in, x, cn));
 
         // this wave's share of W S^T - Tb V (rows t, columns r), two t-tiles
-        f4_t x0 = zero, x1 = zero;
-        if (wv == 0) x0 = __builtin_bit_cast(f4_t, o.a0);
-        else if (wv == 1) x1 = __builtin_bit_cast(f4_t, o.a0);
-        x0 = mma(o.w[0].l, s.h, x0);
-        x1 = mma(o.w[1].l, s.h, x1);
-        x0 = mma(o.w[0].h, s.l, x0);
-        x1 = mma(o.w[1].h, s.l, x1);
-        x0 = mma(o.w[0].m, s.m, x0);
-        x1 = mma(o.w[1].m, s.m, x1);
-        x0 = mma(o.w[0].m, s.h, x0);
-        x1 = mma(o.w[1].m, s.h, x1);
-        x0 = mma(o.w[0].h, s.m, x0);
-        x1 = mma(o.w[1].h, s.m, x1);
-        x0 = mma(o.w[0].h, s.h, x0);
-        x1 = mma(o.w[1].h, s.h, x1);
+        // per row tile
+        f4_t x0[NR], x1[NR];
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            x0[rt] = zero;
+            x1[rt] = zero;
+            if (wv == 0) x0[rt] = __builtin_bit_cast(f4_t, o.a0[rt]);
+            else if (wv == 1) x1[rt] = __builtin_bit_cast(f4_t, o.a0[rt]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            x0[rt] = mma(o.w[0].l, s[rt].h, x0[rt]);
+            x1[rt] = mma(o.w[1].l, s[rt].h, x1[rt]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            x0[rt] = mma(o.w[0].h, s[rt].l, x0[rt]);
+            x1[rt] = mma(o.w[1].h, s[rt].l, x1[rt]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            x0[rt] = mma(o.w[0].m, s[rt].m, x0[rt]);
+            x1[rt] = mma(o.w[1].m, s[rt].m, x1[rt]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            x0[rt] = mma(o.w[0].m, s[rt].h, x0[rt]);
+            x1[rt] = mma(o.w[1].m, s[rt].h, x1[rt]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            x0[rt] = mma(o.w[0].h, s[rt].m, x0[rt]);
+            x1[rt] = mma(o.w[1].h, s[rt].m, x1[rt]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            x0[rt] = mma(o.w[0].h, s[rt].h, x0[rt]);
+            x1[rt] = mma(o.w[1].h, s[rt].h, x1[rt]);
+        }
 
         // this wave's share of S Q^T (rows r, columns t); y is rounded to
         // bf16, so the state's two leading planes suffice (2^-16)
-        f4_t y0v = mma(s.m, o.q[0], zero);
-        f4_t y1v = mma(s.m, o.q[1], zero);
-        y0v = mma(s.h, o.q[0], y0v);
-        y1v = mma(s.h, o.q[1], y1v);
+        f4_t y0v[NR], y1v[NR];
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            y0v[rt] = mma(s[rt].m, o.q[0], zero);
+            y1v[rt] = mma(s[rt].m, o.q[1], zero);
+        }
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            y0v[rt] = mma(s[rt].h, o.q[0], y0v[rt]);
+            y1v[rt] = mma(s[rt].h, o.q[1], y1v[rt]);
+        }
 
-        SEQ_PIN(nx.load<1>(in, x, cn));
+        SEQ_PIN(nx.template load<1>(in, x, cn));
         n1.split_w(no);
 
-        f4_t* xb = sh.x[c & 1];
-        f4_t* yb = sh.y[b3];
-        xb[(2 * wv) * 64 + lane] = x0;
-        xb[(2 * wv + 1) * 64 + lane] = x1;
-        yb[(2 * wv) * 64 + lane] = y0v;
-        yb[(2 * wv + 1) * 64 + lane] = y1v;
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            f4_t* xb = sh.x[c & 1][rt];
+            f4_t* yb = sh.y[b3][rt];
+            xb[(2 * wv) * 64 + lane] = x0[rt];
+            xb[(2 * wv + 1) * 64 + lane] = x1[rt];
+            yb[(2 * wv) * 64 + lane] = y0v[rt];
+            yb[(2 * wv + 1) * 64 + lane] = y1v[rt];
+        }
         float* rg = sh.rg[b3];
         if (wv == 0) rg[lane] = o.rg;
         __syncthreads();
 
-        SEQ_PIN(nx.load<2>(in, x, cn));
+        SEQ_PIN(nx.template load<2>(in, x, cn));
         // D = W S^T - Tb V = -Delta, summed in wave order (identical in every wave)
-        const f4_t p00 = xb[0 * 64 + lane], p10 = xb[2 * 64 + lane], p20 = xb[4 * 64 + lane], p30 = xb[6 * 64 + lane];
-        const f4_t p01 = xb[1 * 64 + lane], p11 = xb[3 * 64 + lane], p21 = xb[5 * 64 + lane], p31 = xb[7 * 64 + lane];
-        const f4_t d0 = ((p00 + p10) + p20) + p30;
-        const f4_t d1 = ((p01 + p11) + p21) + p31;
+        f4_t d0[NR], d1[NR];
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            const f4_t* xb = sh.x[c & 1][rt];
+            const f4_t p00 = xb[0 * 64 + lane], p10 = xb[2 * 64 + lane], p20 = xb[4 * 64 + lane], p30 = xb[6 * 64 + lane];
+            const f4_t p01 = xb[1 * 64 + lane], p11 = xb[3 * 64 + lane], p21 = xb[5 * 64 + lane], p31 = xb[7 * 64 + lane];
+            d0[rt] = ((p00 + p10) + p20) + p30;
+            d1[rt] = ((p01 + p11) + p21) + p31;
+        }
 
         // S = gamma_{C-1} S + K^T (diag(rho) Delta)
         const f4_t rh0 = *reinterpret_cast<const f4_t*>(rg + 8 * lq);
         const f4_t rh1 = *reinterpret_cast<const f4_t*>(rg + 8 * lq + 4);
         const float gc = rg[2 * CK - 1];
-        const Planes bs = split8(no, rh0 * d0, rh1 * d1);
-        S[0] = S[0] * gc;
-        S[1] = S[1] * gc;
-        S[0] = mma3b(o.k[0], bs, S[0]);
-        S[1] = mma3b(o.k[1], bs, S[1]);
-        if (wv == 0) {
-            sh.d[c & 1][0][lane] = d0;
-            sh.d[c & 1][1][lane] = d1;
+        Planes bs[NR];
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) bs[rt] = split8(no, rh0 * d0[rt], rh1 * d1[rt]);
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            S[rt][0] = S[rt][0] * gc;
+            S[rt][1] = S[rt][1] * gc;
+            S[rt][0] = mma3b(o.k[0], bs[rt], S[rt][0]);
+            S[rt][1] = mma3b(o.k[1], bs[rt], S[rt][1]);
         }
-        SEQ_PIN(nx.load<3>(in, x, cn));
+        if (wv == 0) {
+#pragma unroll
+            for (int rt = 0; rt < NR; ++rt) {
+                sh.d[c & 1][rt][0][lane] = d0[rt];
+                sh.d[c & 1][rt][1][lane] = d1[rt];
+            }
+        }
+        SEQ_PIN(nx.template load<3>(in, x, cn));
     };
 
     // three operand sets: chunk c + 2 loads while chunk c runs
-    SeqOps o0, o1, o2;
+    SeqOps<NR> o0, o1, o2;
     o0.load_all(in, x, 0);
     o1.load_all(in, x, min(1, NC - 1));
     o0.split_w(no);
@@ -861,8 +925,12 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
     if (c + 1 < NC) step(c + 1, 1, o1, o2, o0, min(c + 3, NC - 1));
     __syncthreads();                  // the output waves' last chunk
 
-    *reinterpret_cast<f4_t*>(sp_out + soff) = S[0];
-    *reinterpret_cast<f4_t*>(sp_out + soff + 16) = S[1];
+#pragma unroll
+    for (int rt = 0; rt < NR; ++rt) {
+        float* so = sp_out + (int64_t)RB * rt * DKC;
+        *reinterpret_cast<f4_t*>(so + soff) = S[rt][0];
+        *reinterpret_cast<f4_t*>(so + soff + 16) = S[rt][1];
+    }
 }
 
 // ================================================================== launch
@@ -955,10 +1023,21 @@ static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, 
     in.rg = o.rg;
     in.qsw = o.qsw;
     in.ksw = o.ksw;
-    const int row_blocks = a.Dv / RB;
+    // two row tiles per block once one tile per block would need more blocks
+    // than the device has CUs (the sequential blocks run one per CU)
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 0;
+    const bool two = a.Dv % (2 * RB) == 0 && cus > 0 && (int64_t)a.B * a.Hv * (a.Dv / RB) > cus;
+    const int row_blocks = a.Dv / (RB * (two ? 2 : 1));
     const int64_t blocks = (int64_t)a.B * a.Hv * row_blocks;
-    hipLaunchKernelGGL(chunk_seq_kernel, dim3((unsigned)blocks), dim3(SEQ_THREADS), 0, stream, in, a.state_in,
-                       a.state_out, a.y, a.mask, a.T, a.Hk, a.Hv, a.Dv, L.nc, row_blocks, (int)blocks);
+    if (two)
+        hipLaunchKernelGGL(chunk_seq_kernel<2>, dim3((unsigned)blocks), dim3(SEQ_THREADS), 0, stream, in,
+                           a.state_in, a.state_out, a.y, a.mask, a.T, a.Hk, a.Hv, a.Dv, L.nc, row_blocks, (int)blocks);
+    else
+        hipLaunchKernelGGL(chunk_seq_kernel<1>, dim3((unsigned)blocks), dim3(SEQ_THREADS), 0, stream, in,
+                           a.state_in, a.state_out, a.y, a.mask, a.T, a.Hk, a.Hv, a.Dv, L.nc, row_blocks, (int)blocks);
     return hipGetLastError();
 }
 

@@ -507,6 +507,29 @@ def test_recurrent_chunked_matches_oracle(case):
     say("chunked state err", e)
 
 
+@pytest.mark.parametrize("B,Hv,Dv", [(2, 32, 128), (3, 32, 64)])
+def test_recurrent_chunked_two_row_tiles(B, Hv, Dv):
+    """Once B*Hv*Dv/16 exceeds the CU count the sequential pass serves two
+    16-row tiles per block (one tile per block below it).  Sequences of a
+    batch are independent, so each must be bit-identical to itself run alone
+    (one tile per block), and the batch must meet the oracle."""
+    say("recurrent_chunked two row tiles", B, Hv, Dv)
+    ri = rec_inputs(B, 100, Hv // 2, Hv, 128, Dv, 421)
+    mask = np.ones((B, 100), dtype=np.uint8)
+    mask[-1, 37:41] = 0
+    y, s = gpu_recurrent_chunked(ri, mask=mask)
+    for b in range(B):
+        one = {k: (None if ri[k] is None else np.ascontiguousarray(ri[k][b:b + 1]))
+               for k in ("q", "k", "v", "g", "beta", "state")}
+        y1, s1 = gpu_recurrent_chunked(one, mask=mask[b:b + 1])
+        assert np.array_equal(y[b:b + 1], y1) and np.array_equal(s[b:b + 1], s1), b
+    y_ref, s_ref = oracle.recurrent(*[oracle.bf16_to_f64(ri[k]) for k in ("q", "k", "v")],
+                                    ri["g"].astype(np.float64), ri["beta"].astype(np.float64),
+                                    ri["state"].astype(np.float64), mask=mask)
+    H.check_y(y, y_ref, "two tiles")
+    H.check_state(s, s_ref, 1e-4, "two tiles")
+
+
 def test_recurrent_chunked_properties():
     say("recurrent_chunked properties")
     ri = rec_inputs(2, 96, 2, 8, 128, 32, 410)
