@@ -162,6 +162,9 @@ __device__ __forceinline__ f4_t mma3b(u4_t a, const Planes& b, f4_t c) {
 
 // ========================================================= chunk preparation
 
+// One block serves NH v-heads of the same k-head (NH = 2 when the GQA group
+// size is even): q, k, k k^T and q k^T are shared, the rest is per head.
+template <int NH>
 struct alignas(16) PrepSmem {
     uint16_t kb[CK][DKC + 8];    // bf16 rows, padded against bank conflicts
     union {
@@ -173,16 +176,16 @@ struct alignas(16) PrepSmem {
         struct {                 // written once the inputs above are dead
             uint16_t tw[3][CK][CK + 8];    // planes of T diag(beta gamma)
             uint16_t tb[3][CK][CK + 8];    // planes of -T diag(beta)
-        } pl;
+        } pl[NH];
     } u;
     union {
         struct {
             float a[CK][CK + 4];     // strictly lower A (row-major, 16-byte rows)
             float tm[CK][CK + 4];    // T = (I + A)^-1
-        } s;
-        uint16_t vs[CK][128 + 8];    // a 128-column slice of the chunk's v rows
+        } s[NH];
+        uint16_t vs[NH][CK][128 + 8];    // a 128-column slice of the chunk's v rows
     } w;
-    float gs[CK], bs[CK], gm[CK];
+    float gs[NH][CK], bs[NH][CK], gm[NH][CK];
 };
 
 struct ChunkPtrs {
@@ -197,43 +200,55 @@ struct ChunkPtrs {
 // KF = 0: q, k, v, g, beta are inputs.  KF = 2..4: they are computed here,
 // from the mixed projection qkv, with the prologue's arithmetic (the same
 // device functions as the prologue kernel, so the same bits) and a conv of
-// width KF; then Dv <= 128.
-template <int KF>
-__global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __restrict__ q,
+// width KF; then Dv <= 128.  NH v-heads (of one k-head) per block, four
+// waves per head: wave group h (waves 4h .. 4h + 3) does head h's own steps
+// exactly as a one-head block would, so the results do not depend on NH.
+template <int KF, int NH>
+__global__ __launch_bounds__(256 * NH, 4 / NH) void chunk_prep_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const float* __restrict__ g,
                                                             const float* __restrict__ beta,
                                                             const uint8_t* __restrict__ mask,
                                                             const uint16_t* __restrict__ v, PrologueIn pin,
                                                             ChunkPtrs o, int T, int Hk, int Hv, int Dv, int NC) {
-    __shared__ PrepSmem sh;
-    const int64_t unit = blockIdx.x;          // (b * Hv + hv) * NC + c
-    const int c = (int)(unit % NC);
-    const int n = (int)(unit / NC);
-    const int b = n / Hv, hv = n % Hv;
+    __shared__ PrepSmem<NH> sh;
+    const int c = (int)(blockIdx.x % NC);
+    const int np = (int)(blockIdx.x / NC);    // b * (Hv / NH) + head pair
+    const int b = np / (Hv / NH);
+    const int hv0 = (np % (Hv / NH)) * NH;    // the block's first v-head
     const int G = Hv / Hk;
-    const int hk = hv / G;
+    const int hk = hv0 / G;
     const int64_t kunit = ((int64_t)b * Hk + hk) * NC + c;
     const int t0 = c * CK;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wv >> 2, wl = wv & 3;     // this wave's head in the block, its wave in the group
+    const int tl = tid & 255;                 // thread in the group
+    const int hv = hv0 + grp;
+    const int64_t unit = ((int64_t)b * Hv + hv) * NC + c;
     const int lr = lane & 15, lq = lane >> 4;
     const NegOnes no = neg_ones();
 
     // 1. k, q rows of the chunk (zero past T), g and beta
     constexpr int kVPre = CK * 128 / 8 / 256;      // 16-byte vectors per thread (first v slice)
     uint4 vpre[kVPre];
-    uint4 vrow[KF > 0 ? CK / 4 : 1];              // fused: this lane's v rows (8 tokens)
+    constexpr int TPW = CK / (4 * NH);            // fused: tokens per wave
+    uint4 vrow[KF > 0 ? TPW : 1];                 // fused: this lane's v rows
     if constexpr (KF > 0) {
-        // Wave w computes tokens t0 + 8w .. t0 + 8w + 7.  Lanes 0-15 hold the
-        // q head's 8-channel groups, 16-31 the k head's (aligned 16-lane
-        // groups, as in the prologue kernel, for the norm's cross-lane sum),
-        // 32 .. 32 + Dv/8 - 1 the v head's.
+      {
+        // Wave w computes tokens t0 + TPW w .. t0 + TPW (w + 1) - 1 (every wave
+        // of the block: the per-wave chain of loads, conv, SiLU and norm is
+        // what bounds this phase).  Lanes 0-15 hold the q head's 8-channel
+        // groups, 16-31 the k head's (aligned 16-lane groups, as in the
+        // prologue kernel, for the norm's cross-lane sum), 32 .. 32 + Dv/8 - 1
+        // the first v-head's and, with two heads, 48 .. 48 + Dv/8 - 1 the
+        // second's.
         const int C = 2 * Hk * DKC + Hv * Dv;
         int region = 3, c0 = 0;
         if (lane < 16) { region = 0; c0 = hk * DKC + 8 * lane; }
         else if (lane < 32) { region = 1; c0 = Hk * DKC + hk * DKC + 8 * (lane - 16); }
-        else if (lane < 32 + Dv / 8) { region = 2; c0 = 2 * Hk * DKC + hv * Dv + 8 * (lane - 32); }
+        else if (lane < 32 + Dv / 8) { region = 2; c0 = 2 * Hk * DKC + hv0 * Dv + 8 * (lane - 32); }
+        else if (NH == 2 && lane >= 48 && lane < 48 + Dv / 8) { region = 2; c0 = 2 * Hk * DKC + (hv0 + 1) * Dv + 8 * (lane - 48); }
         const bool valid = region < 3;
         const float scale = region == 0 ? pin.q_scale : pin.k_scale;
         const uint16_t* xb = pin.qkv + (int64_t)b * T * C + c0;
@@ -261,22 +276,22 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
             if (csb) return *reinterpret_cast<const uint4*>(csb + (int64_t)pr * C);
             return make_uint4(0, 0, 0, 0);
         };
-        const int tw0 = t0 + 8 * wv;
+        const int tw0 = t0 + TPW * wv;
         float h[KF - 1][8];
 #pragma unroll
         for (int j = 0; j < KF - 1; ++j) unpack8(xpad_row(tw0 + j), h[j]);
-        uint4 rows[8];
+        uint4 rows[TPW];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rows[i] = xpad_row(tw0 + i + KF - 1);
+        for (int i = 0; i < TPW; ++i) rows[i] = xpad_row(tw0 + i + KF - 1);
         // the new conv state (chunk 0's blocks; q/k channels from the first
         // v-head of the group): the last KF-1 rows of the spliced input
-        if (c == 0 && wv == 0 && valid && pin.conv_state_out && (region == 2 || hv % G == 0)) {
+        if (c == 0 && wv == 0 && valid && pin.conv_state_out && (region == 2 || hv0 % G == 0)) {
             uint16_t* out = pin.conv_state_out + (int64_t)b * (KF - 1) * C + c0;
 #pragma unroll
             for (int i = 0; i < KF - 1; ++i) *reinterpret_cast<uint4*>(out + (int64_t)i * C) = xpad_row(T + i);
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < TPW; ++i) {
             const int t = tw0 + i;
             float x[8];
             unpack8(rows[i], x);
@@ -295,8 +310,9 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
             else if (region == 1) *reinterpret_cast<uint4*>(&sh.kb[t - t0][8 * (lane - 16)]) = live ? qk : make_uint4(0, 0, 0, 0);
             vrow[i] = live ? pack8(act) : make_uint4(0, 0, 0, 0);
         }
+      }
     } else {
-    for (int idx = tid; idx < CK * DKC / 8; idx += 256) {
+    for (int idx = tid; idx < CK * DKC / 8; idx += 256 * NH) {
         const int t = idx / (DKC / 8), c8 = idx % (DKC / 8);
         uint4 kv = make_uint4(0, 0, 0, 0), qv = kv;
         if (t0 + t < T) {
@@ -313,7 +329,7 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
         const int wdt = min(128, Dv);
 #pragma unroll
         for (int i = 0; i < kVPre; ++i) {
-            const int idx = tid + i * 256;
+            const int idx = tl + i * 256;
             const int t = idx / (wdt / 8), c8 = idx % (wdt / 8);
             vpre[i] = make_uint4(0, 0, 0, 0);
             if (idx < CK * (wdt / 8) && t0 + t < T)
@@ -321,9 +337,9 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
         }
     }
     }
-    if (tid < CK) {
+    if (tl < CK) {
         // steps past T and masked steps: g = 1, beta = 0 (no decay, no write)
-        const int t = t0 + tid;
+        const int t = t0 + tl;
         const int64_t bt = (int64_t)b * T + min(t, T - 1);
         const int64_t i = bt * Hv + hv;
         float gv, bv;
@@ -334,8 +350,8 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
             bv = beta[i];
         }
         const bool on = t < T && (mask == nullptr || mask[bt] != 0);
-        sh.gs[tid] = on ? gv : 1.f;
-        sh.bs[tid] = on ? bv : 0.f;
+        sh.gs[grp][tl] = on ? gv : 1.f;
+        sh.bs[grp][tl] = on ? bv : 0.f;
     }
     __syncthreads();
 
@@ -346,42 +362,48 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
     u4_t kt[2];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-        const int d = 32 * wv + 16 * tt + lr;
+        const int d = 32 * wl + 16 * tt + lr;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int s0 = p < 2 ? 4 * lq + 2 * p : 16 + 4 * lq + 2 * (p - 2);
             kt[tt][p] = (uint32_t)sh.kb[s0][d] | ((uint32_t)sh.kb[s0 + 1][d] << 16);
         }
     }
-    if (hv % G == 0) {
-        u4_t* kd = o.ksw + kunit * kQVec + wv * 2 * 64 + lane;
-        u4_t* qd = o.qsw + kunit * kQVec + wv * 2 * 64 + lane;
+    if (grp == 0 && hv0 % G == 0) {
+        u4_t* kd = o.ksw + kunit * kQVec + wl * 2 * 64 + lane;
+        u4_t* qd = o.qsw + kunit * kQVec + wl * 2 * 64 + lane;
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
             kd[jt * 64] = kt[jt];
-            const u2_t lo = *reinterpret_cast<const u2_t*>(&sh.u.in.qb[16 * jt + lr][32 * wv + 4 * lq]);
-            const u2_t hi = *reinterpret_cast<const u2_t*>(&sh.u.in.qb[16 * jt + lr][32 * wv + 16 + 4 * lq]);
+            const u2_t lo = *reinterpret_cast<const u2_t*>(&sh.u.in.qb[16 * jt + lr][32 * wl + 4 * lq]);
+            const u2_t hi = *reinterpret_cast<const u2_t*>(&sh.u.in.qb[16 * jt + lr][32 * wl + 16 + 4 * lq]);
             qd[jt * 64] = u4_t{lo[0], lo[1], hi[0], hi[1]};
         }
     }
 
-    // 2b. k k^T and q k^T, 32 x 32 each: wave w owns output tile (w / 2, w % 2)
+    // 2b. k k^T and q k^T, 32 x 32 each: wave w owns output tile
+    //     ((w % 4) / 2, w % 2), of both products in a one-head block, of
+    //     k k^T (waves 0-3) or q k^T (waves 4-7) in a two-head block
     {
-        const int mi = wv >> 1, ni = wv & 1;
+        const int mi = wl >> 1, ni = wl & 1;
         f4_t ckk = {0.f, 0.f, 0.f, 0.f}, cqk = ckk;
 #pragma unroll
         for (int ks = 0; ks < DKC / 32; ++ks) {
             const int col = ks * 32 + 8 * lq;
-            const u4_t ka = *reinterpret_cast<const u4_t*>(&sh.kb[16 * mi + lr][col]);
-            const u4_t qa = *reinterpret_cast<const u4_t*>(&sh.u.in.qb[16 * mi + lr][col]);
             const u4_t kb = *reinterpret_cast<const u4_t*>(&sh.kb[16 * ni + lr][col]);
-            ckk = mma(ka, kb, ckk);
-            cqk = mma(qa, kb, cqk);
+            if (NH == 1 || grp == 0) {
+                const u4_t ka = *reinterpret_cast<const u4_t*>(&sh.kb[16 * mi + lr][col]);
+                ckk = mma(ka, kb, ckk);
+            }
+            if (NH == 1 || grp == 1) {
+                const u4_t qa = *reinterpret_cast<const u4_t*>(&sh.u.in.qb[16 * mi + lr][col]);
+                cqk = mma(qa, kb, cqk);
+            }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sh.u.in.kk[16 * mi + 4 * lq + i][16 * ni + lr] = ckk[i];
-            sh.u.in.qk[16 * mi + 4 * lq + i][16 * ni + lr] = cqk[i];
+            if (NH == 1 || grp == 0) sh.u.in.kk[16 * mi + 4 * lq + i][16 * ni + lr] = ckk[i];
+            if (NH == 1 || grp == 1) sh.u.in.qk[16 * mi + 4 * lq + i][16 * ni + lr] = cqk[i];
         }
     }
     __syncthreads();
@@ -389,24 +411,25 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
     // 3. decay ratios R[t][s] = g_{s+1}...g_t (s <= t) for s in this thread's
     //    four columns, then A, -P (two planes), gamma, -rho
     {
-        const int t = tid >> 3, s0 = (tid & 7) * 4;
+        const int t = tl >> 3, s0 = (tl & 7) * 4;
+        const float* gs = sh.gs[grp];
         float r[4];
         // R[t][s0+3] = g_{s0+4}...g_t, then R[t][s] = R[t][s+1] g_{s+1} while
         // s+1 <= t; R[t][s] = 1 for s >= t (only s = t is used)
         float acc = 1.f;
-        for (int u = s0 + 4; u <= t; ++u) acc *= sh.gs[u];
+        for (int u = s0 + 4; u <= t; ++u) acc *= gs[u];
         r[3] = acc;
-        r[2] = s0 + 3 <= t ? r[3] * sh.gs[s0 + 3] : 1.f;
-        r[1] = s0 + 2 <= t ? r[2] * sh.gs[s0 + 2] : 1.f;
-        r[0] = s0 + 1 <= t ? r[1] * sh.gs[s0 + 1] : 1.f;
+        r[2] = s0 + 3 <= t ? r[3] * gs[s0 + 3] : 1.f;
+        r[1] = s0 + 2 <= t ? r[2] * gs[s0 + 2] : 1.f;
+        r[0] = s0 + 1 <= t ? r[1] * gs[s0 + 1] : 1.f;
         float av[4], pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int s = s0 + e;
-            av[e] = s < t ? sh.bs[t] * r[e] * sh.u.in.kk[t][s] : 0.f;
+            av[e] = s < t ? sh.bs[grp][t] * r[e] * sh.u.in.kk[t][s] : 0.f;
             pv[e] = s <= t ? -(r[e] * sh.u.in.qk[t][s]) : 0.f;
         }
-        *reinterpret_cast<float4*>(&sh.w.s.a[t][s0]) = make_float4(av[0], av[1], av[2], av[3]);
+        *reinterpret_cast<float4*>(&sh.w.s[grp].a[t][s0]) = make_float4(av[0], av[1], av[2], av[3]);
         // these four columns are elements 4 half .. 4 half + 3 of quarter q4
         const int half = s0 >> 4, q4 = (s0 & 15) >> 2;
         const int l = 16 * q4 + (t & 15), jt = t >> 4;
@@ -415,8 +438,8 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
         pdst[0] = u2_t{p0.h, p1.h};
         pdst[2 * 64] = u2_t{p0.m, p1.m};
         if (s0 == 0) {
-            const float gm = sh.gs[0] * r[0];     // gamma_t = g_0 R[t][0]
-            sh.gm[t] = gm;
+            const float gm = gs[0] * r[0];        // gamma_t = g_0 R[t][0]
+            sh.gm[grp][t] = gm;
             o.rg[unit * 2 * CK + CK + t] = gm;
         }
         if (t == CK - 1)
@@ -432,79 +455,80 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
     //        are known; lanes 32-63 zero T12.  The scheduling barrier per row
     //        keeps the row's operands from being hoisted.
     constexpr int CH = CK / 2;
-    if (tid < CK) {
-        const int j = tid % CH, base = tid < CH ? 0 : CH;
+    auto& sw = sh.w.s[grp];
+    if (tl < CK) {
+        const int j = tl % CH, base = tl < CH ? 0 : CH;
         float x[CH];
 #pragma unroll
         for (int t = 0; t < CH; ++t) {
             float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
             for (int s4 = 0; s4 < t; s4 += 4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(&sh.w.s.a[base + t][base + s4]);
+                const float4 a4 = *reinterpret_cast<const float4*>(&sw.a[base + t][base + s4]);
                 acc0 = fmaf(a4.x, x[s4], acc0);
                 if (s4 + 1 < t) acc1 = fmaf(a4.y, x[s4 + 1], acc1);
                 if (s4 + 2 < t) acc0 = fmaf(a4.z, x[s4 + 2], acc0);
                 if (s4 + 3 < t) acc1 = fmaf(a4.w, x[s4 + 3], acc1);
             }
             x[t] = (t == j ? 1.f : 0.f) - (acc0 + acc1);
-            sh.w.s.tm[base + t][base + j] = x[t];
+            sw.tm[base + t][base + j] = x[t];
             __builtin_amdgcn_sched_barrier(0);
         }
-    } else if (tid < 2 * CK) {
+    } else if (tl < 2 * CK) {
         // T12 = 0: rows 0..15, columns 16..31, one row per lane pair
-        const int t = (tid - CK) >> 1, h = (tid - CK) & 1;
-        *reinterpret_cast<float4*>(&sh.w.s.tm[t][CH + 8 * h]) = make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(&sh.w.s.tm[t][CH + 8 * h + 4]) = make_float4(0.f, 0.f, 0.f, 0.f);
+        const int t = (tl - CK) >> 1, h = (tl - CK) & 1;
+        *reinterpret_cast<float4*>(&sw.tm[t][CH + 8 * h]) = make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(&sw.tm[t][CH + 8 * h + 4]) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
     //    4b. M = A21 T11 (16 x 16, one entry per thread) into the unused upper
     //        right block of A, then T21 = -T22 M.
     {
-        const int i = tid >> 4, j = tid & 15;
+        const int i = tl >> 4, j = tl & 15;
         float m0 = 0.f, m1 = 0.f;
 #pragma unroll
         for (int k4 = 0; k4 < CH; k4 += 4) {
-            const float4 a4 = *reinterpret_cast<const float4*>(&sh.w.s.a[CH + i][k4]);
-            m0 = fmaf(a4.x, sh.w.s.tm[k4][j], m0);
-            m1 = fmaf(a4.y, sh.w.s.tm[k4 + 1][j], m1);
-            m0 = fmaf(a4.z, sh.w.s.tm[k4 + 2][j], m0);
-            m1 = fmaf(a4.w, sh.w.s.tm[k4 + 3][j], m1);
+            const float4 a4 = *reinterpret_cast<const float4*>(&sw.a[CH + i][k4]);
+            m0 = fmaf(a4.x, sw.tm[k4][j], m0);
+            m1 = fmaf(a4.y, sw.tm[k4 + 1][j], m1);
+            m0 = fmaf(a4.z, sw.tm[k4 + 2][j], m0);
+            m1 = fmaf(a4.w, sw.tm[k4 + 3][j], m1);
         }
-        sh.w.s.a[i][CH + j] = m0 + m1;
+        sw.a[i][CH + j] = m0 + m1;
         __syncthreads();
         float u0 = 0.f, u1 = 0.f;
 #pragma unroll
         for (int k4 = 0; k4 < CH; k4 += 4) {
-            const float4 t4 = *reinterpret_cast<const float4*>(&sh.w.s.tm[CH + i][CH + k4]);
-            u0 = fmaf(t4.x, sh.w.s.a[k4][CH + j], u0);
-            u1 = fmaf(t4.y, sh.w.s.a[k4 + 1][CH + j], u1);
-            u0 = fmaf(t4.z, sh.w.s.a[k4 + 2][CH + j], u0);
-            u1 = fmaf(t4.w, sh.w.s.a[k4 + 3][CH + j], u1);
+            const float4 t4 = *reinterpret_cast<const float4*>(&sw.tm[CH + i][CH + k4]);
+            u0 = fmaf(t4.x, sw.a[k4][CH + j], u0);
+            u1 = fmaf(t4.y, sw.a[k4 + 1][CH + j], u1);
+            u0 = fmaf(t4.z, sw.a[k4 + 2][CH + j], u0);
+            u1 = fmaf(t4.w, sw.a[k4 + 3][CH + j], u1);
         }
-        sh.w.s.tm[CH + i][j] = -(u0 + u1);
+        sw.tm[CH + i][j] = -(u0 + u1);
     }
     __syncthreads();
 
     // 5. planes of T diag(beta gamma) and of -T diag(beta), four entries per thread
     {
-        const int t = tid >> 3, s0 = (tid & 7) * 4;
-        const float4 tv = *reinterpret_cast<const float4*>(&sh.w.s.tm[t][s0]);
+        const int t = tl >> 3, s0 = (tl & 7) * 4;
+        const float4 tv = *reinterpret_cast<const float4*>(&sw.tm[t][s0]);
         const float x[4] = {tv.x, tv.y, tv.z, tv.w};
         float w4[4], b4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float bs = sh.bs[s0 + e];
-            w4[e] = x[e] * (bs * sh.gm[s0 + e]);
+            const float bs = sh.bs[grp][s0 + e];
+            w4[e] = x[e] * (bs * sh.gm[grp][s0 + e]);
             b4[e] = -(x[e] * bs);
         }
         const Split2 w0 = split2(no, w4[0], w4[1]), w1 = split2(no, w4[2], w4[3]);
         const Split2 b0 = split2(no, b4[0], b4[1]), b1 = split2(no, b4[2], b4[3]);
-        *reinterpret_cast<u2_t*>(&sh.u.pl.tw[0][t][s0]) = u2_t{w0.h, w1.h};
-        *reinterpret_cast<u2_t*>(&sh.u.pl.tw[1][t][s0]) = u2_t{w0.m, w1.m};
-        *reinterpret_cast<u2_t*>(&sh.u.pl.tw[2][t][s0]) = u2_t{w0.l, w1.l};
-        *reinterpret_cast<u2_t*>(&sh.u.pl.tb[0][t][s0]) = u2_t{b0.h, b1.h};
-        *reinterpret_cast<u2_t*>(&sh.u.pl.tb[1][t][s0]) = u2_t{b0.m, b1.m};
-        *reinterpret_cast<u2_t*>(&sh.u.pl.tb[2][t][s0]) = u2_t{b0.l, b1.l};
+        *reinterpret_cast<u2_t*>(&sh.u.pl[grp].tw[0][t][s0]) = u2_t{w0.h, w1.h};
+        *reinterpret_cast<u2_t*>(&sh.u.pl[grp].tw[1][t][s0]) = u2_t{w0.m, w1.m};
+        *reinterpret_cast<u2_t*>(&sh.u.pl[grp].tw[2][t][s0]) = u2_t{w0.l, w1.l};
+        *reinterpret_cast<u2_t*>(&sh.u.pl[grp].tb[0][t][s0]) = u2_t{b0.h, b1.h};
+        *reinterpret_cast<u2_t*>(&sh.u.pl[grp].tb[1][t][s0]) = u2_t{b0.m, b1.m};
+        *reinterpret_cast<u2_t*>(&sh.u.pl[grp].tb[2][t][s0]) = u2_t{b0.l, b1.l};
     }
     __syncthreads();
 
@@ -516,19 +540,19 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
     for (int jt = 0; jt < 2; ++jt) {
         Planes tw;
         const int row = 16 * jt + lr;
-        const u2_t h0 = *reinterpret_cast<const u2_t*>(&sh.u.pl.tw[0][row][4 * lq]);
-        const u2_t h1 = *reinterpret_cast<const u2_t*>(&sh.u.pl.tw[0][row][16 + 4 * lq]);
-        const u2_t m0 = *reinterpret_cast<const u2_t*>(&sh.u.pl.tw[1][row][4 * lq]);
-        const u2_t m1 = *reinterpret_cast<const u2_t*>(&sh.u.pl.tw[1][row][16 + 4 * lq]);
-        const u2_t l0 = *reinterpret_cast<const u2_t*>(&sh.u.pl.tw[2][row][4 * lq]);
-        const u2_t l1 = *reinterpret_cast<const u2_t*>(&sh.u.pl.tw[2][row][16 + 4 * lq]);
+        const u2_t h0 = *reinterpret_cast<const u2_t*>(&sh.u.pl[grp].tw[0][row][4 * lq]);
+        const u2_t h1 = *reinterpret_cast<const u2_t*>(&sh.u.pl[grp].tw[0][row][16 + 4 * lq]);
+        const u2_t m0 = *reinterpret_cast<const u2_t*>(&sh.u.pl[grp].tw[1][row][4 * lq]);
+        const u2_t m1 = *reinterpret_cast<const u2_t*>(&sh.u.pl[grp].tw[1][row][16 + 4 * lq]);
+        const u2_t l0 = *reinterpret_cast<const u2_t*>(&sh.u.pl[grp].tw[2][row][4 * lq]);
+        const u2_t l1 = *reinterpret_cast<const u2_t*>(&sh.u.pl[grp].tw[2][row][16 + 4 * lq]);
         tw.h = u4_t{h0[0], h0[1], h1[0], h1[1]};
         tw.m = u4_t{m0[0], m0[1], m1[0], m1[1]};
         tw.l = u4_t{l0[0], l0[1], l1[0], l1[1]};
         const f4_t zero = {0.f, 0.f, 0.f, 0.f};
         const f4_t w0 = mma3b(kt[0], tw, zero);
         const f4_t w1 = mma3b(kt[1], tw, zero);
-        u4_t* dst = o.wsw + unit * kWVec + ((wv * 2 + jt) * 2) * 64 + lane;
+        u4_t* dst = o.wsw + unit * kWVec + ((wl * 2 + jt) * 2) * 64 + lane;
         dst[0] = __builtin_bit_cast(u4_t, w0);
         dst[64] = __builtin_bit_cast(u4_t, w1);
     }
@@ -541,41 +565,47 @@ __global__ __launch_bounds__(256, 4) void chunk_prep_kernel(const uint16_t* __re
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
         const int row = 16 * jt + lr;
-        tb[jt].h = *reinterpret_cast<const u4_t*>(&sh.u.pl.tb[0][row][8 * lq]);
-        tb[jt].m = *reinterpret_cast<const u4_t*>(&sh.u.pl.tb[1][row][8 * lq]);
-        tb[jt].l = *reinterpret_cast<const u4_t*>(&sh.u.pl.tb[2][row][8 * lq]);
+        tb[jt].h = *reinterpret_cast<const u4_t*>(&sh.u.pl[grp].tb[0][row][8 * lq]);
+        tb[jt].m = *reinterpret_cast<const u4_t*>(&sh.u.pl[grp].tb[1][row][8 * lq]);
+        tb[jt].l = *reinterpret_cast<const u4_t*>(&sh.u.pl[grp].tb[2][row][8 * lq]);
     }
     for (int c0 = 0; c0 < Dv; c0 += 128) {
         const int wdt = min(128, Dv - c0);
         if (KF > 0) {
-            // fused: lane 32 + j of wave w holds column group j of tokens 8w .. 8w + 7
-            if (lane >= 32 && lane < 32 + wdt / 8) {
+            // fused: lane 32 + j (48 + j) of wave w holds column group j of
+            // tokens TPW w .. TPW (w + 1) - 1 of the first (second) v-head
+            {
+                const int hs = lane >= 48 ? 1 : 0;
+                const int j = lane - 32 - 16 * hs;
+                if (lane >= 32 && hs < NH && j < wdt / 8) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&sh.w.vs[8 * wv + i][8 * (lane - 32)]) = vrow[i];
+                    for (int i = 0; i < TPW; ++i) *reinterpret_cast<uint4*>(&sh.w.vs[hs][TPW * wv + i][8 * j]) = vrow[i];
+                }
             }
         } else if (c0 == 0) {
 #pragma unroll
             for (int i = 0; i < kVPre; ++i) {
-                const int idx = tid + i * 256;
+                const int idx = tl + i * 256;
                 const int t = idx / (wdt / 8), c8 = idx % (wdt / 8);
-                if (idx < CK * (wdt / 8)) *reinterpret_cast<uint4*>(&sh.w.vs[t][c8 * 8]) = vpre[i];
+                if (idx < CK * (wdt / 8)) *reinterpret_cast<uint4*>(&sh.w.vs[grp][t][c8 * 8]) = vpre[i];
             }
         } else {
-            for (int idx = tid; idx < CK * (wdt / 8); idx += 256) {
+            for (int idx = tl; idx < CK * (wdt / 8); idx += 256) {
                 const int t = idx / (wdt / 8), c8 = idx % (wdt / 8);
                 uint4 vv = make_uint4(0, 0, 0, 0);
                 if (t0 + t < T)
                     vv = *reinterpret_cast<const uint4*>(v + (((int64_t)b * T + t0 + t) * Hv + hv) * Dv + c0 + c8 * 8);
-                *reinterpret_cast<uint4*>(&sh.w.vs[t][c8 * 8]) = vv;
+                *reinterpret_cast<uint4*>(&sh.w.vs[grp][t][c8 * 8]) = vv;
             }
         }
         __syncthreads();
-        for (int rb = wv; rb < wdt / 16; rb += 4) {
+        for (int rb = wl; rb < wdt / 16; rb += 4) {
             const int col = 16 * rb + lr;
+            const auto& vsh = sh.w.vs[grp];
             u4_t vb;
 #pragma unroll
             for (int p = 0; p < 4; ++p)
-                vb[p] = (uint32_t)sh.w.vs[8 * lq + 2 * p][col] | ((uint32_t)sh.w.vs[8 * lq + 2 * p + 1][col] << 16);
+                vb[p] = (uint32_t)vsh[8 * lq + 2 * p][col] | ((uint32_t)vsh[8 * lq + 2 * p + 1][col] << 16);
             const f4_t zero = {0.f, 0.f, 0.f, 0.f};
             u4_t* dst = o.u + (unit * (Dv / 16) + c0 / 16 + rb) * 2 * 64 + lane;
             dst[0] = __builtin_bit_cast(u4_t, mma3a(tb[0], vb, zero));
@@ -991,29 +1021,26 @@ static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, 
     o.rg = reinterpret_cast<float*>(base + L.rg);
     o.qsw = reinterpret_cast<u4_t*>(base + L.qsw);
     o.ksw = reinterpret_cast<u4_t*>(base + L.ksw);
-    const int64_t units = (int64_t)a.B * a.Hv * L.nc;
+    // two v-heads per preparation block when the GQA group size is even
+    const int nh = (a.Hv / a.Hk) % 2 == 0 ? 2 : 1;
+    const int64_t pblocks = (int64_t)a.B * (a.Hv / nh) * L.nc;
     const PrologueIn none{};
     const PrologueIn& pi = pin ? *pin : none;
-    switch (K) {
-        case 0:
-            hipLaunchKernelGGL(chunk_prep_kernel<0>, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g,
-                               a.beta, a.mask, a.v, pi, o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
-            break;
-        case 2:
-            hipLaunchKernelGGL(chunk_prep_kernel<2>, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g,
-                               a.beta, a.mask, a.v, pi, o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
-            break;
-        case 3:
-            hipLaunchKernelGGL(chunk_prep_kernel<3>, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g,
-                               a.beta, a.mask, a.v, pi, o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
-            break;
-        case 4:
-            hipLaunchKernelGGL(chunk_prep_kernel<4>, dim3((unsigned)units), dim3(256), 0, stream, a.q, a.k, a.g,
-                               a.beta, a.mask, a.v, pi, o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
-            break;
-        default:
-            return hipErrorInvalidValue;
+#define GDN_PREP(KF_, NH_)                                                                                     \
+    hipLaunchKernelGGL((chunk_prep_kernel<KF_, NH_>), dim3((unsigned)pblocks), dim3(256 * NH_), 0, stream, a.q, \
+                       a.k, a.g, a.beta, a.mask, a.v, pi, o, a.T, a.Hk, a.Hv, a.Dv, L.nc)
+    switch (K * 2 + nh - 1) {
+        case 0: GDN_PREP(0, 1); break;
+        case 1: GDN_PREP(0, 2); break;
+        case 4: GDN_PREP(2, 1); break;
+        case 5: GDN_PREP(2, 2); break;
+        case 6: GDN_PREP(3, 1); break;
+        case 7: GDN_PREP(3, 2); break;
+        case 8: GDN_PREP(4, 1); break;
+        case 9: GDN_PREP(4, 2); break;
+        default: return hipErrorInvalidValue;
     }
+#undef GDN_PREP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     SeqIn in;
