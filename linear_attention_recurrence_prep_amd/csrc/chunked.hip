@@ -35,18 +35,19 @@
 // the next product: the state and the chunk's deltas never leave registers.
 //
 // Two kernels:
-//  * chunk_prep_kernel, one block per (b, hv, chunk), independent of the
-//    state: k k^T and q k^T on bf16 MFMA, the decay ratios as direct products
-//    (never quotients of cumulative decays, so underflow to zero is
-//    harmless), and the unit lower-triangular solve by forward substitution
-//    for W and T.  It writes W, -Tb and -P as bf16 planes, q and k (bf16) and
+//  * chunk_prep_kernel, one block per (b, chunk) and one v-head or the two
+//    v-heads of a pair sharing a k-head, independent of the state: k k^T and
+//    q k^T on bf16 MFMA, the decay ratios as direct products (never
+//    quotients of cumulative decays, so underflow to zero is harmless), and
+//    the unit lower-triangular solve by forward substitution for W and T.
+//    It writes W and -Tb V (f32), -P (two bf16 planes), q and k (bf16) and
 //    gamma, -rho, each already in the register layout of the sequential pass.
-//  * chunk_seq_kernel, one block per (b, hv, 16 state rows), walks the chunks
-//    in order.  Wave w holds state columns [32w, 32w + 32) of its 16 rows in
-//    MFMA accumulators.  Per chunk each wave forms its share of
-//    W S_0^T - Tb V and of Q S_0^T over its columns, the four shares are summed
-//    through LDS (the only exchange, one barrier per chunk), and every wave
-//    then updates its state columns; two waves finish Y.
+//  * chunk_seq_kernel, one block per (b, hv, 16 or 32 state rows), walks the
+//    chunks in order.  Wave w holds state columns [32w, 32w + 32) of its rows
+//    in MFMA accumulators.  Per chunk each wave forms its share of
+//    W S_0^T - Tb V and of Q S_0^T over its columns, the four shares are
+//    summed through LDS (the only exchange, one barrier per chunk), and every
+//    wave then updates its state columns; two waves finish Y.
 // Padding steps past T and masked steps carry g = 1, beta = 0: their Delta is
 // 0 and they leave S unchanged (a masked step's y is written as zero).
 #include <algorithm>
