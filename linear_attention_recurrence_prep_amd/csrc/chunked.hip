@@ -51,6 +51,7 @@
 // Padding steps past T and masked steps carry g = 1, beta = 0: their Delta is
 // 0 and they leave S unchanged (a masked step's y is written as zero).
 #include <algorithm>
+#include <atomic>
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -1010,6 +1011,22 @@ hipError_t launch_layer_chunked(const RecurrentArgs& a, const PrologueIn& p, int
     return launch_chunked(a, &p, K, ws, stream);
 }
 
+// The current device's CU count, looked up once per device (0 if unknown).
+static int device_cu_count() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int c = cached[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 0) cus = 0;
+    if (dev < kMaxDevices && cus > 0) cached[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, int K, void* ws,
                                  hipStream_t stream) {
     if (!chunked_supported(a.Hv, a.Dk, a.Dv) || a.T <= 0 || a.B <= 0) return hipErrorInvalidValue;
@@ -1053,10 +1070,7 @@ static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, 
     in.ksw = o.ksw;
     // two row tiles per block once one tile per block would need more blocks
     // than the device has CUs (the sequential blocks run one per CU)
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 0;
+    const int cus = device_cu_count();
     const bool two = a.Dv % (2 * RB) == 0 && cus > 0 && (int64_t)a.B * a.Hv * (a.Dv / RB) > cus;
     const int row_blocks = a.Dv / (RB * (two ? 2 : 1));
     const int64_t blocks = (int64_t)a.B * a.Hv * row_blocks;
