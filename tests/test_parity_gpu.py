@@ -334,6 +334,8 @@ CORE_CASES = [
     (1, 64, 2, 4, 32, 32, 4, 300),
     (2, 45, 2, 4, 64, 24, 3, 301),
     (1, 130, 4, 8, 128, 128, 4, 302),
+    (1, 100, 3, 3, 128, 64, 2, 303),       # GQA 1: one v-head per preparation block, conv K=2
+    (1, 70, 2, 4, 128, 96, 3, 305),        # two v-heads per preparation block, Dv < 128, K=3
 ]
 
 
@@ -353,14 +355,18 @@ def test_layer_core_matches_oracle(case):
     assert np.array_equal(cs, cs_ref)
 
 
-@pytest.mark.parametrize("shape", [(2, 70, 2, 4, 128, 64), (2, 40, 2, 4, 128, 64), (1, 90, 1, 2, 64, 32)],
-                         ids=["chunked", "short", "Dk64"])
+@pytest.mark.parametrize("shape", [(2, 70, 2, 4, 128, 64, 4), (2, 40, 2, 4, 128, 64, 4), (1, 90, 1, 2, 64, 32, 4),
+                                   (1, 100, 3, 3, 128, 64, 2), (2, 96, 2, 6, 128, 32, 3),
+                                   (1, 70, 2, 4, 128, 96, 3)],
+                         ids=["chunked", "short", "Dk64", "chunked_G1_K2", "chunked_G3_K3", "chunked_G2_Dv96_K3"])
 def test_layer_core_equals_prep_then_recurrent(shape):
     """The layer core is the prologue followed by the chunked recurrence
-    (Dk = 128, Dv % 16 == 0, T >= 64) or else the per-step one, bit for bit."""
-    B, T, Hk, Hv, Dk, Dv = shape
+    (Dk = 128, Dv % 16 == 0, T >= 64) or else the per-step one, bit for bit
+    (in the chunked form the prologue runs inside the chunk preparation, one
+    or two v-heads per block by the parity of the GQA group size)."""
+    B, T, Hk, Hv, Dk, Dv, K = shape
     say("layer_core composition", shape)
-    raw = layer_inputs(B, T, Hk, Hv, Dk, Dv, 4, 310)
+    raw = layer_inputs(B, T, Hk, Hv, Dk, Dv, K, 310)
     y, s, cs = gpu_layer_core(raw, Hk, Hv, Dk, Dv, 0.01, 0.09)
     p = gpu_prep(raw, Hk, Hv, Dk, Dv, 0.01, 0.09)
     ri = dict(q=p["q"], k=p["k"], v=p["v"], g=p["g"], beta=p["beta"], state=raw["state"])
