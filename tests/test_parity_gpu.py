@@ -498,6 +498,8 @@ CHUNK_CASES = [
     (3, 5, 2, 4, 128, 128, 403),           # shorter than a chunk
     (64, 1, 16, 32, 128, 128, 2),          # decode-sized batch, one step
     (1, 257, 4, 8, 128, 64, 404),          # GQA 2, nine chunks
+    (1, 70, 2, 4, 128, 256, 405),          # Dv = 256: two v slices, two heads per preparation block
+    (2, 50, 3, 3, 128, 160, 406),          # Dv = 160 (128 + 32), one head per preparation block
 ]
 
 
