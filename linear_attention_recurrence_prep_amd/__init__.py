@@ -6,6 +6,6 @@ tensors to that ABI; ``inputs`` draws seeded synthetic inputs.  The library
 is loaded on first use; if it has not been built, that first call raises.
 """
 from .binding import (  # noqa: F401
-    GdnError, layer_core, layer_core_workspace_bytes, lib, prep, recurrent, recurrent_chunked,
-    recurrent_chunked_workspace_bytes,
+    Bound, GdnError, bind, gated_rmsnorm, layer_core, layer_core_gated, layer_core_workspace_bytes, lib, prep,
+    recurrent, recurrent_chunked, recurrent_chunked_workspace_bytes, recurrent_per_key, recurrent_snapshots,
 )

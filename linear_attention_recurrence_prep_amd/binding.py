@@ -14,6 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
+import threading
 
 import torch
 
@@ -91,6 +92,47 @@ def _check(status: int):
         raise GdnError(status, f"{L.gdn_status_string(status).decode()}: {L.gdn_last_error().decode()}")
 
 
+_capture = threading.local()
+
+
+def _invoke(fn, *args):
+    """Call a library entry point, or hand it to :func:`bind` when binding."""
+    if getattr(_capture, "active", False):
+        _capture.call = (fn, args)
+        return
+    _check(fn(*args))
+
+
+class Bound:
+    """One library call with its arguments marshalled once (see :func:`bind`)."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+
+
+def bind(func, *args, **kwargs):
+    """Marshal ``func(*args, **kwargs)`` (one of this module's entry points)
+    once and return a zero-argument callable that issues the same library
+    call again: the same kernels on the same buffers, on the stream that was
+    current (or passed) at bind time, without the per-call tensor checks.
+    The tensors are kept alive by the returned object; their contents may
+    change between calls, their storage must not (the pointers are fixed)."""
+    _capture.active = True
+    _capture.call = None
+    try:
+        func(*args, **kwargs)
+    finally:
+        _capture.active = False
+    if _capture.call is None:
+        raise TypeError(f"{getattr(func, '__name__', func)} is not a library call of this module")
+    fn, cargs = _capture.call
+    _capture.call = None
+    return Bound(fn, cargs, (args, kwargs))
+
+
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 _MASK = (torch.uint8, torch.bool)
 
@@ -136,7 +178,7 @@ def recurrent(q, k, v, g, beta, state_in, state_out, y, *, mask=None, stream=Non
         _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
     ]
     m = _ptr(mask, "mask", _MASK, (B, T), dev)
-    _check(lib().gdn_recurrent_masked(*args[:5], m, *args[5:], B, T, Hk, Hv, Dk, Dv, _stream(dev, stream)))
+    _invoke(lib().gdn_recurrent_masked, *args[:5], m, *args[5:], B, T, Hk, Hv, Dk, Dv, _stream(dev, stream))
 
 
 def recurrent_chunked_workspace_bytes(B, T, Hk, Hv, Dk, Dv) -> int:
@@ -172,8 +214,8 @@ def recurrent_chunked(q, k, v, g, beta, state_in, state_out, y, workspace, *, ma
     ]
     ws, nws = _workspace(workspace, dev)
     m = _ptr(mask, "mask", _MASK, (B, T), dev)
-    _check(lib().gdn_recurrent_chunked_masked(*args[:5], m, *args[5:], ws, nws, B, T, Hk, Hv, Dk, Dv,
-                                              _stream(dev, stream)))
+    _invoke(lib().gdn_recurrent_chunked_masked, *args[:5], m, *args[5:], ws, nws, B, T, Hk, Hv, Dk, Dv,
+            _stream(dev, stream))
 
 
 def prep(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, q, k, v, g, beta, *,
@@ -200,8 +242,8 @@ def prep(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, q, k,
         _ptr(g, "g", (torch.float32,), (B, T, Hv), dev),
         _ptr(beta, "beta", (torch.float32,), (B, T, Hv), dev),
     ]
-    _check(lib().gdn_prep(*args, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps,
-                          _stream(dev, stream)))
+    _invoke(lib().gdn_prep, *args, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps,
+            _stream(dev, stream))
 
 
 def layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv) -> int:
@@ -234,8 +276,8 @@ def layer_core(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias,
         ws_ptr,
     ]
     m = _ptr(mask, "mask", _MASK, (B, T), dev)
-    _check(lib().gdn_layer_core_masked(*args[:8], m, *args[8:], ws_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale,
-                                       k_scale, eps, _stream(dev, stream)))
+    _invoke(lib().gdn_layer_core_masked, *args[:8], m, *args[8:], ws_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale,
+            k_scale, eps, _stream(dev, stream))
 
 
 def gated_rmsnorm(y, z, norm_weight, out, *, eps=1e-6, stream=None):
@@ -250,7 +292,7 @@ def gated_rmsnorm(y, z, norm_weight, out, *, eps=1e-6, stream=None):
         _ptr(norm_weight, "norm_weight", _BF16, (Dv,), dev),
         _ptr(out, "out", _BF16, (B, T, Hv, Dv), dev),
     ]
-    _check(lib().gdn_gated_rmsnorm(*args, B, T, Hv, Dv, eps, _stream(dev, stream)))
+    _invoke(lib().gdn_gated_rmsnorm, *args, B, T, Hv, Dv, eps, _stream(dev, stream))
 
 
 def layer_core_gated(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, z, norm_weight,
@@ -280,8 +322,8 @@ def layer_core_gated(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt
         _ptr(out, "out", _BF16, (B, T, Hv, Dv), dev),
         ws_ptr,
     ]
-    _check(lib().gdn_layer_core_gated(*args, ws_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps,
-                                      norm_eps, _stream(dev, stream)))
+    _invoke(lib().gdn_layer_core_gated, *args, ws_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps,
+            norm_eps, _stream(dev, stream))
 
 
 def recurrent_snapshots(q, k, v, g, beta, state_in, state_out, y, snap_steps, snapshots, *, mask=None,
@@ -311,8 +353,8 @@ def recurrent_snapshots(q, k, v, g, beta, state_in, state_out, y, snap_steps, sn
         _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
     ]
     snaps = _ptr(snapshots, "snapshots", (torch.float32,), (len(steps), B, Hv, Dv, Dk), dev)
-    _check(lib().gdn_recurrent_snapshots(*args, int(per_key), *rest, ctypes.cast(arr, ctypes.c_void_p),
-                                         len(steps), snaps, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream)))
+    _invoke(lib().gdn_recurrent_snapshots, *args, int(per_key), *rest, ctypes.cast(arr, ctypes.c_void_p),
+            len(steps), snaps, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream))
 
 
 def recurrent_per_key(q, k, v, g, beta, state_in, state_out, y, *, mask=None, stream=None):
@@ -332,5 +374,5 @@ def recurrent_per_key(q, k, v, g, beta, state_in, state_out, y, *, mask=None, st
         _ptr(state_out, "state_out", (torch.float32,), (B, Hv, Dv, Dk), dev),
         _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
     ]
-    _check(lib().gdn_recurrent_per_key(*args, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream)))
+    _invoke(lib().gdn_recurrent_per_key, *args, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream))
 

@@ -325,3 +325,9 @@ def test_per_key_gate_span_is_checked(L):
     assert call_snap(L, snaps=inside, per_key=1) == OVERLAP
     assert L.gdn_recurrent_per_key(p["q"], p["k"], p["v"], None, p["beta"], None, p["state_in"], addr(6),
                                    p["y"], d["B"], d["T"], d["Hk"], d["Hv"], d["Dk"], d["Dv"], None) == NULLP
+
+
+def test_bind_rejects_non_library_calls():
+    from linear_attention_recurrence_prep_amd import binding
+    with pytest.raises(TypeError):
+        binding.bind(len, [1, 2])
