@@ -876,31 +876,14 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
             x1[rt] = mma(o.w[1].h, s[rt].h, x1[rt]);
         }
 
-        // this wave's share of S Q^T (rows r, columns t); y is rounded to
-        // bf16, so the state's two leading planes suffice (2^-16)
-        f4_t y0v[NR], y1v[NR];
-#pragma unroll
-        for (int rt = 0; rt < NR; ++rt) {
-            y0v[rt] = mma(s[rt].m, o.q[0], zero);
-            y1v[rt] = mma(s[rt].m, o.q[1], zero);
-        }
-#pragma unroll
-        for (int rt = 0; rt < NR; ++rt) {
-            y0v[rt] = mma(s[rt].h, o.q[0], y0v[rt]);
-            y1v[rt] = mma(s[rt].h, o.q[1], y1v[rt]);
-        }
-
         SEQ_PIN(nx.template load<1>(in, x, cn));
         n1.split_w(no);
 
 #pragma unroll
         for (int rt = 0; rt < NR; ++rt) {
             f4_t* xb = sh.x[c & 1][rt];
-            f4_t* yb = sh.y[b3][rt];
             xb[(2 * wv) * 64 + lane] = x0[rt];
             xb[(2 * wv + 1) * 64 + lane] = x1[rt];
-            yb[(2 * wv) * 64 + lane] = y0v[rt];
-            yb[(2 * wv + 1) * 64 + lane] = y1v[rt];
         }
         float* rg = sh.rg[b3];
         if (wv == 0) rg[lane] = o.rg;
@@ -916,6 +899,21 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
             const f4_t p01 = xb[1 * 64 + lane], p11 = xb[3 * 64 + lane], p21 = xb[5 * 64 + lane], p31 = xb[7 * 64 + lane];
             d0[rt] = ((p00 + p10) + p20) + p30;
             d1[rt] = ((p01 + p11) + p21) + p31;
+        }
+
+        // this wave's share of S Q^T (rows r, columns t), formed after the
+        // barrier, beside the D sums and split (the output waves read it one
+        // chunk later); y is rounded to bf16, so the state's two leading
+        // planes suffice (2^-16)
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            f4_t y0v = mma(s[rt].m, o.q[0], zero);
+            f4_t y1v = mma(s[rt].m, o.q[1], zero);
+            y0v = mma(s[rt].h, o.q[0], y0v);
+            y1v = mma(s[rt].h, o.q[1], y1v);
+            f4_t* yb = sh.y[b3][rt];
+            yb[(2 * wv) * 64 + lane] = y0v;
+            yb[(2 * wv + 1) * 64 + lane] = y1v;
         }
 
         // S = gamma_{C-1} S + K^T (diag(rho) Delta)
