@@ -168,9 +168,9 @@ __device__ __forceinline__ f4_t mma3b(u4_t a, const Planes& b, f4_t c) {
 // size is even): q, k, k k^T and q k^T are shared, the rest is per head.
 template <int NH>
 struct alignas(16) PrepSmem {
-    uint16_t kb[CK][DKC + 8];    // bf16 rows, padded against bank conflicts
     union {
         struct {
+            uint16_t kb[CK][DKC + 8];    // bf16 rows, padded against bank conflicts
             uint16_t qb[CK][DKC + 8];
             float kk[CK][CK + 1];
             float qk[CK][CK + 1];
@@ -205,8 +205,10 @@ struct ChunkPtrs {
 // width KF; then Dv <= 128.  NH v-heads (of one k-head) per block, four
 // waves per head: wave group h (waves 4h .. 4h + 3) does head h's own steps
 // exactly as a one-head block would, so the results do not depend on NH.
+// A two-head block takes just under 50 KB of LDS (the k rows share space
+// with the T planes), so three fit a CU where the registers allow it.
 template <int KF, int NH>
-__global__ __launch_bounds__(256 * NH, 4 / NH) void chunk_prep_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256 * NH, NH == 2 ? 3 : 4) void chunk_prep_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const float* __restrict__ g,
                                                             const float* __restrict__ beta,
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(256 * NH, 4 / NH) void chunk_prep_kernel(const uint
             for (int e = 0; e < 8; ++e) h[KF - 2][e] = x[e];
             const bool live = t < T;      // rows past T are zero, as for stored inputs
             if (region == 0) *reinterpret_cast<uint4*>(&sh.u.in.qb[t - t0][8 * lane]) = live ? qk : make_uint4(0, 0, 0, 0);
-            else if (region == 1) *reinterpret_cast<uint4*>(&sh.kb[t - t0][8 * (lane - 16)]) = live ? qk : make_uint4(0, 0, 0, 0);
+            else if (region == 1) *reinterpret_cast<uint4*>(&sh.u.in.kb[t - t0][8 * (lane - 16)]) = live ? qk : make_uint4(0, 0, 0, 0);
             vrow[i] = live ? pack8(act) : make_uint4(0, 0, 0, 0);
         }
       }
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(256 * NH, 4 / NH) void chunk_prep_kernel(const uint
             kv = *reinterpret_cast<const uint4*>(k + off);
             qv = *reinterpret_cast<const uint4*>(q + off);
         }
-        *reinterpret_cast<uint4*>(&sh.kb[t][c8 * 8]) = kv;
+        *reinterpret_cast<uint4*>(&sh.u.in.kb[t][c8 * 8]) = kv;
         *reinterpret_cast<uint4*>(&sh.u.in.qb[t][c8 * 8]) = qv;
     }
     // the first 128-column slice of this chunk's v rows, loaded now (its
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(256 * NH, 4 / NH) void chunk_prep_kernel(const uint
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int s0 = p < 2 ? 4 * lq + 2 * p : 16 + 4 * lq + 2 * (p - 2);
-            kt[tt][p] = (uint32_t)sh.kb[s0][d] | ((uint32_t)sh.kb[s0 + 1][d] << 16);
+            kt[tt][p] = (uint32_t)sh.u.in.kb[s0][d] | ((uint32_t)sh.u.in.kb[s0 + 1][d] << 16);
         }
     }
     if (grp == 0 && hv0 % G == 0) {
@@ -392,9 +394,9 @@ __global__ __launch_bounds__(256 * NH, 4 / NH) void chunk_prep_kernel(const uint
 #pragma unroll
         for (int ks = 0; ks < DKC / 32; ++ks) {
             const int col = ks * 32 + 8 * lq;
-            const u4_t kb = *reinterpret_cast<const u4_t*>(&sh.kb[16 * ni + lr][col]);
+            const u4_t kb = *reinterpret_cast<const u4_t*>(&sh.u.in.kb[16 * ni + lr][col]);
             if (NH == 1 || grp == 0) {
-                const u4_t ka = *reinterpret_cast<const u4_t*>(&sh.kb[16 * mi + lr][col]);
+                const u4_t ka = *reinterpret_cast<const u4_t*>(&sh.u.in.kb[16 * mi + lr][col]);
                 ckk = mma(ka, kb, ckk);
             }
             if (NH == 1 || grp == 1) {
