@@ -236,6 +236,7 @@ def main():
     decode = bench_decode(args, torch, dev, up, inputs, binding, np)
     serving = bench_verify_and_per_key(args, torch, dev, up, inputs, binding, np)
     decode1 = bench_decode_b1(args, torch, dev, up, inputs, binding, np)
+    per_key_prefill = bench_per_key_prefill(args, torch, dev, up, inputs, binding, np)
     long_prefill = None if args.no_long else bench_long_prefill(args, torch, dev, up, inputs, binding, np)
 
     # -------------------------------------------------------- CPU baseline
@@ -283,6 +284,7 @@ def main():
         "long_prefill_b4": long_prefill,
         "verify_window_b64": serving["verify_window"],
         "per_key_decode_b64": serving["per_key_decode"],
+        "per_key_prefill_b1": per_key_prefill,
         "cpu_baseline": cpu,
         "wall_s_timed": t_wall,
     }
@@ -438,6 +440,46 @@ def bench_verify_and_per_key(args, torch, dev, up, inputs, binding, np):
         print(f"[bench] {name}: {us:.1f} us ({gbs:.0f} GB/s, {gbs / HBM_PEAK_GBS:.0%} of HBM)", file=sys.stderr,
               flush=True)
     return res
+
+
+def bench_per_key_prefill(args, torch, dev, up, inputs, binding, np):
+    """The per-key decay gate g [B,T,Hv,Dk] over a prefill-length sequence
+    (B=1 T=4096 Hk=16 Hv=32 Dk=Dv=128): the per-step form with k, q and the
+    gate rows staged through LDS, and, for comparison, the staging-free
+    per-step kernel (reached through the snapshot entry point with one
+    snapshot, of the final state)."""
+    B, T, Hk, Hv, Dk, Dv = 1, 4096, 16, 32, 128, 128
+    raw = inputs.recurrence_raw(B=B, T=T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, workload_id=8, state=True)
+    # unit-norm-scale keys and queries, beta in (0, 1)
+    q = (up(raw["q_raw"]).view(torch.bfloat16).float() / Dk ** 0.5).to(torch.bfloat16)
+    k = (up(raw["k_raw"]).view(torch.bfloat16).float() / Dk ** 0.5).to(torch.bfloat16)
+    v, st = up(raw["v"]), up(raw["state"])
+    beta = torch.sigmoid(up(raw["b"]).view(torch.bfloat16).float())
+    g = up(inputs.per_key_gate(B=B, T=T, Hv=Hv, Dk=Dk, workload_id=8))
+    s_out = torch.empty_like(st)
+    y = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+    snap = torch.empty(1, B, Hv, Dv, Dk, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def staged():
+        binding.recurrent_per_key(q, k, v, g, beta, st, s_out, y)
+
+    def staging_free():
+        binding.recurrent_snapshots(q, k, v, g, beta, st, s_out, y, [T], snap)
+
+    out = {}
+    for name, fn in (("staged", staged), ("staging_free", staging_free)):
+        fn()
+        torch.cuda.synchronize()
+        out[name] = time_kernel(torch, stream, fn, 10)
+    flops = 7 * B * T * Hv * Dk * Dv
+    tf = flops / (out["staged"] * 1e-6) / 1e12
+    print(f"[bench] per-key prefill B=1 T=4096: staged {out['staged']:.1f} us ({tf:.1f} TFLOP/s), "
+          f"staging-free {out['staging_free']:.1f} us", file=sys.stderr, flush=True)
+    return {"workload": f"B={B} T={T} Hk={Hk} Hv={Hv} Dk=Dv={Dk}, per-key gate U[0.3, 1), random state",
+            "kernel": "recurrent_chunk_kernel<128, 16, true>", "avg_launch_us": out["staged"],
+            "achieved_TFLOPs": tf, "frac_fp32_peak": tf / FP32_PEAK_TFLOPS,
+            "staging_free_us": out["staging_free"]}
 
 
 def bench_decode_b1(args, torch, dev, up, inputs, binding, np):

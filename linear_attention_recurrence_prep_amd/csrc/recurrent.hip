@@ -56,8 +56,16 @@ __device__ __forceinline__ int xcd_block(int n_blocks) {
 // an LDS buffer as bf16 and written to HBM only when that buffer is full or
 // the sequence ends.
 
+// Per-key gate rows of a chunk (f32, the layout of k); nothing without it.
+template <int DK, int TC, bool VG>
+struct GateRows {
+    float4 g[TC][DK / 4];
+};
 template <int DK, int TC>
-struct ChunkBuf {
+struct GateRows<DK, TC, false> {};
+
+template <int DK, int TC, bool VG = false>
+struct ChunkBuf : GateRows<DK, TC, VG> {
     float4 k[TC][DK / 4];
     float4 q[TC][DK / 4];
     float4 sc[TC];                           // g, beta, k.q, 0
@@ -77,19 +85,20 @@ struct ChunkCfg {
     static_assert(TC % 4 == 0 && 2 * TC <= C::NT, "chunk length");
 };
 
-template <int DK, int TC>
+template <int DK, int TC, bool VG = false>
 struct ChunkSmem {
-    ChunkBuf<DK, TC> buf[2];
+    ChunkBuf<DK, TC, VG> buf[2];
     uint16_t y[ChunkCfg<DK, TC>::YSTEPS][RecCfg<DK>::ROWS];
 };
 
-template <int DK, int TC>
+template <int DK, int TC, bool VG = false>
 struct ChunkStage {
     using C = RecCfg<DK>;
     using CC = ChunkCfg<DK, TC>;
     uint4 kr[CC::PPT];
     uint4 qr[CC::PPT];
     uint4 vr[CC::VPT];
+    float4 gr[VG ? 2 * CC::PPT : 1];    // per-key gate: 8 columns per (step, 8 cols) pair
     float gb;
 
     __device__ __forceinline__ void load(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -105,6 +114,16 @@ struct ChunkStage {
             const int64_t off = (((int64_t)b * T + t) * Hk + hk) * DK + (p % (DK / 8)) * 8;
             kr[i] = *reinterpret_cast<const uint4*>(k + off);
             qr[i] = *reinterpret_cast<const uint4*>(q + off);
+            if constexpr (VG) {
+                // padding and masked steps decay by 1 (the state is kept)
+                const int ts = t0 + p / (DK / 8);
+                const bool on = ts < T && (mask == nullptr || mask[(int64_t)b * T + t] != 0);
+                const float4* gp = reinterpret_cast<const float4*>(
+                    g + (((int64_t)b * T + t) * Hv + hv) * DK + (p % (DK / 8)) * 8);
+                const float4 g0 = gp[0], g1 = gp[1];    // in bounds (t is clamped)
+                gr[2 * i] = make_float4(on ? g0.x : 1.f, on ? g0.y : 1.f, on ? g0.z : 1.f, on ? g0.w : 1.f);
+                gr[2 * i + 1] = make_float4(on ? g1.x : 1.f, on ? g1.y : 1.f, on ? g1.z : 1.f, on ? g1.w : 1.f);
+            }
         }
 #pragma unroll
         for (int i = 0; i < CC::VPT; ++i) {
@@ -120,13 +139,13 @@ struct ChunkStage {
             const int64_t bt = (int64_t)b * T + min(t, T - 1);
             const int64_t i = bt * Hv + hv;
             const bool is_g = (tid % (2 * TC)) < TC;
-            const float x = is_g ? g[i] : beta[i];
+            const float x = is_g ? (VG ? 1.f : g[i]) : beta[i];    // VG: gate rows above
             const bool on = t < T && (mask == nullptr || mask[bt] != 0);
             gb = on ? x : (is_g ? 1.f : 0.f);
         }
     }
 
-    __device__ __forceinline__ void store(ChunkBuf<DK, TC>& sb, int tid) const {
+    __device__ __forceinline__ void store(ChunkBuf<DK, TC, VG>& sb, int tid) const {
 #pragma unroll
         for (int i = 0; i < CC::PPT; ++i) {
             const int p = tid + i * C::NT;
@@ -139,11 +158,17 @@ struct ChunkStage {
             sb.k[step][2 * c8 + 1] = make_float4(kf[4], kf[5], kf[6], kf[7]);
             sb.q[step][2 * c8] = make_float4(qf[0], qf[1], qf[2], qf[3]);
             sb.q[step][2 * c8 + 1] = make_float4(qf[4], qf[5], qf[6], qf[7]);
-            float kq = 0.f;
+            if constexpr (VG) {
+                sb.g[step][2 * c8] = gr[2 * i];
+                sb.g[step][2 * c8 + 1] = gr[2 * i + 1];
+            }
+            if constexpr (!VG) {              // (the per-key step forms k.q itself)
+                float kq = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kq = fmaf(kf[e], qf[e], kq);
-            kq = group_sum<DK / 8>(kq);       // the DK/8 lanes of this step
-            if (c8 == 0) sb.sc[step].z = kq;
+                for (int e = 0; e < 8; ++e) kq = fmaf(kf[e], qf[e], kq);
+                kq = group_sum<DK / 8>(kq);   // the DK/8 lanes of this step
+                if (c8 == 0) sb.sc[step].z = kq;
+            }
         }
 #pragma unroll
         for (int i = 0; i < CC::VPT; ++i) {
@@ -167,9 +192,11 @@ __device__ __forceinline__ float pick(const float4& x, int i) {
     return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
 }
 
-// TC steps of one chunk on this lane's 8 state elements.
-template <int DK, int TC>
-__device__ __forceinline__ void run_chunk(const ChunkBuf<DK, TC>& sb, float (&s)[8],
+// TC steps of one chunk on this lane's 8 state elements.  With the per-key
+// gate (VG) each step is the staging-free kernel's per-key step, term for
+// term (k.q included), so the two forms give the same bits.
+template <int DK, int TC, bool VG = false>
+__device__ __forceinline__ void run_chunk(const ChunkBuf<DK, TC, VG>& sb, float (&s)[8],
                                           float (&yr)[(TC + DK / 8 - 1) / (DK / 8)], int j, int rloc) {
     constexpr int L = DK / 8;
     float4 vv;
@@ -181,6 +208,27 @@ __device__ __forceinline__ void run_chunk(const ChunkBuf<DK, TC>& sb, float (&s)
         const float4 sc = sb.sc[t];
         const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
         const float qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        if constexpr (VG) {
+            const float4 g0 = sb.g[t][j], g1 = sb.g[t][L + j];
+            const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            float a = 0.f, c = 0.f, kq = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float gs = gg[i] * s[i];
+                a = fmaf(gs, kk[i], a);
+                c = fmaf(gs, qq[i], c);
+                kq = fmaf(kk[i], qq[i], kq);
+                s[i] = gs;
+            }
+            group_sum2<L>(a, c);
+            kq = group_sum<L>(kq);
+            const float delta = (pick(vv, t % 4) - a) * sc.y;
+            const float yo = fmaf(delta, kq, c);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s[i] = fmaf(delta, kk[i], s[i]);
+            if (j == t % L) yr[t / L] = yo;
+            continue;
+        }
         float a = 0.f, c = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -197,8 +245,8 @@ __device__ __forceinline__ void run_chunk(const ChunkBuf<DK, TC>& sb, float (&s)
     }
 }
 
-template <int DK, int TC>
-__device__ __forceinline__ void flush_y(const ChunkSmem<DK, TC>& sh, uint16_t* __restrict__ y,
+template <int DK, int TC, class Smem>
+__device__ __forceinline__ void flush_y(const Smem& sh, uint16_t* __restrict__ y,
                                         const uint8_t* __restrict__ mask, int b, int hv, int dv0, int tbase,
                                         int nsteps, int T, int Hv, int Dv, int tid) {
     using C = RecCfg<DK>;
@@ -216,7 +264,7 @@ __device__ __forceinline__ void flush_y(const ChunkSmem<DK, TC>& sh, uint16_t* _
     }
 }
 
-template <int DK, int TC>
+template <int DK, int TC, bool VG>
 __global__ __launch_bounds__(256) void recurrent_chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const uint8_t* __restrict__ mask,
@@ -226,7 +274,7 @@ __global__ __launch_bounds__(256) void recurrent_chunk_kernel(
     using CC = ChunkCfg<DK, TC>;
     constexpr int L = C::L;
     constexpr int NY = (TC + L - 1) / L;
-    __shared__ ChunkSmem<DK, TC> sh;
+    __shared__ ChunkSmem<DK, TC, VG> sh;
 
     const int lb = xcd_block(n_blocks);
     const int n = lb / row_blocks;          // b * Hv + hv
@@ -256,7 +304,7 @@ __global__ __launch_bounds__(256) void recurrent_chunk_kernel(
     }
 
     const int nchunks = (T + TC - 1) / TC;   // >= 1 (this kernel runs for T > 0)
-    ChunkStage<DK, TC> st;
+    ChunkStage<DK, TC, VG> st;
     st.load(q, k, v, g, beta, mask, b, hk, hv, dv0, 0, T, Hk, Hv, Dv, tid);
     __builtin_amdgcn_s_waitcnt(0);           // state and chunk 0 resident
     st.store(sh.buf[0], tid);
@@ -267,7 +315,7 @@ __global__ __launch_bounds__(256) void recurrent_chunk_kernel(
         const int t0 = c * TC;
         if (c + 1 < nchunks) st.load(q, k, v, g, beta, mask, b, hk, hv, dv0, t0 + TC, T, Hk, Hv, Dv, tid);
         float yr[NY];
-        run_chunk<DK, TC>(sh.buf[c & 1], s, yr, j, rloc);
+        run_chunk<DK, TC, VG>(sh.buf[c & 1], s, yr, j, rloc);
         // y of this chunk -> LDS (bf16); each lane holds steps t = i*L + j
         const int yoff = t0 - ybase;
 #pragma unroll
@@ -444,18 +492,18 @@ int64_t recurrent_blocks(int B, int Hv, int Dk, int Dv) {
     return (int64_t)B * Hv * ((Dv + rows - 1) / rows);
 }
 
-template <int DK, int TC>
+template <int DK, int TC, bool VG = false>
 static hipError_t launch_rec(const RecurrentArgs& a, hipStream_t stream, bool chunked) {
     using C = RecCfg<DK>;
     const int row_blocks = (a.Dv + C::ROWS - 1) / C::ROWS;
     const int64_t blocks = (int64_t)a.B * a.Hv * row_blocks;
     if (blocks <= 0) return hipSuccess;
     if (chunked)
-        hipLaunchKernelGGL((recurrent_chunk_kernel<DK, TC>), dim3((unsigned)blocks), dim3(C::NT), 0, stream,
+        hipLaunchKernelGGL((recurrent_chunk_kernel<DK, TC, VG>), dim3((unsigned)blocks), dim3(C::NT), 0, stream,
                            a.q, a.k, a.v, a.g, a.beta, a.mask, a.state_in, a.state_out, a.y, a.T, a.Hk, a.Hv,
                            a.Dv, row_blocks, (int)blocks);
     else
-        hipLaunchKernelGGL((recurrent_step_kernel<DK, false, false>), dim3((unsigned)blocks), dim3(C::NT), 0,
+        hipLaunchKernelGGL((recurrent_step_kernel<DK, VG, false>), dim3((unsigned)blocks), dim3(C::NT), 0,
                            stream, a.q, a.k, a.v, a.g, a.beta, a.mask, a.state_in, a.state_out, a.y, a.T, a.Hk,
                            a.Hv, a.Dv, row_blocks, (int)blocks, SnapList{}, (int64_t)0);
     return hipGetLastError();
@@ -477,26 +525,34 @@ static hipError_t launch_step_opt(const RecurrentArgs& a, hipStream_t stream) {
 }
 
 template <int DK>
-static hipError_t launch_opt(const RecurrentArgs& a, hipStream_t stream) {
-    const bool snap = a.snap != nullptr && a.snap->n > 0;
-    if (a.g_per_key) return snap ? launch_step_opt<DK, true, true>(a, stream) : launch_step_opt<DK, true, false>(a, stream);
-    return snap ? launch_step_opt<DK, false, true>(a, stream) : launch_step_opt<DK, false, false>(a, stream);
+static hipError_t launch_snap(const RecurrentArgs& a, hipStream_t stream) {
+    return a.g_per_key ? launch_step_opt<DK, true, true>(a, stream) : launch_step_opt<DK, false, true>(a, stream);
 }
 
 // Sequences shorter than this run the staging-free kernel.
 constexpr int kChunkedMinT = 8;
 
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream) {
-    if (a.g_per_key || (a.snap != nullptr && a.snap->n > 0)) {
+    if (a.snap != nullptr && a.snap->n > 0) {
         switch (a.Dk) {
-            case 32: return launch_opt<32>(a, stream);
-            case 64: return launch_opt<64>(a, stream);
-            case 128: return launch_opt<128>(a, stream);
-            case 256: return launch_opt<256>(a, stream);
+            case 32: return launch_snap<32>(a, stream);
+            case 64: return launch_snap<64>(a, stream);
+            case 128: return launch_snap<128>(a, stream);
+            case 256: return launch_snap<256>(a, stream);
             default: return hipErrorInvalidValue;
         }
     }
     const bool chunked = a.T >= kChunkedMinT;
+    if (a.g_per_key) {
+        // the gate rows take LDS beside k and q: half-length chunks at Dk >= 128
+        switch (a.Dk) {
+            case 32: return launch_rec<32, 64, true>(a, stream, chunked);
+            case 64: return launch_rec<64, 32, true>(a, stream, chunked);
+            case 128: return launch_rec<128, 16, true>(a, stream, chunked);
+            case 256: return launch_rec<256, 8, true>(a, stream, chunked);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (a.Dk) {
         case 32: return launch_rec<32, 64>(a, stream, chunked);
         case 64: return launch_rec<64, 32>(a, stream, chunked);

@@ -133,6 +133,11 @@ PK_CASES = [
     (4, 1, 2, 4, 128, 128, 712),      # decode
     (1, 20, 2, 4, 128, 64, 713),
     (1, 9, 1, 1, 256, 40, 714),
+    # staged (LDS) per-key kernel: several chunks and a ragged tail at each Dk
+    (1, 100, 2, 4, 128, 64, 716),
+    (2, 70, 1, 2, 64, 48, 717),
+    (1, 41, 1, 2, 256, 32, 718),
+    (1, 130, 2, 2, 32, 16, 719),
 ]
 
 
@@ -167,10 +172,11 @@ def test_per_key_gate_matches_oracle(case):
         H.check_state(snaps[i], ref[i], 1e-4, f"per-key snapshot {steps[i]}")
 
 
-def test_per_key_gate_identities():
+@pytest.mark.parametrize("T", [6, 40], ids=["step_kernel", "staged_kernel"])
+def test_per_key_gate_identities(T):
     """g = 1 with beta = 0 keeps the state exactly; a gate constant over the
     keys matches the per-head gate within the tolerances."""
-    B, T, Hk, Hv, Dk, Dv = 2, 6, 2, 4, 128, 32
+    B, Hk, Hv, Dk, Dv = 2, 2, 4, 128, 32
     ri = rec_inputs(B, T, Hk, Hv, Dk, Dv, 715)
     d = {n: H.to_dev(ri[n]) for n in ("q", "k", "v")}
     s_out = torch.empty(B, Hv, Dv, Dk, device=H.DEV)
