@@ -589,6 +589,23 @@ def test_recurrent_chunked_invariants():
         np.testing.assert_allclose(s[0, h], ref, rtol=1e-6, atol=1e-7 * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("case", [(1, 20, 1, 1, 256, 4096, "per-step", 420), (1, 40, 1, 2, 128, 4096, "per-step", 421),
+                                  (1, 70, 1, 2, 128, 1024, "chunked", 422), (1, 96, 1, 1, 128, 2048, "chunked", 423)],
+                         ids=lambda c: "Dk%dDv%d-%s" % (c[4], c[5], c[6]))
+def test_largest_value_head_sizes(case):
+    """Value heads up to the largest size the library takes (Dv = 4096), in
+    the per-step form with Dk = 256 and 128, and wide value heads in the
+    chunked form (many 128-column slices per preparation block, many row
+    tiles per head), against the oracle."""
+    B, T, Hk, Hv, Dk, Dv, form, wid = case
+    say("largest value heads", case)
+    ri = rec_inputs(B, T, Hk, Hv, Dk, Dv, wid)
+    y, s = gpu_recurrent_chunked(ri) if form == "chunked" else gpu_recurrent(ri)
+    y_ref, s_ref = oracle_recurrent(ri)
+    H.check_y(y, y_ref, str(case))
+    H.check_state(s, s_ref, 1e-4, str(case))
+
+
 def test_recurrent_chunked_rejects_unsupported_sizes():
     ri = rec_inputs(1, 10, 1, 1, 64, 16, 413)
     with pytest.raises(binding.GdnError):
