@@ -444,10 +444,10 @@ def bench_verify_and_per_key(args, torch, dev, up, inputs, binding, np):
 
 def bench_per_key_prefill(args, torch, dev, up, inputs, binding, np):
     """The per-key decay gate g [B,T,Hv,Dk] over a prefill-length sequence
-    (B=1 T=4096 Hk=16 Hv=32 Dk=Dv=128): the per-step form with k, q and the
-    gate rows staged through LDS, and, for comparison, the staging-free
-    per-step kernel (reached through the snapshot entry point with one
-    snapshot, of the final state)."""
+    (B=1 T=4096 Hk=16 Hv=32 Dk=Dv=128): the chunked matrix-core form, the
+    per-step form with k, q and the gate rows staged through LDS, and the
+    staging-free per-step kernel (reached through the snapshot entry point
+    with one snapshot, of the final state)."""
     B, T, Hk, Hv, Dk, Dv = 1, 4096, 16, 32, 128, 128
     raw = inputs.recurrence_raw(B=B, T=T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, workload_id=8, state=True)
     # unit-norm-scale keys and queries, beta in (0, 1)
@@ -461,6 +461,12 @@ def bench_per_key_prefill(args, torch, dev, up, inputs, binding, np):
     snap = torch.empty(1, B, Hv, Dv, Dk, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    ws = torch.empty(binding.recurrent_chunked_per_key_workspace_bytes(B, T, Hk, Hv, Dk, Dv), dtype=torch.uint8,
+                     device=dev)
+
+    def chunked():
+        binding.recurrent_chunked_per_key(q, k, v, g, beta, st, s_out, y, ws)
+
     def staged():
         binding.recurrent_per_key(q, k, v, g, beta, st, s_out, y)
 
@@ -468,18 +474,18 @@ def bench_per_key_prefill(args, torch, dev, up, inputs, binding, np):
         binding.recurrent_snapshots(q, k, v, g, beta, st, s_out, y, [T], snap)
 
     out = {}
-    for name, fn in (("staged", staged), ("staging_free", staging_free)):
+    for name, fn in (("chunked", chunked), ("staged", staged), ("staging_free", staging_free)):
         fn()
         torch.cuda.synchronize()
         out[name] = time_kernel(torch, stream, fn, 10)
     flops = 7 * B * T * Hv * Dk * Dv
-    tf = flops / (out["staged"] * 1e-6) / 1e12
-    print(f"[bench] per-key prefill B=1 T=4096: staged {out['staged']:.1f} us ({tf:.1f} TFLOP/s), "
-          f"staging-free {out['staging_free']:.1f} us", file=sys.stderr, flush=True)
+    tf = flops / (out["chunked"] * 1e-6) / 1e12
+    print(f"[bench] per-key prefill B=1 T=4096: chunked {out['chunked']:.1f} us ({tf:.1f} TFLOP/s), per-step "
+          f"staged {out['staged']:.1f} us, staging-free {out['staging_free']:.1f} us", file=sys.stderr, flush=True)
     return {"workload": f"B={B} T={T} Hk={Hk} Hv={Hv} Dk=Dv={Dk}, per-key gate U[0.3, 1), random state",
-            "kernel": "recurrent_chunk_kernel<128, 16, true>", "avg_launch_us": out["staged"],
-            "achieved_TFLOPs": tf, "frac_fp32_peak": tf / FP32_PEAK_TFLOPS,
-            "staging_free_us": out["staging_free"]}
+            "kernel": "chunk_prep_kernel<0, 1, true> + chunk_seq_kernel<1, true> (gdn_recurrent_chunked_per_key)",
+            "avg_launch_us": out["chunked"], "achieved_TFLOPs": tf, "frac_fp32_peak": tf / FP32_PEAK_TFLOPS,
+            "per_step_staged_us": out["staged"], "per_step_staging_free_us": out["staging_free"]}
 
 
 def bench_decode_b1(args, torch, dev, up, inputs, binding, np):

@@ -253,12 +253,36 @@ gdn_status gdn_recurrent_snapshots(const gdn_bf16 *q, const gdn_bf16 *k, const g
 /*
  * gdn_recurrent_per_key -- the recurrence with the per-key decay gate g
  * [B, T, Hv, Dk] f32 (gdn_recurrent_snapshots with g_per_key = 1 and no
- * snapshots).  Per-step form for every T.
+ * snapshots).  Per-step form for every T (for T >= 8 with k, q and the gate
+ * rows staged through LDS; the same bits as the snapshot entry point).
  */
 gdn_status gdn_recurrent_per_key(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_bf16 *v,
                                  const float *g, const float *beta, const uint8_t *mask,
                                  const float *state_in, float *state_out, gdn_bf16 *y,
                                  int B, int T, int Hk, int Hv, int Dk, int Dv, void *stream);
+
+/*
+ * gdn_recurrent_chunked_per_key -- the recurrence with the per-key decay gate
+ * of gdn_recurrent_per_key, in the chunked matrix-core form of
+ * gdn_recurrent_chunked (equal to the per-step loop up to rounding order).
+ * Within a chunk the decay from step s to step t is per key column,
+ * g_{s+1}[j] ... g_t[j]; it is formed as running products, never as a
+ * quotient of cumulative decays, so any gate values in [0, 1] are safe.
+ * Arguments as gdn_recurrent_per_key (mask: 0 = inactive step, y written +0,
+ * state untouched; NULL = every step active) plus a caller-owned device
+ * workspace of at least gdn_recurrent_chunked_per_key_workspace_bytes(...)
+ * bytes (256-byte aligned; not read before written; NULL allowed when that
+ * size is 0).  Supported sizes and errors as gdn_recurrent_chunked.
+ */
+gdn_status gdn_recurrent_chunked_per_key(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_bf16 *v,
+                                         const float *g, const float *beta, const uint8_t *mask,
+                                         const float *state_in, float *state_out, gdn_bf16 *y,
+                                         void *workspace, size_t workspace_bytes,
+                                         int B, int T, int Hk, int Hv, int Dk, int Dv, void *stream);
+
+/* Workspace bytes of gdn_recurrent_chunked_per_key (0 for unsupported sizes
+ * or B*T == 0). */
+size_t gdn_recurrent_chunked_per_key_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv);
 
 /*
  * gdn_gated_rmsnorm -- output epilogue of the layer: gated RMS normalisation

@@ -70,6 +70,10 @@ def lib():
         L.gdn_recurrent_snapshots.restype = _i
         L.gdn_recurrent_per_key.argtypes = [_p] * 9 + [_i] * 6 + [_p]
         L.gdn_recurrent_per_key.restype = _i
+        L.gdn_recurrent_chunked_per_key.argtypes = [_p] * 10 + [ctypes.c_size_t] + [_i] * 6 + [_p]
+        L.gdn_recurrent_chunked_per_key.restype = _i
+        L.gdn_recurrent_chunked_per_key_workspace_bytes.argtypes = [_i] * 6
+        L.gdn_recurrent_chunked_per_key_workspace_bytes.restype = ctypes.c_size_t
         L.gdn_gated_rmsnorm.argtypes = [_p] * 4 + [_i] * 4 + [_f, _p]
         L.gdn_gated_rmsnorm.restype = _i
         L.gdn_layer_core_gated.argtypes = [_p] * 15 + [ctypes.c_size_t] + [_i] * 7 + [_f] * 4 + [_p]
@@ -376,3 +380,29 @@ def recurrent_per_key(q, k, v, g, beta, state_in, state_out, y, *, mask=None, st
     ]
     _invoke(lib().gdn_recurrent_per_key, *args, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream))
 
+
+def recurrent_chunked_per_key_workspace_bytes(B, T, Hk, Hv, Dk, Dv) -> int:
+    return int(lib().gdn_recurrent_chunked_per_key_workspace_bytes(B, T, Hk, Hv, Dk, Dv))
+
+
+def recurrent_chunked_per_key(q, k, v, g, beta, state_in, state_out, y, workspace, *, mask=None, stream=None):
+    """The recurrence with the per-key decay gate g [B,T,Hv,Dk] f32 in 32-step
+    chunks on the matrix cores (gdn_recurrent_chunked_per_key).  Arguments as
+    ``recurrent_per_key`` plus a device ``workspace`` tensor of at least
+    ``recurrent_chunked_per_key_workspace_bytes`` bytes."""
+    B, T, Hk, Dk = q.shape
+    Hv, Dv = v.shape[2], v.shape[3]
+    dev = q.device
+    args = [
+        _ptr(q, "q", _BF16, (B, T, Hk, Dk), dev),
+        _ptr(k, "k", _BF16, (B, T, Hk, Dk), dev),
+        _ptr(v, "v", _BF16, (B, T, Hv, Dv), dev),
+        _ptr(g, "g", (torch.float32,), (B, T, Hv, Dk), dev),
+        _ptr(beta, "beta", (torch.float32,), (B, T, Hv), dev),
+        _ptr(mask, "mask", _MASK, (B, T), dev),
+        _ptr(state_in, "state_in", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(state_out, "state_out", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
+    ]
+    ws, nws = _workspace(workspace, dev)
+    _invoke(lib().gdn_recurrent_chunked_per_key, *args, ws, nws, B, T, Hk, Hv, Dk, Dv, _stream(dev, stream))

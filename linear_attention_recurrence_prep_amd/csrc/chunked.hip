@@ -162,11 +162,49 @@ __device__ __forceinline__ f4_t mma3b(u4_t a, const Planes& b, f4_t c) {
     return mma(a, b.h, c);
 }
 
+// -P entries (t, s0 .. s0+3) as two bf16 planes in the operand layout of
+// the sequential pass, as step 3 of the per-head form stores them: the four
+// columns are elements 4 half .. 4 half + 3 of quarter q4 of lane
+// 16 q4 + t % 16, t-tile t / 16
+__device__ __forceinline__ void store_neg_p(u4_t* pn, int64_t unit, int t, int s0, const float (&pv)[4],
+                                            const NegOnes& no) {
+    const int half = s0 >> 4, q4 = (s0 & 15) >> 2;
+    const int l = 16 * q4 + (t & 15), jt = t >> 4;
+    const Split2 p0 = split2(no, pv[0], pv[1]), p1 = split2(no, pv[2], pv[3]);
+    u2_t* pdst = reinterpret_cast<u2_t*>(pn + unit * kPVec + (jt * 2) * 64 + l) + half;
+    pdst[0] = u2_t{p0.h, p1.h};
+    pdst[2 * 64] = u2_t{p0.m, p1.m};
+}
+
+// f32 (planes) x f32 (planes): the six plane products down to 2^-16 of the
+// leading one, smallest first
+__device__ __forceinline__ f4_t mma6(const Planes& a, const Planes& b, f4_t c) {
+    c = mma(a.l, b.h, c);
+    c = mma(a.h, b.l, c);
+    c = mma(a.m, b.m, c);
+    c = mma(a.m, b.h, c);
+    c = mma(a.h, b.m, c);
+    return mma(a.h, b.h, c);
+}
+
 // ========================================================= chunk preparation
+
+// Inputs of the per-key form's preparation: k and q rows in f32, the gate
+// rows (then the suffix decays E_t = g_{t+1} ... g_{C-1}) and the prefix
+// decays Gamma_t = g_0 ... g_t, per key column.  Nothing in the per-head form.
+template <bool PK>
+struct PkIn {
+    float kf[CK][DKC + 4];
+    float qf[CK][DKC + 4];
+    float ge[CK][DKC + 4];
+    float gam[CK][DKC + 4];
+};
+template <>
+struct PkIn<false> {};
 
 // One block serves NH v-heads of the same k-head (NH = 2 when the GQA group
 // size is even): q, k, k k^T and q k^T are shared, the rest is per head.
-template <int NH>
+template <int NH, bool PK = false>
 struct alignas(16) PrepSmem {
     union {
         struct {
@@ -175,6 +213,7 @@ struct alignas(16) PrepSmem {
             float kk[CK][CK + 1];
             float qk[CK][CK + 1];
         } in;
+        PkIn<PK> pk;
         struct {                 // written once the inputs above are dead
             uint16_t tw[3][CK][CK + 8];    // planes of T diag(beta gamma)
             uint16_t tb[3][CK][CK + 8];    // planes of -T diag(beta)
@@ -195,9 +234,14 @@ struct ChunkPtrs {
     u4_t* u;        // -Tb V (f32 accumulator tiles)
     u4_t* pn;       // -P planes (two)
     float* rg;      // per unit: -rho in kperm order [32], then gamma_t [32]
-    u4_t* qsw;      // q rows
-    u4_t* ksw;      // k columns
+                    // (per-key form: -1, 1, then Gamma_{C-1} per key column [Dk])
+    u4_t* qsw;      // q rows (per-key form: Q o Gamma, two planes per v-unit)
+    u4_t* ksw;      // k columns (per-key form: (K o E)^T, three planes per v-unit)
 };
+
+// floats of the per-unit decay record (-rho, gamma; per-key form: and Gamma_{C-1})
+template <bool PK>
+constexpr int rg_floats() { return PK ? 2 * CK + DKC : 2 * CK; }
 
 // KF = 0: q, k, v, g, beta are inputs.  KF = 2..4: they are computed here,
 // from the mixed projection qkv, with the prologue's arithmetic (the same
@@ -207,15 +251,20 @@ struct ChunkPtrs {
 // exactly as a one-head block would, so the results do not depend on NH.
 // A two-head block takes just under 50 KB of LDS (the k rows share space
 // with the T planes), so three fit a CU where the registers allow it.
-template <int KF, int NH>
-__global__ __launch_bounds__(256 * NH, NH == 2 ? 3 : 4) void chunk_prep_kernel(const uint16_t* __restrict__ q,
+// PK: the per-key gate g [B, T, Hv, Dk] (KF = 0, NH = 1): the decay ratios
+// are per key column, so A and P are formed as running products instead of
+// scaled k k^T, q k^T; K o Gamma enters W, and the sequential pass gets
+// Q o Gamma, (K o E)^T and Gamma_{C-1} in place of q, k and gamma.
+template <int KF, int NH, bool PK = false>
+__global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const float* __restrict__ g,
                                                             const float* __restrict__ beta,
                                                             const uint8_t* __restrict__ mask,
                                                             const uint16_t* __restrict__ v, PrologueIn pin,
                                                             ChunkPtrs o, int T, int Hk, int Hv, int Dv, int NC) {
-    __shared__ PrepSmem<NH> sh;
+    static_assert(!PK || (KF == 0 && NH == 1), "the per-key form takes prepared inputs, one v-head per block");
+    __shared__ PrepSmem<NH, PK> sh;
     const int c = (int)(blockIdx.x % NC);
     const int np = (int)(blockIdx.x / NC);    // b * (Hv / NH) + head pair
     const int b = np / (Hv / NH);
@@ -324,8 +373,31 @@ __global__ __launch_bounds__(256 * NH, NH == 2 ? 3 : 4) void chunk_prep_kernel(c
             kv = *reinterpret_cast<const uint4*>(k + off);
             qv = *reinterpret_cast<const uint4*>(q + off);
         }
-        *reinterpret_cast<uint4*>(&sh.u.in.kb[t][c8 * 8]) = kv;
-        *reinterpret_cast<uint4*>(&sh.u.in.qb[t][c8 * 8]) = qv;
+        if constexpr (PK) {
+            float kf8[8], qf8[8];
+            unpack8(kv, kf8);
+            unpack8(qv, qf8);
+            float* kd = &sh.u.pk.kf[t][c8 * 8];
+            float* qd = &sh.u.pk.qf[t][c8 * 8];
+            *reinterpret_cast<float4*>(kd) = make_float4(kf8[0], kf8[1], kf8[2], kf8[3]);
+            *reinterpret_cast<float4*>(kd + 4) = make_float4(kf8[4], kf8[5], kf8[6], kf8[7]);
+            *reinterpret_cast<float4*>(qd) = make_float4(qf8[0], qf8[1], qf8[2], qf8[3]);
+            *reinterpret_cast<float4*>(qd + 4) = make_float4(qf8[4], qf8[5], qf8[6], qf8[7]);
+        } else {
+            *reinterpret_cast<uint4*>(&sh.u.in.kb[t][c8 * 8]) = kv;
+            *reinterpret_cast<uint4*>(&sh.u.in.qb[t][c8 * 8]) = qv;
+        }
+    }
+    if constexpr (PK) {
+        // the gate rows; steps past T and masked steps decay by 1
+        for (int idx = tid; idx < CK * DKC / 4; idx += 256) {
+            const int t = idx / (DKC / 4), c4 = idx % (DKC / 4);
+            const int64_t bt = (int64_t)b * T + min(t0 + t, T - 1);
+            const bool on = t0 + t < T && (mask == nullptr || mask[bt] != 0);
+            const float4 gv = *reinterpret_cast<const float4*>(g + (bt * Hv + hv) * DKC + 4 * c4);   // in bounds
+            *reinterpret_cast<float4*>(&sh.u.pk.ge[t][4 * c4]) =
+                make_float4(on ? gv.x : 1.f, on ? gv.y : 1.f, on ? gv.z : 1.f, on ? gv.w : 1.f);
+        }
     }
     // the first 128-column slice of this chunk's v rows, loaded now (its
     // latency hides behind steps 2-6) and staged through LDS in step 7
@@ -350,7 +422,7 @@ __global__ __launch_bounds__(256 * NH, NH == 2 ? 3 : 4) void chunk_prep_kernel(c
         if constexpr (KF > 0) {
             gate_g_beta(pin.a[i], pin.b[i], pin.A_log[hv], pin.dt_bias[hv], gv, bv);
         } else {
-            gv = g[i];
+            gv = PK ? 1.f : g[i];    // (per-key gate rows are loaded above)
             bv = beta[i];
         }
         const bool on = t < T && (mask == nullptr || mask[bt] != 0);
@@ -364,31 +436,34 @@ __global__ __launch_bounds__(256 * NH, NH == 2 ? 3 : 4) void chunk_prep_kernel(c
     //     it and q (rows 16j + r, columns 32w + kperm(q, e)) for the
     //     sequential pass
     u4_t kt[2];
+    Planes kwp[2];        // per-key form: (K o Gamma)^T planes, formed in step 3'
+    if constexpr (!PK) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const int d = 32 * wl + 16 * tt + lr;
+        for (int tt = 0; tt < 2; ++tt) {
+            const int d = 32 * wl + 16 * tt + lr;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int s0 = p < 2 ? 4 * lq + 2 * p : 16 + 4 * lq + 2 * (p - 2);
-            kt[tt][p] = (uint32_t)sh.u.in.kb[s0][d] | ((uint32_t)sh.u.in.kb[s0 + 1][d] << 16);
+            for (int p = 0; p < 4; ++p) {
+                const int s0 = p < 2 ? 4 * lq + 2 * p : 16 + 4 * lq + 2 * (p - 2);
+                kt[tt][p] = (uint32_t)sh.u.in.kb[s0][d] | ((uint32_t)sh.u.in.kb[s0 + 1][d] << 16);
+            }
         }
-    }
-    if (grp == 0 && hv0 % G == 0) {
-        u4_t* kd = o.ksw + kunit * kQVec + wl * 2 * 64 + lane;
-        u4_t* qd = o.qsw + kunit * kQVec + wl * 2 * 64 + lane;
+        if (grp == 0 && hv0 % G == 0) {
+            u4_t* kd = o.ksw + kunit * kQVec + wl * 2 * 64 + lane;
+            u4_t* qd = o.qsw + kunit * kQVec + wl * 2 * 64 + lane;
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-            kd[jt * 64] = kt[jt];
-            const u2_t lo = *reinterpret_cast<const u2_t*>(&sh.u.in.qb[16 * jt + lr][32 * wl + 4 * lq]);
-            const u2_t hi = *reinterpret_cast<const u2_t*>(&sh.u.in.qb[16 * jt + lr][32 * wl + 16 + 4 * lq]);
-            qd[jt * 64] = u4_t{lo[0], lo[1], hi[0], hi[1]};
+            for (int jt = 0; jt < 2; ++jt) {
+                kd[jt * 64] = kt[jt];
+                const u2_t lo = *reinterpret_cast<const u2_t*>(&sh.u.in.qb[16 * jt + lr][32 * wl + 4 * lq]);
+                const u2_t hi = *reinterpret_cast<const u2_t*>(&sh.u.in.qb[16 * jt + lr][32 * wl + 16 + 4 * lq]);
+                qd[jt * 64] = u4_t{lo[0], lo[1], hi[0], hi[1]};
+            }
         }
     }
 
     // 2b. k k^T and q k^T, 32 x 32 each: wave w owns output tile
     //     ((w % 4) / 2, w % 2), of both products in a one-head block, of
     //     k k^T (waves 0-3) or q k^T (waves 4-7) in a two-head block
-    {
+    if constexpr (!PK) {
         const int mi = wl >> 1, ni = wl & 1;
         f4_t ckk = {0.f, 0.f, 0.f, 0.f}, cqk = ckk;
 #pragma unroll
@@ -414,7 +489,7 @@ __global__ __launch_bounds__(256 * NH, NH == 2 ? 3 : 4) void chunk_prep_kernel(c
 
     // 3. decay ratios R[t][s] = g_{s+1}...g_t (s <= t) for s in this thread's
     //    four columns, then A, -P (two planes), gamma, -rho
-    {
+    if constexpr (!PK) {
         const int t = tl >> 3, s0 = (tl & 7) * 4;
         const float* gs = sh.gs[grp];
         float r[4];
@@ -448,6 +523,126 @@ __global__ __launch_bounds__(256 * NH, NH == 2 ? 3 : 4) void chunk_prep_kernel(c
         }
         if (t == CK - 1)
             *reinterpret_cast<float4*>(o.rg + unit * 2 * CK + 8 * q4 + 4 * half) = make_float4(-r[0], -r[1], -r[2], -r[3]);
+    } else {
+        // 3'. per-key decay ratios R_j(t, s) = g_{s+1}[j] ... g_t[j]:
+        //     A[t][s] = beta_t sum_j k_t[j] k_s[j] R_j(t, s)   (s < t)
+        //     P[t][s] = sum_j q_t[j] k_s[j] R_j(t, s)          (s <= t)
+        //     Thread (s, jg) carries u = k_s o R(t, s) over key columns
+        //     16 jg .. 16 jg + 15 while t runs up from s (a running product,
+        //     never a quotient of cumulative decays); the eight column groups
+        //     of a row s are adjacent lanes, summed by DPP.  A wave's rows s
+        //     start at s_lo, so its loop starts there.
+        auto& sw = sh.w.s[0];
+        const int s = tl >> 3, jg = tl & 7, s_lo = s & ~7;
+        float u[16];
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const float4 x = *reinterpret_cast<const float4*>(&sh.u.pk.kf[s][16 * jg + 4 * e4]);
+            u[4 * e4] = x.x;
+            u[4 * e4 + 1] = x.y;
+            u[4 * e4 + 2] = x.z;
+            u[4 * e4 + 3] = x.w;
+        }
+        for (int t = s_lo; t < CK; ++t) {
+            float pa = 0.f, pp = 0.f;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int j = 16 * jg + 4 * e4;
+                const float4 gt = *reinterpret_cast<const float4*>(&sh.u.pk.ge[t][j]);
+                const float4 kt4 = *reinterpret_cast<const float4*>(&sh.u.pk.kf[t][j]);
+                const float4 qt4 = *reinterpret_cast<const float4*>(&sh.u.pk.qf[t][j]);
+                const float ga[4] = {gt.x, gt.y, gt.z, gt.w};
+                const float ka[4] = {kt4.x, kt4.y, kt4.z, kt4.w};
+                const float qa[4] = {qt4.x, qt4.y, qt4.z, qt4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float& ue = u[4 * e4 + i];
+                    if (t > s) ue *= ga[i];
+                    pa = fmaf(ka[i], ue, pa);
+                    pp = fmaf(qa[i], ue, pp);
+                }
+            }
+            pa = group_sum<8>(pa);
+            pp = group_sum<8>(pp);
+            if (jg == 0) {
+                sw.a[t][s] = t > s ? sh.bs[0][t] * pa : 0.f;
+                sw.tm[t][s] = t >= s ? pp : 0.f;       // P, kept here until its planes are cut
+            }
+        }
+        if (jg == 0)
+            for (int t = 0; t < s_lo; ++t) {
+                sw.a[t][s] = 0.f;
+                sw.tm[t][s] = 0.f;
+            }
+        __syncthreads();
+        {
+            // -P planes; gamma = 1 and -rho = -1 (the decay is in the operands)
+            const int t = tl >> 3, s0 = (tl & 7) * 4;
+            const float4 p4 = *reinterpret_cast<const float4*>(&sw.tm[t][s0]);
+            const float pv[4] = {-p4.x, -p4.y, -p4.z, -p4.w};
+            store_neg_p(o.pn, unit, t, s0, pv, no);
+            if (tl < CK) sh.gm[0][tl] = 1.f;
+            if (tl < 2 * CK) o.rg[unit * rg_floats<PK>() + tl] = tl < CK ? -1.f : 1.f;
+        }
+        // prefix decays Gamma_t = g_0 ... g_t and suffix decays
+        // E_t = g_{t+1} ... g_{C-1} (over the gate rows) per key column
+        if (tl < DKC) {
+            float gc[CK];
+#pragma unroll
+            for (int t = 0; t < CK; ++t) gc[t] = sh.u.pk.ge[t][tl];
+            float gp = 1.f, ep = 1.f;
+#pragma unroll
+            for (int t = 0; t < CK; ++t) {
+                gp *= gc[t];
+                sh.u.pk.gam[t][tl] = gp;
+                sh.u.pk.ge[CK - 1 - t][tl] = ep;
+                ep *= gc[CK - 1 - t];
+            }
+            o.rg[unit * rg_floats<PK>() + 2 * CK + tl] = gp;      // Gamma_{C-1}
+        }
+        __syncthreads();
+        // operands: (K o Gamma)^T planes for W (kept in registers until step
+        // 6), (K o E)^T planes and Q o Gamma planes for the sequential pass
+        Planes kw[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int d = 32 * wl + 16 * tt + lr;
+            float xw[8], xe[8];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int s0 = p < 2 ? 4 * lq + 2 * p : 16 + 4 * lq + 2 * (p - 2);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float kv = sh.u.pk.kf[s0 + h][d];
+                    xw[2 * p + h] = kv * sh.u.pk.gam[s0 + h][d];
+                    xe[2 * p + h] = kv * sh.u.pk.ge[s0 + h][d];
+                }
+            }
+            kw[tt] = split8(no, f4_t{xw[0], xw[1], xw[2], xw[3]}, f4_t{xw[4], xw[5], xw[6], xw[7]});
+            const Planes ke = split8(no, f4_t{xe[0], xe[1], xe[2], xe[3]}, f4_t{xe[4], xe[5], xe[6], xe[7]});
+            u4_t* kd = o.ksw + unit * 3 * kQVec + (wl * 2 + tt) * 64 + lane;
+            kd[0] = ke.h;
+            kd[kQVec] = ke.m;
+            kd[2 * kQVec] = ke.l;
+        }
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+            const int t = 16 * jt + lr;
+            f4_t x0, x1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c0 = 32 * wl + 4 * lq + i, c1 = c0 + 16;
+                x0[i] = sh.u.pk.qf[t][c0] * sh.u.pk.gam[t][c0];
+                x1[i] = sh.u.pk.qf[t][c1] * sh.u.pk.gam[t][c1];
+            }
+            u4_t qh, qm;
+            split8hm(no, x0, x1, qh, qm);
+            u4_t* qd = o.qsw + unit * 2 * kQVec + (wl * 2 + jt) * 64 + lane;
+            qd[0] = qh;
+            qd[kQVec] = qm;
+        }
+        kwp[0] = kw[0];
+        kwp[1] = kw[1];
     }
     __syncthreads();
 
@@ -540,6 +735,7 @@ __global__ __launch_bounds__(256 * NH, NH == 2 ? 3 : 4) void chunk_prep_kernel(c
     //    column tiles 2w, 2w+1 of W^T for both t-tiles; its accumulators are
     //    W rows 16j + r at columns 32w + kperm(q, e), the layout of the
     //    sequential pass (stored in f32; that pass cuts them into planes).
+    //    Per-key form: W^T = (K o Gamma)^T (T diag(beta))^T, f32 by f32.
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
         Planes tw;
@@ -554,8 +750,14 @@ __global__ __launch_bounds__(256 * NH, NH == 2 ? 3 : 4) void chunk_prep_kernel(c
         tw.m = u4_t{m0[0], m0[1], m1[0], m1[1]};
         tw.l = u4_t{l0[0], l0[1], l1[0], l1[1]};
         const f4_t zero = {0.f, 0.f, 0.f, 0.f};
-        const f4_t w0 = mma3b(kt[0], tw, zero);
-        const f4_t w1 = mma3b(kt[1], tw, zero);
+        f4_t w0, w1;
+        if constexpr (PK) {
+            w0 = mma6(kwp[0], tw, zero);
+            w1 = mma6(kwp[1], tw, zero);
+        } else {
+            w0 = mma3b(kt[0], tw, zero);
+            w1 = mma3b(kt[1], tw, zero);
+        }
         u4_t* dst = o.wsw + unit * kWVec + ((wl * 2 + jt) * 2) * 64 + lane;
         dst[0] = __builtin_bit_cast(u4_t, w0);
         dst[64] = __builtin_bit_cast(u4_t, w1);
@@ -657,8 +859,9 @@ __device__ __forceinline__ __attribute__((address_space(1))) T* uniform_ptr_w(T*
     return (__attribute__((address_space(1))) T*)(((uint64_t)hi << 32) | lo);
 }
 
-// One chunk's operands in registers (NR row tiles of 16 state rows).
-template <int NR>
+// One chunk's operands in registers (NR row tiles of 16 state rows).  The
+// per-key form (PK) takes q and k from PkOps instead.
+template <int NR, bool PK = false>
 struct SeqOps {
     f4_t wf[2][2];    // W of t-tiles 0 and 1 (f32, elements 0..3 and 4..7)
     Planes w[2];      // the same as bf16 planes (cut one step before use)
@@ -680,6 +883,7 @@ struct SeqOps {
             wf[PART][0] = __builtin_bit_cast(f4_t, ws[lane]);
             wf[PART][1] = __builtin_bit_cast(f4_t, ws[64 + lane]);
         } else if constexpr (PART == 2) {
+            if constexpr (PK) return;
             const auto qs = uniform_ptr(in.qsw + kunit * kQVec + wv * 2 * 64);
             const auto ks = uniform_ptr(in.ksw + kunit * kQVec + wv * 2 * 64);
             q[0] = qs[lane];
@@ -692,7 +896,7 @@ struct SeqOps {
 #pragma unroll
             for (int rt = 0; rt < NR; ++rt)
                 a0[rt] = uniform_ptr(in.u + ((unit * x.row_tiles + x.tile0 + rt) * 2 + (wv & 1)) * 64)[lane];
-            rg = uniform_ptr(in.rg + unit * 2 * CK)[lane];
+            rg = uniform_ptr(in.rg + unit * rg_floats<PK>())[lane];
         }
     }
 
@@ -706,6 +910,33 @@ struct SeqOps {
         load<1>(in, x, c);
         load<2>(in, x, c);
         load<3>(in, x, c);
+    }
+};
+
+// The per-key form's operands of one chunk: Q o Gamma (two planes, t-tiles 0
+// and 1), (K o E)^T (three planes, this wave's two column tiles) and
+// Gamma_{C-1} at this lane's state columns 32 w + 16 tt + 4 q .. + 3.
+struct PkOps {
+    u4_t qh[2], qm[2];
+    Planes k[2];
+    f4_t gd[2];
+
+    __device__ __forceinline__ void load(const SeqIn& in, const SeqCtx& x, int c) {
+        const int64_t unit = x.unit0 + c;
+        const int wv = x.wv, lane = x.lane;
+        const auto qs = uniform_ptr(in.qsw + unit * 2 * kQVec + wv * 2 * 64);
+        const auto ks = uniform_ptr(in.ksw + unit * 3 * kQVec + wv * 2 * 64);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            qh[t] = qs[t * 64 + lane];
+            qm[t] = qs[kQVec + t * 64 + lane];
+            k[t].h = ks[t * 64 + lane];
+            k[t].m = ks[kQVec + t * 64 + lane];
+            k[t].l = ks[2 * kQVec + t * 64 + lane];
+        }
+        const auto gs = uniform_ptr(reinterpret_cast<const f4_t*>(in.rg + unit * rg_floats<true>() + 2 * CK + 32 * wv));
+        gd[0] = gs[lane >> 4];
+        gd[1] = gs[4 + (lane >> 4)];
     }
 };
 
@@ -736,7 +967,7 @@ struct SeqSmem {
     f4_t d[2][NR][2][64];         // D of the chunk (B-operand layout), by chunk parity
 };
 
-template <int NR>
+template <int NR, bool PK = false>
 __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const float* state_in,
                                                                 float* state_out, uint16_t* __restrict__ y,
                                                                 const uint8_t* __restrict__ mask, int T, int Hk,
@@ -830,7 +1061,8 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
 
     // one chunk c (b3 = c mod 3) with o; W of the next chunk (n1) is cut into
     // planes and the loads of chunk cn into nx are spread over it
-    auto step = [&](int c, int b3, const SeqOps<NR>& o, SeqOps<NR>& n1, SeqOps<NR>& nx, int cn) {
+    PkOps pk;         // per-key form: the chunk's q, k and column decays
+    auto step = [&](int c, int b3, const SeqOps<NR, PK>& o, SeqOps<NR, PK>& n1, SeqOps<NR, PK>& nx, int cn) {
         // state planes: element e of quarter lq is column kperm(lq, e)
         Planes s[NR];
 #pragma unroll
@@ -909,10 +1141,21 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
         // planes suffice (2^-16)
 #pragma unroll
         for (int rt = 0; rt < NR; ++rt) {
-            f4_t y0v = mma(s[rt].m, o.q[0], zero);
-            f4_t y1v = mma(s[rt].m, o.q[1], zero);
-            y0v = mma(s[rt].h, o.q[0], y0v);
-            y1v = mma(s[rt].h, o.q[1], y1v);
+            f4_t y0v, y1v;
+            if constexpr (PK) {
+                // Q o Gamma in two planes: h.h, h.m and m.h
+                y0v = mma(s[rt].m, pk.qh[0], zero);
+                y1v = mma(s[rt].m, pk.qh[1], zero);
+                y0v = mma(s[rt].h, pk.qm[0], y0v);
+                y1v = mma(s[rt].h, pk.qm[1], y1v);
+                y0v = mma(s[rt].h, pk.qh[0], y0v);
+                y1v = mma(s[rt].h, pk.qh[1], y1v);
+            } else {
+                y0v = mma(s[rt].m, o.q[0], zero);
+                y1v = mma(s[rt].m, o.q[1], zero);
+                y0v = mma(s[rt].h, o.q[0], y0v);
+                y1v = mma(s[rt].h, o.q[1], y1v);
+            }
             f4_t* yb = sh.y[b3][rt];
             yb[(2 * wv) * 64 + lane] = y0v;
             yb[(2 * wv + 1) * 64 + lane] = y1v;
@@ -927,10 +1170,18 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
         for (int rt = 0; rt < NR; ++rt) bs[rt] = split8(no, rh0 * d0[rt], rh1 * d1[rt]);
 #pragma unroll
         for (int rt = 0; rt < NR; ++rt) {
-            S[rt][0] = S[rt][0] * gc;
-            S[rt][1] = S[rt][1] * gc;
-            S[rt][0] = mma3b(o.k[0], bs[rt], S[rt][0]);
-            S[rt][1] = mma3b(o.k[1], bs[rt], S[rt][1]);
+            if constexpr (PK) {
+                // per-key: S = S diag(Gamma_{C-1}) + ((K o E)^T Delta)^T
+                S[rt][0] = S[rt][0] * pk.gd[0];
+                S[rt][1] = S[rt][1] * pk.gd[1];
+                S[rt][0] = mma6(pk.k[0], bs[rt], S[rt][0]);
+                S[rt][1] = mma6(pk.k[1], bs[rt], S[rt][1]);
+            } else {
+                S[rt][0] = S[rt][0] * gc;
+                S[rt][1] = S[rt][1] * gc;
+                S[rt][0] = mma3b(o.k[0], bs[rt], S[rt][0]);
+                S[rt][1] = mma3b(o.k[1], bs[rt], S[rt][1]);
+            }
         }
         if (wv == 0) {
 #pragma unroll
@@ -940,10 +1191,14 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
             }
         }
         SEQ_PIN(nx.template load<3>(in, x, cn));
+        // per-key form: the next chunk's q, k and column decays (one set in
+        // registers, loaded once this chunk's are consumed)
+        if constexpr (PK) SEQ_PIN(pk.load(in, x, min(c + 1, NC - 1)));
     };
 
     // three operand sets: chunk c + 2 loads while chunk c runs
-    SeqOps<NR> o0, o1, o2;
+    if constexpr (PK) pk.load(in, x, 0);
+    SeqOps<NR, PK> o0, o1, o2;
     o0.load_all(in, x, 0);
     o1.load_all(in, x, min(1, NC - 1));
     o0.split_w(no);
@@ -972,7 +1227,7 @@ bool chunked_supported(int Hv, int Dk, int Dv) {
     return Dk == DKC && Dv % RB == 0 && (int64_t)Hv * Dv <= (int64_t(1) << 25);
 }
 
-ChunkedLayout chunked_layout(int B, int T, int Hk, int Hv, int Dk, int Dv) {
+ChunkedLayout chunked_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, bool per_key) {
     (void)Dk;
     ChunkedLayout L;
     const int64_t NC = (T + CK - 1) / CK;
@@ -984,9 +1239,16 @@ ChunkedLayout chunked_layout(int B, int T, int Hk, int Hv, int Dk, int Dv) {
     L.u = L.wsw + a256(units * kWVec * 16);
     L.pn = L.u + a256(units * CK * (uint64_t)Dv * 4);
     L.rg = L.pn + a256(units * kPVec * 16);
-    L.qsw = L.rg + a256(units * 2 * CK * 4);
-    L.ksw = L.qsw + a256(kunits * kQVec * 16);
-    L.total = L.ksw + a256(kunits * kQVec * 16);
+    if (per_key) {
+        // Q o Gamma (two planes) and (K o E)^T (three) per v-unit, Gamma_{C-1} in the decay record
+        L.qsw = L.rg + a256(units * rg_floats<true>() * 4);
+        L.ksw = L.qsw + a256(units * 2 * kQVec * 16);
+        L.total = L.ksw + a256(units * 3 * kQVec * 16);
+    } else {
+        L.qsw = L.rg + a256(units * 2 * CK * 4);
+        L.ksw = L.qsw + a256(kunits * kQVec * 16);
+        L.total = L.ksw + a256(kunits * kQVec * 16);
+    }
     return L;
 }
 
@@ -1030,7 +1292,8 @@ static int device_cu_count() {
 static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, int K, void* ws,
                                  hipStream_t stream) {
     if (!chunked_supported(a.Hv, a.Dk, a.Dv) || a.T <= 0 || a.B <= 0) return hipErrorInvalidValue;
-    const ChunkedLayout L = chunked_layout(a.B, a.T, a.Hk, a.Hv, a.Dk, a.Dv);
+    if (a.g_per_key && pin) return hipErrorInvalidValue;      // the per-key form takes prepared inputs
+    const ChunkedLayout L = chunked_layout(a.B, a.T, a.Hk, a.Hv, a.Dk, a.Dv, a.g_per_key);
     char* base = static_cast<char*>(ws);
     ChunkPtrs o;
     o.wsw = reinterpret_cast<u4_t*>(base + L.wsw);
@@ -1040,14 +1303,18 @@ static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, 
     o.qsw = reinterpret_cast<u4_t*>(base + L.qsw);
     o.ksw = reinterpret_cast<u4_t*>(base + L.ksw);
     // two v-heads per preparation block when the GQA group size is even
-    const int nh = (a.Hv / a.Hk) % 2 == 0 ? 2 : 1;
+    // (per-key form: one)
+    const int nh = !a.g_per_key && (a.Hv / a.Hk) % 2 == 0 ? 2 : 1;
     const int64_t pblocks = (int64_t)a.B * (a.Hv / nh) * L.nc;
     const PrologueIn none{};
     const PrologueIn& pi = pin ? *pin : none;
 #define GDN_PREP(KF_, NH_)                                                                                     \
     hipLaunchKernelGGL((chunk_prep_kernel<KF_, NH_>), dim3((unsigned)pblocks), dim3(256 * NH_), 0, stream, a.q, \
                        a.k, a.g, a.beta, a.mask, a.v, pi, o, a.T, a.Hk, a.Hv, a.Dv, L.nc)
-    switch (K * 2 + nh - 1) {
+    if (a.g_per_key)
+        hipLaunchKernelGGL((chunk_prep_kernel<0, 1, true>), dim3((unsigned)pblocks), dim3(256), 0, stream, a.q, a.k,
+                           a.g, a.beta, a.mask, a.v, pi, o, a.T, a.Hk, a.Hv, a.Dv, L.nc);
+    else switch (K * 2 + nh - 1) {
         case 0: GDN_PREP(0, 1); break;
         case 1: GDN_PREP(0, 2); break;
         case 4: GDN_PREP(2, 1); break;
@@ -1071,10 +1338,13 @@ static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, 
     // two row tiles per block once one tile per block would need more blocks
     // than the device has CUs (the sequential blocks run one per CU)
     const int cus = device_cu_count();
-    const bool two = a.Dv % (2 * RB) == 0 && cus > 0 && (int64_t)a.B * a.Hv * (a.Dv / RB) > cus;
+    const bool two = !a.g_per_key && a.Dv % (2 * RB) == 0 && cus > 0 && (int64_t)a.B * a.Hv * (a.Dv / RB) > cus;
     const int row_blocks = a.Dv / (RB * (two ? 2 : 1));
     const int64_t blocks = (int64_t)a.B * a.Hv * row_blocks;
-    if (two)
+    if (a.g_per_key)
+        hipLaunchKernelGGL((chunk_seq_kernel<1, true>), dim3((unsigned)blocks), dim3(SEQ_THREADS), 0, stream, in,
+                           a.state_in, a.state_out, a.y, a.mask, a.T, a.Hk, a.Hv, a.Dv, L.nc, row_blocks, (int)blocks);
+    else if (two)
         hipLaunchKernelGGL(chunk_seq_kernel<2>, dim3((unsigned)blocks), dim3(SEQ_THREADS), 0, stream, in,
                            a.state_in, a.state_out, a.y, a.mask, a.T, a.Hk, a.Hv, a.Dv, L.nc, row_blocks, (int)blocks);
     else

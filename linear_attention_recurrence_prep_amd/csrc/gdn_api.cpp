@@ -242,9 +242,9 @@ bool workspace_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, Workspace& w
     return true;
 }
 
-uint64_t chunked_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv) {
+uint64_t chunked_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv, bool per_key = false) {
     if ((int64_t)B * T == 0 || !gdn::chunked_supported(Hv, Dk, Dv)) return 0;
-    return gdn::chunked_layout(B, T, Hk, Hv, Dk, Dv).total;
+    return gdn::chunked_layout(B, T, Hk, Hv, Dk, Dv, per_key).total;
 }
 
 }  // namespace
@@ -334,19 +334,21 @@ size_t gdn_recurrent_chunked_workspace_bytes(int B, int T, int Hk, int Hv, int D
     return (size_t)chunked_bytes(B, T, Hk, Hv, Dk, Dv);
 }
 
-gdn_status gdn_recurrent_chunked_masked(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v,
-                                        const float* g, const float* beta, const uint8_t* mask,
-                                        const float* state_in, float* state_out, gdn_bf16* y, void* workspace,
-                                        size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk, int Dv,
-                                        void* stream) {
-    gdn_status st = validate_recurrent(q, k, v, g, beta, mask, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv);
+// The chunked recurrence, per-head gate g [B,T,Hv] or per-key gate g [B,T,Hv,Dk].
+static gdn_status recurrent_chunked_impl(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,
+                                         bool per_key, const float* beta, const uint8_t* mask,
+                                         const float* state_in, float* state_out, gdn_bf16* y, void* workspace,
+                                         size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk, int Dv,
+                                         void* stream) {
+    gdn_status st = validate_recurrent(q, k, v, g, beta, mask, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, true,
+                                       per_key);
     if (st != GDN_OK) return st;
     if (!gdn::chunked_supported(Hv, Dk, Dv))
         return fail(GDN_ERR_UNSUPPORTED,
                     "chunked recurrence needs Dk == 128, Dv %% 16 == 0 and Hv * Dv <= 2^25 (Dk=%d, Dv=%d, Hv=%d)", Dk,
                     Dv, Hv);
     if (gdn::chunked_blocks(B, T, Hv, Dv) > kMaxBlocks) return fail(GDN_ERR_BAD_DIMS, "grid too large");
-    const uint64_t need = chunked_bytes(B, T, Hk, Hv, Dk, Dv);
+    const uint64_t need = chunked_bytes(B, T, Hk, Hv, Dk, Dv, per_key);
     if (need > 0) {
         if (!workspace) return fail(GDN_ERR_WORKSPACE, "workspace is NULL but %llu bytes are needed",
                                     (unsigned long long)need);
@@ -355,14 +357,15 @@ gdn_status gdn_recurrent_chunked_masked(const gdn_bf16* q, const gdn_bf16* k, co
                         (unsigned long long)need);
         if (reinterpret_cast<uintptr_t>(workspace) & 255u)
             return fail(GDN_ERR_MISALIGNED, "workspace is not 256-byte aligned");
-        uint64_t nqk, nv, ng, ns;
+        uint64_t nqk, nv, ng, ns, ngate;
         elems(nqk, {B, T, Hk, Dk});
         elems(nv, {B, T, Hv, Dv});
         elems(ng, {B, T, Hv});
         elems(ns, {B, Hv, Dv, Dk});
+        elems(ngate, {B, T, Hv, per_key ? Dk : 1});
         std::vector<Span> s = {
             {"q", q, nqk * 2, false},      {"k", k, nqk * 2, false},
-            {"v", v, nv * 2, false},       {"g", g, ng * 4, false},
+            {"v", v, nv * 2, false},       {"g", g, ngate * 4, false},
             {"beta", beta, ng * 4, false}, {"state_in", state_in, ns * 4, false},
             {"state_out", state_out, ns * 4, true}, {"y", y, nv * 2, true},
             {"workspace", workspace, need, true}, {"mask", mask, (uint64_t)B * T, false, 1},
@@ -372,9 +375,34 @@ gdn_status gdn_recurrent_chunked_masked(const gdn_bf16* q, const gdn_bf16* k, co
     }
     if (B == 0) return ok();
     gdn::RecurrentArgs a{q, k, v, g, beta, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, mask};
+    a.g_per_key = per_key;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (T == 0) return hip_result(gdn::launch_recurrent(a, s), "recurrent");
     return hip_result(gdn::launch_recurrent_chunked(a, workspace, s), "chunked recurrent");
+}
+
+gdn_status gdn_recurrent_chunked_masked(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v,
+                                        const float* g, const float* beta, const uint8_t* mask,
+                                        const float* state_in, float* state_out, gdn_bf16* y, void* workspace,
+                                        size_t workspace_bytes, int B, int T, int Hk, int Hv, int Dk, int Dv,
+                                        void* stream) {
+    return recurrent_chunked_impl(q, k, v, g, false, beta, mask, state_in, state_out, y, workspace,
+                                  workspace_bytes, B, T, Hk, Hv, Dk, Dv, stream);
+}
+
+gdn_status gdn_recurrent_chunked_per_key(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,
+                                         const float* beta, const uint8_t* mask, const float* state_in,
+                                         float* state_out, gdn_bf16* y, void* workspace, size_t workspace_bytes,
+                                         int B, int T, int Hk, int Hv, int Dk, int Dv, void* stream) {
+    return recurrent_chunked_impl(q, k, v, g, true, beta, mask, state_in, state_out, y, workspace,
+                                  workspace_bytes, B, T, Hk, Hv, Dk, Dv, stream);
+}
+
+size_t gdn_recurrent_chunked_per_key_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv) {
+    if (check_dims(B, T, Hk, Hv, Dk, Dv) != GDN_OK) return 0;
+    uint64_t n;
+    if (!elems(n, {B, T, Hv, Dk})) return 0;
+    return (size_t)chunked_bytes(B, T, Hk, Hv, Dk, Dv, true);
 }
 
 gdn_status gdn_recurrent_chunked(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf16* v, const float* g,

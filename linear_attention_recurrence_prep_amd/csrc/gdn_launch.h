@@ -59,13 +59,16 @@ hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream);
 // [32 x Dk] and -T diag(beta) V [32 x Dv] in f32, -P
 // [32 x 32] as two bf16 planes, -rho and gamma [32 each] in f32, and per
 // (b, hk, chunk) q and k [32 x Dk] in bf16, all in the register layout of the
-// sequential kernel (byte offsets below, each 256-byte aligned).
+// sequential kernel (byte offsets below, each 256-byte aligned).  With the
+// per-key gate (RecurrentArgs::g_per_key) q and k are replaced per (b, hv,
+// chunk) by q o Gamma_t (two bf16 planes) and k o (Gamma_{C-1} / Gamma_t)
+// (three planes), and the decay record also holds Gamma_{C-1} [Dk].
 struct ChunkedLayout {
     int nc;                 // chunks per sequence
     uint64_t wsw, u, pn, rg, qsw, ksw, total;
 };
 bool chunked_supported(int Hv, int Dk, int Dv);
-ChunkedLayout chunked_layout(int B, int T, int Hk, int Hv, int Dk, int Dv);
+ChunkedLayout chunked_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, bool per_key = false);
 int64_t chunked_blocks(int B, int T, int Hv, int Dv);
 hipError_t launch_recurrent_chunked(const RecurrentArgs& a, void* workspace, hipStream_t stream);
 

@@ -13,7 +13,7 @@ import torch
 import oracle
 from linear_attention_recurrence_prep_amd import binding, inputs
 from tests import helpers as H
-from tests.test_parity_gpu import gpu_recurrent, rec_inputs, step_mask
+from tests.test_parity_gpu import gpu_recurrent, gpu_recurrent_chunked, rec_inputs, step_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -194,3 +194,114 @@ def test_per_key_gate_identities(T):
     y_ref, s_ref = oracle.recurrent(f(ri["q"]), f(ri["k"]), f(ri["v"]), ri["g"], ri["beta"], ri["state"])
     H.check_y(H.bits(y), y_ref)
     H.check_state(H.f32(s_out), s_ref, 1e-4)
+
+
+# ------------------------------------------ per-key gate, chunked matrix-core form
+
+def gpu_chunked_per_key(ri, gk, mask=None, in_place=False):
+    """Run gdn_recurrent_chunked_per_key; returns (y bits, state_out)."""
+    B, T, Hk, Dk = ri["q"].shape
+    Hv, Dv = ri["v"].shape[2], ri["v"].shape[3]
+    d = {n: H.to_dev(ri[n]) for n in ("q", "k", "v", "beta")}
+    s_in = H.to_dev(ri["state"]) if ri.get("state") is not None else None
+    if in_place:
+        sfull, s_out = None, s_in
+    else:
+        sfull, s_out = H.guarded((B, Hv, Dv, Dk), torch.float32, float("nan"))
+    yfull, y = H.guarded((B, T, Hv, Dv), torch.int16, NAN_BF16)
+    nws = binding.recurrent_chunked_per_key_workspace_bytes(B, T, Hk, Hv, Dk, Dv)
+    wfull, ws = H.guarded((max(nws, 1),), torch.uint8, 0xA5)
+    m = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).to(H.DEV)
+    binding.recurrent_chunked_per_key(d["q"], d["k"], d["v"], H.to_dev(gk), d["beta"], s_in, s_out, y, ws, mask=m)
+    torch.cuda.synchronize()
+    assert H.guards_intact(yfull, NAN_BF16), "y guard band written"
+    assert sfull is None or H.guards_intact(sfull, float("nan")), "state guard band written"
+    assert H.guards_intact(wfull, 0xA5), "workspace guard band written"
+    return H.bits(y), H.f32(s_out)
+
+
+PKC_CASES = [
+    # B, T, Hk, Hv, Dk, Dv, wid, gate
+    (1, 100, 2, 4, 128, 64, 720, "uniform"),       # four chunks, ragged tail
+    (2, 70, 1, 2, 128, 48, 721, "uniform"),        # two sequences, Dv not a multiple of 32
+    (1, 64, 1, 1, 128, 128, 722, "uniform"),       # whole chunks
+    (1, 33, 2, 2, 128, 256, 723, "uniform"),       # one step past a chunk, Dv = 256
+    (1, 96, 1, 3, 128, 32, 724, "steep"),          # gates down to 1e-3 on half the keys: decays underflow
+]
+
+
+def pk_gate(B, T, Hv, Dk, wid, kind):
+    gk = inputs.per_key_gate(B=B, T=T, Hv=Hv, Dk=Dk, workload_id=wid)
+    if kind == "steep":
+        # half of the key columns decay hard (products of a few steps underflow f32)
+        gk[..., ::2] = np.float32(1e-3) + (gk[..., ::2] - np.float32(0.3)) * np.float32(0.01)
+    return np.ascontiguousarray(gk, dtype=np.float32)
+
+
+@pytest.mark.parametrize("case", PKC_CASES, ids=lambda c: "B%dT%dHv%dDv%d-%s" % (c[0], c[1], c[3], c[5], c[7]))
+def test_per_key_chunked_matches_oracle(case):
+    B, T, Hk, Hv, Dk, Dv, wid, kind = case
+    say("per-key chunked", case)
+    ri = rec_inputs(B, T, Hk, Hv, Dk, Dv, wid)
+    gk = pk_gate(B, T, Hv, Dk, wid, kind)
+    mask = step_mask(wid, B, T) if wid % 2 else None
+    y, s = gpu_chunked_per_key(ri, gk, mask=mask)
+    f = oracle.bf16_to_f64
+    y_ref, s_ref = oracle.recurrent(f(ri["q"]), f(ri["k"]), f(ri["v"]), gk.astype(np.float64), ri["beta"],
+                                    ri["state"], mask=mask)
+    H.check_y(y, y_ref, str(case))
+    e = H.check_state(s, s_ref, 1e-4, str(case))
+    say("per-key chunked state err", e)
+
+
+def test_per_key_chunked_identities():
+    """A gate constant over the keys reproduces the per-head chunked form
+    within the tolerances; g = 1 with beta = 0 keeps the state exactly (and
+    y = S q of the unchanged state); in place equals out of place; a split at
+    a chunk boundary with the state carried is bit-identical."""
+    B, T, Hk, Hv, Dk, Dv = 2, 80, 2, 4, 128, 64
+    say("per-key chunked identities")
+    ri = rec_inputs(B, T, Hk, Hv, Dk, Dv, 725)
+    gk = np.ascontiguousarray(np.repeat(ri["g"][..., None], Dk, axis=-1), dtype=np.float32)
+    y, s = gpu_chunked_per_key(ri, gk)
+    y2, s2 = gpu_recurrent_chunked(ri)
+    f = oracle.bf16_to_f64
+    y_ref, s_ref = oracle.recurrent(f(ri["q"]), f(ri["k"]), f(ri["v"]), ri["g"], ri["beta"], ri["state"])
+    for yy, ss in ((y, s), (y2, s2)):
+        H.check_y(yy, y_ref)
+        H.check_state(ss, s_ref, 1e-4)
+    keep = dict(ri, beta=np.zeros_like(ri["beta"]))
+    _, s0 = gpu_chunked_per_key(keep, np.ones_like(gk))
+    assert np.array_equal(s0, ri["state"])
+    yi, si = gpu_chunked_per_key(ri, gk, in_place=True)
+    assert np.array_equal(yi, y) and np.array_equal(si, s)
+    gk8 = pk_gate(B, T, Hv, Dk, 726, "uniform")
+    yf, sf = gpu_chunked_per_key(ri, gk8)
+    head = {n: (v if n == "state" else np.ascontiguousarray(v[:, :32])) for n, v in ri.items()}
+    tail = {n: (v if n == "state" else np.ascontiguousarray(v[:, 32:])) for n, v in ri.items()}
+    ya, sa = gpu_chunked_per_key(head, np.ascontiguousarray(gk8[:, :32]))
+    tail["state"] = sa
+    yb, sb = gpu_chunked_per_key(tail, np.ascontiguousarray(gk8[:, 32:]))
+    assert np.array_equal(np.concatenate([ya, yb], axis=1), yf) and np.array_equal(sb, sf)
+
+
+def test_per_key_chunked_prefill_full_size_sampled():
+    """The per-key gate through the chunked form at the prefill size (B=1,
+    T=4096, Hk=16, Hv=32, Dk=Dv=128) as the benchmark runs it; two v-heads of
+    different k-heads recomputed by the oracle over the whole sequence."""
+    B, T, Hk, Hv, Dk, Dv = 1, 4096, 16, 32, 128, 128
+    say("per-key chunked, full prefill size")
+    ri = rec_inputs(B, T, Hk, Hv, Dk, Dv, 727)
+    gk = pk_gate(B, T, Hv, Dk, 727, "uniform")
+    y, s = gpu_chunked_per_key(ri, gk)
+    f = oracle.bf16_to_f64
+    G = Hv // Hk
+    for hv in (0, 29):
+        hk = hv // G
+        sub = lambda a, h: np.ascontiguousarray(a[:, :, h:h + 1])
+        y_ref, s_ref = oracle.recurrent(f(sub(ri["q"], hk)), f(sub(ri["k"], hk)), f(sub(ri["v"], hv)),
+                                        sub(gk, hv).astype(np.float64), sub(ri["beta"], hv),
+                                        np.ascontiguousarray(ri["state"][:, hv:hv + 1]))
+        H.check_y(np.ascontiguousarray(y[:, :, hv:hv + 1]), y_ref, f"hv={hv}")
+        e = H.check_state(np.ascontiguousarray(s[:, hv:hv + 1]), s_ref, 1e-4, f"hv={hv}")
+        say("per-key chunked full size, hv", hv, "state err", e)
