@@ -174,15 +174,16 @@ gdn_status gdn_prep(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
 /*
  * Bytes of device workspace gdn_layer_core needs for these sizes: the bf16
  * q, k, v and f32 g, beta of the prologue, plus the chunked recurrence's
- * workspace when that form is used (T >= 64 and sizes gdn_recurrent_chunked
- * supports); each part 256-byte aligned.  Returns 0 for invalid sizes (and when B*T == 0).
+ * workspace when that form is used (see gdn_layer_core); each part 256-byte
+ * aligned.  Returns 0 for invalid sizes (and when B*T == 0).
  */
 size_t gdn_layer_core_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv);
 
 /*
  * gdn_layer_core -- gdn_prep followed by the recurrence, on one stream:
- * gdn_recurrent_chunked when T >= 64 and it supports the sizes, else
- * gdn_recurrent; results are bit-identical to making those two calls.
+ * gdn_recurrent_chunked when it supports the sizes and T >= 64, or T > 32
+ * with B * Hv * Dv / 16 >= 512, or T >= 8 with B * Hv * Dv / 16 >= 1024;
+ * else gdn_recurrent.  Results are bit-identical to making those two calls.
  * ("mlex ... gated_delta.rs", GatedDeltaNet::forward between the input
  *  projections and the output normalisation.)
  *

@@ -220,11 +220,17 @@ struct Workspace {
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-// The layer core switches to the chunked recurrence from this length on.
-constexpr int kLayerChunkedMinT = 64;
-
-bool layer_uses_chunked(int T, int Hv, int Dk, int Dv) {
-    return T >= kLayerChunkedMinT && gdn::chunked_supported(Hv, Dk, Dv);
+// The layer core takes the chunked recurrence for sequences of 64 steps and
+// more, and for shorter ones once the per-step form would need several rounds
+// of blocks on the device (one block per 16 state rows, one block per CU at a
+// time): measured on MI355X at Hv = 32, Dk = Dv = 128, the chunked form is
+// as fast from T = 33 on with 512 state tiles and faster at every T >= 8 with
+// 1024.  A fixed rule (no device query), so the composition is the same on
+// every device.
+bool layer_uses_chunked(int B, int T, int Hv, int Dk, int Dv) {
+    if (!gdn::chunked_supported(Hv, Dk, Dv)) return false;
+    const int64_t tiles = (int64_t)B * Hv * (Dv / 16);
+    return T >= 64 || (T > 32 && tiles >= 512) || (T >= 8 && tiles >= 1024);
 }
 
 bool workspace_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, Workspace& w) {
@@ -236,7 +242,7 @@ bool workspace_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, Workspace& w
     w.g = w.v + align256(nv * 2);
     w.beta = w.g + align256(ng * 4);
     w.chunked = w.beta + align256(ng * 4);
-    w.use_chunked = B > 0 && layer_uses_chunked(T, Hv, Dk, Dv);
+    w.use_chunked = B > 0 && layer_uses_chunked(B, T, Hv, Dk, Dv);
     w.total = w.chunked + (w.use_chunked ? gdn::chunked_layout(B, T, Hk, Hv, Dk, Dv).total : 0);
     if ((int64_t)B * T == 0) w.total = 0;
     return true;

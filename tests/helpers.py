@@ -94,6 +94,16 @@ def check_gates(g_gpu, beta_gpu, g_ref, beta_ref, label=""):
     assert not badb.any(), f"{label}: {badb.sum()} beta values out of tolerance"
 
 
+def layer_uses_chunked(B, T, Hv, Dk, Dv):
+    """Whether gdn_layer_core runs the chunked recurrence for these sizes (the
+    rule its header states): chunked sizes and T >= 64, or T > 32 with 512
+    state tiles of 16 rows and more, or T >= 8 with 1024 and more."""
+    if Dk != 128 or Dv % 16 != 0:
+        return False
+    tiles = B * Hv * (Dv // 16)
+    return T >= 64 or (T > 32 and tiles >= 512) or (T >= 8 and tiles >= 1024)
+
+
 def recurrence_sub(ri, b, hv, rows, Hk, Hv, state=None):
     """Slice the recurrence inputs of one (b, hv) and a subset of its rows
     into a self-contained problem (rows of S evolve independently)."""

@@ -357,11 +357,13 @@ def test_layer_core_matches_oracle(case):
 
 @pytest.mark.parametrize("shape", [(2, 70, 2, 4, 128, 64, 4), (2, 40, 2, 4, 128, 64, 4), (1, 90, 1, 2, 64, 32, 4),
                                    (1, 100, 3, 3, 128, 64, 2), (2, 96, 2, 6, 128, 32, 3),
-                                   (1, 70, 2, 4, 128, 96, 3)],
-                         ids=["chunked", "short", "Dk64", "chunked_G1_K2", "chunked_G3_K3", "chunked_G2_Dv96_K3"])
+                                   (1, 70, 2, 4, 128, 96, 3), (4, 16, 4, 32, 128, 128, 4),
+                                   (2, 40, 4, 32, 128, 128, 4), (2, 32, 4, 32, 128, 128, 4)],
+                         ids=["chunked", "short", "Dk64", "chunked_G1_K2", "chunked_G3_K3", "chunked_G2_Dv96_K3",
+                              "short_wide_chunked", "mid_2rounds_chunked", "short_2rounds_per_step"])
 def test_layer_core_equals_prep_then_recurrent(shape):
     """The layer core is the prologue followed by the chunked recurrence
-    (Dk = 128, Dv % 16 == 0, T >= 64) or else the per-step one, bit for bit
+    (the rule of tests.helpers.layer_uses_chunked) or else the per-step one, bit for bit
     (in the chunked form the prologue runs inside the chunk preparation, one
     or two v-heads per block by the parity of the GQA group size)."""
     B, T, Hk, Hv, Dk, Dv, K = shape
@@ -370,7 +372,7 @@ def test_layer_core_equals_prep_then_recurrent(shape):
     y, s, cs = gpu_layer_core(raw, Hk, Hv, Dk, Dv, 0.01, 0.09)
     p = gpu_prep(raw, Hk, Hv, Dk, Dv, 0.01, 0.09)
     ri = dict(q=p["q"], k=p["k"], v=p["v"], g=p["g"], beta=p["beta"], state=raw["state"])
-    chunked = Dk == 128 and Dv % 16 == 0 and T >= 64
+    chunked = H.layer_uses_chunked(B, T, Hv, Dk, Dv)
     y2, s2 = gpu_recurrent_chunked(ri) if chunked else gpu_recurrent(ri)
     assert np.array_equal(y, y2) and np.array_equal(s, s2) and np.array_equal(cs, p["conv_state"])
 
@@ -714,5 +716,5 @@ def test_masked_layer_core_matches_oracle_and_composition(T):
     assert np.array_equal(cs, cs_ref) and not y[mask == 0].any()
     p = gpu_prep(raw, Hk, Hv, Dk, Dv, qs, ks)
     ri = dict(q=p["q"], k=p["k"], v=p["v"], g=p["g"], beta=p["beta"], state=raw["state"])
-    y2, s2 = run_form("chunked" if T >= 64 else "per-step", ri, mask)
+    y2, s2 = run_form("chunked" if H.layer_uses_chunked(B, T, Hv, Dk, Dv) else "per-step", ri, mask)
     assert np.array_equal(y, y2) and np.array_equal(s, s2)

@@ -3,7 +3,7 @@ counts and sizes, GQA group, conv width, with and without conv / recurrent
 state and step masks): the layer core against the oracle (y within 1 bf16 ulp
 + 1e-3, state within the end-to-end bound, conv state bit-exact), and bit for
 bit against the prologue followed by the recurrence entry point it is defined
-as (chunked for Dk = 128, Dv % 16 == 0, T >= 64, else per-step)."""
+as (chunked or per-step by the rule of tests.helpers.layer_uses_chunked)."""
 import numpy as np
 import pytest
 
@@ -59,6 +59,6 @@ def test_layer_core_random_shapes(i):
     # the composition the layer core is defined as
     p = gpu_prep(raw, Hk, Hv, Dk, Dv, qs, ks)
     ri = dict(q=p["q"], k=p["k"], v=p["v"], g=p["g"], beta=p["beta"], state=raw["state"])
-    chunked = Dk == 128 and Dv % 16 == 0 and T >= 64
+    chunked = H.layer_uses_chunked(B, T, Hv, Dk, Dv)
     y2, s2 = gpu_recurrent_chunked(ri, mask=mask) if chunked else gpu_recurrent(ri, mask=mask)
     assert np.array_equal(y, y2) and np.array_equal(s, s2)
