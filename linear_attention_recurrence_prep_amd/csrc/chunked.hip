@@ -1274,7 +1274,7 @@ hipError_t launch_layer_chunked(const RecurrentArgs& a, const PrologueIn& p, int
 }
 
 // The current device's CU count, looked up once per device (0 if unknown).
-static int device_cu_count() {
+int device_cu_count() {
     constexpr int kMaxDevices = 64;
     static std::atomic<int> cached[kMaxDevices];
     int dev = 0;

@@ -221,16 +221,16 @@ struct Workspace {
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 // The layer core takes the chunked recurrence for sequences of 64 steps and
-// more, and for shorter ones once the per-step form would need several rounds
-// of blocks on the device (one block per 16 state rows, one block per CU at a
-// time): measured on MI355X at Hv = 32, Dk = Dv = 128, the chunked form is
-// as fast from T = 33 on with 512 state tiles and faster at every T >= 8 with
-// 1024.  A fixed rule (no device query), so the composition is the same on
+// more, and for shorter ones once the batch is large: measured on MI355X at
+// Hv = 32, Dk = Dv = 128, the per-step form (whose cost grows with the rounds
+// of state-row blocks the device runs) stays ahead up to T = 16 at every
+// batch, up to T = 32 with 2048 state tiles of 16 rows and up to T = 48 with
+// fewer.  A fixed rule (no device query), so the composition is the same on
 // every device.
 bool layer_uses_chunked(int B, int T, int Hv, int Dk, int Dv) {
     if (!gdn::chunked_supported(Hv, Dk, Dv)) return false;
     const int64_t tiles = (int64_t)B * Hv * (Dv / 16);
-    return T >= 64 || (T > 32 && tiles >= 512) || (T >= 8 && tiles >= 1024);
+    return T >= 64 || (T > 32 && tiles >= 2048) || (T > 16 && tiles >= 4096);
 }
 
 bool workspace_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, Workspace& w) {

@@ -50,6 +50,8 @@ struct PrepArgs {
 
 // Number of blocks each launcher would use (for grid-size validation).
 int64_t recurrent_blocks(int B, int Hv, int Dk, int Dv);
+// The current device's compute-unit count, cached per device (0 if unknown).
+int device_cu_count();
 int64_t prep_blocks(int B, int T, int Hk, int Hv, int Dk, int Dv);
 
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream);

@@ -72,10 +72,10 @@ struct ChunkBuf : GateRows<DK, TC, VG> {
     float4 v4[TC / 4][RecCfg<DK>::ROWS];     // v of steps 4i..4i+3, per row
 };
 
-template <int DK, int TC>
+template <int DK, int TC, int YK = 64>
 struct ChunkCfg {
     using C = RecCfg<DK>;
-    static constexpr int YBYTES = 64 * 1024;                         // y buffer
+    static constexpr int YBYTES = YK * 1024;                         // y buffer
     static constexpr int YSTEPS = YBYTES / (C::ROWS * 2) / TC * TC;  // whole chunks
     static constexpr int PAIRS = TC * DK / 8;                        // (step, 8 cols)
     static constexpr int PPT = PAIRS / C::NT;                        // per thread
@@ -85,10 +85,10 @@ struct ChunkCfg {
     static_assert(TC % 4 == 0 && 2 * TC <= C::NT, "chunk length");
 };
 
-template <int DK, int TC, bool VG = false>
+template <int DK, int TC, bool VG = false, int YK = 64>
 struct ChunkSmem {
     ChunkBuf<DK, TC, VG> buf[2];
-    uint16_t y[ChunkCfg<DK, TC>::YSTEPS][RecCfg<DK>::ROWS];
+    uint16_t y[ChunkCfg<DK, TC, YK>::YSTEPS][RecCfg<DK>::ROWS];
 };
 
 template <int DK, int TC, bool VG = false>
@@ -264,17 +264,17 @@ __device__ __forceinline__ void flush_y(const Smem& sh, uint16_t* __restrict__ y
     }
 }
 
-template <int DK, int TC, bool VG>
+template <int DK, int TC, bool VG, int YK>
 __global__ __launch_bounds__(256) void recurrent_chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, const uint8_t* __restrict__ mask,
     const float* state_in, float* state_out, uint16_t* __restrict__ y,
     int T, int Hk, int Hv, int Dv, int row_blocks, int n_blocks) {
     using C = RecCfg<DK>;
-    using CC = ChunkCfg<DK, TC>;
+    using CC = ChunkCfg<DK, TC, YK>;
     constexpr int L = C::L;
     constexpr int NY = (TC + L - 1) / L;
-    __shared__ ChunkSmem<DK, TC, VG> sh;
+    __shared__ ChunkSmem<DK, TC, VG, YK> sh;
 
     const int lb = xcd_block(n_blocks);
     const int n = lb / row_blocks;          // b * Hv + hv
@@ -492,14 +492,14 @@ int64_t recurrent_blocks(int B, int Hv, int Dk, int Dv) {
     return (int64_t)B * Hv * ((Dv + rows - 1) / rows);
 }
 
-template <int DK, int TC, bool VG = false>
+template <int DK, int TC, bool VG = false, int YK = 64>
 static hipError_t launch_rec(const RecurrentArgs& a, hipStream_t stream, bool chunked) {
     using C = RecCfg<DK>;
     const int row_blocks = (a.Dv + C::ROWS - 1) / C::ROWS;
     const int64_t blocks = (int64_t)a.B * a.Hv * row_blocks;
     if (blocks <= 0) return hipSuccess;
     if (chunked)
-        hipLaunchKernelGGL((recurrent_chunk_kernel<DK, TC, VG>), dim3((unsigned)blocks), dim3(C::NT), 0, stream,
+        hipLaunchKernelGGL((recurrent_chunk_kernel<DK, TC, VG, YK>), dim3((unsigned)blocks), dim3(C::NT), 0, stream,
                            a.q, a.k, a.v, a.g, a.beta, a.mask, a.state_in, a.state_out, a.y, a.T, a.Hk, a.Hv,
                            a.Dv, row_blocks, (int)blocks);
     else
@@ -532,6 +532,22 @@ static hipError_t launch_snap(const RecurrentArgs& a, hipStream_t stream) {
 // Sequences shorter than this run the staging-free kernel.
 constexpr int kChunkedMinT = 8;
 
+// The staged kernel in two configurations of the same arithmetic (so the
+// same bits): long chunks and a 64 KiB y buffer, one block per CU, for a
+// grid that fits the device in one round; for larger grids, or sequences
+// that fill less than half a long chunk, half-length chunks and a 16 KiB y
+// buffer, so that two or three blocks share a CU.
+template <int DK, int TC, int TCS, bool VG>
+static hipError_t launch_staged(const RecurrentArgs& a, hipStream_t stream, bool chunked) {
+    if constexpr (TCS > 0) {
+        using C = RecCfg<DK>;
+        const int cus = device_cu_count();
+        const int64_t blocks = (int64_t)a.B * a.Hv * ((a.Dv + C::ROWS - 1) / C::ROWS);
+        if (chunked && (2 * a.T <= TC || (cus > 0 && blocks > cus))) return launch_rec<DK, TCS, VG, 16>(a, stream, true);
+    }
+    return launch_rec<DK, TC, VG>(a, stream, chunked);
+}
+
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream) {
     if (a.snap != nullptr && a.snap->n > 0) {
         switch (a.Dk) {
@@ -546,18 +562,18 @@ hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream) {
     if (a.g_per_key) {
         // the gate rows take LDS beside k and q: half-length chunks at Dk >= 128
         switch (a.Dk) {
-            case 32: return launch_rec<32, 64, true>(a, stream, chunked);
-            case 64: return launch_rec<64, 32, true>(a, stream, chunked);
-            case 128: return launch_rec<128, 16, true>(a, stream, chunked);
-            case 256: return launch_rec<256, 8, true>(a, stream, chunked);
+            case 32: return launch_staged<32, 64, 0, true>(a, stream, chunked);
+            case 64: return launch_staged<64, 32, 32, true>(a, stream, chunked);
+            case 128: return launch_staged<128, 16, 16, true>(a, stream, chunked);
+            case 256: return launch_staged<256, 8, 8, true>(a, stream, chunked);
             default: return hipErrorInvalidValue;
         }
     }
     switch (a.Dk) {
-        case 32: return launch_rec<32, 64>(a, stream, chunked);
-        case 64: return launch_rec<64, 32>(a, stream, chunked);
-        case 128: return launch_rec<128, 32>(a, stream, chunked);
-        case 256: return launch_rec<256, 16>(a, stream, chunked);
+        case 32: return launch_staged<32, 64, 0, false>(a, stream, chunked);
+        case 64: return launch_staged<64, 32, 32, false>(a, stream, chunked);
+        case 128: return launch_staged<128, 32, 16, false>(a, stream, chunked);
+        case 256: return launch_staged<256, 16, 8, false>(a, stream, chunked);
         default: return hipErrorInvalidValue;
     }
 }

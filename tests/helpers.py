@@ -96,12 +96,12 @@ def check_gates(g_gpu, beta_gpu, g_ref, beta_ref, label=""):
 
 def layer_uses_chunked(B, T, Hv, Dk, Dv):
     """Whether gdn_layer_core runs the chunked recurrence for these sizes (the
-    rule its header states): chunked sizes and T >= 64, or T > 32 with 512
-    state tiles of 16 rows and more, or T >= 8 with 1024 and more."""
+    rule its header states): chunked sizes and T >= 64, or T > 32 with 2048
+    state tiles of 16 rows and more, or T > 16 with 4096 and more."""
     if Dk != 128 or Dv % 16 != 0:
         return False
     tiles = B * Hv * (Dv // 16)
-    return T >= 64 or (T > 32 and tiles >= 512) or (T >= 8 and tiles >= 1024)
+    return T >= 64 or (T > 32 and tiles >= 2048) or (T > 16 and tiles >= 4096)
 
 
 def recurrence_sub(ri, b, hv, rows, Hk, Hv, state=None):

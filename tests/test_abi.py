@@ -148,12 +148,13 @@ def test_workspace_bytes(L):
     assert L.gdn_recurrent_chunked_workspace_bytes(1, 100, 2, 4, 64, 32) == 0     # unsupported Dk
     assert L.gdn_recurrent_chunked_workspace_bytes(1, 100, 2, 4, 128, 24) == 0    # Dv % 16 != 0
     assert f(1, 0, 16, 32, 128, 128) == 0
-    # shorter sequences take the chunked form once the per-step grid would need several rounds
+    # shorter sequences take the chunked form once the batch is large
     pp = lambda B, T: 2 * up(B * T * Hk * Dk * 2) + up(B * T * Hv * Dv * 2) + 2 * up(B * T * Hv * 4)
-    assert f(4, 16, Hk, Hv, Dk, Dv) == pp(4, 16) + chunked_expect(4, 16, Hk, Hv, Dk, Dv)     # 1024 tiles
-    assert f(2, 40, Hk, Hv, Dk, Dv) == pp(2, 40) + chunked_expect(2, 40, Hk, Hv, Dk, Dv)     # 512 tiles, T > 32
-    assert f(2, 32, Hk, Hv, Dk, Dv) == pp(2, 32)
-    assert f(4, 7, Hk, Hv, Dk, Dv) == pp(4, 7)
+    assert f(16, 24, Hk, Hv, Dk, Dv) == pp(16, 24) + chunked_expect(16, 24, Hk, Hv, Dk, Dv)   # 4096 tiles, T > 16
+    assert f(8, 40, Hk, Hv, Dk, Dv) == pp(8, 40) + chunked_expect(8, 40, Hk, Hv, Dk, Dv)      # 2048 tiles, T > 32
+    assert f(8, 32, Hk, Hv, Dk, Dv) == pp(8, 32)
+    assert f(4, 48, Hk, Hv, Dk, Dv) == pp(4, 48)
+    assert f(64, 16, Hk, Hv, Dk, Dv) == pp(64, 16)
     assert f(0, 10, 16, 32, 128, 128) == 0
     assert f(1, 10, 3, 32, 128, 128) == 0     # invalid dims
     assert f(1, 10, 16, 32, 100, 128) == 0

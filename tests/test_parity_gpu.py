@@ -357,10 +357,10 @@ def test_layer_core_matches_oracle(case):
 
 @pytest.mark.parametrize("shape", [(2, 70, 2, 4, 128, 64, 4), (2, 40, 2, 4, 128, 64, 4), (1, 90, 1, 2, 64, 32, 4),
                                    (1, 100, 3, 3, 128, 64, 2), (2, 96, 2, 6, 128, 32, 3),
-                                   (1, 70, 2, 4, 128, 96, 3), (4, 16, 4, 32, 128, 128, 4),
-                                   (2, 40, 4, 32, 128, 128, 4), (2, 32, 4, 32, 128, 128, 4)],
+                                   (1, 70, 2, 4, 128, 96, 3), (16, 24, 4, 32, 128, 128, 4),
+                                   (8, 40, 4, 32, 128, 128, 4), (8, 32, 4, 32, 128, 128, 4)],
                          ids=["chunked", "short", "Dk64", "chunked_G1_K2", "chunked_G3_K3", "chunked_G2_Dv96_K3",
-                              "short_wide_chunked", "mid_2rounds_chunked", "short_2rounds_per_step"])
+                              "short_wide_chunked", "mid_wide_chunked", "short_wide_per_step"])
 def test_layer_core_equals_prep_then_recurrent(shape):
     """The layer core is the prologue followed by the chunked recurrence
     (the rule of tests.helpers.layer_uses_chunked) or else the per-step one, bit for bit
