@@ -190,14 +190,15 @@ __device__ __forceinline__ f4_t mma6(const Planes& a, const Planes& b, f4_t c) {
 // ========================================================= chunk preparation
 
 // Inputs of the per-key form's preparation: k and q rows in f32, the gate
-// rows (then the suffix decays E_t = g_{t+1} ... g_{C-1}) and the prefix
-// decays Gamma_t = g_0 ... g_t, per key column.  Nothing in the per-head form.
+// rows (then the suffix decays within each half chunk) and the prefix decays
+// within each half chunk, per key column.  Nothing in the per-head form.
 template <bool PK>
 struct PkIn {
     float kf[CK][DKC + 4];
     float qf[CK][DKC + 4];
     float ge[CK][DKC + 4];
     float gam[CK][DKC + 4];
+    float gb[2][DKC];          // the product of each half chunk's gates
 };
 template <>
 struct PkIn<false> {};
@@ -527,13 +528,16 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
         // 3'. per-key decay ratios R_j(t, s) = g_{s+1}[j] ... g_t[j]:
         //     A[t][s] = beta_t sum_j k_t[j] k_s[j] R_j(t, s)   (s < t)
         //     P[t][s] = sum_j q_t[j] k_s[j] R_j(t, s)          (s <= t)
-        //     Thread (s, jg) carries u = k_s o R(t, s) over key columns
-        //     16 jg .. 16 jg + 15 while t runs up from s (a running product,
-        //     never a quotient of cumulative decays); the eight column groups
-        //     of a row s are adjacent lanes, summed by DPP.  A wave's rows s
-        //     start at s_lo, so its loop starts there.
+        //     Within each half chunk (s, t both below 16 or both from 16 on)
+        //     thread (s, jg) carries u = k_s o R(t, s) over key columns
+        //     16 jg .. 16 jg + 15 while t runs up from s to the half's end (a
+        //     running product, never a quotient of cumulative decays); the
+        //     eight column groups of a row s are adjacent lanes, summed by DPP.
+        //     A wave's rows s start at s_lo, so its loop starts there.  Across
+        //     the halves (t >= 16 > s) R(t, s) = R(t, 15) o R(15, s), two
+        //     factors <= 1: that block is one f32 product on the matrix cores.
         auto& sw = sh.w.s[0];
-        const int s = tl >> 3, jg = tl & 7, s_lo = s & ~7;
+        const int s = tl >> 3, jg = tl & 7, s_lo = s & ~7, t_hi = s < CK / 2 ? CK / 2 : CK;
         float u[16];
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
@@ -543,7 +547,7 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
             u[4 * e4 + 2] = x.z;
             u[4 * e4 + 3] = x.w;
         }
-        for (int t = s_lo; t < CK; ++t) {
+        for (int t = s_lo; t < t_hi; ++t) {
             float pa = 0.f, pp = 0.f;
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
@@ -575,6 +579,57 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
                 sw.tm[t][s] = 0.f;
             }
         __syncthreads();
+        // decays per key column within each half chunk: prefix products
+        // (gam) and suffix products (ge, over the gate rows), and the product
+        // of each half's gates
+        constexpr int CH2 = CK / 2;
+        if (tl < DKC) {
+            float gc[CK];
+#pragma unroll
+            for (int t = 0; t < CK; ++t) gc[t] = sh.u.pk.ge[t][tl];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float gp = 1.f, ep = 1.f;
+#pragma unroll
+                for (int i = 0; i < CH2; ++i) {
+                    const int t = CH2 * h + i, r = CH2 * h + CH2 - 1 - i;
+                    gp *= gc[t];
+                    sh.u.pk.gam[t][tl] = gp;
+                    sh.u.pk.ge[r][tl] = ep;
+                    ep *= gc[r];
+                }
+                sh.u.pk.gb[h][tl] = gp;
+            }
+            o.rg[unit * rg_floats<PK>() + 2 * CK + tl] = sh.u.pk.gb[0][tl] * sh.u.pk.gb[1][tl];   // Gamma_{C-1}
+        }
+        __syncthreads();
+        // across the halves: A21 = diag(beta) (K2 o G2)(K1 o E1)^T (wave 1) and
+        // P21 = (Q2 o G2)(K1 o E1)^T (wave 3), G2 the second half's prefix and
+        // E1 the first half's suffix decays; f32 operands as planes, six products
+        if (wl == 1 || wl == 3) {
+            f4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DKC / 32; ++ks) {
+                const int c = 32 * ks + 8 * lq;
+                float av[8], bv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = wl == 1 ? sh.u.pk.kf[CH2 + lr][c + e] : sh.u.pk.qf[CH2 + lr][c + e];
+                    av[e] = x * sh.u.pk.gam[CH2 + lr][c + e];
+                    bv[e] = sh.u.pk.kf[lr][c + e] * sh.u.pk.ge[lr][c + e];
+                }
+                const Planes pa = split8(no, f4_t{av[0], av[1], av[2], av[3]}, f4_t{av[4], av[5], av[6], av[7]});
+                const Planes pb = split8(no, f4_t{bv[0], bv[1], bv[2], bv[3]}, f4_t{bv[4], bv[5], bv[6], bv[7]});
+                acc = mma6(pa, pb, acc);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = CH2 + 4 * lq + i;
+                if (wl == 1) sw.a[t][lr] = sh.bs[0][t] * acc[i];
+                else sw.tm[t][lr] = acc[i];
+            }
+        }
+        __syncthreads();
         {
             // -P planes; gamma = 1 and -rho = -1 (the decay is in the operands)
             const int t = tl >> 3, s0 = (tl & 7) * 4;
@@ -584,23 +639,14 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
             if (tl < CK) sh.gm[0][tl] = 1.f;
             if (tl < 2 * CK) o.rg[unit * rg_floats<PK>() + tl] = tl < CK ? -1.f : 1.f;
         }
-        // prefix decays Gamma_t = g_0 ... g_t and suffix decays
-        // E_t = g_{t+1} ... g_{C-1} (over the gate rows) per key column
-        if (tl < DKC) {
-            float gc[CK];
-#pragma unroll
-            for (int t = 0; t < CK; ++t) gc[t] = sh.u.pk.ge[t][tl];
-            float gp = 1.f, ep = 1.f;
-#pragma unroll
-            for (int t = 0; t < CK; ++t) {
-                gp *= gc[t];
-                sh.u.pk.gam[t][tl] = gp;
-                sh.u.pk.ge[CK - 1 - t][tl] = ep;
-                ep *= gc[CK - 1 - t];
-            }
-            o.rg[unit * rg_floats<PK>() + 2 * CK + tl] = gp;      // Gamma_{C-1}
-        }
-        __syncthreads();
+        // the chunk's decays from the half ones: Gamma_t = g_0 ... g_t and
+        // E_t = g_{t+1} ... g_{C-1}
+        auto gamma_at = [&](int t, int j) {
+            return t < CH2 ? sh.u.pk.gam[t][j] : sh.u.pk.gb[0][j] * sh.u.pk.gam[t][j];
+        };
+        auto e_at = [&](int t, int j) {
+            return t < CH2 ? sh.u.pk.ge[t][j] * sh.u.pk.gb[1][j] : sh.u.pk.ge[t][j];
+        };
         // operands: (K o Gamma)^T planes for W (kept in registers until step
         // 6), (K o E)^T planes and Q o Gamma planes for the sequential pass
         Planes kw[2];
@@ -614,8 +660,8 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const float kv = sh.u.pk.kf[s0 + h][d];
-                    xw[2 * p + h] = kv * sh.u.pk.gam[s0 + h][d];
-                    xe[2 * p + h] = kv * sh.u.pk.ge[s0 + h][d];
+                    xw[2 * p + h] = kv * gamma_at(s0 + h, d);
+                    xe[2 * p + h] = kv * e_at(s0 + h, d);
                 }
             }
             kw[tt] = split8(no, f4_t{xw[0], xw[1], xw[2], xw[3]}, f4_t{xw[4], xw[5], xw[6], xw[7]});
@@ -632,8 +678,8 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c0 = 32 * wl + 4 * lq + i, c1 = c0 + 16;
-                x0[i] = sh.u.pk.qf[t][c0] * sh.u.pk.gam[t][c0];
-                x1[i] = sh.u.pk.qf[t][c1] * sh.u.pk.gam[t][c1];
+                x0[i] = sh.u.pk.qf[t][c0] * gamma_at(t, c0);
+                x1[i] = sh.u.pk.qf[t][c1] * gamma_at(t, c1);
             }
             u4_t qh, qm;
             split8hm(no, x0, x1, qh, qm);
