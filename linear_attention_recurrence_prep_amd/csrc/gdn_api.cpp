@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kVersion = 3;
+constexpr int kVersion = 4;
 constexpr int64_t kMaxBlocks = (1LL << 31) - 1;
 
 thread_local char g_err[512] = "";
