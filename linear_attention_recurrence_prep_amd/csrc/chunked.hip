@@ -340,9 +340,13 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
         // the new conv state (chunk 0's blocks; q/k channels from the first
         // v-head of the group): the last KF-1 rows of the spliced input
         if (c == 0 && wv == 0 && valid && pin.conv_state_out && (region == 2 || hv0 % G == 0)) {
+            // every row read before any is written (the state may be updated in place)
+            uint4 tail[KF - 1];
+#pragma unroll
+            for (int i = 0; i < KF - 1; ++i) tail[i] = xpad_row(T + i);
             uint16_t* out = pin.conv_state_out + (int64_t)b * (KF - 1) * C + c0;
 #pragma unroll
-            for (int i = 0; i < KF - 1; ++i) *reinterpret_cast<uint4*>(out + (int64_t)i * C) = xpad_row(T + i);
+            for (int i = 0; i < KF - 1; ++i) *reinterpret_cast<uint4*>(out + (int64_t)i * C) = tail[i];
         }
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
@@ -1303,8 +1307,13 @@ int64_t chunked_blocks(int B, int T, int Hv, int Dv) {
     return std::max<int64_t>((int64_t)B * Hv * NC, (int64_t)B * Hv * (Dv / RB));
 }
 
-bool layer_chunked_fusable(int Dv, int K, const void* conv_state_in, const void* conv_state_out) {
-    return Dv <= 128 && K >= 2 && K <= 4 && (conv_state_out == nullptr || conv_state_out != conv_state_in);
+// An in-place conv state is read and rewritten by the same lane of the chunk-0
+// block that owns the channel; that is race-free when no other block reads
+// the channel, i.e. when one preparation block serves each k-head (Hv / Hk
+// of 1 or 2).
+bool layer_chunked_fusable(int Hk, int Hv, int Dv, int K, const void* conv_state_in, const void* conv_state_out) {
+    const bool in_place = conv_state_out != nullptr && conv_state_out == conv_state_in;
+    return Dv <= 128 && K >= 2 && K <= 4 && (!in_place || Hv / Hk <= 2);
 }
 
 static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, int K, void* ws,
@@ -1315,7 +1324,7 @@ hipError_t launch_recurrent_chunked(const RecurrentArgs& a, void* ws, hipStream_
 }
 
 hipError_t launch_layer_chunked(const RecurrentArgs& a, const PrologueIn& p, int K, void* ws, hipStream_t stream) {
-    if (!layer_chunked_fusable(a.Dv, K, p.conv_state_in, p.conv_state_out)) return hipErrorInvalidValue;
+    if (!layer_chunked_fusable(a.Hk, a.Hv, a.Dv, K, p.conv_state_in, p.conv_state_out)) return hipErrorInvalidValue;
     return launch_chunked(a, &p, K, ws, stream);
 }
 

@@ -514,7 +514,7 @@ static gdn_status layer_core_impl(const gdn_bf16* qkv, const gdn_bf16* conv_w, c
     if (B == 0) return ok();
     hipStream_t s = static_cast<hipStream_t>(stream);
     gdn::RecurrentArgs r{wq, wk, wv, wg, wb, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, mask};
-    if (w.use_chunked && gdn::layer_chunked_fusable(Dv, K, conv_state_in, conv_state_out)) {
+    if (w.use_chunked && gdn::layer_chunked_fusable(Hk, Hv, Dv, K, conv_state_in, conv_state_out)) {
         // the prologue runs inside the chunk preparation (same arithmetic, same bits)
         const gdn::PrologueIn p{qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias,
                                 q_scale, k_scale, eps};

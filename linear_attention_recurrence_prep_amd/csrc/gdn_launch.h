@@ -80,7 +80,7 @@ struct PrologueIn {
     const uint16_t* qkv;
     const uint16_t* conv_w;
     const uint16_t* conv_state_in;   // may be null (zeros)
-    uint16_t* conv_state_out;        // may be null; never conv_state_in itself
+    uint16_t* conv_state_out;        // may be null; conv_state_in itself only if Hv / Hk <= 2
     const uint16_t* a;
     const uint16_t* b;
     const float* A_log;
@@ -90,10 +90,10 @@ struct PrologueIn {
 
 // The layer core's chunked recurrence with the prologue fused into the chunk
 // preparation: q, k, v, g, beta of RecurrentArgs are not read (computed from
-// p), conv_state_out is written.  Needs Dv <= 128, K in {2, 3, 4} and
-// conv_state_out not aliasing conv_state_in; the result is bit-identical to
+// p), conv_state_out is written.  Needs Dv <= 128, K in {2, 3, 4} and, for
+// an in-place conv state, Hv / Hk <= 2; the result is bit-identical to
 // launch_prep followed by launch_recurrent_chunked.
-bool layer_chunked_fusable(int Dv, int K, const void* conv_state_in, const void* conv_state_out);
+bool layer_chunked_fusable(int Hk, int Hv, int Dv, int K, const void* conv_state_in, const void* conv_state_out);
 hipError_t launch_layer_chunked(const RecurrentArgs& a, const PrologueIn& p, int K, void* workspace,
                                 hipStream_t stream);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);

@@ -304,14 +304,14 @@ def test_prep_conv_state_in_place_and_T0():
 
 # ------------------------------------------------------------- layer core
 
-def gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks, eps=1e-6, mask=None):
+def gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks, eps=1e-6, mask=None, cs_in_place=False):
     B, T, C = raw["qkv"].shape
     K = raw["conv_w"].shape[1]
     d = {k: H.to_dev(raw[k]) for k in ("qkv", "conv_w", "conv_state", "a", "b", "A_log", "dt_bias",
                                        "state")}
     y = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=H.DEV)
     s_out = torch.empty(B, Hv, Dv, Dk, dtype=torch.float32, device=H.DEV)
-    cs_out = torch.empty(B, K - 1, C, dtype=torch.int16, device=H.DEV)
+    cs_out = d["conv_state"] if cs_in_place else torch.empty(B, K - 1, C, dtype=torch.int16, device=H.DEV)
     nws = binding.layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=H.DEV)
     m = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).to(H.DEV)
@@ -375,6 +375,21 @@ def test_layer_core_equals_prep_then_recurrent(shape):
     chunked = H.layer_uses_chunked(B, T, Hv, Dk, Dv)
     y2, s2 = gpu_recurrent_chunked(ri) if chunked else gpu_recurrent(ri)
     assert np.array_equal(y, y2) and np.array_equal(s, s2) and np.array_equal(cs, p["conv_state"])
+
+
+@pytest.mark.parametrize("shape", [(2, 96, 2, 4, 128, 64, 4), (1, 70, 2, 2, 128, 128, 3), (2, 96, 1, 4, 128, 32, 4),
+                                   (2, 5, 2, 4, 128, 64, 4), (1, 2, 2, 4, 128, 32, 4)],
+                         ids=["chunked_G2_fused", "chunked_G1_fused", "chunked_G4_unfused", "per_step", "T_below_K"])
+def test_layer_core_conv_state_in_place(shape):
+    """The conv state updated in place (conv_state_out == conv_state_in) gives
+    the same bits as a separate output, in the chunked form with the prologue
+    fused (one preparation block per k-head) or not, and in the per-step form."""
+    B, T, Hk, Hv, Dk, Dv, K = shape
+    say("layer_core conv state in place", shape)
+    raw = layer_inputs(B, T, Hk, Hv, Dk, Dv, K, 320)
+    y, s, cs = gpu_layer_core(raw, Hk, Hv, Dk, Dv, 0.01, 0.09)
+    y2, s2, cs2 = gpu_layer_core(raw, Hk, Hv, Dk, Dv, 0.01, 0.09, cs_in_place=True)
+    assert np.array_equal(y, y2) and np.array_equal(s, s2) and np.array_equal(cs, cs2)
 
 
 def test_prefill_workload_full_size_sampled():
