@@ -50,6 +50,15 @@
 //    wave then updates its state columns; two waves finish Y.
 // Padding steps past T and masked steps carry g = 1, beta = 0: their Delta is
 // 0 and they leave S unchanged (a masked step's y is written as zero).
+//
+// Per-key gate (S <- S diag(g_t), g_t a vector over the key columns): the
+// same algebra with every scalar decay turned into a column scaling,
+//   A[t][s] = beta_t (k_t o R(t, s)) . k_s,   P[t][s] = (q_t o R(t, s)) . k_s,
+//   W = T diag(beta) (K o Gamma),   Y = (Q o Gamma) S_0^T + P Delta,
+//   S_C = S_0 diag(Gamma_{C-1}) + Delta^T (K o E),
+// Gamma_t = g_0 o ... o g_t, E_t = g_{t+1} o ... o g_{C-1}; chunk_prep_kernel
+// <0, 1, true> forms the ratios as running products and chunk_seq_kernel
+// <1, true> takes Q o Gamma, (K o E)^T and Gamma_{C-1} per v-head.
 #include <algorithm>
 #include <atomic>
 
@@ -653,7 +662,6 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
         };
         // operands: (K o Gamma)^T planes for W (kept in registers until step
         // 6), (K o E)^T planes and Q o Gamma planes for the sequential pass
-        Planes kw[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int d = 32 * wl + 16 * tt + lr;
@@ -668,7 +676,7 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
                     xe[2 * p + h] = kv * e_at(s0 + h, d);
                 }
             }
-            kw[tt] = split8(no, f4_t{xw[0], xw[1], xw[2], xw[3]}, f4_t{xw[4], xw[5], xw[6], xw[7]});
+            kwp[tt] = split8(no, f4_t{xw[0], xw[1], xw[2], xw[3]}, f4_t{xw[4], xw[5], xw[6], xw[7]});
             const Planes ke = split8(no, f4_t{xe[0], xe[1], xe[2], xe[3]}, f4_t{xe[4], xe[5], xe[6], xe[7]});
             u4_t* kd = o.ksw + unit * 3 * kQVec + (wl * 2 + tt) * 64 + lane;
             kd[0] = ke.h;
@@ -691,8 +699,6 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
             qd[0] = qh;
             qd[kQVec] = qm;
         }
-        kwp[0] = kw[0];
-        kwp[1] = kw[1];
     }
     __syncthreads();
 
