@@ -148,7 +148,7 @@ def _ptr(t, name, dtypes, shape, device):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:      # torch.Size compares equal to a tuple of the same ints
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
@@ -157,9 +157,16 @@ def _ptr(t, name, dtypes, shape, device):
     return t.data_ptr() if t.numel() else None
 
 
+# the current stream's raw handle without building a Stream object (the
+# public call is the fallback where the accessor is absent)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device, stream):
     if stream is not None:
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
     return torch.cuda.current_stream(device).cuda_stream
 
 
