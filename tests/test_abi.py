@@ -334,6 +334,29 @@ def test_per_key_gate_span_is_checked(L):
                                    p["y"], d["B"], d["T"], d["Hk"], d["Hv"], d["Dk"], d["Dv"], None) == NULLP
 
 
+def call_chunked_pk(L, ws=addr(20), ws_bytes=1 << 32, **over):
+    p, d = rec_args(**over)
+    return L.gdn_recurrent_chunked_per_key(p["q"], p["k"], p["v"], p["g"], p["beta"], None, p["state_in"],
+                                           p["state_out"], p["y"], ws, ctypes.c_size_t(ws_bytes), d["B"], d["T"],
+                                           d["Hk"], d["Hv"], d["Dk"], d["Dv"], None)
+
+
+def test_recurrent_chunked_per_key_rejects(L):
+    assert call_chunked_pk(L, Dk=64) == UNSUP
+    assert call_chunked_pk(L, Dk=128, Dv=24) == UNSUP
+    assert call_chunked_pk(L, Dk=128, ws=None) == WS
+    need = L.gdn_recurrent_chunked_per_key_workspace_bytes(2, 8, 2, 4, 128, 32)
+    assert need > L.gdn_recurrent_chunked_workspace_bytes(2, 8, 2, 4, 128, 32)   # per-v-head q, k planes
+    assert call_chunked_pk(L, Dk=128, ws_bytes=need - 1) == WS
+    assert call_chunked_pk(L, Dk=128, g=None) == NULLP
+    # g spans B*T*Hv*Dk floats: an output inside that extent overlaps it
+    p, d = rec_args(Dk=128)
+    assert call_chunked_pk(L, Dk=128, y=addr(3) + d["B"] * d["T"] * d["Hv"] * 4 + 64) == OVERLAP
+    assert call_chunked_pk(L, Dk=128, B=0) == OK
+    assert L.gdn_recurrent_chunked_per_key_workspace_bytes(1, 0, 2, 4, 128, 32) == 0
+    assert L.gdn_recurrent_chunked_per_key_workspace_bytes(1, 8, 2, 4, 64, 32) == 0
+
+
 def test_bind_rejects_non_library_calls():
     from linear_attention_recurrence_prep_amd import binding
     with pytest.raises(TypeError):

@@ -227,6 +227,8 @@ PKC_CASES = [
     (1, 64, 1, 1, 128, 128, 722, "uniform"),       # whole chunks
     (1, 33, 2, 2, 128, 256, 723, "uniform"),       # one step past a chunk, Dv = 256
     (1, 96, 1, 3, 128, 32, 724, "steep"),          # gates down to 1e-3 on half the keys: decays underflow
+    (3, 1, 3, 3, 128, 16, 728, "uniform"),         # one step (31 padding steps), smallest Dv
+    (1, 31, 1, 2, 128, 16, 729, "uniform"),        # one step short of a chunk
 ]
 
 
@@ -252,6 +254,15 @@ def test_per_key_chunked_matches_oracle(case):
     H.check_y(y, y_ref, str(case))
     e = H.check_state(s, s_ref, 1e-4, str(case))
     say("per-key chunked state err", e)
+
+
+def test_per_key_chunked_T0_copies_state():
+    B, T, Hk, Hv, Dk, Dv = 2, 0, 1, 2, 128, 32
+    ri = rec_inputs(B, 1, Hk, Hv, Dk, Dv, 730)
+    ri = {n: (v if n == "state" else np.ascontiguousarray(v[:, :0])) for n, v in ri.items()}
+    gk = np.zeros((B, 0, Hv, Dk), dtype=np.float32)
+    y, s = gpu_chunked_per_key(ri, gk)
+    assert y.size == 0 and np.array_equal(s, ri["state"])
 
 
 def test_per_key_chunked_identities():
