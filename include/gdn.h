@@ -183,7 +183,9 @@ size_t gdn_layer_core_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int 
  * gdn_layer_core -- gdn_prep followed by the recurrence, on one stream:
  * gdn_recurrent_chunked when it supports the sizes and T >= 64, or T > 32
  * with B * Hv * Dv / 16 >= 2048, or T > 16 with B * Hv * Dv / 16 >= 4096;
- * else gdn_recurrent.  Results are bit-identical to making those two calls.
+ * else gdn_recurrent.  Results are bit-identical to making those two calls
+ * (which the library may fuse: the prologue runs inside the chunk preparation,
+ * and single-token decode of a large batch is one launch).
  * ("mlex ... gated_delta.rs", GatedDeltaNet::forward between the input
  *  projections and the output normalisation.)
  *

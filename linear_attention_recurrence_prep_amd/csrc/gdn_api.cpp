@@ -519,6 +519,11 @@ static gdn_status layer_core_impl(const gdn_bf16* qkv, const gdn_bf16* conv_w, c
         const gdn::PrologueIn p{qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias,
                                 q_scale, k_scale, eps};
         st = hip_result(gdn::launch_layer_chunked(r, p, K, ws + w.chunked, s), "chunked layer core");
+    } else if (T == 1 && gdn::decode_fusable(B, Hk, Hv, Dk, Dv, K)) {
+        // single-token decode of a large batch: prologue and step in one launch (same bits)
+        gdn::PrepArgs p{qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, wq, wk, wv, wg, wb,
+                        B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps};
+        st = hip_result(gdn::launch_decode_core(p, mask, state_in, state_out, y, s), "decode layer core");
     } else {
         if (T > 0 || conv_state_out) {
             gdn::PrepArgs p{qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, wq, wk, wv, wg, wb,

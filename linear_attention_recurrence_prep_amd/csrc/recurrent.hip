@@ -485,6 +485,179 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     if (row_ok) store_row<DK>(state_out + srow, s, j);
 }
 
+// ======================================================= single-token decode
+//
+// The layer core at T = 1 in one launch, one 512-thread block per (b,
+// k-head): the block computes the prologue of its k-head's q and k channels,
+// its v-heads' v channels and their gates, then advances those v-heads' state
+// rows by one step.  Every channel is read, and its conv state rewritten, by
+// one lane of one block, so the conv state may be updated in place.  The
+// prologue uses the prologue kernel's device functions and the step is the
+// staging-free kernel's arithmetic term for term (q, k, v rounded to bf16
+// first), so the results are the bits of the two-launch composition.
+
+constexpr int DEC_NT = 512;
+constexpr int kDecMaxRows = 1024;   // (Hv / Hk) * Dv of one block
+
+template <int DK, int KC>
+__global__ __launch_bounds__(DEC_NT) void decode_core_kernel(PrepArgs p, const uint8_t* __restrict__ mask,
+                                                             const float* state_in, float* state_out,
+                                                             uint16_t* __restrict__ y) {
+    __shared__ float qs[DK], ks[DK], vs[kDecMaxRows], gsh[kDecMaxRows / 8], bsh[kDecMaxRows / 8];
+    constexpr int L = DK / 8;                 // lanes per state row (and per q/k head)
+    const int Hk = p.Hk, Hv = p.Hv, Dv = p.Dv;
+    const int b = blockIdx.x / Hk, hk = blockIdx.x % Hk;
+    const int G = Hv / Hk, R = G * Dv;
+    const int C = 2 * Hk * DK + Hv * Dv;
+    const int tid = threadIdx.x;
+
+    // prologue: thread i < L the q channels 8i.., L <= i < 2L the k channels,
+    // 2L <= i < 2L + R/8 the v channels; threads 256.. the gates
+    const int nv = R / 8;
+    if (tid < 2 * L + nv) {
+        const int region = tid < L ? 0 : tid < 2 * L ? 1 : 2;
+        const int c0 = region == 0   ? hk * DK + 8 * tid
+                       : region == 1 ? Hk * DK + hk * DK + 8 * (tid - L)
+                                     : 2 * Hk * DK + hk * G * Dv + 8 * (tid - 2 * L);
+        float w[KC][8];
+        {
+            const uint4* wp = reinterpret_cast<const uint4*>(p.conv_w + (int64_t)c0 * KC);
+            float f[8 * KC];
+#pragma unroll
+            for (int v4 = 0; v4 < KC; ++v4) unpack8(wp[v4], f + 8 * v4);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < KC; ++j) w[j][i] = f[i * KC + j];
+        }
+        uint4 hr[KC - 1];
+        float h[KC - 1][8];
+#pragma unroll
+        for (int r = 0; r < KC - 1; ++r) {
+            hr[r] = p.conv_state_in
+                        ? *reinterpret_cast<const uint4*>(p.conv_state_in + ((int64_t)b * (KC - 1) + r) * C + c0)
+                        : make_uint4(0, 0, 0, 0);
+            unpack8(hr[r], h[r]);
+        }
+        const uint4 xr = *reinterpret_cast<const uint4*>(p.qkv + (int64_t)b * C + c0);
+        float x[8], act[8];
+        unpack8(xr, x);
+        conv_silu8<KC>(w, h, x, act);
+        // q/k: the head norm over the head's L lanes (aligned lane groups of
+        // wave 0; the v lanes never join this branch)
+        uint4 packed;
+        if (region < 2) packed = qk_norm8<DK>(act, region == 0 ? p.q_scale : p.k_scale, p.eps);
+        else packed = pack8(act);
+        float o[8];
+        unpack8(packed, o);
+        float* dst = region == 0 ? qs + 8 * tid : region == 1 ? ks + 8 * (tid - L) : vs + 8 * (tid - 2 * L);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = o[e];
+        // the new conv state: rows 1.. of the old one, then the token (every
+        // row read above, before this write)
+        if (p.conv_state_out) {
+#pragma unroll
+            for (int r = 0; r < KC - 1; ++r)
+                *reinterpret_cast<uint4*>(p.conv_state_out + ((int64_t)b * (KC - 1) + r) * C + c0) =
+                    r + 1 < KC - 1 ? hr[r + 1] : xr;
+        }
+    }
+    if (tid >= 256 && tid < 256 + G) {
+        const int hl = tid - 256, hv = hk * G + hl;
+        const int64_t i = (int64_t)b * Hv + hv;
+        float gv, bv;
+        gate_g_beta(p.a[i], p.b[i], p.A_log[hv], p.dt_bias[hv], gv, bv);
+        gsh[hl] = gv;
+        bsh[hl] = bv;
+    }
+    __syncthreads();
+
+    // the step, RPP state rows per pass (L lanes per row, 8 elements per lane)
+    constexpr int RPP = DEC_NT / L;
+    const int j = tid % L, rr = tid / L;
+    const bool active = mask == nullptr || mask[b] != 0;
+    float kk[8], qq[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        kk[e] = ks[4 * j + e];
+        kk[4 + e] = ks[DK / 2 + 4 * j + e];
+        qq[e] = qs[4 * j + e];
+        qq[4 + e] = qs[DK / 2 + 4 * j + e];
+    }
+    float kq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kq = fmaf(kk[i], qq[i], kq);
+    kq = group_sum<L>(kq);
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    for (int r0 = 0; r0 < R; r0 += RPP) {
+        const int r = r0 + rr;
+        const bool ok = r < R;
+        const int rc = ok ? r : R - 1;
+        const int hl = rc / Dv, dv = rc % Dv, hv = hk * G + hl;
+        const int64_t srow = (((int64_t)b * Hv + hv) * Dv + dv) * DK;
+        float s[8];
+        if (state_in != nullptr && ok) {
+            const f4v a0 = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(state_in + srow + 4 * j));
+            const f4v a1 = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(state_in + srow + DK / 2 + 4 * j));
+            s[0] = a0.x; s[1] = a0.y; s[2] = a0.z; s[3] = a0.w;
+            s[4] = a1.x; s[5] = a1.y; s[6] = a1.z; s[7] = a1.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s[i] = 0.f;
+        }
+        const int64_t yi = ((int64_t)b * Hv + hv) * Dv + dv;
+        if (active) {
+            const float gt = gsh[hl], bt = bsh[hl], vt = vs[rc];
+            float a = 0.f, c = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                a = fmaf(s[i], kk[i], a);
+                c = fmaf(s[i], qq[i], c);
+            }
+            group_sum2<L>(a, c);
+            const float delta = fmaf(-gt, a, vt) * bt;
+            const float yo = fmaf(gt, c, delta * kq);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s[i] = fmaf(delta, kk[i], gt * s[i]);
+            if (j == 0 && ok) y[yi] = (uint16_t)f32_to_bf16(yo);
+        } else if (j == 0 && ok) {
+            y[yi] = 0;                        // masked step: state kept, y = 0
+        }
+        if (ok) store_row<DK>(state_out + srow, s, j);
+    }
+}
+
+bool decode_fusable(int B, int Hk, int Hv, int Dk, int Dv, int K) {
+    (void)B;
+    return (Dk == 32 || Dk == 64 || Dk == 128 || Dk == 256) && K >= 2 && K <= 4 &&
+           (int64_t)(Hv / Hk) * Dv <= kDecMaxRows && (int64_t)B * Hk >= 256;
+}
+
+template <int DK>
+static hipError_t launch_decode_k(const PrepArgs& p, const uint8_t* mask, const float* si, float* so, uint16_t* y,
+                                  hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)p.B * p.Hk));
+    switch (p.K) {
+        case 2: hipLaunchKernelGGL((decode_core_kernel<DK, 2>), grid, dim3(DEC_NT), 0, stream, p, mask, si, so, y); break;
+        case 3: hipLaunchKernelGGL((decode_core_kernel<DK, 3>), grid, dim3(DEC_NT), 0, stream, p, mask, si, so, y); break;
+        case 4: hipLaunchKernelGGL((decode_core_kernel<DK, 4>), grid, dim3(DEC_NT), 0, stream, p, mask, si, so, y); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_core(const PrepArgs& p, const uint8_t* mask, const float* state_in, float* state_out,
+                              uint16_t* y, hipStream_t stream) {
+    if (p.T != 1 || !decode_fusable(p.B, p.Hk, p.Hv, p.Dk, p.Dv, p.K)) return hipErrorInvalidValue;
+    switch (p.Dk) {
+        case 32: return launch_decode_k<32>(p, mask, state_in, state_out, y, stream);
+        case 64: return launch_decode_k<64>(p, mask, state_in, state_out, y, stream);
+        case 128: return launch_decode_k<128>(p, mask, state_in, state_out, y, stream);
+        case 256: return launch_decode_k<256>(p, mask, state_in, state_out, y, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 // ================================================================== launch
 
 int64_t recurrent_blocks(int B, int Hv, int Dk, int Dv) {

@@ -392,6 +392,39 @@ def test_layer_core_conv_state_in_place(shape):
     assert np.array_equal(y, y2) and np.array_equal(s, s2) and np.array_equal(cs, cs2)
 
 
+DECODE_CASES = [
+    # B, Hk, Hv, Dk, Dv, K, masked, conv state in place, wid
+    (64, 16, 32, 128, 128, 4, False, True, 330),      # the batched-decode workload
+    (128, 2, 4, 64, 32, 3, True, False, 331),
+    (256, 1, 4, 256, 48, 2, True, True, 332),         # four v-heads per k-head, Dv not a multiple of 32
+    (32, 8, 8, 32, 16, 4, False, False, 333),         # one v-head per k-head
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "B%dHk%dHv%dDk%dDv%dK%d-m%dip%d" % c[:8])
+def test_layer_core_single_token_decode(case):
+    """Single-token decode of a large batch (one launch: prologue and step per
+    (b, k-head) block) equals the prologue followed by the per-step
+    recurrence bit for bit, with masks and the conv state in place, and the
+    oracle within the tolerances."""
+    B, Hk, Hv, Dk, Dv, K, masked, ip, wid = case
+    say("layer_core decode", case)
+    raw = layer_inputs(B, 1, Hk, Hv, Dk, Dv, K, wid)
+    qs, ks = 1.0 / Dk, Dk ** -0.5
+    mask = step_mask(wid, B, 1, p=0.6) if masked else None
+    y, s, cs = gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks, mask=mask, cs_in_place=ip)
+    p = gpu_prep(raw, Hk, Hv, Dk, Dv, qs, ks)
+    ri = dict(q=p["q"], k=p["k"], v=p["v"], g=p["g"], beta=p["beta"], state=raw["state"])
+    y2, s2 = gpu_recurrent(ri, mask=mask)
+    assert np.array_equal(y, y2) and np.array_equal(s, s2) and np.array_equal(cs, p["conv_state"])
+    y_ref, s_ref, cs_ref = oracle.layer_core(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
+                                             raw["A_log"], raw["dt_bias"], raw["state"], Hk=Hk, Hv=Hv, Dk=Dk,
+                                             Dv=Dv, q_scale=qs, k_scale=ks, mask=mask)
+    H.check_y(y, y_ref, str(case))
+    H.check_state(s, s_ref, CORE_STATE_TOL, str(case))
+    assert np.array_equal(cs, cs_ref)
+
+
 def test_prefill_workload_full_size_sampled():
     """The T=4096 prefill workload at full size; four v-heads recomputed by the
     oracle end to end (all rows), plus the whole prologue output."""
