@@ -628,7 +628,6 @@ __global__ __launch_bounds__(DEC_NT) void decode_core_kernel(PrepArgs p, const u
 }
 
 bool decode_fusable(int B, int Hk, int Hv, int Dk, int Dv, int K) {
-    (void)B;
     return (Dk == 32 || Dk == 64 || Dk == 128 || Dk == 256) && K >= 2 && K <= 4 &&
            (int64_t)(Hv / Hk) * Dv <= kDecMaxRows && (int64_t)B * Hk >= 256;
 }
