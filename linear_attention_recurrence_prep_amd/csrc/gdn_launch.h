@@ -57,9 +57,9 @@ int64_t prep_blocks(int B, int T, int Hk, int Hv, int Dk, int Dv);
 hipError_t launch_recurrent(const RecurrentArgs& a, hipStream_t stream);
 
 // The layer core at T = 1 in one launch (prologue and step per (b, k-head)
-// block; the bits of launch_prep followed by launch_recurrent).  For batches
-// of at least 256 (b, k-head) pairs, (Hv / Hk) * Dv <= 1024, K in {2, 3, 4};
-// the conv state may be updated in place.
+// block; the bits of launch_prep followed by launch_recurrent).  For one to
+// four (b, k-head) pairs per CU, (Hv / Hk) * Dv <= 1024, K in {2, 3, 4}; the
+// conv state may be updated in place.
 bool decode_fusable(int B, int Hk, int Hv, int Dk, int Dv, int K);
 hipError_t launch_decode_core(const PrepArgs& p, const uint8_t* mask, const float* state_in, float* state_out,
                               uint16_t* y, hipStream_t stream);

@@ -627,9 +627,15 @@ __global__ __launch_bounds__(DEC_NT) void decode_core_kernel(PrepArgs p, const u
     }
 }
 
+// The fused form pays while its (b, k-head) blocks fill the device in one
+// round (four 512-thread blocks per CU): below that too few CUs stream the
+// state, above it the blocks' serial row passes fall behind the per-step
+// kernel's finer grid.  Both forms give the same bits, so the choice may
+// depend on the device.
 bool decode_fusable(int B, int Hk, int Hv, int Dk, int Dv, int K) {
+    const int64_t cus = device_cu_count(), blocks = (int64_t)B * Hk;
     return (Dk == 32 || Dk == 64 || Dk == 128 || Dk == 256) && K >= 2 && K <= 4 &&
-           (int64_t)(Hv / Hk) * Dv <= kDecMaxRows && (int64_t)B * Hk >= 256;
+           (int64_t)(Hv / Hk) * Dv <= kDecMaxRows && cus > 0 && blocks >= cus && blocks <= 4 * cus;
 }
 
 template <int DK>
