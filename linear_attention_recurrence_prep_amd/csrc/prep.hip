@@ -10,10 +10,21 @@
 // A 64-lane wave covers 512 channels; q/k heads (Dk channels = Dk/8 lanes)
 // are aligned lane groups, so the per-head sum of squares is a DPP butterfly.
 // Gates (g, beta) are computed by extra blocks of the same launch.
+// q/k/v are written with non-temporal stores: each is written once and not
+// read again by this kernel, and streaming them past the caches' normal
+// retention measured faster both alone and followed by the recurrence.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
+
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+
+// one 16-byte vector store with the non-temporal hint (a global_store ... nt)
+__device__ __forceinline__ void store_stream16(uint16_t* dst, const uint4 v) {
+    const u32x4_nt x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_nt*>(dst));
+}
 
 constexpr int PREP_NT = 256;   // threads per block: 2048 channels
 constexpr int PREP_TT = 16;    // tokens per thread
@@ -133,9 +144,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int 
         const int64_t tok = (int64_t)b * T + t;
         if (region < 2) {
             uint16_t* dst = region == 0 ? p.q + tok * HKDK + c0 : p.k + tok * HKDK + (c0 - HKDK);
-            *reinterpret_cast<uint4*>(dst) = qk;
+            store_stream16(dst, qk);
         } else {
-            *reinterpret_cast<uint4*>(p.v + tok * Hv * Dv + (c0 - 2 * HKDK)) = pack8(act);
+            store_stream16(p.v + tok * Hv * Dv + (c0 - 2 * HKDK), pack8(act));
         }
     }
 }
