@@ -35,6 +35,16 @@ __device__ __forceinline__ float lane_group_sum(float x) {
 
 constexpr int kThreads = 256;
 
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+
+// One 16-byte store with the non-temporal hint (a global_store ... nt): the
+// output is written once and not read again here, and streaming it past the
+// caches' normal retention measured faster (plain loads stay faster for y, z).
+__device__ __forceinline__ void store_stream16(uint4* dst, const uint4 v) {
+    const u32x4_nt x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<u32x4_nt*>(dst));
+}
+
 // y, z, out: 16-byte vectors of the [rows, Dv] arrays (nvec = Dv / 8 per
 // row).  out may be y or z itself: every lane reads all of its values before
 // it writes any, and writes only the positions it read.
@@ -79,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void gated_rmsnorm_kernel(const uint4* y,
         unpack8(wv[i], wf);
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = silu_fast(zf[e]) * (yf[i][e] * r * wf[e]);
-        out[row * nvec + lane_in_row + i * L] = pack8(o);
+        store_stream16(out + row * nvec + lane_in_row + i * L, pack8(o));
     }
 }
 
