@@ -172,10 +172,17 @@ gdn_status gdn_prep(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
                     float q_scale, float k_scale, float eps, void *stream);
 
 /*
- * Bytes of device workspace gdn_layer_core needs for these sizes: the bf16
- * q, k, v and f32 g, beta of the prologue, plus the chunked recurrence's
- * workspace when that form is used (see gdn_layer_core); each part 256-byte
- * aligned.  Returns 0 for invalid sizes (and when B*T == 0).
+ * Bytes of device workspace gdn_layer_core needs for these sizes, sized to
+ * the path the call takes (see gdn_layer_core):
+ *   - chunked form with Dv <= 128: the chunked recurrence's workspace only
+ *     (the prologue runs inside the chunk preparation; its q, k, v, g, beta
+ *     never reach memory);
+ *   - chunked form with Dv > 128: the bf16 q, k, v and f32 g, beta of the
+ *     prologue, then the chunked recurrence's workspace;
+ *   - per-step form: the prologue's q, k, v, g, beta only.
+ * Each part is 256-byte aligned.  Returns 0 for invalid sizes (and when
+ * B*T == 0).  The same for every conv kernel size K and every aliasing of
+ * the conv state.
  */
 size_t gdn_layer_core_workspace_bytes(int B, int T, int Hk, int Hv, int Dk, int Dv);
 

@@ -1313,14 +1313,7 @@ int64_t chunked_blocks(int B, int T, int Hv, int Dv) {
     return std::max<int64_t>((int64_t)B * Hv * NC, (int64_t)B * Hv * (Dv / RB));
 }
 
-// An in-place conv state is read and rewritten by the same lane of the chunk-0
-// block that owns the channel; that is race-free when no other block reads
-// the channel, i.e. when one preparation block serves each k-head (Hv / Hk
-// of 1 or 2).
-bool layer_chunked_fusable(int Hk, int Hv, int Dv, int K, const void* conv_state_in, const void* conv_state_out) {
-    const bool in_place = conv_state_out != nullptr && conv_state_out == conv_state_in;
-    return Dv <= 128 && K >= 2 && K <= 4 && (!in_place || Hv / Hk <= 2);
-}
+bool layer_chunked_fusable(int Dv, int K) { return Dv <= 128 && K >= 2 && K <= 4; }
 
 static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, int K, void* ws,
                                  hipStream_t stream);
@@ -1329,9 +1322,22 @@ hipError_t launch_recurrent_chunked(const RecurrentArgs& a, void* ws, hipStream_
     return launch_chunked(a, nullptr, 0, ws, stream);
 }
 
+// An in-place conv state is read and rewritten by the same lane of the chunk-0
+// block that owns the channel; that is race-free when no other block reads
+// the channel, i.e. when one preparation block serves each k-head (Hv / Hk
+// of 1 or 2).  Otherwise the preparation leaves the conv state alone and a
+// copy after it writes the new one (its rows are the last K - 1 tokens).
 hipError_t launch_layer_chunked(const RecurrentArgs& a, const PrologueIn& p, int K, void* ws, hipStream_t stream) {
-    if (!layer_chunked_fusable(a.Hk, a.Hv, a.Dv, K, p.conv_state_in, p.conv_state_out)) return hipErrorInvalidValue;
-    return launch_chunked(a, &p, K, ws, stream);
+    if (!layer_chunked_fusable(a.Dv, K)) return hipErrorInvalidValue;
+    const bool in_place = p.conv_state_out != nullptr && p.conv_state_out == p.conv_state_in;
+    if (!in_place || a.Hv / a.Hk <= 2) return launch_chunked(a, &p, K, ws, stream);
+    if (a.T < K - 1) return hipErrorInvalidValue;
+    PrologueIn pn = p;
+    pn.conv_state_out = nullptr;
+    const hipError_t e = launch_chunked(a, &pn, K, ws, stream);
+    if (e != hipSuccess) return e;
+    const int C = 2 * a.Hk * a.Dk + a.Hv * a.Dv;
+    return launch_conv_tail(p.qkv, p.conv_state_out, a.B, a.T, C, K, stream);
 }
 
 // The current device's CU count, looked up once per device (0 if unknown).

@@ -104,7 +104,8 @@ gdn_status validate_recurrent(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf
                               const float* beta, const uint8_t* mask, const float* state_in, float* state_out,
                               gdn_bf16* y, int B, int T, int Hk, int Hv, int Dk, int Dv,
                               bool check_overlap = true, bool g_per_key = false,
-                              const float* snapshots = nullptr, uint64_t snapshot_bytes = 0) {
+                              const float* snapshots = nullptr, uint64_t snapshot_bytes = 0,
+                              bool need_inputs = true) {
     gdn_status st = check_dims(B, T, Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
     uint64_t nqk, nv, ng, ns, ngate;
@@ -114,11 +115,13 @@ gdn_status validate_recurrent(const gdn_bf16* q, const gdn_bf16* k, const gdn_bf
     if (gdn::recurrent_blocks(B, Hv, Dk, Dv) > kMaxBlocks) return fail(GDN_ERR_BAD_DIMS, "grid too large");
     if (B > 0 && !state_out) return fail(GDN_ERR_NULL_POINTER, "state_out is NULL");
     if ((int64_t)B * T > 0) {
-        if (!q) return fail(GDN_ERR_NULL_POINTER, "q is NULL");
-        if (!k) return fail(GDN_ERR_NULL_POINTER, "k is NULL");
-        if (!v) return fail(GDN_ERR_NULL_POINTER, "v is NULL");
-        if (!g) return fail(GDN_ERR_NULL_POINTER, "g is NULL");
-        if (!beta) return fail(GDN_ERR_NULL_POINTER, "beta is NULL");
+        if (need_inputs) {
+            if (!q) return fail(GDN_ERR_NULL_POINTER, "q is NULL");
+            if (!k) return fail(GDN_ERR_NULL_POINTER, "k is NULL");
+            if (!v) return fail(GDN_ERR_NULL_POINTER, "v is NULL");
+            if (!g) return fail(GDN_ERR_NULL_POINTER, "g is NULL");
+            if (!beta) return fail(GDN_ERR_NULL_POINTER, "beta is NULL");
+        }
         if (!y) return fail(GDN_ERR_NULL_POINTER, "y is NULL");
     }
     if (!check_overlap) return GDN_OK;
@@ -165,7 +168,7 @@ gdn_status validate_prep(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_
                          gdn_bf16* conv_state_out, const gdn_bf16* a, const gdn_bf16* b, const float* A_log,
                          const float* dt_bias, gdn_bf16* q, gdn_bf16* k, gdn_bf16* v, float* g, float* beta,
                          int B, int T, int Hk, int Hv, int Dk, int Dv, int K, float q_scale, float k_scale,
-                         float eps, bool check_overlap = true) {
+                         float eps, bool check_overlap = true, bool need_outputs = true) {
     gdn_status st = check_dims(B, T, Hk, Hv, Dk, Dv);
     if (st != GDN_OK) return st;
     if (K < 2 || K > 4) return fail(GDN_ERR_UNSUPPORTED, "K=%d not in {2, 3, 4}", K);
@@ -186,6 +189,8 @@ gdn_status validate_prep(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_
         if (!b) return fail(GDN_ERR_NULL_POINTER, "b is NULL");
         if (!A_log) return fail(GDN_ERR_NULL_POINTER, "A_log is NULL");
         if (!dt_bias) return fail(GDN_ERR_NULL_POINTER, "dt_bias is NULL");
+    }
+    if ((int64_t)B * T > 0 && need_outputs) {
         if (!q) return fail(GDN_ERR_NULL_POINTER, "q is NULL");
         if (!k) return fail(GDN_ERR_NULL_POINTER, "k is NULL");
         if (!v) return fail(GDN_ERR_NULL_POINTER, "v is NULL");
@@ -216,6 +221,7 @@ gdn_status validate_prep(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_
 struct Workspace {
     uint64_t q, k, v, g, beta, chunked, total;
     bool use_chunked;
+    bool fused;      // chunked with the prologue inside its preparation: no q/k/v/g/beta region
 };
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -233,16 +239,23 @@ bool layer_uses_chunked(int B, int T, int Hv, int Dk, int Dv) {
     return T >= 64 || (T > 32 && tiles >= 2048) || (T > 16 && tiles >= 4096);
 }
 
+// The layer core's workspace: the prologue's q, k, v (bf16) and g, beta (f32)
+// when they pass through memory, then the chunked recurrence's part when that
+// form is used.  With the chunked form and Dv <= 128 the prologue runs inside
+// the chunk preparation for every aliasing of the conv state, so the first
+// part is absent.
 bool workspace_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, Workspace& w) {
     uint64_t nqk, nv, ng;
     if (!elems(nqk, {B, T, Hk, Dk}) || !elems(nv, {B, T, Hv, Dv}) || !elems(ng, {B, T, Hv})) return false;
+    w.use_chunked = B > 0 && layer_uses_chunked(B, T, Hv, Dk, Dv);
+    w.fused = w.use_chunked && gdn::layer_chunked_fusable(Dv, 4);
+    if (w.fused) nqk = nv = ng = 0;
     w.q = 0;
     w.k = w.q + align256(nqk * 2);
     w.v = w.k + align256(nqk * 2);
     w.g = w.v + align256(nv * 2);
     w.beta = w.g + align256(ng * 4);
     w.chunked = w.beta + align256(ng * 4);
-    w.use_chunked = B > 0 && layer_uses_chunked(B, T, Hv, Dk, Dv);
     w.total = w.chunked + (w.use_chunked ? gdn::chunked_layout(B, T, Hk, Hv, Dk, Dv).total : 0);
     if ((int64_t)B * T == 0) w.total = 0;
     return true;
@@ -464,18 +477,21 @@ static gdn_status layer_core_impl(const gdn_bf16* qkv, const gdn_bf16* conv_w, c
             return fail(GDN_ERR_MISALIGNED, "workspace is not 256-byte aligned");
     }
     char* ws = static_cast<char*>(workspace);
-    gdn_bf16* wq = w.total ? reinterpret_cast<gdn_bf16*>(ws + w.q) : nullptr;
-    gdn_bf16* wk = w.total ? reinterpret_cast<gdn_bf16*>(ws + w.k) : nullptr;
-    gdn_bf16* wv = w.total ? reinterpret_cast<gdn_bf16*>(ws + w.v) : nullptr;
-    float* wg = w.total ? reinterpret_cast<float*>(ws + w.g) : nullptr;
-    float* wb = w.total ? reinterpret_cast<float*>(ws + w.beta) : nullptr;
+    const bool staged = w.total && !w.fused;     // prologue outputs pass through the workspace
+    gdn_bf16* wq = staged ? reinterpret_cast<gdn_bf16*>(ws + w.q) : nullptr;
+    gdn_bf16* wk = staged ? reinterpret_cast<gdn_bf16*>(ws + w.k) : nullptr;
+    gdn_bf16* wv = staged ? reinterpret_cast<gdn_bf16*>(ws + w.v) : nullptr;
+    float* wg = staged ? reinterpret_cast<float*>(ws + w.g) : nullptr;
+    float* wb = staged ? reinterpret_cast<float*>(ws + w.beta) : nullptr;
 
-    // the prologue half (its outputs are the workspace; overlap of the user
-    // buffers is checked below across both halves)
+    // the prologue half (its outputs are the workspace, or registers and LDS
+    // when fused; overlap of the user buffers is checked below across both
+    // halves)
     st = validate_prep(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, wq, wk, wv, wg, wb, B, T,
-                       Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps, false);
+                       Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps, false, !w.fused);
     if (st != GDN_OK) return st;
-    st = validate_recurrent(wq, wk, wv, wg, wb, mask, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, false);
+    st = validate_recurrent(wq, wk, wv, wg, wb, mask, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, false, false,
+                            nullptr, 0, !w.fused);
     if (st != GDN_OK) return st;
     if (gated) {
         st = validate_gated(y, z, norm_weight, y, B, T, Hv, Dv, norm_eps, false);
@@ -514,7 +530,7 @@ static gdn_status layer_core_impl(const gdn_bf16* qkv, const gdn_bf16* conv_w, c
     if (B == 0) return ok();
     hipStream_t s = static_cast<hipStream_t>(stream);
     gdn::RecurrentArgs r{wq, wk, wv, wg, wb, state_in, state_out, y, B, T, Hk, Hv, Dk, Dv, mask};
-    if (w.use_chunked && gdn::layer_chunked_fusable(Hk, Hv, Dv, K, conv_state_in, conv_state_out)) {
+    if (w.fused) {
         // the prologue runs inside the chunk preparation (same arithmetic, same bits)
         const gdn::PrologueIn p{qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias,
                                 q_scale, k_scale, eps};

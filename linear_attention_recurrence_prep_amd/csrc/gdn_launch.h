@@ -88,7 +88,7 @@ struct PrologueIn {
     const uint16_t* qkv;
     const uint16_t* conv_w;
     const uint16_t* conv_state_in;   // may be null (zeros)
-    uint16_t* conv_state_out;        // may be null; conv_state_in itself only if Hv / Hk <= 2
+    uint16_t* conv_state_out;        // may be null, or conv_state_in itself
     const uint16_t* a;
     const uint16_t* b;
     const float* A_log;
@@ -98,13 +98,20 @@ struct PrologueIn {
 
 // The layer core's chunked recurrence with the prologue fused into the chunk
 // preparation: q, k, v, g, beta of RecurrentArgs are not read (computed from
-// p), conv_state_out is written.  Needs Dv <= 128, K in {2, 3, 4} and, for
-// an in-place conv state, Hv / Hk <= 2; the result is bit-identical to
-// launch_prep followed by launch_recurrent_chunked.
-bool layer_chunked_fusable(int Hk, int Hv, int Dv, int K, const void* conv_state_in, const void* conv_state_out);
+// p), conv_state_out is written.  Needs Dv <= 128 and K in {2, 3, 4}; the
+// result is bit-identical to launch_prep followed by launch_recurrent_chunked.
+// An in-place conv state with Hv / Hk > 2 (several preparation blocks read a
+// k-head's old conv state) is written by a separate copy after the
+// preparation, which needs T >= K - 1 (always true where the layer core
+// takes the chunked form).
+bool layer_chunked_fusable(int Dv, int K);
 hipError_t launch_layer_chunked(const RecurrentArgs& a, const PrologueIn& p, int K, void* workspace,
                                 hipStream_t stream);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
+// conv_state_out = the last K - 1 tokens of qkv (needs T >= K - 1); stream
+// ordered after the launches that read conv_state_in, so in place is safe.
+hipError_t launch_conv_tail(const uint16_t* qkv, uint16_t* conv_state_out, int B, int T, int C, int K,
+                            hipStream_t stream);
 
 // Output epilogue: out = bf16(silu(z) * rms_norm(y) * w) per row of Dv
 // values (Dv a multiple of 8); out may alias y or z exactly.

@@ -151,6 +151,31 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int 
     }
 }
 
+// The new conv state alone, for T >= K - 1: its K - 1 rows are the last
+// K - 1 tokens of qkv, copied one 16-byte vector per thread.  Launched after
+// every reader of the old conv state has finished (stream order), so the
+// state may be updated in place.
+__global__ __launch_bounds__(256) void conv_tail_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ out,
+                                                         int T, int C, int K, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t c8n = C / 8, per_b = (int64_t)(K - 1) * c8n;
+    const int64_t b = i / per_b, r = i % per_b;
+    const int64_t row = r / c8n, c8 = r % c8n;
+    const uint4 v = *reinterpret_cast<const uint4*>(qkv + ((b * T + T - (K - 1) + row) * C + 8 * c8));
+    *reinterpret_cast<uint4*>(out + ((b * (K - 1) + row) * C + 8 * c8)) = v;
+}
+
+hipError_t launch_conv_tail(const uint16_t* qkv, uint16_t* conv_state_out, int B, int T, int C, int K,
+                            hipStream_t stream) {
+    if (T < K - 1 || C % 8 != 0 || K < 2) return hipErrorInvalidValue;
+    const int64_t n = (int64_t)B * (K - 1) * (C / 8);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(conv_tail_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, qkv,
+                       conv_state_out, T, C, K, n);
+    return hipGetLastError();
+}
+
 static void prep_grid(int B, int T, int Hk, int Hv, int Dk, int Dv, int& c_tiles, int& t_chunks,
                       int64_t& conv_blocks, int64_t& gate_blocks) {
     const int64_t C = 2LL * Hk * Dk + (int64_t)Hv * Dv;

@@ -41,18 +41,53 @@ def bf16_ulp(x):
     return np.exp2(e - 7)
 
 
-def check_y(y_bits, y_ref, label=""):
-    """y within 1 bf16 ulp of the fp64 value plus 1e-3 absolute."""
+# y against the fp64 reference, per (b, v-head).  Beside the stated bound
+# (1 bf16 ulp + 1e-3 absolute), which does not bind where |y| is far below
+# 1e-3, two bounds that do:
+#   |dy| <= ulp(y_ref) + Y_HEAD_TOL * max|y_ref| over the head, elementwise;
+#   at most 1 ulp from y_ref where |y_ref| >= Y_ULP_FLOOR * max|y_ref|.
+# The device rounds an f32 value to bf16 (half an ulp) whose own error is a
+# few units of 2^-16 (chunked form: the leading two planes of the y path) or
+# of 2^-24 * Dk (per-step form) times the size of the terms, which are of the
+# order of the head's largest outputs; so Y_HEAD_TOL leaves a margin of 16
+# over the chunked form's truncation, and above Y_ULP_FLOOR the pre-rounding
+# error is below a quarter of an ulp.  y = 0, or a 1 % error in any output
+# above 2^-5 of its head's largest, fails both.
+Y_HEAD_TOL = 2.0 ** -12
+Y_ULP_FLOOR = 2.0 ** -4
+
+
+def _head_max(y_ref):
+    """max |y_ref| per (b, v-head) of a [B, T, Hv, Dv] array, broadcastable."""
+    return np.abs(y_ref).max(axis=(1, 3), keepdims=True) if y_ref.size else np.zeros((1, 1, 1, 1))
+
+
+def check_y(y_bits, y_ref, label="", strict=True):
+    """y (bf16 bits [B,T,Hv,Dv]) against the fp64 reference.  Always: within 1
+    bf16 ulp + 1e-3 absolute.  strict: also the per-head bounds above (the
+    reference must then be the recurrence on the very inputs the device used).
+    Returns the observed figures."""
     y = oracle.bf16_to_f64(y_bits)
-    err = np.abs(y - y_ref)
-    tol = bf16_ulp(y_ref) + 1e-3
-    bad = err > tol
-    ulps = err / bf16_ulp(y_ref)
     assert not np.isnan(y).any(), f"{label}: NaN in y"
-    assert not bad.any(), (f"{label}: {bad.sum()} y elements out of tolerance; worst err "
+    err = np.abs(y - y_ref)
+    ulp = bf16_ulp(y_ref)
+    bad = err > ulp + 1e-3
+    assert not bad.any(), (f"{label}: {bad.sum()} y elements beyond 1 ulp + 1e-3; worst err "
                            f"{err.max():.3e}")
-    return dict(max_abs=float(err.max()) if err.size else 0.0,
-                max_ulp=float(ulps.max()) if err.size else 0.0)
+    out = dict(max_abs=float(err.max()) if err.size else 0.0,
+               max_ulp=float((err / ulp).max()) if err.size else 0.0)
+    if not strict or not err.size:
+        return out
+    hm = _head_max(y_ref)
+    rel = err / np.maximum(hm, 1e-300)
+    bad = err > ulp + Y_HEAD_TOL * hm
+    assert not bad.any(), (f"{label}: {bad.sum()} y elements beyond 1 ulp + 2^-12 of the head's largest; "
+                           f"worst {rel.max():.3e} of it")
+    big = np.abs(y_ref) >= Y_ULP_FLOOR * hm
+    ulps_big = float((err / ulp)[big].max()) if big.any() else 0.0
+    assert ulps_big <= 1.0, f"{label}: y {ulps_big:.2f} ulp from the reference where |y| >= 2^-4 of its head's max"
+    out.update(head_rel=float(rel.max()), max_ulp_big=ulps_big)
+    return out
 
 
 def state_err(s_gpu, s_ref):

@@ -134,24 +134,33 @@ def chunked_expect(B, T, Hk, Hv, Dk, Dv):
 
 
 def test_workspace_bytes(L):
+    """Sized to the path the layer core takes: the chunked form with Dv <= 128
+    runs the prologue inside its preparation, so only the chunked part is
+    needed; the chunked form with wider value heads and the per-step form pass
+    q, k, v, g, beta through the workspace."""
     f = L.gdn_layer_core_workspace_bytes
     up = lambda x: (x + 255) // 256 * 256
     B, T, Hk, Hv, Dk, Dv = 1, 4096, 16, 32, 128, 128
-    prep_part = 2 * up(B * T * Hk * Dk * 2) + up(B * T * Hv * Dv * 2) + 2 * up(B * T * Hv * 4)
-    # Dk = 128, Dv % 16 == 0, T >= 64: the layer core adds the chunked recurrence's part
-    assert f(B, T, Hk, Hv, Dk, Dv) == prep_part + chunked_expect(B, T, Hk, Hv, Dk, Dv)
+    pp = lambda B, T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv: (2 * up(B * T * Hk * Dk * 2) + up(B * T * Hv * Dv * 2)
+                                                 + 2 * up(B * T * Hv * 4))
+    # Dk = 128, Dv <= 128, T >= 64: fused chunked form, the chunked part only
+    assert f(B, T, Hk, Hv, Dk, Dv) == chunked_expect(B, T, Hk, Hv, Dk, Dv)
     assert L.gdn_recurrent_chunked_workspace_bytes(B, T, Hk, Hv, Dk, Dv) == chunked_expect(B, T, Hk, Hv, Dk, Dv)
+    assert f(4, 32768, Hk, Hv, Dk, Dv) == chunked_expect(4, 32768, Hk, Hv, Dk, Dv)
+    # GQA group of 4 (an in-place conv state then takes a separate conv-state copy): still fused
+    assert f(1, 100, 2, 8, 128, 64) == chunked_expect(1, 100, 2, 8, 128, 64)
+    # wider value heads: the chunked form after a separate prologue
+    assert f(1, 100, 2, 4, 128, 256) == pp(1, 100, 2, 4, 128, 256) + chunked_expect(1, 100, 2, 4, 128, 256)
     # short sequences and other head sizes use the per-step kernels: prologue part only
     T2 = 63
-    assert f(B, T2, Hk, Hv, Dk, Dv) == 2 * up(T2 * Hk * Dk * 2) + up(T2 * Hv * Dv * 2) + 2 * up(T2 * Hv * 4)
+    assert f(B, T2, Hk, Hv, Dk, Dv) == pp(B, T2)
     assert f(2, 100, 2, 4, 64, 32) == 2 * up(200 * 2 * 64 * 2) + up(200 * 4 * 32 * 2) + 2 * up(200 * 4 * 4)
     assert L.gdn_recurrent_chunked_workspace_bytes(1, 100, 2, 4, 64, 32) == 0     # unsupported Dk
     assert L.gdn_recurrent_chunked_workspace_bytes(1, 100, 2, 4, 128, 24) == 0    # Dv % 16 != 0
     assert f(1, 0, 16, 32, 128, 128) == 0
     # shorter sequences take the chunked form once the batch is large
-    pp = lambda B, T: 2 * up(B * T * Hk * Dk * 2) + up(B * T * Hv * Dv * 2) + 2 * up(B * T * Hv * 4)
-    assert f(16, 24, Hk, Hv, Dk, Dv) == pp(16, 24) + chunked_expect(16, 24, Hk, Hv, Dk, Dv)   # 4096 tiles, T > 16
-    assert f(8, 40, Hk, Hv, Dk, Dv) == pp(8, 40) + chunked_expect(8, 40, Hk, Hv, Dk, Dv)      # 2048 tiles, T > 32
+    assert f(16, 24, Hk, Hv, Dk, Dv) == chunked_expect(16, 24, Hk, Hv, Dk, Dv)   # 4096 tiles, T > 16
+    assert f(8, 40, Hk, Hv, Dk, Dv) == chunked_expect(8, 40, Hk, Hv, Dk, Dv)     # 2048 tiles, T > 32
     assert f(8, 32, Hk, Hv, Dk, Dv) == pp(8, 32)
     assert f(4, 48, Hk, Hv, Dk, Dv) == pp(4, 48)
     assert f(64, 16, Hk, Hv, Dk, Dv) == pp(64, 16)
@@ -361,3 +370,4 @@ def test_bind_rejects_non_library_calls():
     from linear_attention_recurrence_prep_amd import binding
     with pytest.raises(TypeError):
         binding.bind(len, [1, 2])
+

@@ -12,7 +12,7 @@ import torch
 import oracle
 from linear_attention_recurrence_prep_amd import binding, inputs
 from tests import helpers as H
-from tests.test_parity_gpu import gpu_layer_core, layer_inputs
+from tests.test_parity_gpu import gpu_layer_core, gpu_prep, layer_inputs, oracle_on_gpu_prologue
 
 pytestmark = pytest.mark.gpu
 
@@ -174,13 +174,17 @@ def test_layer_core_gated_matches_oracle_and_composition(T):
     y2, s2, cs2 = gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks, mask=mask)
     out2 = gpu_gated(y2, gate["z"], gate["norm_weight"], 1e-6)
     assert np.array_equal(out, out2) and np.array_equal(s, s2) and np.array_equal(cs, cs2)
-    # the oracle's composition
-    y_ref, s_ref, _ = oracle.layer_core(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
-                                        raw["A_log"], raw["dt_bias"], raw["state"], Hk=Hk, Hv=Hv, Dk=Dk,
-                                        Dv=Dv, q_scale=qs, k_scale=ks, mask=mask)
+    # the oracle's composition: its recurrence on the device's prologue
+    # outputs (state 1e-4), its layer core then the epilogue (output within
+    # the bound y's tolerance implies)
+    p = gpu_prep(raw, Hk, Hv, Dk, Dv, qs, ks)
+    _, s_r = oracle_on_gpu_prologue(p, raw["state"], mask)
+    e = H.check_state(s, s_r, 1e-4, f"T={T}")
+    y_ref, _, _ = oracle.layer_core(raw["qkv"], raw["conv_w"], raw["conv_state"], raw["a"], raw["b"],
+                                    raw["A_log"], raw["dt_bias"], raw["state"], Hk=Hk, Hv=Hv, Dk=Dk,
+                                    Dv=Dv, q_scale=qs, k_scale=ks, mask=mask)
     worst = check_end_to_end(out, y_ref, gate, 1e-6)
-    say("gated layer core: worst error / bound", worst)
-    H.check_state(s, s_ref, 2.0 ** -8, f"T={T}")
+    say("gated layer core: worst error / bound", worst, "state err", e)
 
 
 def test_layer_core_gated_prefill_workload_sampled_heads():

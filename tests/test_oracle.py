@@ -738,3 +738,99 @@ def test_snapshots_are_prefix_states():
     # the state after 3 steps, carried into the remaining 5, reproduces the run
     _, s_rest = oracle.recurrent(q[:, 3:], k[:, 3:], v[:, 3:], g[:, 3:], beta[:, 3:], snaps[1])
     assert np.array_equal(s_rest, s_full)
+
+
+# ------------------------------------------------- layer-core rounding points
+#
+# The layer core hands the recurrence the prologue's outputs in their stored
+# dtypes: q, k, v rounded once to bf16 (nearest even), g and beta to f32.  The
+# cases below are worked by hand so that every value is exact in fp64 and each
+# rounding point visibly moves the result.
+
+def bf16_bits_of(vals):
+    """bf16 bit patterns of values that are exactly bf16 (checked)."""
+    x = np.asarray(vals, dtype=np.float64)
+    h = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.bf16_to_f64(h), x), vals
+    return h
+
+
+def test_layer_core_rounds_q_k_v_to_bf16_hand_worked():
+    """B = T = Hk = Hv = 1, Dk = Dv = 2, K = 2, eps = 0, conv weights (1, 1)
+    on every channel.  Conv state row (0, 0, 0, 0, 3/8, 3/8), token row
+    (64, 64, 64, 64, 64, 96):
+      u = (64, 64 | 64, 64 | 64.375, 96.375), and silu(u) = u exactly in
+      fp64 (e^-64 is far below half an ulp of 1);
+      q_hat = 64 / sqrt((64^2 + 64^2) / 2) * q_scale = q_scale per channel:
+        q_scale = 1 + 2^-8 + 2^-10 rounds (bf16 spacing 2^-7 at 1, past its
+        half) to 1 + 2^-7;
+      k_hat = k_scale = 1/2 + 2^-9 + 2^-11 rounds (spacing 2^-8, past its
+        half) to 1/2 + 2^-8;
+      v = 64.375 -> 64.5 and 96.375 -> 96.5 (spacing 1/2 in [64, 128));
+      b = 0: beta = 1/2 exactly; the zero state makes g irrelevant at T = 1.
+    From S_0 = 0: delta = beta v, S = beta v k^T, y = S q, so with the rounded
+    values S[i][j] = 0.5 v_i k_r and y_i = 2 (0.5 v_i k_r) q_r."""
+    qs, ks = 1 + 2.0 ** -8 + 2.0 ** -10, 0.5 + 2.0 ** -9 + 2.0 ** -11
+    q_r, k_r, v_r = 1 + 2.0 ** -7, 0.5 + 2.0 ** -8, np.array([64.5, 96.5])
+    qkv = bf16_bits_of([64, 64, 64, 64, 64, 96]).reshape(1, 1, 6)
+    cs = bf16_bits_of([0, 0, 0, 0, 0.375, 0.375]).reshape(1, 1, 6)
+    w = bf16_bits_of(np.ones((6, 2)))
+    zero = bf16_bits_of([0.0]).reshape(1, 1, 1)
+    A_log, dt_bias = np.zeros(1, np.float32), np.zeros(1, np.float32)
+    y, s, cs_out = oracle.layer_core(qkv, w, cs, zero, zero, A_log, dt_bias, None, Hk=1, Hv=1, Dk=2, Dv=2,
+                                     q_scale=qs, k_scale=ks, eps=0.0)
+    s_hand = np.array([[0.5 * v_r[0] * k_r] * 2, [0.5 * v_r[1] * k_r] * 2])
+    y_hand = np.array([s_hand[0, 0] * q_r + s_hand[0, 1] * q_r, s_hand[1, 0] * q_r + s_hand[1, 1] * q_r])
+    assert np.array_equal(s[0, 0], s_hand)
+    assert np.array_equal(y[0, 0, 0], y_hand)
+    assert np.array_equal(cs_out, qkv)           # K - 1 = 1 row: the token itself
+    # each rounding moves the result: without it y would be this instead
+    for qq, kk, vv in ((qs, k_r, v_r), (q_r, ks, v_r), (q_r, k_r, np.array([64.375, 96.375]))):
+        y_unr = 2 * (0.5 * vv * kk) * qq
+        assert not np.array_equal(y_unr, y_hand)
+
+
+def test_layer_core_rounds_beta_to_f32():
+    """As the hand-worked case, with b = 0.69921875 (a bf16 value): beta =
+    sigmoid(b) is rounded to f32, so y_i = 2 (((v_i beta32) k_r) q_r) with
+    beta32 the f32 rounding of the prologue's beta; every product is exact
+    in fp64 (at most 8 + 24 + 8 + 8 significant bits)."""
+    qs, ks = 1 + 2.0 ** -8 + 2.0 ** -10, 0.5 + 2.0 ** -9 + 2.0 ** -11
+    q_r, k_r, v_r = 1 + 2.0 ** -7, 0.5 + 2.0 ** -8, np.array([64.5, 96.5])
+    qkv = bf16_bits_of([64, 64, 64, 64, 64, 96]).reshape(1, 1, 6)
+    cs = bf16_bits_of([0, 0, 0, 0, 0.375, 0.375]).reshape(1, 1, 6)
+    w = bf16_bits_of(np.ones((6, 2)))
+    a = bf16_bits_of([0.0]).reshape(1, 1, 1)
+    b = bf16_bits_of([0.69921875]).reshape(1, 1, 1)
+    A_log, dt_bias = np.zeros(1, np.float32), np.zeros(1, np.float32)
+    kw = dict(Hk=1, Hv=1, Dk=2, Dv=2, q_scale=qs, k_scale=ks, eps=0.0)
+    beta = oracle.prep(qkv, w, cs, a, b, A_log, dt_bias, **kw)["beta"][0, 0, 0]
+    beta32 = float(np.float32(beta))
+    assert beta32 != beta
+    y, _, _ = oracle.layer_core(qkv, w, cs, a, b, A_log, dt_bias, None, **kw)
+    assert np.array_equal(y[0, 0, 0], 2 * (((v_r * beta32) * k_r) * q_r))
+    assert not np.array_equal(y[0, 0, 0], 2 * (((v_r * beta) * k_r) * q_r))
+
+
+def test_layer_core_rounds_g_to_f32():
+    """beta = 0 (b = -1000: sigmoid underflows to 0 exactly) makes every
+    delta zero, so from a dyadic S_0 the state is S_0 decayed by each step's
+    gate in turn (closed form I6), with each gate the f32 rounding of the
+    prologue's g."""
+    T = 3
+    qkv = bf16_bits_of(np.tile([64, 64, 64, 64, 64, 96], (T, 1))).reshape(1, T, 6)
+    w = bf16_bits_of(np.ones((6, 2)))
+    a = bf16_bits_of([0.5, -1.25, 2.0]).reshape(1, T, 1)
+    b = bf16_bits_of([-1000.0] * T).reshape(1, T, 1)
+    A_log, dt_bias = np.array([1.0986123], np.float32), np.array([0.1], np.float32)
+    s0 = np.array([[[[1.0, -2.0], [0.5, 3.0]]]])
+    kw = dict(Hk=1, Hv=1, Dk=2, Dv=2, q_scale=0.5, k_scale=0.5, eps=0.0)
+    g = oracle.prep(qkv, w, None, a, b, A_log, dt_bias, **kw)["g"][0, :, 0]
+    assert not np.array_equal(g.astype(np.float32).astype(np.float64), g)
+    _, s, _ = oracle.layer_core(qkv, w, None, a, b, A_log, dt_bias, s0, **kw)
+    expect, unrounded = s0.copy(), s0.copy()
+    for t in range(T):
+        expect = expect * float(np.float32(g[t]))
+        unrounded = unrounded * g[t]
+    assert np.array_equal(s, expect)
+    assert not np.array_equal(s, unrounded)
