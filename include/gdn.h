@@ -342,6 +342,40 @@ gdn_status gdn_layer_core_gated(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
                                 float q_scale, float k_scale, float eps, float norm_eps,
                                 void *stream);
 
+/*
+ * gdn_layer_core_no_alloc -- gdn_layer_core_masked with no workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * allocates nothing and frees nothing; its workspace is a device array of
+ * GDN_NO_ALLOC_SCRATCH_BYTES that the library holds on each device where it
+ * runs, until the process ends.
+ *
+ * Arguments, results and rules are those of gdn_layer_core_masked (mask may
+ * be NULL); the results are bit-identical to that call with a caller
+ * workspace.  The caller still owns every input and output.
+ *   - Sizes whose workspace (gdn_layer_core_workspace_bytes) exceeds
+ *     GDN_NO_ALLOC_SCRATCH_BYTES return GDN_ERR_WORKSPACE before anything
+ *     else happens.  At Hk = 16, Hv = 32, Dk = Dv = 128 that is B*T above
+ *     about 2900 tokens on the chunked path.
+ *   - The first call on a device looks up that device's array (no launch,
+ *     no allocation by this library); a call with B == 0 does only that, so
+ *     it can be made once before a graph capture starts.
+ *   - Every call on a device shares that device's array and leaves its last
+ *     contents there (nothing in it needs to start at zero: each call writes
+ *     before it reads).  Calls that can overlap in time on one device -- on
+ *     different streams without ordering, or from several threads -- race
+ *     on the array and give undefined results; serialise them.
+ */
+#define GDN_NO_ALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+gdn_status gdn_layer_core_no_alloc(const gdn_bf16 *qkv, const gdn_bf16 *conv_w,
+                                   const gdn_bf16 *conv_state_in, gdn_bf16 *conv_state_out,
+                                   const gdn_bf16 *a, const gdn_bf16 *b,
+                                   const float *A_log, const float *dt_bias, const uint8_t *mask,
+                                   const float *state_in, float *state_out, gdn_bf16 *y,
+                                   int B, int T, int Hk, int Hv, int Dk, int Dv, int K,
+                                   float q_scale, float k_scale, float eps, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

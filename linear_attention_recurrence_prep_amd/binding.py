@@ -78,6 +78,8 @@ def lib():
         L.gdn_gated_rmsnorm.restype = _i
         L.gdn_layer_core_gated.argtypes = [_p] * 15 + [ctypes.c_size_t] + [_i] * 7 + [_f] * 4 + [_p]
         L.gdn_layer_core_gated.restype = _i
+        L.gdn_layer_core_no_alloc.argtypes = [_p] * 12 + [_i] * 7 + [_f] * 3 + [_p]
+        L.gdn_layer_core_no_alloc.restype = _i
         _lib = L
     return _lib
 
@@ -289,6 +291,39 @@ def layer_core(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias,
     m = _ptr(mask, "mask", _MASK, (B, T), dev)
     _invoke(lib().gdn_layer_core_masked, *args[:8], m, *args[8:], ws_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale,
             k_scale, eps, _stream(dev, stream))
+
+
+# workspace bytes held by the library for layer_core_no_alloc (the header's
+# GDN_NO_ALLOC_SCRATCH_BYTES)
+NO_ALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def layer_core_no_alloc(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias,
+                        state_in, state_out, y, *, Hk, Hv, Dk, Dv, q_scale, k_scale,
+                        eps=1e-6, mask=None, stream=None):
+    """The layer core with the library's own device scratch as its workspace
+    (gdn_layer_core_no_alloc): arguments as ``layer_core`` without
+    ``workspace``; sizes whose workspace exceeds NO_ALLOC_SCRATCH_BYTES raise.
+    Calls that can overlap in time on one device race on that scratch."""
+    B, T, C = qkv.shape
+    K = conv_w.shape[1]
+    dev = qkv.device
+    args = [
+        _ptr(qkv, "qkv", _BF16, (B, T, C), dev),
+        _ptr(conv_w, "conv_w", _BF16, (C, K), dev),
+        _ptr(conv_state_in, "conv_state_in", _BF16, (B, K - 1, C), dev),
+        _ptr(conv_state_out, "conv_state_out", _BF16, (B, K - 1, C), dev),
+        _ptr(a, "a", _BF16, (B, T, Hv), dev),
+        _ptr(b, "b", _BF16, (B, T, Hv), dev),
+        _ptr(A_log, "A_log", (torch.float32,), (Hv,), dev),
+        _ptr(dt_bias, "dt_bias", (torch.float32,), (Hv,), dev),
+        _ptr(mask, "mask", _MASK, (B, T), dev),
+        _ptr(state_in, "state_in", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(state_out, "state_out", (torch.float32,), (B, Hv, Dv, Dk), dev),
+        _ptr(y, "y", _BF16, (B, T, Hv, Dv), dev),
+    ]
+    _invoke(lib().gdn_layer_core_no_alloc, *args, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale, eps,
+            _stream(dev, stream))
 
 
 def gated_rmsnorm(y, z, norm_weight, out, *, eps=1e-6, stream=None):

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
 
-SOURCES = ["gdn_api.cpp", "prep.hip", "recurrent.hip", "chunked.hip", "epilogue.hip"]
+SOURCES = ["gdn_api.cpp", "prep.hip", "recurrent.hip", "chunked.hip", "epilogue.hip", "scratch.hip"]
 # Matrix-core accumulators in ordinary VGPRs (no AGPR copies around the
 # element-wise work on them).
 SOURCE_FLAGS = {"chunked.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}

@@ -15,7 +15,8 @@
 
 namespace {
 
-constexpr int kVersion = 4;
+constexpr int kVersion = 5;
+static_assert(GDN_NO_ALLOC_SCRATCH_BYTES == gdn::kScratchBytes, "the header states the scratch size");
 constexpr int64_t kMaxBlocks = (1LL << 31) - 1;
 
 thread_local char g_err[512] = "";
@@ -564,6 +565,29 @@ gdn_status gdn_layer_core_masked(const gdn_bf16* qkv, const gdn_bf16* conv_w, co
     return layer_core_impl(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, mask, state_in,
                            state_out, y, workspace, workspace_bytes, B, T, Hk, Hv, Dk, Dv, K, q_scale, k_scale,
                            eps, false, nullptr, nullptr, 0.f, stream);
+}
+
+gdn_status gdn_layer_core_no_alloc(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_bf16* conv_state_in,
+                                   gdn_bf16* conv_state_out, const gdn_bf16* a, const gdn_bf16* b,
+                                   const float* A_log, const float* dt_bias, const uint8_t* mask,
+                                   const float* state_in, float* state_out, gdn_bf16* y, int B, int T, int Hk,
+                                   int Hv, int Dk, int Dv, int K, float q_scale, float k_scale, float eps,
+                                   void* stream) {
+    gdn_status st = check_dims(B, T, Hk, Hv, Dk, Dv);
+    if (st != GDN_OK) return st;
+    Workspace w;
+    if (!workspace_layout(B, T, Hk, Hv, Dk, Dv, w)) return fail(GDN_ERR_BAD_DIMS, "tensor sizes overflow");
+    if (w.total > gdn::kScratchBytes)
+        return fail(GDN_ERR_WORKSPACE,
+                    "these sizes need %llu bytes of workspace, more than the %llu bytes of library scratch; "
+                    "call gdn_layer_core_masked with a caller workspace instead",
+                    (unsigned long long)w.total, (unsigned long long)gdn::kScratchBytes);
+    void* scratch = nullptr;
+    const hipError_t e = gdn::scratch_buffer(&scratch);
+    if (e != hipSuccess) return fail(GDN_ERR_HIP, "library scratch set-up failed: %s", hipGetErrorString(e));
+    return layer_core_impl(qkv, conv_w, conv_state_in, conv_state_out, a, b, A_log, dt_bias, mask, state_in,
+                           state_out, y, scratch, (size_t)gdn::kScratchBytes, B, T, Hk, Hv, Dk, Dv, K, q_scale,
+                           k_scale, eps, false, nullptr, nullptr, 0.f, stream);
 }
 
 gdn_status gdn_layer_core_gated(const gdn_bf16* qkv, const gdn_bf16* conv_w, const gdn_bf16* conv_state_in,

@@ -124,6 +124,14 @@ struct GatedNormArgs {
     int Dv;
     float eps;
 };
+// The allocation-free layer core's workspace: a device array of kScratchBytes
+// per device, held by the library until the process ends.  scratch_buffer
+// returns its address on the current device (looked up on the first call on
+// each device; thread-safe).  Every call on a device shares that device's
+// array.
+constexpr uint64_t kScratchBytes = 128ull << 20;
+hipError_t scratch_buffer(void** ptr);
+
 int gated_norm_lanes(int Dv);
 int64_t gated_norm_blocks(int64_t rows, int Dv);
 hipError_t launch_gated_rmsnorm(const GatedNormArgs& a, hipStream_t stream);

@@ -371,3 +371,22 @@ def test_bind_rejects_non_library_calls():
     with pytest.raises(TypeError):
         binding.bind(len, [1, 2])
 
+
+def test_no_alloc_rejects_before_set_up(L):
+    """gdn_layer_core_no_alloc checks the sizes against its scratch before it
+    touches the device (these calls run without a GPU)."""
+    import re
+    with open(binding.HEADER) as fh:
+        m = re.search(r"#define GDN_NO_ALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", fh.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.NO_ALLOC_SCRATCH_BYTES
+
+    def call(B=1, T=4096, Hk=16, Hv=32, Dk=128, Dv=128, K=4):
+        return L.gdn_layer_core_no_alloc(addr(0), addr(1), None, addr(2), addr(3), addr(4), addr(5), addr(6),
+                                         None, None, addr(7), addr(8), B, T, Hk, Hv, Dk, Dv, K, 1.0, 1.0, 1e-6,
+                                         None)
+    assert L.gdn_layer_core_workspace_bytes(1, 4096, 16, 32, 128, 128) > binding.NO_ALLOC_SCRATCH_BYTES
+    assert call() == WS
+    assert "scratch" in L.gdn_last_error().decode()
+    assert call(Hk=3) == DIMS
+    assert call(Dk=100) == UNSUP
+    assert call(B=-1) == DIMS
