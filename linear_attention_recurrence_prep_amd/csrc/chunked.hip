@@ -60,6 +60,7 @@
 // <0, 1, true> forms the ratios as running products and chunk_seq_kernel
 // <1, true> takes Q o Gamma, (K o E)^T and Gamma_{C-1} per v-head.
 #include <algorithm>
+#include <cstddef>
 #include <atomic>
 
 #include "gdn_device.h"
@@ -239,6 +240,9 @@ struct alignas(16) PrepSmem {
     float gs[NH][CK], bs[NH][CK], gm[NH][CK];
 };
 
+// the decay step reads the gates four at a time
+static_assert(offsetof(PrepSmem<1>, gs) % 16 == 0 && offsetof(PrepSmem<2>, gs) % 16 == 0, "16-byte gate rows");
+
 struct ChunkPtrs {
     u4_t* wsw;      // W (f32)
     u4_t* u;        // -Tb V (f32 accumulator tiles)
@@ -266,7 +270,7 @@ constexpr int rg_floats() { return PK ? 2 * CK + DKC : 2 * CK; }
 // scaled k k^T, q k^T; K o Gamma enters W, and the sequential pass gets
 // Q o Gamma, (K o E)^T and Gamma_{C-1} in place of q, k and gamma.
 template <int KF, int NH, bool PK = false>
-__global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) void chunk_prep_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const float* __restrict__ g,
                                                             const float* __restrict__ beta,
@@ -313,39 +317,50 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
         else if (lane < 32 + Dv / 8) { region = 2; c0 = 2 * Hk * DKC + hv0 * Dv + 8 * (lane - 32); }
         else if (NH == 2 && lane >= 48 && lane < 48 + Dv / 8) { region = 2; c0 = 2 * Hk * DKC + (hv0 + 1) * Dv + 8 * (lane - 48); }
         const bool valid = region < 3;
+        // lanes without channels (v lanes past Dv/8) read a channel of the
+        // first v-head instead, so that every load of the wave is taken;
+        // nothing they compute is stored
+        const int cr = valid ? c0 : 2 * Hk * DKC + hv0 * Dv;
         const float scale = region == 0 ? pin.q_scale : pin.k_scale;
-        const uint16_t* xb = pin.qkv + (int64_t)b * T * C + c0;
-        const uint16_t* csb = pin.conv_state_in ? pin.conv_state_in + (int64_t)b * (KF - 1) * C + c0 : nullptr;
-        float w[KF][8];
-        if (valid) {
-            const uint4* wp = reinterpret_cast<const uint4*>(pin.conv_w + (int64_t)c0 * KF);
-            float f[8 * KF];
-#pragma unroll
-            for (int v4 = 0; v4 < KF; ++v4) unpack8(wp[v4], f + 8 * v4);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < KF; ++j) w[j][i] = f[i * KF + j];
-        } else {
-#pragma unroll
-            for (int j = 0; j < KF; ++j)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) w[j][i] = 0.f;
+        // the gate inputs of the group's head (one token per thread of the
+        // first 32) are loaded first, so that the gate arithmetic below
+        // overlaps the row loads
+        uint16_t ga = 0, gb = 0;
+        bool gon = false;
+        if (tl < CK) {
+            const int t = t0 + tl;
+            const int64_t bt = (int64_t)b * T + min(t, T - 1);
+            gon = t < T && (mask == nullptr || mask[bt] != 0);     // else g = 1, beta = 0
+            ga = pin.a[bt * Hv + hv];
+            gb = pin.b[bt * Hv + hv];
         }
-        // spliced input row pr (conv state rows, then qkv rows; zero past T)
+        const uint16_t* xb = pin.qkv + (int64_t)b * T * C + cr;
+        const uint16_t* csb = pin.conv_state_in ? pin.conv_state_in + (int64_t)b * (KF - 1) * C + cr : nullptr;
+        // conv weights as stored bf16 pairs
+        uint4 wk[KF];
+#pragma unroll
+        for (int v4 = 0; v4 < KF; ++v4) wk[v4] = reinterpret_cast<const uint4*>(pin.conv_w + (int64_t)cr * KF)[v4];
+        const ConvW<KF> cw = conv_weights<KF>(wk);
+        // spliced input row pr: conv state rows, then qkv rows, zero past T
+        // (the same case for every lane of the wave)
         auto xpad_row = [&](int pr) -> uint4 {
-            if (!valid || pr - (KF - 1) >= T) return make_uint4(0, 0, 0, 0);
-            if (pr >= KF - 1) return *reinterpret_cast<const uint4*>(xb + (int64_t)(pr - (KF - 1)) * C);
+            const int tr = pr - (KF - 1);
+            if (tr >= T) return make_uint4(0, 0, 0, 0);
+            if (tr >= 0) return *reinterpret_cast<const uint4*>(xb + (int64_t)tr * C);
             if (csb) return *reinterpret_cast<const uint4*>(csb + (int64_t)pr * C);
             return make_uint4(0, 0, 0, 0);
         };
+        // the spliced input rows this wave's tokens read: tw0 .. tw0 + TPW + KF - 2
         const int tw0 = t0 + TPW * wv;
-        float h[KF - 1][8];
+        uint4 rows[TPW + KF - 1];
 #pragma unroll
-        for (int j = 0; j < KF - 1; ++j) unpack8(xpad_row(tw0 + j), h[j]);
-        uint4 rows[TPW];
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) rows[i] = xpad_row(tw0 + i + KF - 1);
+        for (int i = 0; i < TPW + KF - 1; ++i) rows[i] = xpad_row(tw0 + i);
+        if (tl < CK) {
+            float gv, bv;
+            gate_g_beta(ga, gb, pin.A_log[hv], pin.dt_bias[hv], gv, bv);
+            sh.gs[grp][tl] = gon ? gv : 1.f;
+            sh.bs[grp][tl] = gon ? bv : 0.f;
+        }
         // the new conv state (chunk 0's blocks; q/k channels from the first
         // v-head of the group): the last KF-1 rows of the spliced input
         if (c == 0 && wv == 0 && valid && pin.conv_state_out && (region == 2 || hv0 % G == 0)) {
@@ -360,22 +375,18 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int t = tw0 + i;
-            float x[8];
-            unpack8(rows[i], x);
+            uint4 win[KF];
+#pragma unroll
+            for (int j = 0; j < KF; ++j) win[j] = rows[i + j];
             float act[8];
-            conv_silu8<KF>(w, h, x, act);
-            uint4 qk = make_uint4(0, 0, 0, 0);
-            if (region < 2) qk = qk_norm8<DKC>(act, scale, pin.eps);
-#pragma unroll
-            for (int j = 0; j < KF - 2; ++j)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) h[j][e] = h[j + 1][e];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) h[KF - 2][e] = x[e];
+            conv_silu8<KF>(cw, win, act);
+            // q/k lanes: the head norm; v lanes: act itself
             const bool live = t < T;      // rows past T are zero, as for stored inputs
-            if (region == 0) *reinterpret_cast<uint4*>(&sh.u.in.qb[t - t0][8 * lane]) = live ? qk : make_uint4(0, 0, 0, 0);
-            else if (region == 1) *reinterpret_cast<uint4*>(&sh.u.in.kb[t - t0][8 * (lane - 16)]) = live ? qk : make_uint4(0, 0, 0, 0);
-            vrow[i] = live ? pack8(act) : make_uint4(0, 0, 0, 0);
+            const uint4 n = qk_norm8<DKC>(act, region < 2, scale, pin.eps);
+            const uint4 o = live ? n : make_uint4(0, 0, 0, 0);
+            if (region == 0) *reinterpret_cast<uint4*>(&sh.u.in.qb[t - t0][8 * lane]) = o;
+            else if (region == 1) *reinterpret_cast<uint4*>(&sh.u.in.kb[t - t0][8 * (lane - 16)]) = o;
+            vrow[i] = o;
         }
       }
     } else {
@@ -427,18 +438,14 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
         }
     }
     }
-    if (tl < CK) {
-        // steps past T and masked steps: g = 1, beta = 0 (no decay, no write)
+    if (KF == 0 && tl < CK) {
+        // steps past T and masked steps: g = 1, beta = 0 (no decay, no write);
+        // the fused form computed its gates above
         const int t = t0 + tl;
         const int64_t bt = (int64_t)b * T + min(t, T - 1);
         const int64_t i = bt * Hv + hv;
-        float gv, bv;
-        if constexpr (KF > 0) {
-            gate_g_beta(pin.a[i], pin.b[i], pin.A_log[hv], pin.dt_bias[hv], gv, bv);
-        } else {
-            gv = PK ? 1.f : g[i];    // (per-key gate rows are loaded above)
-            bv = beta[i];
-        }
+        const float gv = PK ? 1.f : g[i];    // (per-key gate rows are loaded above)
+        const float bv = beta[i];
         const bool on = t < T && (mask == nullptr || mask[bt] != 0);
         sh.gs[grp][tl] = on ? gv : 1.f;
         sh.bs[grp][tl] = on ? bv : 0.f;
@@ -506,15 +513,22 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? 3 : 4) void chunk_prep
     if constexpr (!PK) {
         const int t = tl >> 3, s0 = (tl & 7) * 4;
         const float* gs = sh.gs[grp];
+        // The eight threads of row t are adjacent lanes.  Thread k (s0 = 4k)
+        // forms its block's gates up to step t, G_k = g_{4k} ... g_{min(4k+3, t)}
+        // (1 if 4k > t); the product of the later blocks G_{k+1} ... G_7 is
+        // R[t][s0+3] = g_{s0+4} ... g_t, and R[t][s] = R[t][s+1] g_{s+1} while
+        // s+1 <= t; R[t][s] = 1 for s >= t (only s = t is used).
+        const float4 g4 = *reinterpret_cast<const float4*>(gs + s0);
+        float blk = s0 <= t ? g4.x : 1.f;
+        blk *= s0 + 1 <= t ? g4.y : 1.f;
+        blk *= s0 + 2 <= t ? g4.z : 1.f;
+        blk *= s0 + 3 <= t ? g4.w : 1.f;
+        const float later = dpp_mov<DPP_ROW_SHL1>(suffix_prod8(blk));
         float r[4];
-        // R[t][s0+3] = g_{s0+4}...g_t, then R[t][s] = R[t][s+1] g_{s+1} while
-        // s+1 <= t; R[t][s] = 1 for s >= t (only s = t is used)
-        float acc = 1.f;
-        for (int u = s0 + 4; u <= t; ++u) acc *= gs[u];
-        r[3] = acc;
-        r[2] = s0 + 3 <= t ? r[3] * gs[s0 + 3] : 1.f;
-        r[1] = s0 + 2 <= t ? r[2] * gs[s0 + 2] : 1.f;
-        r[0] = s0 + 1 <= t ? r[1] * gs[s0 + 1] : 1.f;
+        r[3] = (tl & 7) < 7 ? later : 1.f;
+        r[2] = s0 + 3 <= t ? r[3] * g4.w : 1.f;
+        r[1] = s0 + 2 <= t ? r[2] * g4.z : 1.f;
+        r[0] = s0 + 1 <= t ? r[1] * g4.y : 1.f;
         float av[4], pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

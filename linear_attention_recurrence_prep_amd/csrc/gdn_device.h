@@ -81,18 +81,76 @@ __device__ __forceinline__ void gate_g_beta(uint16_t a, uint16_t b, float A_log,
     beta = bb >= 0.f ? s : e * s;
 }
 
-// One token of 8 channels: the depthwise conv over the K-1 window rows h and
-// the new row x (weights w[j][e] for tap j, w[K-1] on the newest row), then
-// SiLU (overflow-free, about 2 f32 ulp).
+// The depthwise conv on its operands as stored bf16 pairs.  The dot-product
+// instruction (v_dot2_f32_bf16) multiplies two bf16 pairs, each product
+// exact, and adds both to an f32 addend in f32.  A channel's taps (w0, w1)
+// and (w2, w3) are adjacent in conv_w [C, K], so for K = 2 and 4 the weight
+// pairs are the stored words; the data pair (x_s, x_{s+1}) of a channel is
+// one byte permutation of two token rows, and each pair serves two tokens
+// (the newer pair of one is the older pair of the token two steps on).
+// Nothing is widened to f32, which halves the registers the conv holds.
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// bf16 element i (0..7) of a 16-byte vector, widened exactly
+__device__ __forceinline__ float bf16_at(const uint4& v, int i) {
+    const uint32_t w = word_of(v, i / 2);
+    return (i & 1) ? bf16hi(w) : bf16lo(w);
+}
+
+// channel e (0..7) of two token rows as the bf16 pair (older, newer), older
+// in the low half: one v_perm_b32
+__device__ __forceinline__ uint32_t row_pair(const uint4& older, const uint4& newer, int e) {
+    return __builtin_amdgcn_perm(word_of(newer, e / 2), word_of(older, e / 2), (e & 1) ? 0x07060302u : 0x05040100u);
+}
+
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+// w.lo * x.lo + w.hi * x.hi + c (bf16 pairs, f32 addend and result)
+__device__ __forceinline__ float dot2_bf16(uint32_t w, uint32_t x, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, w), __builtin_bit_cast(bf16x2v_t, x), c,
+                                           false);
+}
+
+// Conv weights of 8 channels: pairs (w_{2i}, w_{2i+1}) per channel and, for
+// odd K, the last tap widened to f32.
 template <int K>
-__device__ __forceinline__ void conv_silu8(const float (&w)[K][8], const float (&h)[K - 1][8], const float (&x)[8],
-                                           float (&act)[8]) {
+struct ConvW {
+    uint32_t p[8][K / 2];
+    float last[K % 2 ? 8 : 1];
+};
+
+// From the K stored 16-byte vectors of conv_w [c0 .. c0 + 7][0 .. K - 1]
+// (bf16 element e * K + j is channel c0 + e, tap j).
+template <int K>
+__device__ __forceinline__ ConvW<K> conv_weights(const uint4 (&wk)[K]) {
+    auto bf = [&](int i) -> uint32_t {
+        const uint32_t x = word_of(wk[i / 8], (i % 8) / 2);
+        return (i & 1) ? x >> 16 : x & 0xFFFFu;
+    };
+    ConvW<K> w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+        for (int i = 0; i < K / 2; ++i) w.p[e][i] = bf(e * K + 2 * i) | (bf(e * K + 2 * i + 1) << 16);
+        if constexpr (K % 2 != 0) w.last[e] = __uint_as_float(bf(e * K + K - 1) << 16);
+    }
+    return w;
+}
+
+// One token of 8 channels from the K rows of the spliced input that the
+// conv reads (oldest first; the last is the token's own row; w_{K-1} on it),
+// then SiLU (overflow-free, about 2 f32 ulp).
+template <int K>
+__device__ __forceinline__ void conv_silu8(const ConvW<K>& w, const uint4 (&r)[K], float (&act)[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         float u = 0.f;
 #pragma unroll
-        for (int j = 0; j < K - 1; ++j) u = fmaf(w[j][e], h[j][e], u);
-        u = fmaf(w[K - 1][e], x[e], u);
+        for (int i = 0; i < K / 2; ++i) u = dot2_bf16(w.p[e][i], row_pair(r[2 * i], r[2 * i + 1], e), u);
+        if constexpr (K % 2 != 0) u = fmaf(w.last[e], bf16_at(r[K - 1], e), u);
         act[e] = silu_fast(u);
     }
 }
@@ -104,6 +162,9 @@ __device__ __forceinline__ void conv_silu8(const float (&w)[K][8], const float (
 enum : int {
     DPP_QUAD_XOR1 = 0xB1,  // quad_perm [1,0,3,2]
     DPP_QUAD_XOR2 = 0x4E,  // quad_perm [2,3,0,1]
+    DPP_ROW_SHL1 = 0x101,  // lane i reads lane i + n of its 16-lane row
+    DPP_ROW_SHL2 = 0x102,
+    DPP_ROW_SHL4 = 0x104,
     DPP_ROW_MIRROR = 0x140,
     DPP_ROW_HALF_MIRROR = 0x141,
 };
@@ -111,6 +172,19 @@ enum : int {
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Product over lanes k .. 7 of each aligned group of 8 lanes (k = lane & 7):
+// Hillis-Steele suffix scan, three DPP row shifts.
+__device__ __forceinline__ float suffix_prod8(float x) {
+    const int k = threadIdx.x & 7;
+    float y = dpp_mov<DPP_ROW_SHL1>(x);
+    x *= k + 1 < 8 ? y : 1.f;
+    y = dpp_mov<DPP_ROW_SHL2>(x);
+    x *= k + 2 < 8 ? y : 1.f;
+    y = dpp_mov<DPP_ROW_SHL4>(x);
+    x *= k + 4 < 8 ? y : 1.f;
+    return x;
 }
 
 // Sum over aligned groups of W lanes (W in {4, 8, 16, 32}); every lane of a
@@ -154,15 +228,18 @@ __device__ __forceinline__ void group_sum2(float& x, float& y) {
 }
 
 // The q/k head norm of 8 channels held by each of the head's DK/8 lanes (an
-// aligned lane group; every lane of it must execute this): sum of squares
-// across the group, then act * scale / sqrt(mean + eps), rounded to bf16.
+// aligned lane group; every lane of the group executes this): sum of
+// squares across the group, then act * scale / sqrt(mean + eps), rounded to
+// bf16.  Lanes whose channels are v (norm = false) run the same
+// instructions, as the rest of the wave does, and return act rounded to bf16
+// (act * 1 is act exactly).
 template <int DK>
-__device__ __forceinline__ uint4 qk_norm8(const float (&act)[8], float scale, float eps) {
+__device__ __forceinline__ uint4 qk_norm8(const float (&act)[8], bool norm, float scale, float eps) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(act[e], act[e], ss);
     ss = group_sum<DK / 8>(ss);
-    const float rs = scale * __builtin_amdgcn_rsqf(ss * (1.0f / DK) + eps);
+    const float rs = norm ? scale * __builtin_amdgcn_rsqf(ss * (1.0f / DK) + eps) : 1.0f;
     float o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = act[e] * rs;

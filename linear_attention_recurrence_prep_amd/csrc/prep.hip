@@ -64,23 +64,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int 
     const uint16_t* xb = p.qkv + (int64_t)b * T * C + c0;
     const uint16_t* csb = p.conv_state_in ? p.conv_state_in + (int64_t)b * (K - 1) * C + c0 : nullptr;
 
-    // conv weights of the 8 channels: conv_w[c0 + i][j] -> w[j][i]
-    float w[K][8];
-    if (valid) {
-        const uint4* wp = reinterpret_cast<const uint4*>(p.conv_w + (int64_t)c0 * K);
-        float f[8 * K];
+    // conv weights of the 8 channels, as stored bf16 pairs
+    uint4 wk[K];
 #pragma unroll
-        for (int v4 = 0; v4 < K; ++v4) unpack8(wp[v4], f + 8 * v4);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < K; ++j) w[j][i] = f[i * K + j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < K; ++j)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) w[j][i] = 0.f;
-    }
+    for (int v4 = 0; v4 < K; ++v4)
+        wk[v4] = valid ? reinterpret_cast<const uint4*>(p.conv_w + (int64_t)c0 * K)[v4] : make_uint4(0, 0, 0, 0);
+    const ConvW<K> w = conv_weights<K>(wk);
 
     // spliced input row p (0 <= p < T + K - 1): conv state rows, then qkv rows
     auto xpad_row = [&](int pr) -> uint4 {
@@ -90,10 +79,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int 
         return make_uint4(0, 0, 0, 0);
     };
 
-    // window = xpad rows t0 .. t0+K-2
-    float h[K - 1][8];
+    // win[0 .. K-2] = xpad rows t0 .. t0+K-2 (stored bf16), win[K-1] the token's row
+    uint4 win[K];
 #pragma unroll
-    for (int j = 0; j < K - 1; ++j) unpack8(xpad_row(t0 + j), h[j]);
+    for (int j = 0; j < K - 1; ++j) win[j] = xpad_row(t0 + j);
 
     // the new conv state: last K-1 rows of xpad (read before any write, so
     // conv_state_out may alias conv_state_in)
@@ -123,31 +112,23 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int 
     for (int i = 0; i < PREP_TT; ++i) {
         if (t0 + i >= t1) break;   // uniform across the block
         const int t = t0 + i;
-        float x[8];
-        unpack8(rows[i], x);
+        win[K - 1] = rows[i];
         float act[8];
-        conv_silu8<K>(w, h, x, act);
-        // q/k heads: the norm over the head's Dk/8 lanes.  Region boundaries
-        // are multiples of Dk, so every lane group is wholly inside or outside
-        // this branch (the cross-lane sum never reads an idle lane).
-        uint4 qk = make_uint4(0, 0, 0, 0);
-        if (region < 2) qk = qk_norm8<DK>(act, scale, p.eps);
+        conv_silu8<K>(w, win, act);
+        // q/k heads: the norm over the head's Dk/8 lanes (region boundaries
+        // are multiples of Dk, so a lane group never mixes regions); v lanes
+        // pass act through
+        const uint4 o = qk_norm8<DK>(act, region < 2, scale, p.eps);
         // slide the window
 #pragma unroll
-        for (int j = 0; j < K - 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) h[j][e] = h[j + 1][e];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[K - 2][e] = x[e];
+        for (int j = 0; j < K - 1; ++j) win[j] = win[j + 1];
 
         if (!valid) continue;
         const int64_t tok = (int64_t)b * T + t;
-        if (region < 2) {
-            uint16_t* dst = region == 0 ? p.q + tok * HKDK + c0 : p.k + tok * HKDK + (c0 - HKDK);
-            store_stream16(dst, qk);
-        } else {
-            store_stream16(p.v + tok * Hv * Dv + (c0 - 2 * HKDK), pack8(act));
-        }
+        uint16_t* dst = region == 0   ? p.q + tok * HKDK + c0
+                        : region == 1 ? p.k + tok * HKDK + (c0 - HKDK)
+                                      : p.v + tok * Hv * Dv + (c0 - 2 * HKDK);
+        store_stream16(dst, o);
     }
 }
 

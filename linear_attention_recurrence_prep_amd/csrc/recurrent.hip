@@ -519,35 +519,24 @@ __global__ __launch_bounds__(DEC_NT) void decode_core_kernel(PrepArgs p, const u
         const int c0 = region == 0   ? hk * DK + 8 * tid
                        : region == 1 ? Hk * DK + hk * DK + 8 * (tid - L)
                                      : 2 * Hk * DK + hk * G * Dv + 8 * (tid - 2 * L);
-        float w[KC][8];
-        {
-            const uint4* wp = reinterpret_cast<const uint4*>(p.conv_w + (int64_t)c0 * KC);
-            float f[8 * KC];
+        uint4 wk[KC];
 #pragma unroll
-            for (int v4 = 0; v4 < KC; ++v4) unpack8(wp[v4], f + 8 * v4);
+        for (int v4 = 0; v4 < KC; ++v4) wk[v4] = reinterpret_cast<const uint4*>(p.conv_w + (int64_t)c0 * KC)[v4];
+        const ConvW<KC> w = conv_weights<KC>(wk);
+        // the conv state rows, then the token's own row
+        uint4 hr[KC];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < KC; ++j) w[j][i] = f[i * KC + j];
-        }
-        uint4 hr[KC - 1];
-        float h[KC - 1][8];
-#pragma unroll
-        for (int r = 0; r < KC - 1; ++r) {
+        for (int r = 0; r < KC - 1; ++r)
             hr[r] = p.conv_state_in
                         ? *reinterpret_cast<const uint4*>(p.conv_state_in + ((int64_t)b * (KC - 1) + r) * C + c0)
                         : make_uint4(0, 0, 0, 0);
-            unpack8(hr[r], h[r]);
-        }
         const uint4 xr = *reinterpret_cast<const uint4*>(p.qkv + (int64_t)b * C + c0);
-        float x[8], act[8];
-        unpack8(xr, x);
-        conv_silu8<KC>(w, h, x, act);
+        hr[KC - 1] = xr;
+        float act[8];
+        conv_silu8<KC>(w, hr, act);
         // q/k: the head norm over the head's L lanes (aligned lane groups of
-        // wave 0; the v lanes never join this branch)
-        uint4 packed;
-        if (region < 2) packed = qk_norm8<DK>(act, region == 0 ? p.q_scale : p.k_scale, p.eps);
-        else packed = pack8(act);
+        // wave 0); v lanes pass act through
+        const uint4 packed = qk_norm8<DK>(act, region < 2, region == 0 ? p.q_scale : p.k_scale, p.eps);
         float o[8];
         unpack8(packed, o);
         float* dst = region == 0 ? qs + 8 * tid : region == 1 ? ks + 8 * (tid - L) : vs + 8 * (tid - 2 * L);
@@ -559,7 +548,7 @@ __global__ __launch_bounds__(DEC_NT) void decode_core_kernel(PrepArgs p, const u
 #pragma unroll
             for (int r = 0; r < KC - 1; ++r)
                 *reinterpret_cast<uint4*>(p.conv_state_out + ((int64_t)b * (KC - 1) + r) * C + c0) =
-                    r + 1 < KC - 1 ? hr[r + 1] : xr;
+                    hr[r + 1];
         }
     }
     if (tid >= 256 && tid < 256 + G) {
