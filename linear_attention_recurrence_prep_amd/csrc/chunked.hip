@@ -61,6 +61,7 @@
 // <1, true> takes Q o Gamma, (K o E)^T and Gamma_{C-1} per v-head.
 #include <algorithm>
 #include <cstddef>
+#include <type_traits>
 #include <atomic>
 
 #include "gdn_device.h"
@@ -390,14 +391,40 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) 
         }
       }
     } else {
-    for (int idx = tid; idx < CK * DKC / 8; idx += 256 * NH) {
+    constexpr int kQKPer = CK * DKC / 8 / (256 * NH);     // 16-byte k (and q) vectors per thread
+    uint4 kva[kQKPer], qva[kQKPer];
+#pragma unroll
+    for (int i = 0; i < kQKPer; ++i) {
+        // rows past T are read clamped (in bounds) and zeroed below, so the
+        // loads need no branch and all issue before the first LDS store
+        const int idx = tid + i * 256 * NH;
         const int t = idx / (DKC / 8), c8 = idx % (DKC / 8);
-        uint4 kv = make_uint4(0, 0, 0, 0), qv = kv;
-        if (t0 + t < T) {
-            const int64_t off = (((int64_t)b * T + t0 + t) * Hk + hk) * DKC + c8 * 8;
-            kv = *reinterpret_cast<const uint4*>(k + off);
-            qv = *reinterpret_cast<const uint4*>(q + off);
+        const int64_t off = (((int64_t)b * T + min(t0 + t, T - 1)) * Hk + hk) * DKC + c8 * 8;
+        kva[i] = *reinterpret_cast<const uint4*>(k + off);
+        qva[i] = *reinterpret_cast<const uint4*>(q + off);
+    }
+    // per-key form: the gate rows too, before any LDS store (steps past T
+    // and masked steps decay by 1)
+    constexpr int kGPer = PK ? CK * DKC / 4 / 256 : 1;
+    float4 gva[kGPer];
+    bool gon[kGPer];
+    if constexpr (PK) {
+#pragma unroll
+        for (int i = 0; i < kGPer; ++i) {
+            const int idx = tid + i * 256;
+            const int t = idx / (DKC / 4), c4 = idx % (DKC / 4);
+            const int64_t bt = (int64_t)b * T + min(t0 + t, T - 1);
+            gon[i] = t0 + t < T && (mask == nullptr || mask[bt] != 0);
+            gva[i] = *reinterpret_cast<const float4*>(g + (bt * Hv + hv) * DKC + 4 * c4);   // in bounds
         }
+    }
+#pragma unroll
+    for (int i = 0; i < kQKPer; ++i) {
+        const int idx = tid + i * 256 * NH;
+        const int t = idx / (DKC / 8), c8 = idx % (DKC / 8);
+        const bool live = t0 + t < T;
+        const uint4 kv = live ? kva[i] : make_uint4(0, 0, 0, 0);
+        const uint4 qv = live ? qva[i] : make_uint4(0, 0, 0, 0);
         if constexpr (PK) {
             float kf8[8], qf8[8];
             unpack8(kv, kf8);
@@ -414,12 +441,13 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) 
         }
     }
     if constexpr (PK) {
-        // the gate rows; steps past T and masked steps decay by 1
-        for (int idx = tid; idx < CK * DKC / 4; idx += 256) {
+        // the gate rows loaded above
+#pragma unroll
+        for (int i = 0; i < kGPer; ++i) {
+            const int idx = tid + i * 256;
             const int t = idx / (DKC / 4), c4 = idx % (DKC / 4);
-            const int64_t bt = (int64_t)b * T + min(t0 + t, T - 1);
-            const bool on = t0 + t < T && (mask == nullptr || mask[bt] != 0);
-            const float4 gv = *reinterpret_cast<const float4*>(g + (bt * Hv + hv) * DKC + 4 * c4);   // in bounds
+            const float4 gv = gva[i];
+            const bool on = gon[i];
             *reinterpret_cast<float4*>(&sh.u.pk.ge[t][4 * c4]) =
                 make_float4(on ? gv.x : 1.f, on ? gv.y : 1.f, on ? gv.z : 1.f, on ? gv.w : 1.f);
         }
@@ -564,7 +592,10 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) 
         //     the halves (t >= 16 > s) R(t, s) = R(t, 15) o R(15, s), two
         //     factors <= 1: that block is one f32 product on the matrix cores.
         auto& sw = sh.w.s[0];
-        const int s = tl >> 3, jg = tl & 7, s_lo = s & ~7, t_hi = s < CK / 2 ? CK / 2 : CK;
+        const int s = tl >> 3, jg = tl & 7;
+        // a wave's eight rows s share s_lo and the half's end: scalar bounds
+        const int s_lo = __builtin_amdgcn_readfirstlane(s & ~7);
+        const int t_hi = __builtin_amdgcn_readfirstlane(s < CK / 2 ? CK / 2 : CK);
         float u[16];
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
@@ -574,31 +605,58 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) 
             u[4 * e4 + 2] = x.z;
             u[4 * e4 + 3] = x.w;
         }
-        for (int t = s_lo; t < t_hi; ++t) {
-            float pa = 0.f, pp = 0.f;
+        // the operands of step t (gate, key and query row, this thread's 16
+        // columns), read one step ahead so that their LDS latency overlaps
+        // the step before
+        struct RowOps {
+            float4 g[4], k[4], q[4];
+        };
+        auto row_ops = [&](int t) {
+            RowOps r;
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
                 const int j = 16 * jg + 4 * e4;
-                const float4 gt = *reinterpret_cast<const float4*>(&sh.u.pk.ge[t][j]);
-                const float4 kt4 = *reinterpret_cast<const float4*>(&sh.u.pk.kf[t][j]);
-                const float4 qt4 = *reinterpret_cast<const float4*>(&sh.u.pk.qf[t][j]);
-                const float ga[4] = {gt.x, gt.y, gt.z, gt.w};
-                const float ka[4] = {kt4.x, kt4.y, kt4.z, kt4.w};
-                const float qa[4] = {qt4.x, qt4.y, qt4.z, qt4.w};
+                r.g[e4] = *reinterpret_cast<const float4*>(&sh.u.pk.ge[t][j]);
+                r.k[e4] = *reinterpret_cast<const float4*>(&sh.u.pk.kf[t][j]);
+                r.q[e4] = *reinterpret_cast<const float4*>(&sh.u.pk.qf[t][j]);
+            }
+            return r;
+        };
+        // one step t: decay u by g_t (from the step after row s on; MASK is
+        // false where every row of the wave is already behind t), the two
+        // dot products, their 8-lane sums, A and P of (t, s)
+        auto pk_step = [&](int t, const RowOps& r, auto mask) {
+            constexpr bool MASK = decltype(mask)::value;
+            float pa = 0.f, pp = 0.f;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const float ga[4] = {r.g[e4].x, r.g[e4].y, r.g[e4].z, r.g[e4].w};
+                const float ka[4] = {r.k[e4].x, r.k[e4].y, r.k[e4].z, r.k[e4].w};
+                const float qa[4] = {r.q[e4].x, r.q[e4].y, r.q[e4].z, r.q[e4].w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float& ue = u[4 * e4 + i];
-                    if (t > s) ue *= ga[i];
+                    if (!MASK || t > s) ue *= ga[i];
                     pa = fmaf(ka[i], ue, pa);
                     pp = fmaf(qa[i], ue, pp);
                 }
             }
-            pa = group_sum<8>(pa);
-            pp = group_sum<8>(pp);
+            group_sum2<8>(pa, pp);
             if (jg == 0) {
                 sw.a[t][s] = t > s ? sh.bs[0][t] * pa : 0.f;
                 sw.tm[t][s] = t >= s ? pp : 0.f;       // P, kept here until its planes are cut
             }
+        };
+        // steps s_lo .. t_hi - 1 in pairs (8 or 16 of them); the first eight
+        // cover the wave's own rows, where the decay starts row by row
+        RowOps ra = row_ops(s_lo);
+        for (int t = s_lo; t < t_hi; t += 2) {
+            const RowOps rb = row_ops(t + 1);
+            if (t < s_lo + 8) pk_step(t, ra, std::true_type{});
+            else pk_step(t, ra, std::false_type{});
+            ra = row_ops(min(t + 2, t_hi - 1));
+            if (t + 1 < s_lo + 8) pk_step(t + 1, rb, std::true_type{});
+            else pk_step(t + 1, rb, std::false_type{});
         }
         if (jg == 0)
             for (int t = 0; t < s_lo; ++t) {

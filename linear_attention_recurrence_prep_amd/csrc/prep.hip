@@ -115,10 +115,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int 
         win[K - 1] = rows[i];
         float act[8];
         conv_silu8<K>(w, win, act);
-        // q/k heads: the norm over the head's Dk/8 lanes (region boundaries
-        // are multiples of Dk, so a lane group never mixes regions); v lanes
-        // pass act through
-        const uint4 o = qk_norm8<DK>(act, region < 2, scale, p.eps);
+        // q/k heads: the norm over the head's Dk/8 lanes; v lanes pass act
+        // through.  Region boundaries are multiples of Dk, so a lane group
+        // never mixes regions, and most waves lie wholly inside one region
+        // and skip the other branch.
+        uint4 o;
+        if (region < 2) o = qk_norm8<DK>(act, true, scale, p.eps);
+        else o = pack8(act);
         // slide the window
 #pragma unroll
         for (int j = 0; j < K - 1; ++j) win[j] = win[j + 1];
