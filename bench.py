@@ -3,13 +3,21 @@
 One step = one gdn_layer_core call (prologue + recurrence, every step of the
 hot path) over the prefill workload: B=1, T=4096, Hk=16, Hv=32, Dk=Dv=128,
 conv K=4, zero conv and recurrent state, seeded synthetic inputs resident in
-HBM before timing.  Metric: recurrence tokens/s*head = B*T*Hv / step time.
+HBM before timing.  The timed steps rotate over 4 sets of inputs and outputs
+(qkv, a, b, y, state and conv-state outputs: 401 MB together, more than the
+256 MB last-level cache), so each step reads inputs the previous steps did
+not leave in that cache; the single-set (warm) step time is reported beside
+it.  Metric: recurrence tokens/s*head = B*T*Hv / step time.
 
 Also measured in the same run (same JSON line):
-  * the dominant work, the chunked recurrence (its two launches, chunk
-    preparation and the sequential pass, one gdn_recurrent_chunked call),
-    timed alone with HIP events on the stream it is launched on -> roofline
-    of its algorithmic fp32 flops against the fp32 peak;
+  * roofline of the timed step (its two launches: the chunk preparation with
+    the prologue fused in, and the sequential pass): algorithmic fp32 flops
+    against the fp32 peak, computed on bf16 matrix cores through exact plane
+    splits; the bf16 matrix flops those launches issue (rocprofv3 counter,
+    committed under profiles/) against the bf16 matrix peak; HBM traffic;
+  * the chunked recurrence alone (one gdn_recurrent_chunked call on prepared
+    inputs), the same roofline;
+  * a plain device copy (read + write) as the practical HBM ceiling;
   * batched decode, B=64, T=1 (layer core, 8 rotating sets of state and conv
     state, 1 GiB, so the 256 MB last-level cache cannot hold them) -> HBM
     roofline of its recurrence kernel;
@@ -17,8 +25,10 @@ Also measured in the same run (same JSON line):
     y, gdn_gated_rmsnorm) on the prefill workload, each over 4 rotating
     buffer sets larger together than the last-level cache -> HBM roofline;
     and the gated layer core (gdn_layer_core_gated) step time;
-  * single-token decode B=1 (per-call time, warm and cold) and the long
-    batched prefill B=4, T=32768 (layer core and chunked recurrence);
+  * single-token decode B=1 (per-call time, warm and cold, marshalled once,
+    replayed from a HIP graph) beside the floor of a plain copy of its 2 MiB
+    state in the same graph form, and the long batched prefill B=4, T=32768
+    (layer core and chunked recurrence);
   * a speculative-verify window (B=64, T=4, state emitted after 1..4 steps)
     and per-key-gate decode (B=64, T=1), both HBM-bound, rotating state sets;
   * the CPU oracle on a bounded sample of the prefill workload, one thread.
@@ -37,6 +47,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_prep_amd", "csrc")
 KERNEL_SOURCES = {
+    "layer_core": ["chunked.hip"],
     "chunked_recurrence": ["chunked.hip"],
     "recurrent_chunk_kernel": ["recurrent.hip"],
     "recurrent_step_kernel": ["recurrent.hip"],
@@ -45,7 +56,9 @@ KERNEL_SOURCES = {
 }
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector alike)
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
 R_HBM = 4                      # rotating buffer sets for the HBM-bound kernels
+R_IN = 4                       # rotating input/output sets of the timed prefill step
 
 
 def source_digest(kernel):
@@ -58,9 +71,10 @@ def source_digest(kernel):
     return h.hexdigest()
 
 
-def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed counter summary, or None when
-    the kernel's source changed after the counters were taken."""
+def measured_counter(kernel, workload, key="traffic_bytes"):
+    """A per-launch figure from the committed counter summary
+    (profiles/traffic.txt: HBM traffic bytes, or issued bf16 matrix flops),
+    or None when the kernel's source changed after the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.txt")
     if not os.path.exists(path):
         return None
@@ -69,11 +83,27 @@ def measured_traffic(kernel, workload):
             if line.startswith("#") or not line.strip():
                 continue
             kv = dict(x.split("=", 1) for x in line.split())
-            if kv.get("kernel") == kernel and kv.get("workload") == workload:
+            if kv.get("kernel") == kernel and kv.get("workload") == workload and key in kv:
                 if kv.get("source_sha256") != source_digest(kernel):
                     return None
-                return int(kv["traffic_bytes"])
+                return int(kv[key])
     return None
+
+
+def measured_traffic(kernel, workload):
+    return measured_counter(kernel, workload, "traffic_bytes")
+
+
+def host_cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), else the platform string."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def parse():
@@ -84,8 +114,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-long", action="store_true", help="skip the B=4 T=32768 long-prefill leg")
-    ap.add_argument("--kernel-only", default=None, choices=[None, "recurrent", "prep", "decode", "copy", "chunked",
-                                                         "epilogue"],
+    ap.add_argument("--kernel-only", default=None,
+                    choices=[None, "recurrent", "prep", "decode", "copy", "chunked", "epilogue", "layer", "verify",
+                             "per_key_decode"],
                     help="launch only this kernel (for counter collection)")
     return ap.parse_args()
 
@@ -127,10 +158,19 @@ def main():
     cs_out = torch.empty(B, K - 1, C, dtype=torch.int16, device=dev)
     ws = torch.empty(binding.layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv), dtype=torch.uint8,
                      device=dev)
+    # the timed step's rotating sets: the same inputs in fresh buffers, own outputs
+    in_sets = [dict(qkv=d["qkv"].clone(), a=d["a"].clone(), b=d["b"].clone(), y=torch.empty_like(y),
+                    s=torch.empty_like(s_out), cs=torch.empty_like(cs_out)) for _ in range(R_IN)]
 
-    def step():
-        binding.layer_core(d["qkv"], d["conv_w"], d["conv_state"], cs_out, d["a"], d["b"], d["A_log"],
-                           d["dt_bias"], d["state"], s_out, y, ws, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv,
+    def step(i=None):
+        if i is None:      # the single resident set (warm)
+            binding.layer_core(d["qkv"], d["conv_w"], d["conv_state"], cs_out, d["a"], d["b"], d["A_log"],
+                               d["dt_bias"], d["state"], s_out, y, ws, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv,
+                               q_scale=qs, k_scale=ks, eps=eps)
+            return
+        x = in_sets[i % R_IN]
+        binding.layer_core(x["qkv"], d["conv_w"], d["conv_state"], x["cs"], x["a"], x["b"], d["A_log"],
+                           d["dt_bias"], d["state"], x["s"], x["y"], ws, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv,
                            q_scale=qs, k_scale=ks, eps=eps)
 
     # prologue outputs for timing the recurrence kernel alone
@@ -188,26 +228,28 @@ def main():
 
     if args.kernel_only:
         return kernel_only(args, torch, dev, prep_rot, rec_only, up, inputs, binding, np, chunked_only,
-                           epilogue_rot, epi_sets, y)
+                           epilogue_rot, epi_sets, y, step)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(max(args.warmup, R_IN)):
+        step(i)
     torch.cuda.synchronize()
-    print(f"[bench] prefill warmup done ({args.warmup})", file=sys.stderr, flush=True)
+    print(f"[bench] prefill warmup done ({max(args.warmup, R_IN)})", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     e1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     ms_step = e0.elapsed_time(e1) / args.steps
     value = B * T * Hv / (ms_step * 1e-3)
-    print(f"[bench] prefill layer core {ms_step * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    warm_us = time_kernel(torch, stream, step, args.steps)
+    print(f"[bench] prefill layer core {ms_step * 1e3:.1f} us/step ({R_IN} rotating sets), "
+          f"{warm_us:.1f} us/step warm (one set)", file=sys.stderr, flush=True)
 
     # dominant work alone, events on the stream it runs on: the chunked
     # recurrence (chunk_prep_kernel + chunk_seq_kernel), then for reference
@@ -222,10 +264,14 @@ def main():
     epi_bytes = 3 * B * T * Hv * Dv * 2 + Dv * 2
     flops = 7 * B * T * Hv * Dk * Dv
     achieved_tflops = flops / (chunk_us * 1e-6) / 1e12
+    step_tflops = flops / (ms_step * 1e-3) / 1e12
+    copy = bench_copy(torch, dev, stream)
     rec_bytes = (2 * B * T * Hk * Dk * 2 + B * T * Hv * Dv * 2 + 2 * B * T * Hv * 4 + B * T * Hv * Dv * 2
                  + B * Hv * Dv * Dk * 4)
     prep_bytes = (B * T * C * 2 + C * K * 2 + 2 * B * T * Hv * 2 + 2 * Hv * 4 + 2 * B * T * Hk * Dk * 2
                   + B * T * Hv * Dv * 2 + 2 * B * T * Hv * 4 + B * (K - 1) * C * 2)
+    print(f"[bench] layer core step {step_tflops:.1f} TFLOP/s ({step_tflops / FP32_PEAK_TFLOPS:.1%} of fp32 peak); "
+          f"device copy {copy['GBs_1GiB']:.0f} GB/s", file=sys.stderr, flush=True)
     print(f"[bench] chunked recurrence {chunk_us:.1f} us ({achieved_tflops:.1f} TFLOP/s, "
           f"{achieved_tflops / FP32_PEAK_TFLOPS:.1%} of fp32 peak); per-step form {step_form_us:.1f} us; "
           f"prep kernel {prep_us:.1f} us ({prep_bytes / prep_us / 1e3:.0f} GB/s)", file=sys.stderr, flush=True)
@@ -259,13 +305,15 @@ def main():
         "data": "synthetic (seeded)",
         "config": {"workload": "prefill B=1 T=4096 Hk=16 Hv=32 Dk=Dv=128 K=4, zero conv/recurrent state",
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "chunk_prep_kernel + chunk_seq_kernel (gdn_recurrent_chunked)",
-                     "achieved": achieved_tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tflops / FP32_PEAK_TFLOPS,
-                     "traffic": measured_traffic("chunked_recurrence", "prefill_T4096"),
-                     "traffic_algorithmic": rec_bytes,
-                     "flops_per_launch": flops, "avg_launch_us": chunk_us,
-                     "arithmetic": "fp32, on bf16 matrix cores through exact three-plane splits"},
+        "roofline": roofline_step(flops, ms_step * 1e3, step_tflops, B, T, Hk, Hv, Dk, Dv, C, K),
+        "recurrence_chunked_alone": {
+            "kernel": "chunk_prep_kernel<0, 2> + chunk_seq_kernel<1> (gdn_recurrent_chunked on prepared q/k/v/g/beta)",
+            "avg_launch_us": chunk_us, "achieved": achieved_tflops, "unit": "TFLOP/s",
+            "frac_fp32": achieved_tflops / FP32_PEAK_TFLOPS,
+            "traffic": measured_traffic("chunked_recurrence", "prefill_T4096"), "traffic_algorithmic": rec_bytes,
+            "bf16_matrix_flops": measured_counter("chunked_recurrence", "prefill_T4096", "mfma_bf16_flops")},
+        "prefill_warm_us_per_step": warm_us,
+        "device_copy": copy,
         "recurrence_per_step_form": {"kernel": "recurrent_chunk_kernel<128,32>", "avg_launch_us": step_form_us,
                                      "achieved_TFLOPs": flops / (step_form_us * 1e-6) / 1e12},
         "prologue": {"kernel": "prep_kernel<128,4>", "avg_launch_us": prep_us,
@@ -289,6 +337,43 @@ def main():
         "wall_s_timed": t_wall,
     }
     print(json.dumps(line), flush=True)
+
+
+def roofline_step(flops, step_us, step_tflops, B, T, Hk, Hv, Dk, Dv, C, K):
+    """Roofline of the timed step (its two launches).  The work is fp32
+    arithmetic, 7 Dk Dv flop per token*head, computed on the bf16 matrix
+    cores through exact three-plane splits of the f32 operands: the
+    fp32-equivalent rate against the fp32 peak, and the bf16 matrix flops the
+    launches issue against the bf16 matrix peak."""
+    mf = measured_counter("layer_core", "prefill_T4096", "mfma_bf16_flops")
+    # algorithmic bytes: qkv, a, b, conv weights read; y, state, conv-state tail written
+    alg = B * T * C * 2 + 2 * B * T * Hv * 2 + C * K * 2 + B * T * Hv * Dv * 2 + B * Hv * Dv * Dk * 4 \
+        + B * (K - 1) * C * 2
+    return {"bound": "mfma", "kernel": "chunk_prep_kernel<4, 2> + chunk_seq_kernel<1> (gdn_layer_core step)",
+            "dtype": "fp32 arithmetic on bf16 matrix cores (exact three-plane splits)",
+            "achieved": step_tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": step_tflops / FP32_PEAK_TFLOPS,
+            "traffic": measured_traffic("layer_core", "prefill_T4096"), "traffic_algorithmic": alg,
+            "flops_per_launch": flops, "avg_launch_us": step_us,
+            "bf16_matrix": None if mf is None else {
+                "flops_per_launch": mf, "achieved": mf / (step_us * 1e-6) / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": mf / (step_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}}
+
+
+def bench_copy(torch, dev, stream):
+    """A plain device copy (read + write), the practical HBM ceiling: 256 MiB
+    and 1 GiB buffers, two destinations alternating."""
+    out = {}
+    for name, nbytes in (("256MiB", 256 << 20), ("1GiB", 1 << 30)):
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = [torch.empty_like(src) for _ in range(2)]
+        ctr = iter(range(1 << 30))
+        us = time_kernel(torch, stream, lambda: dst[next(ctr) % 2].copy_(src), 10)
+        out[f"GBs_{name}"] = 2 * nbytes / us / 1e3
+        del src, dst
+    out["note"] = "torch copy_ of a device buffer, bytes read + written per microsecond"
+    return out
 
 
 def time_rotating(torch, stream, fn, n):
@@ -442,6 +527,31 @@ def bench_verify_and_per_key(args, torch, dev, up, inputs, binding, np):
     return res
 
 
+def serving_kernel(name, torch, dev, up, inputs, binding):
+    """One launch of the verify-window (snapshots) or per-key-decode call of
+    bench_verify_and_per_key, rotating its state sets (for counter passes)."""
+    B, Hk, Hv, Dk, Dv = 64, 16, 32, 128, 128
+    T, R, per_key, steps = (4, 2, False, [1, 2, 3, 4]) if name == "verify" else (1, 8, True, [])
+    raw = inputs.recurrence_raw(B=B, T=T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, workload_id=7, state=True)
+    q = (up(raw["q_raw"]).view(torch.bfloat16).float() / Dk ** 0.5).to(torch.bfloat16)
+    k = (up(raw["k_raw"]).view(torch.bfloat16).float() / Dk ** 0.5).to(torch.bfloat16)
+    v = up(raw["v"])
+    g = torch.full((B, T, Hv, Dk), 0.9, device=dev) if per_key else torch.full((B, T, Hv), 0.9, device=dev)
+    beta = torch.full((B, T, Hv), 0.5, device=dev)
+    y = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=dev)
+    sets = [dict(st=up(raw["state"]).clone(),
+                 snaps=torch.empty(len(steps), B, Hv, Dv, Dk, device=dev) if steps else None) for _ in range(R)]
+    ctr = iter(range(1 << 30))
+
+    def fn():
+        s_ = sets[next(ctr) % R]
+        if steps:
+            binding.recurrent_snapshots(q, k, v, g, beta, s_["st"], s_["st"], y, steps, s_["snaps"])
+        else:
+            binding.recurrent_per_key(q, k, v, g, beta, s_["st"], s_["st"], y)
+    return fn
+
+
 def bench_per_key_prefill(args, torch, dev, up, inputs, binding, np):
     """The per-key decay gate g [B,T,Hv,Dk] over a prefill-length sequence
     (B=1 T=4096 Hk=16 Hv=32 Dk=Dv=128): the chunked matrix-core form, the
@@ -579,6 +689,45 @@ def bench_decode_b1(args, torch, dev, up, inputs, binding, np):
         torch.cuda.synchronize()
         out[f"{name}_graph_us"] = a.elapsed_time(b) * 1e3 / 1000
         del graph
+    # the floor: a plain device copy of one 2 MiB state into another (the
+    # bytes the step must move, less q/k/v/g/beta/y), back to back over the
+    # same cold ring, eager and replayed from a graph of 100 copies
+    dst = [torch.empty_like(states[0]) for _ in range(2)]
+
+    def copy_state(st, i=[0]):
+        i[0] += 1
+        dst[i[0] % 2].copy_(st)
+    for i in range(R):
+        copy_state(states[i])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        copy_state(states[i % R])
+    b.record(stream)
+    torch.cuda.synchronize()
+    out["copy_state_eager_us"] = a.elapsed_time(b) * 1e3 / n
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        for i in range(100):
+            copy_state(states[i % R])
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(100):
+            copy_state(states[i % R])
+    graph.replay()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(10):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    out["copy_state_graph_us"] = a.elapsed_time(b) * 1e3 / 1000
+    del graph
+    print(f"[bench] decode B=1 floor: 2 MiB state copy {out['copy_state_eager_us']:.2f} us eager, "
+          f"{out['copy_state_graph_us']:.2f} us in a graph", file=sys.stderr, flush=True)
     print(f"[bench] decode B=1: recurrence {out['recurrent_warm_us']:.2f} us warm / {out['recurrent_cold_us']:.2f} us "
           f"cold / {out['recurrent_bound_us']:.2f} us bound / {out['recurrent_graph_us']:.2f} us in a graph; "
           f"layer core {out['layer_core_warm_us']:.2f} / {out['layer_core_cold_us']:.2f} / "
@@ -588,7 +737,8 @@ def bench_decode_b1(args, torch, dev, up, inputs, binding, np):
                        "cold = 256 rotating states (512 MiB)")
     out["note"] = ("per-call time of back-to-back calls (device time plus any host launch gap); *_bound_us: the "
                    "cold calls marshalled once with binding.bind and issued back to back; *_graph_us: the same calls "
-                   "captured in a HIP graph of 100 calls over the cold state ring and replayed")
+                   "captured in a HIP graph of 100 calls over the cold state ring and replayed; copy_state_*: the "
+                   "floor, a plain device copy of one 2 MiB state (4 MiB moved) in the same two forms")
     return out
 
 
@@ -669,17 +819,22 @@ def cpu_baseline(raw, Hk, Hv, Dk, Dv, qs, ks, eps):
     return {"value": len(heads) * T / dt, "unit": "token*head/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole prefill workload, computed per v-head (all {len(heads)}): prologue of the head's channels + recurrence "
                       f"over all {T} tokens, fp64, one thread",
-            "seconds": dt, "host": platform.processor() or platform.machine(),
-            "host_cpus": os.cpu_count()}
+            "seconds": dt, "host": host_cpu_model(), "host_cpus": os.cpu_count()}
 
 
 def kernel_only(args, torch, dev, prep_rot, rec_only, up, inputs, binding, np, chunked_only, epilogue_rot,
-                epi_sets, y):
+                epi_sets, y, step):
     """Launch one kernel a few times (for rocprofv3 counter passes), in the
-    configuration the benchmark times (rotating sets for prep and epilogue)."""
+    configuration the benchmark times (rotating sets for the prefill step,
+    prep and epilogue)."""
     n = max(args.steps, 1)
     ctr = iter(range(1 << 30))
-    if args.kernel_only == "recurrent":
+    if args.kernel_only == "layer":
+        def fn():
+            step(next(ctr))
+    elif args.kernel_only in ("verify", "per_key_decode"):
+        fn = serving_kernel(args.kernel_only, torch, dev, up, inputs, binding)
+    elif args.kernel_only == "recurrent":
         fn = rec_only
     elif args.kernel_only == "chunked":
         fn = chunked_only

@@ -108,10 +108,16 @@ gdn_status gdn_recurrent_masked(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_
 
 /*
  * gdn_recurrent_chunked -- the same recurrence as gdn_recurrent, evaluated in
- * chunks of 32 steps on the matrix cores (equal to the per-step loop up to
- * rounding order): within a chunk the deltas of all steps solve one unit
- * lower-triangular system built from k_t . k_s, beta and the decay ratios,
- * and the state advances by one dense product per chunk.
+ * chunks of 32 steps on the matrix cores: within a chunk the deltas of all
+ * steps solve one unit lower-triangular system built from k_t . k_s, beta
+ * and the decay ratios, and the state advances by one dense product per
+ * chunk.  Precision: the state path is fp32 -- every f32 operand of a
+ * product is cut exactly into three bf16 planes and the plane products are
+ * kept down to 2^-16 of the leading one (the dropped terms are below 2^-24
+ * relative), with f32 accumulation; y is formed from the two leading planes
+ * (2^-16 relative) and then rounded to bf16 (nearest even).  Results differ
+ * from gdn_recurrent by rounding only: the same tolerances hold against the
+ * exact recurrence, not bit equality.
  * Arguments as gdn_recurrent plus a caller-owned device workspace of at least
  * gdn_recurrent_chunked_workspace_bytes(...) bytes (256-byte aligned; not
  * read before written; may be NULL when that size is 0).
@@ -274,7 +280,8 @@ gdn_status gdn_recurrent_per_key(const gdn_bf16 *q, const gdn_bf16 *k, const gdn
 /*
  * gdn_recurrent_chunked_per_key -- the recurrence with the per-key decay gate
  * of gdn_recurrent_per_key, in the chunked matrix-core form of
- * gdn_recurrent_chunked (equal to the per-step loop up to rounding order).
+ * gdn_recurrent_chunked (the same precision: fp32 state path, y from two
+ * bf16 planes before its bf16 rounding).
  * Within a chunk the decay from step s to step t is per key column,
  * g_{s+1}[j] ... g_t[j]; it is formed as running products, never as a
  * quotient of cumulative decays, so any gate values in [0, 1] are safe.

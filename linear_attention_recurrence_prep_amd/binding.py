@@ -19,7 +19,8 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdn.so")
+# GDN_LIB selects another build of the same library (e.g. a sanitizer build)
+LIB_PATH = os.environ.get("GDN_LIB") or os.path.join(_HERE, "libgdn.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "gdn.h")
 
 _lib = None

@@ -34,13 +34,16 @@ def _hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose: bool = False, extra_flags=None, lib=LIB, obj_dir=OUT_DIR, link_flags=None) -> str:
+    """Compile every source and link ``lib`` (default: the in-tree
+    libgdn.so).  extra_flags / link_flags are appended to the compile and
+    link lines (a sanitizer build passes host-only flags and another path)."""
+    os.makedirs(obj_dir, exist_ok=True)
     extra = list(extra_flags or [])
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmd = [_hipcc(), *COMMON, *DEVICE_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c",
                os.path.join(CSRC, src), "-o", obj]
@@ -59,13 +62,13 @@ def build(verbose: bool = False, extra_flags=None) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    tmp = lib + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *(link_flags or []), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

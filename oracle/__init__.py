@@ -40,9 +40,13 @@ def lib():
     """Load (building first if absent) the oracle's shared library."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
-            build()
-        L = ctypes.CDLL(LIB)
+        # GDN_ORACLE_LIB selects another build of the oracle (a sanitizer build)
+        path = os.environ.get("GDN_ORACLE_LIB")
+        if path is None:
+            path = LIB
+            if not os.path.exists(path):
+                build()
+        L = ctypes.CDLL(path)
         L.oracle_f64_to_bf16.argtypes = [_d]
         L.oracle_f64_to_bf16.restype = ctypes.c_uint16
         L.oracle_round_bf16_array.argtypes = [_dp, _hp, ctypes.c_size_t]

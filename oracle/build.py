@@ -12,16 +12,16 @@ SRC = os.path.join(HERE, "gdn_oracle.c")
 LIB = os.path.join(HERE, "libgdn_oracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, lib: str = LIB, extra_flags=None) -> str:
     cmd = [
         "gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off",
-        "-Wall", "-Wextra", "-shared", "-fPIC", SRC, "-o", LIB + ".tmp", "-lm",
+        "-Wall", "-Wextra", *(extra_flags or []), "-shared", "-fPIC", SRC, "-o", lib + ".tmp", "-lm",
     ]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":
