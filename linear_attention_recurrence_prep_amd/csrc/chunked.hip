@@ -161,6 +161,11 @@ __device__ __forceinline__ f4_t mma(u4_t a, u4_t b, f4_t c) {
                                                    0, 0, 0);
 }
 
+// 16x16x4 f32 product: lane l gives A[l % 16][l / 16] and B[l / 16][l % 16]
+__device__ __forceinline__ f4_t mma_f32(float a, float b, f4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // f32 (planes) x exact bf16, smallest term first
 __device__ __forceinline__ f4_t mma3a(const Planes& a, u4_t b, f4_t c) {
     c = mma(a.l, b, c);
@@ -251,7 +256,7 @@ struct ChunkPtrs {
     float* rg;      // per unit: -rho in kperm order [32], then gamma_t [32]
                     // (per-key form: -1, 1, then Gamma_{C-1} per key column [Dk])
     u4_t* qsw;      // q rows (per-key form: Q o Gamma, two planes per v-unit)
-    u4_t* ksw;      // k columns (per-key form: (K o E)^T, three planes per v-unit)
+    u4_t* ksw;      // k columns (per-key form: -(K o E)^T in f32 per v-unit)
 };
 
 // floats of the per-unit decay record (-rho, gamma; per-key form: and Gamma_{C-1})
@@ -749,11 +754,10 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) 
                 }
             }
             kwp[tt] = split8(no, f4_t{xw[0], xw[1], xw[2], xw[3]}, f4_t{xw[4], xw[5], xw[6], xw[7]});
-            const Planes ke = split8(no, f4_t{xe[0], xe[1], xe[2], xe[3]}, f4_t{xe[4], xe[5], xe[6], xe[7]});
-            u4_t* kd = o.ksw + unit * 3 * kQVec + (wl * 2 + tt) * 64 + lane;
-            kd[0] = ke.h;
-            kd[kQVec] = ke.m;
-            kd[2 * kQVec] = ke.l;
+            // -(K o E)^T in f32: element 4 jt + i is step 16 jt + 4 lq + i
+            u4_t* kd = o.ksw + unit * 2 * kQVec + (wl * 2 + tt) * 2 * 64 + lane;
+            kd[0] = __builtin_bit_cast(u4_t, f4_t{-xe[0], -xe[1], -xe[2], -xe[3]});
+            kd[64] = __builtin_bit_cast(u4_t, f4_t{-xe[4], -xe[5], -xe[6], -xe[7]});
         }
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
@@ -987,16 +991,20 @@ __device__ __forceinline__ __attribute__((address_space(1))) T* uniform_ptr_w(T*
     return (__attribute__((address_space(1))) T*)(((uint64_t)hi << 32) | lo);
 }
 
-// One chunk's operands in registers (NR row tiles of 16 state rows).  The
-// per-key form (PK) takes q and k from PkOps instead.
+// One chunk's operands in registers (NR row tiles of 16 state rows).
 template <int NR, bool PK = false>
 struct SeqOps {
     f4_t wf[2][2];    // W of t-tiles 0 and 1 (f32, elements 0..3 and 4..7)
-    Planes w[2];      // the same as bf16 planes (cut one step before use)
-    u4_t q[2];        // q, t-tiles 0 and 1
-    u4_t k[2];        // k^T, this wave's two column tiles
+    u4_t q[2];        // q, t-tiles 0 and 1 (per-key form: Q o Gamma, leading plane)
+    u4_t k[2];        // k^T, this wave's two column tiles (per-head form)
     u4_t a0[NR];      // -Tb V of t-tile (wave & 1), per row tile (f32 bits; waves 0, 1 use it)
     float rg;         // -rho[lane] (lanes 0..31), gamma[lane - 32] (lanes 32..63)
+    // per-key form: Q o Gamma's second plane, -(K o E)^T in f32 (this wave's
+    // column tiles tt, t-tiles jt) and Gamma_{C-1} at this lane's state
+    // columns 32 w + 16 tt + 4 q .. + 3
+    u4_t qm[2];
+    f4_t kf[2][2];
+    f4_t gd[2];
 
     // Loads of one chunk in four parts, so that the sequential pass can
     // spread them over the step it overlaps (part 0: W tile 0, 1: W tile 1,
@@ -1010,8 +1018,20 @@ struct SeqOps {
             const auto ws = uniform_ptr(in.wsw + unit * kWVec + wv * 4 * 64 + PART * 2 * 64);
             wf[PART][0] = __builtin_bit_cast(f4_t, ws[lane]);
             wf[PART][1] = __builtin_bit_cast(f4_t, ws[64 + lane]);
+        } else if constexpr (PART == 2 && PK) {
+            const auto qs = uniform_ptr(in.qsw + unit * 2 * kQVec + wv * 2 * 64);
+            const auto ks = uniform_ptr(in.ksw + unit * 2 * kQVec + wv * 4 * 64);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                q[t] = qs[t * 64 + lane];
+                qm[t] = qs[kQVec + t * 64 + lane];
+                kf[t][0] = __builtin_bit_cast(f4_t, ks[(2 * t) * 64 + lane]);
+                kf[t][1] = __builtin_bit_cast(f4_t, ks[(2 * t + 1) * 64 + lane]);
+            }
+            const auto gs = uniform_ptr(reinterpret_cast<const f4_t*>(in.rg + unit * rg_floats<true>() + 2 * CK + 32 * wv));
+            gd[0] = gs[lane >> 4];
+            gd[1] = gs[4 + (lane >> 4)];
         } else if constexpr (PART == 2) {
-            if constexpr (PK) return;
             const auto qs = uniform_ptr(in.qsw + kunit * kQVec + wv * 2 * 64);
             const auto ks = uniform_ptr(in.ksw + kunit * kQVec + wv * 2 * 64);
             q[0] = qs[lane];
@@ -1028,43 +1048,11 @@ struct SeqOps {
         }
     }
 
-    __device__ __forceinline__ void split_w(const NegOnes& no) {
-        w[0] = split8(no, wf[0][0], wf[0][1]);
-        w[1] = split8(no, wf[1][0], wf[1][1]);
-    }
-
     __device__ __forceinline__ void load_all(const SeqIn& in, const SeqCtx& x, int c) {
         load<0>(in, x, c);
         load<1>(in, x, c);
         load<2>(in, x, c);
         load<3>(in, x, c);
-    }
-};
-
-// The per-key form's operands of one chunk: Q o Gamma (two planes, t-tiles 0
-// and 1), (K o E)^T (three planes, this wave's two column tiles) and
-// Gamma_{C-1} at this lane's state columns 32 w + 16 tt + 4 q .. + 3.
-struct PkOps {
-    u4_t qh[2], qm[2];
-    Planes k[2];
-    f4_t gd[2];
-
-    __device__ __forceinline__ void load(const SeqIn& in, const SeqCtx& x, int c) {
-        const int64_t unit = x.unit0 + c;
-        const int wv = x.wv, lane = x.lane;
-        const auto qs = uniform_ptr(in.qsw + unit * 2 * kQVec + wv * 2 * 64);
-        const auto ks = uniform_ptr(in.ksw + unit * 3 * kQVec + wv * 2 * 64);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            qh[t] = qs[t * 64 + lane];
-            qm[t] = qs[kQVec + t * 64 + lane];
-            k[t].h = ks[t * 64 + lane];
-            k[t].m = ks[kQVec + t * 64 + lane];
-            k[t].l = ks[2 * kQVec + t * 64 + lane];
-        }
-        const auto gs = uniform_ptr(reinterpret_cast<const f4_t*>(in.rg + unit * rg_floats<true>() + 2 * CK + 32 * wv));
-        gd[0] = gs[lane >> 4];
-        gd[1] = gs[4 + (lane >> 4)];
     }
 };
 
@@ -1187,18 +1175,16 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
         }
     }
 
-    // one chunk c (b3 = c mod 3) with o; W of the next chunk (n1) is cut into
-    // planes and the loads of chunk cn into nx are spread over it
-    PkOps pk;         // per-key form: the chunk's q, k and column decays
+    // one chunk c (b3 = c mod 3) with o; the loads of chunk cn into nx are
+    // spread over it (n1, the next chunk's set, is already in flight)
     auto step = [&](int c, int b3, const SeqOps<NR, PK>& o, SeqOps<NR, PK>& n1, SeqOps<NR, PK>& nx, int cn) {
-        // state planes: element e of quarter lq is column kperm(lq, e)
-        Planes s[NR];
-#pragma unroll
-        for (int rt = 0; rt < NR; ++rt) s[rt] = split8(no, S[rt][0], S[rt][1]);
+        (void)n1;
         SEQ_PIN(nx.template load<0>(in, x, cn));
 
         // this wave's share of W S^T - Tb V (rows t, columns r), two t-tiles
-        // per row tile
+        // per row tile, on the f32 matrix instruction: element e of quarter
+        // lq of W's row and of S's row is column kperm(lq, e), so element e
+        // of both is the operand of product e (four columns, one per quarter)
         f4_t x0[NR], x1[NR];
 #pragma unroll
         for (int rt = 0; rt < NR; ++rt) {
@@ -1208,38 +1194,20 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
             else if (wv == 1) x1[rt] = __builtin_bit_cast(f4_t, o.a0[rt]);
         }
 #pragma unroll
-        for (int rt = 0; rt < NR; ++rt) {
-            x0[rt] = mma(o.w[0].l, s[rt].h, x0[rt]);
-            x1[rt] = mma(o.w[1].l, s[rt].h, x1[rt]);
-        }
+        for (int e = 0; e < 8; ++e) {
 #pragma unroll
-        for (int rt = 0; rt < NR; ++rt) {
-            x0[rt] = mma(o.w[0].h, s[rt].l, x0[rt]);
-            x1[rt] = mma(o.w[1].h, s[rt].l, x1[rt]);
+            for (int rt = 0; rt < NR; ++rt) {
+                x0[rt] = mma_f32(o.wf[0][e >> 2][e & 3], S[rt][e >> 2][e & 3], x0[rt]);
+                x1[rt] = mma_f32(o.wf[1][e >> 2][e & 3], S[rt][e >> 2][e & 3], x1[rt]);
+            }
         }
+        // the state's two leading bf16 planes, for S Q^T (y is rounded to
+        // bf16: 2^-16 relative suffices)
+        u4_t s_h[NR], s_m[NR];
 #pragma unroll
-        for (int rt = 0; rt < NR; ++rt) {
-            x0[rt] = mma(o.w[0].m, s[rt].m, x0[rt]);
-            x1[rt] = mma(o.w[1].m, s[rt].m, x1[rt]);
-        }
-#pragma unroll
-        for (int rt = 0; rt < NR; ++rt) {
-            x0[rt] = mma(o.w[0].m, s[rt].h, x0[rt]);
-            x1[rt] = mma(o.w[1].m, s[rt].h, x1[rt]);
-        }
-#pragma unroll
-        for (int rt = 0; rt < NR; ++rt) {
-            x0[rt] = mma(o.w[0].h, s[rt].m, x0[rt]);
-            x1[rt] = mma(o.w[1].h, s[rt].m, x1[rt]);
-        }
-#pragma unroll
-        for (int rt = 0; rt < NR; ++rt) {
-            x0[rt] = mma(o.w[0].h, s[rt].h, x0[rt]);
-            x1[rt] = mma(o.w[1].h, s[rt].h, x1[rt]);
-        }
+        for (int rt = 0; rt < NR; ++rt) split8hm(no, S[rt][0], S[rt][1], s_h[rt], s_m[rt]);
 
         SEQ_PIN(nx.template load<1>(in, x, cn));
-        n1.split_w(no);
 
 #pragma unroll
         for (int rt = 0; rt < NR; ++rt) {
@@ -1272,39 +1240,48 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
             f4_t y0v, y1v;
             if constexpr (PK) {
                 // Q o Gamma in two planes: h.h, h.m and m.h
-                y0v = mma(s[rt].m, pk.qh[0], zero);
-                y1v = mma(s[rt].m, pk.qh[1], zero);
-                y0v = mma(s[rt].h, pk.qm[0], y0v);
-                y1v = mma(s[rt].h, pk.qm[1], y1v);
-                y0v = mma(s[rt].h, pk.qh[0], y0v);
-                y1v = mma(s[rt].h, pk.qh[1], y1v);
+                y0v = mma(s_m[rt], o.q[0], zero);
+                y1v = mma(s_m[rt], o.q[1], zero);
+                y0v = mma(s_h[rt], o.qm[0], y0v);
+                y1v = mma(s_h[rt], o.qm[1], y1v);
+                y0v = mma(s_h[rt], o.q[0], y0v);
+                y1v = mma(s_h[rt], o.q[1], y1v);
             } else {
-                y0v = mma(s[rt].m, o.q[0], zero);
-                y1v = mma(s[rt].m, o.q[1], zero);
-                y0v = mma(s[rt].h, o.q[0], y0v);
-                y1v = mma(s[rt].h, o.q[1], y1v);
+                y0v = mma(s_m[rt], o.q[0], zero);
+                y1v = mma(s_m[rt], o.q[1], zero);
+                y0v = mma(s_h[rt], o.q[0], y0v);
+                y1v = mma(s_h[rt], o.q[1], y1v);
             }
             f4_t* yb = sh.y[b3][rt];
             yb[(2 * wv) * 64 + lane] = y0v;
             yb[(2 * wv + 1) * 64 + lane] = y1v;
         }
 
-        // S = gamma_{C-1} S + K^T (diag(rho) Delta)
-        const f4_t rh0 = *reinterpret_cast<const f4_t*>(rg + 8 * lq);
-        const f4_t rh1 = *reinterpret_cast<const f4_t*>(rg + 8 * lq + 4);
-        const float gc = rg[2 * CK - 1];
-        Planes bs[NR];
+        if constexpr (PK) {
+            // per-key: S = S diag(Gamma_{C-1}) + Delta^T (K o E) on the f32
+            // matrix instruction, Delta = -D: product 4 jt + i takes steps
+            // 16 jt + 4 q + i, element i of D's t-tile jt and of -(K o E)^T's
 #pragma unroll
-        for (int rt = 0; rt < NR; ++rt) bs[rt] = split8(no, rh0 * d0[rt], rh1 * d1[rt]);
+            for (int rt = 0; rt < NR; ++rt) {
 #pragma unroll
-        for (int rt = 0; rt < NR; ++rt) {
-            if constexpr (PK) {
-                // per-key: S = S diag(Gamma_{C-1}) + ((K o E)^T Delta)^T
-                S[rt][0] = S[rt][0] * pk.gd[0];
-                S[rt][1] = S[rt][1] * pk.gd[1];
-                S[rt][0] = mma6(pk.k[0], bs[rt], S[rt][0]);
-                S[rt][1] = mma6(pk.k[1], bs[rt], S[rt][1]);
-            } else {
+                for (int tt = 0; tt < 2; ++tt) {
+                    S[rt][tt] = S[rt][tt] * o.gd[tt];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[rt][tt] = mma_f32(o.kf[tt][0][i], d0[rt][i], S[rt][tt]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) S[rt][tt] = mma_f32(o.kf[tt][1][i], d1[rt][i], S[rt][tt]);
+                }
+            }
+        } else {
+            // S = gamma_{C-1} S + K^T (diag(rho) Delta)
+            const f4_t rh0 = *reinterpret_cast<const f4_t*>(rg + 8 * lq);
+            const f4_t rh1 = *reinterpret_cast<const f4_t*>(rg + 8 * lq + 4);
+            const float gc = rg[2 * CK - 1];
+            Planes bs[NR];
+#pragma unroll
+            for (int rt = 0; rt < NR; ++rt) bs[rt] = split8(no, rh0 * d0[rt], rh1 * d1[rt]);
+#pragma unroll
+            for (int rt = 0; rt < NR; ++rt) {
                 S[rt][0] = S[rt][0] * gc;
                 S[rt][1] = S[rt][1] * gc;
                 S[rt][0] = mma3b(o.k[0], bs[rt], S[rt][0]);
@@ -1319,17 +1296,12 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
             }
         }
         SEQ_PIN(nx.template load<3>(in, x, cn));
-        // per-key form: the next chunk's q, k and column decays (one set in
-        // registers, loaded once this chunk's are consumed)
-        if constexpr (PK) SEQ_PIN(pk.load(in, x, min(c + 1, NC - 1)));
     };
 
     // three operand sets: chunk c + 2 loads while chunk c runs
-    if constexpr (PK) pk.load(in, x, 0);
     SeqOps<NR, PK> o0, o1, o2;
     o0.load_all(in, x, 0);
     o1.load_all(in, x, min(1, NC - 1));
-    o0.split_w(no);
     int c = 0;
     for (; c + 3 <= NC; c += 3) {     // one exit: the sets rotate through whole rounds
         step(c, 0, o0, o1, o2, min(c + 2, NC - 1));
@@ -1371,7 +1343,7 @@ ChunkedLayout chunked_layout(int B, int T, int Hk, int Hv, int Dk, int Dv, bool 
         // Q o Gamma (two planes) and (K o E)^T (three) per v-unit, Gamma_{C-1} in the decay record
         L.qsw = L.rg + a256(units * rg_floats<true>() * 4);
         L.ksw = L.qsw + a256(units * 2 * kQVec * 16);
-        L.total = L.ksw + a256(units * 3 * kQVec * 16);
+        L.total = L.ksw + a256(units * 2 * kQVec * 16);
     } else {
         L.qsw = L.rg + a256(units * 2 * CK * 4);
         L.ksw = L.qsw + a256(kunits * kQVec * 16);
