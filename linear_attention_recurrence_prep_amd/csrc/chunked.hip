@@ -632,20 +632,25 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) 
         // dot products, their 8-lane sums, A and P of (t, s)
         auto pk_step = [&](int t, const RowOps& r, auto mask) {
             constexpr bool MASK = decltype(mask)::value;
-            float pa = 0.f, pp = 0.f;
+            // four partial sums per product (short dependent chains)
+            float pa4[4], pp4[4];
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) {
                 const float ga[4] = {r.g[e4].x, r.g[e4].y, r.g[e4].z, r.g[e4].w};
                 const float ka[4] = {r.k[e4].x, r.k[e4].y, r.k[e4].z, r.k[e4].w};
                 const float qa[4] = {r.q[e4].x, r.q[e4].y, r.q[e4].z, r.q[e4].w};
+                pa4[e4] = 0.f;
+                pp4[e4] = 0.f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float& ue = u[4 * e4 + i];
                     if (!MASK || t > s) ue *= ga[i];
-                    pa = fmaf(ka[i], ue, pa);
-                    pp = fmaf(qa[i], ue, pp);
+                    pa4[e4] = fmaf(ka[i], ue, pa4[e4]);
+                    pp4[e4] = fmaf(qa[i], ue, pp4[e4]);
                 }
             }
+            float pa = (pa4[0] + pa4[1]) + (pa4[2] + pa4[3]);
+            float pp = (pp4[0] + pp4[1]) + (pp4[2] + pp4[3]);
             group_sum2<8>(pa, pp);
             if (jg == 0) {
                 sw.a[t][s] = t > s ? sh.bs[0][t] * pa : 0.f;
