@@ -1325,6 +1325,181 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
     }
 }
 
+// ================================================ sequential pass, row waves
+
+// For grids of more than two row tiles per CU: one wave per 16-row state tile
+// over all Dk columns, so that no wave needs another's partial products (no
+// exchange, every wave keeps its matrix pipe busy), four waves (64 rows of
+// one v-head) per block.  The chunk's W, q, k, -Tb V of the block's four
+// tiles, -P and rho/gamma are staged by the whole block into a three-slot
+// LDS ring two chunks ahead, one barrier per chunk.  Column slice s
+// (columns 32 s .. 32 s + 31) takes the part of chunk_seq_kernel's wave s,
+// and every product and sum is formed in that kernel's order, so the results
+// are bit-identical to it.
+constexpr int RWW = 4;                                            // row tiles (waves) per block
+constexpr int RW_THREADS = 64 * RWW;
+constexpr int RW_VEC = kWVec + 2 * kQVec + RWW * 2 * 64 + kPVec;  // 16-byte vectors per slot
+constexpr int RW_PER = RW_VEC / RW_THREADS;                       // staged per thread
+static_assert(RW_VEC % RW_THREADS == 0 && kWVec % RW_THREADS == 0 && kQVec % RW_THREADS == 0 &&
+                  (RWW * 2 * 64) % RW_THREADS == 0 && kPVec % RW_THREADS == 0,
+              "whole staging rounds per region");
+
+struct RowSlot {
+    u4_t v[RW_VEC];       // W | q | k | -Tb V (tiles of the block) | -P, in the workspace layout
+    float rg[2 * CK];     // -rho (kperm order), gamma
+};
+constexpr int RW_Q = kWVec, RW_K = RW_Q + kQVec, RW_U = RW_K + kQVec, RW_P = RW_U + RWW * 2 * 64;
+
+__global__ __launch_bounds__(RW_THREADS) void chunk_seq_rows_kernel(SeqIn in, const float* state_in,
+                                                                    float* state_out, uint16_t* __restrict__ y,
+                                                                    const uint8_t* __restrict__ mask, int T, int Hk,
+                                                                    int Hv, int Dv, int NC, int row_blocks,
+                                                                    int n_blocks) {
+    __shared__ RowSlot ring[3];
+
+    int lb = blockIdx.x;
+    if ((n_blocks & 7) == 0) lb = (lb & 7) * (n_blocks >> 3) + (lb >> 3);
+    const int n = lb / row_blocks;
+    const int rblk = lb % row_blocks;
+    const int b = n / Hv, hv = n % Hv;
+    const int hk = hv / (Hv / Hk);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lq = lane >> 4;
+    const int tile0 = rblk * RWW;
+    const int r0 = (tile0 + wv) * RB;             // this wave's first state row
+    const int row_tiles = Dv / RB;
+    const int64_t unit0 = (int64_t)n * NC, kunit0 = ((int64_t)b * Hk + hk) * NC;
+    const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+    const NegOnes no = neg_ones();
+    const int64_t vstride = (int64_t)Hv * Dv;     // one step of y
+
+    // tile tt, register i: S[r0 + lr][16 tt + 4 lq + i]
+    f4_t S[8];
+    const int64_t soff = ((int64_t)n * Dv + r0 + lr) * DKC + 4 * lq;
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+        S[tt] = state_in ? *reinterpret_cast<const f4_t*>(state_in + soff + 16 * tt) : zero;
+
+    // staging of chunk c by the whole block, coalesced: loads now, LDS stores later
+    u4_t g[RW_PER], grg = {0, 0, 0, 0};
+    auto stage_load = [&](int c) {
+        const int64_t unit = unit0 + c, kunit = kunit0 + c;
+        const auto sw = uniform_ptr(in.wsw + unit * kWVec);
+        const auto sq = uniform_ptr(in.qsw + kunit * kQVec);
+        const auto sk = uniform_ptr(in.ksw + kunit * kQVec);
+        const auto su = uniform_ptr(in.u + (unit * row_tiles + tile0) * 2 * 64);
+        const auto spn = uniform_ptr(in.pn + unit * kPVec);
+#pragma unroll
+        for (int j = 0; j < RW_PER; ++j) {
+            const int i = tid + j * RW_THREADS;   // region of i is fixed by j
+            if (j * RW_THREADS < RW_Q) g[j] = sw[i];
+            else if (j * RW_THREADS < RW_K) g[j] = sq[i - RW_Q];
+            else if (j * RW_THREADS < RW_U) g[j] = sk[i - RW_K];
+            else if (j * RW_THREADS < RW_P) g[j] = su[i - RW_U];
+            else g[j] = spn[i - RW_P];
+        }
+        if (tid < 2 * CK / 4) grg = uniform_ptr(reinterpret_cast<const u4_t*>(in.rg + unit * 2 * CK))[tid];
+    };
+    auto stage_store = [&](int slot) {
+#pragma unroll
+        for (int j = 0; j < RW_PER; ++j) ring[slot].v[tid + j * RW_THREADS] = g[j];
+        if (tid < 2 * CK / 4) reinterpret_cast<u4_t*>(ring[slot].rg)[tid] = grg;
+    };
+
+    stage_load(0);
+    stage_store(0);
+    if (NC > 1) {
+        stage_load(1);
+        stage_store(1);
+    }
+    __syncthreads();
+
+    uint16_t* yw = y + ((int64_t)b * T * Hv + hv) * Dv + r0 + 4 * lq;
+    int slot = 0;
+    for (int c = 0; c < NC; ++c) {
+        const bool pre = c + 2 < NC;
+        if (pre) stage_load(c + 2);
+        const RowSlot& o = ring[slot];
+
+        // W S^T - Tb V: slice s's share as wave s of chunk_seq_kernel forms it
+        // (-Tb V enters slice 0's t-tile 0 and slice 1's t-tile 1)
+        f4_t x[4][2];
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            x[sl][0] = sl == 0 ? __builtin_bit_cast(f4_t, o.v[RW_U + (wv * 2 + 0) * 64 + lane]) : zero;
+            x[sl][1] = sl == 1 ? __builtin_bit_cast(f4_t, o.v[RW_U + (wv * 2 + 1) * 64 + lane]) : zero;
+        }
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            f4_t wf[2][2];
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+                wf[jt][0] = __builtin_bit_cast(f4_t, o.v[(sl * 4 + jt * 2) * 64 + lane]);
+                wf[jt][1] = __builtin_bit_cast(f4_t, o.v[(sl * 4 + jt * 2 + 1) * 64 + lane]);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                x[sl][0] = mma_f32(wf[0][e >> 2][e & 3], S[2 * sl + (e >> 2)][e & 3], x[sl][0]);
+                x[sl][1] = mma_f32(wf[1][e >> 2][e & 3], S[2 * sl + (e >> 2)][e & 3], x[sl][1]);
+            }
+        }
+        // S Q^T shares per slice from the state's two leading planes, summed in slice order
+        f4_t ys[2];
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            u4_t s_h, s_m;
+            split8hm(no, S[2 * sl], S[2 * sl + 1], s_h, s_m);
+            const u4_t q0 = o.v[RW_Q + (sl * 2) * 64 + lane], q1 = o.v[RW_Q + (sl * 2 + 1) * 64 + lane];
+            f4_t y0v = mma(s_m, q0, zero), y1v = mma(s_m, q1, zero);
+            y0v = mma(s_h, q0, y0v);
+            y1v = mma(s_h, q1, y1v);
+            ys[0] = sl == 0 ? y0v : ys[0] + y0v;
+            ys[1] = sl == 0 ? y1v : ys[1] + y1v;
+        }
+        // D = W S^T - Tb V = -Delta, summed in slice order
+        const f4_t d0 = ((x[0][0] + x[1][0]) + x[2][0]) + x[3][0];
+        const f4_t d1 = ((x[0][1] + x[1][1]) + x[2][1]) + x[3][1];
+
+        // S = gamma_{C-1} S + K^T (diag(rho) Delta)
+        const f4_t rh0 = *reinterpret_cast<const f4_t*>(o.rg + 8 * lq);
+        const f4_t rh1 = *reinterpret_cast<const f4_t*>(o.rg + 8 * lq + 4);
+        const float gc = o.rg[2 * CK - 1];
+        const Planes bs = split8(no, rh0 * d0, rh1 * d1);
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+            S[tt] = S[tt] * gc;
+            S[tt] = mma3b(o.v[RW_K + tt * 64 + lane], bs, S[tt]);
+        }
+
+        // y of the chunk: Y^T = gamma_t (S Q^T) + D^T (-P)^T, leading planes of D and P
+        u4_t dh, dm;
+        split8hm(no, d0, d1, dh, dm);
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+            const int yt = 16 * jt + lr;
+            f4_t yv = ys[jt] * o.rg[CK + yt];
+            const u4_t ch = o.v[RW_P + (jt * 2) * 64 + lane], cm = o.v[RW_P + (jt * 2 + 1) * 64 + lane];
+            yv = mma(dm, ch, yv);
+            yv = mma(dh, cm, yv);
+            yv = mma(dh, ch, yv);
+            const int t = c * CK + yt;
+            if (t < T) {
+                u2_t w = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
+                if (mask != nullptr && mask[(int64_t)b * T + t] == 0) w = u2_t{0, 0};   // masked step
+                *reinterpret_cast<u2_t*>(yw + (int64_t)t * vstride) = w;
+            }
+        }
+
+        if (pre) stage_store(slot == 0 ? 2 : slot - 1);    // slot of chunk c + 2, last read in step c - 1
+        __syncthreads();
+        slot = slot == 2 ? 0 : slot + 1;
+    }
+
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) *reinterpret_cast<f4_t*>(state_out + soff + 16 * tt) = S[tt];
+}
+
 // ================================================================== launch
 
 // Lane offsets of v and y rows inside a chunk are 32-bit: Hv * Dv <= 2^25.
@@ -1452,8 +1627,18 @@ static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, 
     in.qsw = o.qsw;
     in.ksw = o.ksw;
     // two row tiles per block once one tile per block would need more blocks
-    // than the device has CUs (the sequential blocks run one per CU)
+    // than the device has CUs (the sequential blocks run one per CU); one
+    // wave per row tile (chunk_seq_rows_kernel) once two tiles per block
+    // would still need more
     const int cus = device_cu_count();
+    const int64_t tiles = (int64_t)a.B * a.Hv * (a.Dv / RB);
+    if (!a.g_per_key && a.Dv % (RWW * RB) == 0 && cus > 0 && tiles > 2 * (int64_t)cus) {
+        const int rb = a.Dv / (RWW * RB);
+        const int64_t nb = (int64_t)a.B * a.Hv * rb;
+        hipLaunchKernelGGL(chunk_seq_rows_kernel, dim3((unsigned)nb), dim3(RW_THREADS), 0, stream, in, a.state_in,
+                           a.state_out, a.y, a.mask, a.T, a.Hk, a.Hv, a.Dv, L.nc, rb, (int)nb);
+        return hipGetLastError();
+    }
     const bool two = !a.g_per_key && a.Dv % (2 * RB) == 0 && cus > 0 && (int64_t)a.B * a.Hv * (a.Dv / RB) > cus;
     const int row_blocks = a.Dv / (RB * (two ? 2 : 1));
     const int64_t blocks = (int64_t)a.B * a.Hv * row_blocks;
