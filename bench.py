@@ -12,9 +12,10 @@ it.  Metric: recurrence tokens/s*head = B*T*Hv / step time.
 Also measured in the same run (same JSON line):
   * roofline of the timed step (its two launches: the chunk preparation with
     the prologue fused in, and the sequential pass): algorithmic fp32 flops
-    against the fp32 peak, computed on bf16 matrix cores through exact plane
-    splits; the bf16 matrix flops those launches issue (rocprofv3 counter,
-    committed under profiles/) against the bf16 matrix peak; HBM traffic;
+    against the fp32 peak, computed on the matrix cores (the f32 matrix
+    instruction for W S^T, bf16 products of exact plane splits elsewhere);
+    the f32 and bf16 matrix flops those launches issue (rocprofv3 counters,
+    committed under profiles/) against those peaks; HBM traffic;
   * the chunked recurrence alone (one gdn_recurrent_chunked call on prepared
     inputs), the same roofline;
   * a plain device copy (read + write) as the practical HBM ceiling;
@@ -57,6 +58,7 @@ KERNEL_SOURCES = {
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 (matrix and vector alike)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
+F32_MATRIX_PEAK_TFLOPS = 157.3 # MI355X dense f32 matrix
 R_HBM = 4                      # rotating buffer sets for the HBM-bound kernels
 R_IN = 4                       # rotating input/output sets of the timed prefill step
 
@@ -311,7 +313,8 @@ def main():
             "avg_launch_us": chunk_us, "achieved": achieved_tflops, "unit": "TFLOP/s",
             "frac_fp32": achieved_tflops / FP32_PEAK_TFLOPS,
             "traffic": measured_traffic("chunked_recurrence", "prefill_T4096"), "traffic_algorithmic": rec_bytes,
-            "bf16_matrix_flops": measured_counter("chunked_recurrence", "prefill_T4096", "mfma_bf16_flops")},
+            "bf16_matrix_flops": measured_counter("chunked_recurrence", "prefill_T4096", "mfma_bf16_flops"),
+            "f32_matrix_flops": measured_counter("chunked_recurrence", "prefill_T4096", "mfma_f32_flops")},
         "prefill_warm_us_per_step": warm_us,
         "device_copy": copy,
         "recurrence_per_step_form": {"kernel": "recurrent_chunk_kernel<128,32>", "avg_launch_us": step_form_us,
@@ -341,23 +344,28 @@ def main():
 
 def roofline_step(flops, step_us, step_tflops, B, T, Hk, Hv, Dk, Dv, C, K):
     """Roofline of the timed step (its two launches).  The work is fp32
-    arithmetic, 7 Dk Dv flop per token*head, computed on the bf16 matrix
-    cores through exact three-plane splits of the f32 operands: the
-    fp32-equivalent rate against the fp32 peak, and the bf16 matrix flops the
-    launches issue against the bf16 matrix peak."""
+    arithmetic, 7 Dk Dv flop per token*head, computed on the matrix cores:
+    W S^T on the f32 matrix instruction, the other products in bf16 on exact
+    plane splits of the f32 operands.  The algorithmic fp32 rate against the
+    fp32 peak, and the f32 and bf16 matrix flops the launches issue (counters)
+    against those peaks."""
     mf = measured_counter("layer_core", "prefill_T4096", "mfma_bf16_flops")
+    mf32 = measured_counter("layer_core", "prefill_T4096", "mfma_f32_flops")
     # algorithmic bytes: qkv, a, b, conv weights read; y, state, conv-state tail written
     alg = B * T * C * 2 + 2 * B * T * Hv * 2 + C * K * 2 + B * T * Hv * Dv * 2 + B * Hv * Dv * Dk * 4 \
         + B * (K - 1) * C * 2
     return {"bound": "mfma", "kernel": "chunk_prep_kernel<4, 2> + chunk_seq_kernel<1> (gdn_layer_core step)",
-            "dtype": "fp32 arithmetic on bf16 matrix cores (exact three-plane splits)",
+            "dtype": "fp32 arithmetic on matrix cores (f32 instruction; bf16 on exact plane splits)",
             "achieved": step_tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": step_tflops / FP32_PEAK_TFLOPS,
             "traffic": measured_traffic("layer_core", "prefill_T4096"), "traffic_algorithmic": alg,
             "flops_per_launch": flops, "avg_launch_us": step_us,
             "bf16_matrix": None if mf is None else {
                 "flops_per_launch": mf, "achieved": mf / (step_us * 1e-6) / 1e12, "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": mf / (step_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS}}
+                "unit": "TFLOP/s", "frac": mf / (step_us * 1e-6) / 1e12 / BF16_PEAK_TFLOPS},
+            "f32_matrix": None if mf32 is None else {
+                "flops_per_launch": mf32, "achieved": mf32 / (step_us * 1e-6) / 1e12, "peak": F32_MATRIX_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": mf32 / (step_us * 1e-6) / 1e12 / F32_MATRIX_PEAK_TFLOPS}}
 
 
 def bench_copy(torch, dev, stream):
@@ -521,7 +529,8 @@ def bench_verify_and_per_key(args, torch, dev, up, inputs, binding, np):
         res[name] = {"workload": f"B={B} T={T} Hk={Hk} Hv={Hv} Dk=Dv={Dk}, {R} rotating state sets"
                                  + (f", snapshots after {steps} steps" if steps else ", per-key gate"),
                      "kernel": kern, "avg_launch_us": us, "bytes_per_launch": nbytes, "achieved_GBs": gbs,
-                     "frac_hbm": gbs / HBM_PEAK_GBS}
+                     "frac_hbm": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("recurrent_step_kernel", f"{name}_B64")}
         print(f"[bench] {name}: {us:.1f} us ({gbs:.0f} GB/s, {gbs / HBM_PEAK_GBS:.0%} of HBM)", file=sys.stderr,
               flush=True)
     return res
@@ -784,6 +793,7 @@ def bench_long_prefill(args, torch, dev, up, inputs, binding, np):
           f"{chunk_us / 1e3:.2f} ms ({tf:.1f} TFLOP/s, {tf / FP32_PEAK_TFLOPS:.1%} of fp32 peak)",
           file=sys.stderr, flush=True)
     return {"workload": "long prefill B=4 T=32768 Hk=16 Hv=32 Dk=Dv=128 K=4, random recurrent state",
+            "kernel": "chunk_prep_kernel<4, 2> + chunk_seq_rows_kernel (one wave per 16-row state tile)",
             "ms_per_step": step_us / 1e3, "value": B * T * Hv / (step_us * 1e-6), "unit": "token*head/s",
             "chunked_recurrence_ms": chunk_us / 1e3, "chunked_TFLOPs": tf, "frac_fp32_peak": tf / FP32_PEAK_TFLOPS,
             "steps_timed": n}

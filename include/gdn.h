@@ -111,11 +111,12 @@ gdn_status gdn_recurrent_masked(const gdn_bf16 *q, const gdn_bf16 *k, const gdn_
  * chunks of 32 steps on the matrix cores: within a chunk the deltas of all
  * steps solve one unit lower-triangular system built from k_t . k_s, beta
  * and the decay ratios, and the state advances by one dense product per
- * chunk.  Precision: the state path is fp32 -- every f32 operand of a
- * product is cut exactly into three bf16 planes and the plane products are
- * kept down to 2^-16 of the leading one (the dropped terms are below 2^-24
- * relative), with f32 accumulation; y is formed from the two leading planes
- * (2^-16 relative) and then rounded to bf16 (nearest even).  Results differ
+ * chunk.  Precision: the state path is fp32 -- W S^T runs on the f32 matrix
+ * instruction; in the other products every f32 operand is cut exactly into
+ * three bf16 planes and the plane products are kept down to 2^-16 of the
+ * leading one (the dropped terms are below 2^-24 relative), with f32
+ * accumulation; y is formed from the two leading planes (2^-16 relative) and
+ * then rounded to bf16 (nearest even).  Results differ
  * from gdn_recurrent by rounding only: the same tolerances hold against the
  * exact recurrence, not bit equality.
  * Arguments as gdn_recurrent plus a caller-owned device workspace of at least

@@ -19,7 +19,9 @@
 // the same arithmetic as the per-step loop up to rounding order: dense
 // products replace the per-step dot products.
 //
-// fp32 products on bf16 matrix cores.  Every f32 operand x is cut into three
+// fp32 products on the matrix cores.  W S^T (and the per-key form's state
+// update) run on the f32 matrix instruction (16x16x4, f32 in, f32 out).  The
+// other products run on bf16 MFMAs: every f32 operand x is cut into three
 // bf16 planes x = h + m + l exactly (h is x rounded to bf16, m the remainder
 // rounded, l what is left), so that a product of an f32 matrix with an exact
 // bf16 matrix (q, k, v) is three bf16 MFMAs with f32 accumulation, and a
@@ -34,7 +36,7 @@
 // rows 4q..4q+3 of column r of each) are, element for element, the operand of
 // the next product: the state and the chunk's deltas never leave registers.
 //
-// Two kernels:
+// Three kernels:
 //  * chunk_prep_kernel, one block per (b, chunk) and one v-head or the two
 //    v-heads of a pair sharing a k-head, independent of the state: k k^T and
 //    q k^T on bf16 MFMA, the decay ratios as direct products (never
@@ -48,6 +50,9 @@
 //    W S_0^T - Tb V and of Q S_0^T over its columns, the four shares are
 //    summed through LDS (the only exchange, one barrier per chunk), and every
 //    wave then updates its state columns; two waves finish Y.
+//  * chunk_seq_rows_kernel, for grids of more than two 16-row tiles per CU:
+//    one wave per tile over all Dk columns (no exchange of partial
+//    products), the same arithmetic in the same order.
 // Padding steps past T and masked steps carry g = 1, beta = 0: their Delta is
 // 0 and they leave S unchanged (a masked step's y is written as zero).
 //
@@ -743,7 +748,7 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) 
             return t < CH2 ? sh.u.pk.ge[t][j] * sh.u.pk.gb[1][j] : sh.u.pk.ge[t][j];
         };
         // operands: (K o Gamma)^T planes for W (kept in registers until step
-        // 6), (K o E)^T planes and Q o Gamma planes for the sequential pass
+        // 6), -(K o E)^T in f32 and Q o Gamma planes for the sequential pass
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int d = 32 * wl + 16 * tt + lr;

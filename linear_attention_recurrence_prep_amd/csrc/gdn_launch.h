@@ -71,8 +71,8 @@ hipError_t launch_decode_core(const PrepArgs& p, const uint8_t* mask, const floa
 // (b, hk, chunk) q and k [32 x Dk] in bf16, all in the register layout of the
 // sequential kernel (byte offsets below, each 256-byte aligned).  With the
 // per-key gate (RecurrentArgs::g_per_key) q and k are replaced per (b, hv,
-// chunk) by q o Gamma_t (two bf16 planes) and k o (Gamma_{C-1} / Gamma_t)
-// (three planes), and the decay record also holds Gamma_{C-1} [Dk].
+// chunk) by q o Gamma_t (two bf16 planes) and -(k o Gamma_{C-1} / Gamma_t)
+// (f32), and the decay record also holds Gamma_{C-1} [Dk].
 struct ChunkedLayout {
     int nc;                 // chunks per sequence
     uint64_t wsw, u, pn, rg, qsw, ksw, total;
