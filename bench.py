@@ -596,7 +596,7 @@ def bench_per_key_prefill(args, torch, dev, up, inputs, binding, np):
     for name, fn in (("chunked", chunked), ("staged", staged), ("staging_free", staging_free)):
         fn()
         torch.cuda.synchronize()
-        out[name] = time_kernel(torch, stream, fn, 10)
+        out[name] = time_kernel(torch, stream, fn, 30 if name == "chunked" else 10)
     flops = 7 * B * T * Hv * Dk * Dv
     tf = flops / (out["chunked"] * 1e-6) / 1e12
     print(f"[bench] per-key prefill B=1 T=4096: chunked {out['chunked']:.1f} us ({tf:.1f} TFLOP/s), per-step "
@@ -784,7 +784,7 @@ def bench_long_prefill(args, torch, dev, up, inputs, binding, np):
     binding.prep(d["qkv"], d["conv_w"], d["conv_state"], None, d["a"], d["b"], d["A_log"], d["dt_bias"], pq, pk,
                  pv, pg, pb, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs, k_scale=ks)
     stream = torch.cuda.current_stream(dev)
-    n = 3
+    n = 6
     step_us = time_kernel(torch, stream, step, n)
     chunk_us = time_kernel(torch, stream, chunked, n)
     flops = 7 * B * T * Hv * Dk * Dv

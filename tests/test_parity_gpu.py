@@ -645,14 +645,22 @@ def test_recurrent_chunked_matches_oracle(case):
     say("chunked state err", e)
 
 
-@pytest.mark.parametrize("B,Hv,Dv", [(2, 32, 128), (3, 32, 64)])
-def test_recurrent_chunked_two_row_tiles(B, Hv, Dv):
+@pytest.mark.parametrize("B,Hv,Dv,zero_state", [(2, 32, 128, False), (3, 32, 64, False), (3, 32, 128, False),
+                                                  (5, 32, 64, False), (4, 32, 128, True)],
+                         ids=["two_tiles_B2", "two_tiles_B3_Dv64", "row_waves_B3", "row_waves_B5_Dv64",
+                              "row_waves_B4_zero_state"])
+def test_recurrent_chunked_two_row_tiles(B, Hv, Dv, zero_state):
     """Once B*Hv*Dv/16 exceeds the CU count the sequential pass serves two
-    16-row tiles per block (one tile per block below it).  Sequences of a
-    batch are independent, so each must be bit-identical to itself run alone
-    (one tile per block), and the batch must meet the oracle."""
-    say("recurrent_chunked two row tiles", B, Hv, Dv)
+    16-row tiles per block, and once it exceeds twice the CU count one wave
+    per tile over all key columns (chunk_seq_rows_kernel); one tile per block
+    below that.  Sequences of a batch are independent, so each must be
+    bit-identical to itself run alone (one tile per block), and the batch
+    must meet the oracle.  T = 100 ends in a partial chunk; the last
+    sequence has masked steps."""
+    say("recurrent_chunked two row tiles / row waves", B, Hv, Dv, zero_state)
     ri = rec_inputs(B, 100, Hv // 2, Hv, 128, Dv, 421)
+    if zero_state:
+        ri["state"] = None
     mask = np.ones((B, 100), dtype=np.uint8)
     mask[-1, 37:41] = 0
     y, s = gpu_recurrent_chunked(ri, mask=mask)
@@ -661,11 +669,11 @@ def test_recurrent_chunked_two_row_tiles(B, Hv, Dv):
                for k in ("q", "k", "v", "g", "beta", "state")}
         y1, s1 = gpu_recurrent_chunked(one, mask=mask[b:b + 1])
         assert np.array_equal(y[b:b + 1], y1) and np.array_equal(s[b:b + 1], s1), b
+    st = np.zeros(s.shape) if ri["state"] is None else ri["state"].astype(np.float64)
     y_ref, s_ref = oracle.recurrent(*[oracle.bf16_to_f64(ri[k]) for k in ("q", "k", "v")],
-                                    ri["g"].astype(np.float64), ri["beta"].astype(np.float64),
-                                    ri["state"].astype(np.float64), mask=mask)
-    H.check_y(y, y_ref, "two tiles")
-    H.check_state(s, s_ref, 1e-4, "two tiles")
+                                    ri["g"].astype(np.float64), ri["beta"].astype(np.float64), st, mask=mask)
+    H.check_y(y, y_ref, "two tiles / row waves")
+    H.check_state(s, s_ref, 1e-4, "two tiles / row waves")
 
 
 def test_recurrent_chunked_properties():
