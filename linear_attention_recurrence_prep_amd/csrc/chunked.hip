@@ -1424,6 +1424,13 @@ __global__ __launch_bounds__(RW_THREADS) void chunk_seq_rows_kernel(SeqIn in, co
     int slot = 0;
     for (int c = 0; c < NC; ++c) {
         const bool pre = c + 2 < NC;
+        // the mask bytes of this lane's two steps, loaded before the staging
+        // loads so that their wait does not cover those
+        bool keep[2] = {true, true};
+        if (mask != nullptr) {
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) keep[jt] = mask[(int64_t)b * T + min(c * CK + 16 * jt + lr, T - 1)] != 0;
+        }
         if (pre) stage_load(c + 2);
         const RowSlot& o = ring[slot];
 
@@ -1491,7 +1498,7 @@ __global__ __launch_bounds__(RW_THREADS) void chunk_seq_rows_kernel(SeqIn in, co
             const int t = c * CK + yt;
             if (t < T) {
                 u2_t w = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
-                if (mask != nullptr && mask[(int64_t)b * T + t] == 0) w = u2_t{0, 0};   // masked step
+                if (!keep[jt]) w = u2_t{0, 0};   // masked step
                 *reinterpret_cast<u2_t*>(yw + (int64_t)t * vstride) = w;
             }
         }
