@@ -7,7 +7,9 @@ HBM before timing.  The timed steps rotate over 4 sets of inputs and outputs
 (qkv, a, b, y, state and conv-state outputs: 401 MB together, more than the
 256 MB last-level cache), so each step reads inputs the previous steps did
 not leave in that cache; the single-set (warm) step time is reported beside
-it.  Metric: recurrence tokens/s*head = B*T*Hv / step time.
+it.  Before the warm-up, 0.3 s of untimed steps bring the GPU to its loaded
+clock state (its first milliseconds of work run measurably slower).
+Metric: recurrence tokens/s*head = B*T*Hv / step time.
 
 Also measured in the same run (same JSON line):
   * roofline of the timed step (its two launches: the chunk preparation with
@@ -61,6 +63,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
 F32_MATRIX_PEAK_TFLOPS = 157.3 # MI355X dense f32 matrix
 R_HBM = 4                      # rotating buffer sets for the HBM-bound kernels
 R_IN = 4                       # rotating input/output sets of the timed prefill step
+SETTLE_S = 0.3                 # untimed steps before the warm-up: the GPU's loaded clock state
 
 
 def source_digest(kernel):
@@ -232,10 +235,24 @@ def main():
         return kernel_only(args, torch, dev, prep_rot, rec_only, up, inputs, binding, np, chunked_only,
                            epilogue_rot, epi_sets, y, step)
 
+    # Settle: the GPU runs its first milliseconds of work at lower clocks
+    # (measured: the same step takes about 191 us in its first 40 calls and
+    # about 167 us from then on), so untimed steps run for SETTLE_S seconds
+    # (synchronised every 20 steps, so the queue never runs ahead) before the
+    # warm-up and the timed steps.
+    t_settle0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_settle0 < SETTLE_S:
+        for _ in range(20):
+            step(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle0
     for i in range(max(args.warmup, R_IN)):
         step(i)
     torch.cuda.synchronize()
-    print(f"[bench] prefill warmup done ({max(args.warmup, R_IN)})", file=sys.stderr, flush=True)
+    print(f"[bench] prefill settle {n_settle} steps ({settle_s:.2f} s), warmup done ({max(args.warmup, R_IN)})",
+          file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -338,6 +355,8 @@ def main():
         "per_key_prefill_b1": per_key_prefill,
         "cpu_baseline": cpu,
         "wall_s_timed": t_wall,
+        "settle": {"steps": n_settle, "seconds": settle_s,
+                   "note": "untimed steps before the warm-up, bringing the GPU to its loaded clock state"},
     }
     print(json.dumps(line), flush=True)
 
@@ -398,8 +417,10 @@ def time_rotating(torch, stream, fn, n):
     return a.elapsed_time(b) * 1e3 / n
 
 
-def time_kernel(torch, stream, fn, n):
-    for _ in range(2):
+def time_kernel(torch, stream, fn, n, warm=5):
+    """Average time of fn() over n back-to-back calls, after warm untimed
+    calls (a freshly allocated set of buffers runs its first calls slower)."""
+    for _ in range(warm):
         fn()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -596,7 +617,8 @@ def bench_per_key_prefill(args, torch, dev, up, inputs, binding, np):
     for name, fn in (("chunked", chunked), ("staged", staged), ("staging_free", staging_free)):
         fn()
         torch.cuda.synchronize()
-        out[name] = time_kernel(torch, stream, fn, 30 if name == "chunked" else 10)
+        out[name] = time_kernel(torch, stream, fn, 30 if name == "chunked" else 10,
+                                warm=20 if name == "chunked" else 3)
     flops = 7 * B * T * Hv * Dk * Dv
     tf = flops / (out["chunked"] * 1e-6) / 1e12
     print(f"[bench] per-key prefill B=1 T=4096: chunked {out['chunked']:.1f} us ({tf:.1f} TFLOP/s), per-step "
