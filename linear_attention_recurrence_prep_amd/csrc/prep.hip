@@ -3,10 +3,11 @@
 //  conv-state splice through g; "mlx-bun 0.4.0 -> 1.0.0, qwen3-delta.ts",
 //  compute_g and the dtype contract in its header).
 //
-// HBM-bound: every qkv element is read once and every q/k/v element written
+// Every qkv element is read from HBM once and every q/k/v element written
 // once.  A thread owns 8 consecutive channels (one 16-byte vector) over TT
 // consecutive tokens and slides a (K-1)-row window of the spliced input
-// through registers, so the conv halo costs K-1 extra rows per TT tokens.
+// through registers, so the conv halo costs K-1 extra row reads per TT
+// tokens (served mostly from L2).
 // A 64-lane wave covers 512 channels; q/k heads (Dk channels = Dk/8 lanes)
 // are aligned lane groups, so the per-head sum of squares is a DPP butterfly.
 // Gates (g, beta) are computed by extra blocks of the same launch.
@@ -26,11 +27,20 @@ __device__ __forceinline__ void store_stream16(uint16_t* dst, const uint4 v) {
     __builtin_nontemporal_store(x, reinterpret_cast<u32x4_nt*>(dst));
 }
 
-constexpr int PREP_NT = 256;   // threads per block: 2048 channels
-constexpr int PREP_TT = 16;    // tokens per thread
+// One wave per block (512 channels) and 4 tokens per thread: measured over a
+// sweep of 2..32 tokens and 64..256 threads at the prefill workload (4
+// rotating buffer sets), 4 x 64 takes 28 us against 35 us for 16 x 256; the
+// short per-thread chain and the many small blocks outweigh re-reading the
+// K - 1 halo rows per 4 tokens (mostly from L2).
+constexpr int PREP_NT = 64;    // threads per block: 512 channels
+constexpr int PREP_TT = 4;     // tokens per thread
+// Only the first token chunk reads the conv state (its window starts there)
+// when PREP_TT >= K - 1, which keeps an in-place conv state race-free: that
+// chunk's block writes the new state after reading its own rows.
+static_assert(PREP_TT >= 3, "the conv state is read by the first token chunk only (K <= 4)");
 
 template <int DK, int K>
-__global__ __launch_bounds__(256) void prep_kernel(PrepArgs p, int c_tiles, int t_chunks,
+__global__ __launch_bounds__(PREP_NT) void prep_kernel(PrepArgs p, int c_tiles, int t_chunks,
                                                     int64_t conv_blocks) {
     const int tid = threadIdx.x;
     const int64_t bid = blockIdx.x;
