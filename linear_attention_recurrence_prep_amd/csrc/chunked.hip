@@ -290,8 +290,12 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) 
                                                             ChunkPtrs o, int T, int Hk, int Hv, int Dv, int NC) {
     static_assert(!PK || (KF == 0 && NH == 1), "the per-key form takes prepared inputs, one v-head per block");
     __shared__ PrepSmem<NH, PK> sh;
-    const int c = (int)(blockIdx.x % NC);
-    const int np = (int)(blockIdx.x / NC);    // b * (Hv / NH) + head pair
+    // head pairs fastest in the grid: the blocks in flight together read
+    // whole qkv rows of a few chunks (measured 59.9 -> 57.3 us at B=1 T=4096
+    // and 1738 -> 1634 us at B=4 T=32768 against chunks fastest)
+    const int npairs = (int)(gridDim.x / NC);
+    const int c = (int)(blockIdx.x / npairs);
+    const int np = (int)(blockIdx.x % npairs);    // b * (Hv / NH) + head pair
     const int b = np / (Hv / NH);
     const int hv0 = (np % (Hv / NH)) * NH;    // the block's first v-head
     const int G = Hv / Hk;
