@@ -815,7 +815,7 @@ def bench_long_prefill(args, torch, dev, up, inputs, binding, np):
           f"{chunk_us / 1e3:.2f} ms ({tf:.1f} TFLOP/s, {tf / FP32_PEAK_TFLOPS:.1%} of fp32 peak)",
           file=sys.stderr, flush=True)
     return {"workload": "long prefill B=4 T=32768 Hk=16 Hv=32 Dk=Dv=128 K=4, random recurrent state",
-            "kernel": "chunk_prep_kernel<4, 2> + chunk_seq_rows_kernel (one wave per 16-row state tile)",
+            "kernel": "chunk_prep_kernel<4, 2> + chunk_seq_pairs_kernel (two waves per 16-row state tile)",
             "ms_per_step": step_us / 1e3, "value": B * T * Hv / (step_us * 1e-6), "unit": "token*head/s",
             "chunked_recurrence_ms": chunk_us / 1e3, "chunked_TFLOPs": tf, "frac_fp32_peak": tf / FP32_PEAK_TFLOPS,
             "steps_timed": n}

@@ -50,9 +50,10 @@
 //    W S_0^T - Tb V and of Q S_0^T over its columns, the four shares are
 //    summed through LDS (the only exchange, one barrier per chunk), and every
 //    wave then updates its state columns; two waves finish Y.
-//  * chunk_seq_rows_kernel, for grids of more than two 16-row tiles per CU:
-//    one wave per tile over all Dk columns (no exchange of partial
-//    products), the same arithmetic in the same order.
+//  * chunk_seq_pairs_kernel, for grids of more than two 16-row tiles per
+//    CU: two waves per tile (one per half of the Dk columns) on one SIMD,
+//    the chunk operands shared by four tiles through an LDS ring, the same
+//    arithmetic in the same order.
 // Padding steps past T and masked steps carry g = 1, beta = 0: their Delta is
 // 0 and they leave S unchanged (a masked step's y is written as zero).
 //
@@ -1142,7 +1143,7 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
                     const f4_t* yb = sh.y[b3][rt];
                     const f4_t q0 = yb[jt * 64 + lane], q1 = yb[(2 + jt) * 64 + lane];
                     const f4_t q2 = yb[(4 + jt) * 64 + lane], q3 = yb[(6 + jt) * 64 + lane];
-                    f4_t ys = ((q0 + q1) + q2) + q3;
+                    f4_t ys = (q0 + q1) + (q2 + q3);
                     ys = ys * sh.rg[b3][CK + yt];
                     u4_t dh, dm;
                     split8hm(no, sh.d[cp & 1][rt][0][lane], sh.d[cp & 1][rt][1][lane], dh, dm);
@@ -1234,15 +1235,16 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
         __syncthreads();
 
         SEQ_PIN(nx.template load<2>(in, x, cn));
-        // D = W S^T - Tb V = -Delta, summed in wave order (identical in every wave)
+        // D = W S^T - Tb V = -Delta: the shares of waves 0, 1 and of waves 2, 3
+        // summed, then the two sums (identical in every wave)
         f4_t d0[NR], d1[NR];
 #pragma unroll
         for (int rt = 0; rt < NR; ++rt) {
             const f4_t* xb = sh.x[c & 1][rt];
             const f4_t p00 = xb[0 * 64 + lane], p10 = xb[2 * 64 + lane], p20 = xb[4 * 64 + lane], p30 = xb[6 * 64 + lane];
             const f4_t p01 = xb[1 * 64 + lane], p11 = xb[3 * 64 + lane], p21 = xb[5 * 64 + lane], p31 = xb[7 * 64 + lane];
-            d0[rt] = ((p00 + p10) + p20) + p30;
-            d1[rt] = ((p01 + p11) + p21) + p31;
+            d0[rt] = (p00 + p10) + (p20 + p30);
+            d1[rt] = (p01 + p11) + (p21 + p31);
         }
 
         // this wave's share of S Q^T (rows r, columns t), formed after the
@@ -1334,37 +1336,46 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
     }
 }
 
-// ================================================ sequential pass, row waves
+// ========================================== sequential pass, row-wave pairs
 
-// For grids of more than two row tiles per CU: one wave per 16-row state tile
-// over all Dk columns, so that no wave needs another's partial products (no
-// exchange, every wave keeps its matrix pipe busy), four waves (64 rows of
-// one v-head) per block.  The chunk's W, q, k, -Tb V of the block's four
-// tiles, -P and rho/gamma are staged by the whole block into a three-slot
-// LDS ring two chunks ahead, one barrier per chunk.  Column slice s
-// (columns 32 s .. 32 s + 31) takes the part of chunk_seq_kernel's wave s,
-// and every product and sum is formed in that kernel's order, so the results
-// are bit-identical to it.
-constexpr int RWW = 4;                                            // row tiles (waves) per block
-constexpr int RW_THREADS = 64 * RWW;
-constexpr int RW_VEC = kWVec + 2 * kQVec + RWW * 2 * 64 + kPVec;  // 16-byte vectors per slot
-constexpr int RW_PER = RW_VEC / RW_THREADS;                       // staged per thread
-static_assert(RW_VEC % RW_THREADS == 0 && kWVec % RW_THREADS == 0 && kQVec % RW_THREADS == 0 &&
-                  (RWW * 2 * 64) % RW_THREADS == 0 && kPVec % RW_THREADS == 0,
-              "whole staging rounds per region");
+// For grids of more than two row tiles per CU: two waves per 16-row state
+// tile, each over one half of the Dk columns (two of the four 32-column
+// slices), eight waves (64 rows of one v-head) per block, so that every SIMD
+// holds two waves whose matrix products and vector work interleave.  The two
+// halves of a tile exchange their shares of W S^T - Tb V and of S Q^T
+// through LDS once per chunk; each half updates its own state columns and
+// finishes y for one t-tile.  The chunk's W, q, k, -P and rho/gamma are
+// staged by the whole block into a three-slot LDS ring two chunks ahead;
+// -Tb V, read by one wave per tile, is loaded by that wave one chunk ahead.
+// One barrier per chunk, between the shares and their sums: the exchange
+// buffer is double-buffered, and a ring slot is refilled after the barrier
+// of the step following its last read.  Slice s takes the part of
+// chunk_seq_kernel's wave s and every sum is formed in that kernel's order,
+// so the results are bit-identical to it.
+constexpr int PWW = 8;                                        // waves per block: 4 row tiles x 2 halves
+constexpr int PW_TILES = PWW / 2;
+constexpr int PW_THREADS = 64 * PWW;
+constexpr int PW_Q = kWVec, PW_K = PW_Q + kQVec, PW_P = PW_K + kQVec, PW_VEC = PW_P + kPVec;
+static_assert(kWVec == 2 * PW_THREADS && kQVec == PW_THREADS && 2 * kPVec == PW_THREADS,
+              "staging: two W vectors, one q and one k vector per thread, -P by half the threads");
 
-struct RowSlot {
-    u4_t v[RW_VEC];       // W | q | k | -Tb V (tiles of the block) | -P, in the workspace layout
-    float rg[2 * CK];     // -rho (kperm order), gamma
+struct PairSmem {
+    struct Slot {
+        u4_t v[PW_VEC];       // W | q | k | -P, in the workspace layout
+        float rg[2 * CK];     // -rho (kperm order), gamma
+    } ring[3];
+    // per chunk parity and wave: its half's W S^T - Tb V share (t-tiles 0, 1)
+    // and its S Q^T share of the t-tile the other half finishes
+    f4_t ex[2][PWW][3][64];
 };
-constexpr int RW_Q = kWVec, RW_K = RW_Q + kQVec, RW_U = RW_K + kQVec, RW_P = RW_U + RWW * 2 * 64;
+static_assert(sizeof(PairSmem) <= 160 * 1024, "LDS of one CU");
 
-__global__ __launch_bounds__(RW_THREADS) void chunk_seq_rows_kernel(SeqIn in, const float* state_in,
-                                                                    float* state_out, uint16_t* __restrict__ y,
-                                                                    const uint8_t* __restrict__ mask, int T, int Hk,
-                                                                    int Hv, int Dv, int NC, int row_blocks,
-                                                                    int n_blocks) {
-    __shared__ RowSlot ring[3];
+__global__ __launch_bounds__(PW_THREADS) void chunk_seq_pairs_kernel(SeqIn in, const float* state_in,
+                                                                     float* state_out, uint16_t* __restrict__ y,
+                                                                     const uint8_t* __restrict__ mask, int T, int Hk,
+                                                                     int Hv, int Dv, int NC, int row_blocks,
+                                                                     int n_blocks) {
+    __shared__ PairSmem sm;
 
     int lb = blockIdx.x;
     if ((n_blocks & 7) == 0) lb = (lb & 7) * (n_blocks >> 3) + (lb >> 3);
@@ -1374,46 +1385,52 @@ __global__ __launch_bounds__(RW_THREADS) void chunk_seq_rows_kernel(SeqIn in, co
     const int hk = hv / (Hv / Hk);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hf = wv / PW_TILES;                 // column half: slices 2 hf, 2 hf + 1
+    const int tile = rblk * PW_TILES + wv % PW_TILES;
     const int lr = lane & 15, lq = lane >> 4;
-    const int tile0 = rblk * RWW;
-    const int r0 = (tile0 + wv) * RB;             // this wave's first state row
+    const int r0 = tile * RB;                     // this wave's first state row
     const int row_tiles = Dv / RB;
     const int64_t unit0 = (int64_t)n * NC, kunit0 = ((int64_t)b * Hk + hk) * NC;
     const f4_t zero = {0.f, 0.f, 0.f, 0.f};
     const NegOnes no = neg_ones();
     const int64_t vstride = (int64_t)Hv * Dv;     // one step of y
 
-    // tile tt, register i: S[r0 + lr][16 tt + 4 lq + i]
-    f4_t S[8];
-    const int64_t soff = ((int64_t)n * Dv + r0 + lr) * DKC + 4 * lq;
+    // tile tt of this half, register i: S[r0 + lr][64 hf + 16 tt + 4 lq + i]
+    f4_t S[4];
+    const int64_t soff = ((int64_t)n * Dv + r0 + lr) * DKC + 64 * hf + 4 * lq;
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt)
+    for (int tt = 0; tt < 4; ++tt)
         S[tt] = state_in ? *reinterpret_cast<const f4_t*>(state_in + soff + 16 * tt) : zero;
 
+    // -Tb V of this tile's two t-tiles (added by half 0), one chunk ahead
+    f4_t un[2] = {zero, zero};
+    auto u_load = [&](int c) {
+        if (hf == 0) {
+            const auto su = uniform_ptr(in.u + ((unit0 + c) * row_tiles + tile) * 2 * 64);
+            un[0] = __builtin_bit_cast(f4_t, su[lane]);
+            un[1] = __builtin_bit_cast(f4_t, su[64 + lane]);
+        }
+    };
     // staging of chunk c by the whole block, coalesced: loads now, LDS stores later
-    u4_t g[RW_PER], grg = {0, 0, 0, 0};
+    u4_t g[5], grg = {0, 0, 0, 0};
     auto stage_load = [&](int c) {
         const int64_t unit = unit0 + c, kunit = kunit0 + c;
         const auto sw = uniform_ptr(in.wsw + unit * kWVec);
-        const auto sq = uniform_ptr(in.qsw + kunit * kQVec);
-        const auto sk = uniform_ptr(in.ksw + kunit * kQVec);
-        const auto su = uniform_ptr(in.u + (unit * row_tiles + tile0) * 2 * 64);
-        const auto spn = uniform_ptr(in.pn + unit * kPVec);
-#pragma unroll
-        for (int j = 0; j < RW_PER; ++j) {
-            const int i = tid + j * RW_THREADS;   // region of i is fixed by j
-            if (j * RW_THREADS < RW_Q) g[j] = sw[i];
-            else if (j * RW_THREADS < RW_K) g[j] = sq[i - RW_Q];
-            else if (j * RW_THREADS < RW_U) g[j] = sk[i - RW_K];
-            else if (j * RW_THREADS < RW_P) g[j] = su[i - RW_U];
-            else g[j] = spn[i - RW_P];
-        }
+        g[0] = sw[tid];
+        g[1] = sw[PW_THREADS + tid];
+        g[2] = uniform_ptr(in.qsw + kunit * kQVec)[tid];
+        g[3] = uniform_ptr(in.ksw + kunit * kQVec)[tid];
+        if (wv < PWW / 2) g[4] = uniform_ptr(in.pn + unit * kPVec)[tid];
         if (tid < 2 * CK / 4) grg = uniform_ptr(reinterpret_cast<const u4_t*>(in.rg + unit * 2 * CK))[tid];
     };
     auto stage_store = [&](int slot) {
-#pragma unroll
-        for (int j = 0; j < RW_PER; ++j) ring[slot].v[tid + j * RW_THREADS] = g[j];
-        if (tid < 2 * CK / 4) reinterpret_cast<u4_t*>(ring[slot].rg)[tid] = grg;
+        PairSmem::Slot& st = sm.ring[slot];
+        st.v[tid] = g[0];
+        st.v[PW_THREADS + tid] = g[1];
+        st.v[PW_Q + tid] = g[2];
+        st.v[PW_K + tid] = g[3];
+        if (wv < PWW / 2) st.v[PW_P + tid] = g[4];
+        if (tid < 2 * CK / 4) reinterpret_cast<u4_t*>(st.rg)[tid] = grg;
     };
 
     stage_load(0);
@@ -1422,32 +1439,34 @@ __global__ __launch_bounds__(RW_THREADS) void chunk_seq_rows_kernel(SeqIn in, co
         stage_load(1);
         stage_store(1);
     }
+    u_load(0);
     __syncthreads();
 
     uint16_t* yw = y + ((int64_t)b * T * Hv + hv) * Dv + r0 + 4 * lq;
+    const int yt = 16 * hf + lr;                  // this wave finishes y of t-tile hf
     int slot = 0;
     for (int c = 0; c < NC; ++c) {
         const bool pre = c + 2 < NC;
-        // the mask bytes of this lane's two steps, loaded before the staging
-        // loads so that their wait does not cover those
-        bool keep[2] = {true, true};
-        if (mask != nullptr) {
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt) keep[jt] = mask[(int64_t)b * T + min(c * CK + 16 * jt + lr, T - 1)] != 0;
-        }
+        // the mask byte of this lane's step, loaded before the staging loads
+        // so that its wait does not cover those
+        bool keep = true;
+        if (mask != nullptr) keep = mask[(int64_t)b * T + min(c * CK + yt, T - 1)] != 0;
+        const f4_t uc0 = un[0], uc1 = un[1];
+        if (c + 1 < NC) u_load(c + 1);
         if (pre) stage_load(c + 2);
-        const RowSlot& o = ring[slot];
+        const PairSmem::Slot& o = sm.ring[slot];
 
-        // W S^T - Tb V: slice s's share as wave s of chunk_seq_kernel forms it
-        // (-Tb V enters slice 0's t-tile 0 and slice 1's t-tile 1)
-        f4_t x[4][2];
+        // this half's slices of W S^T - Tb V, each as the wave of chunk_seq_kernel
+        // with that slice forms its share (-Tb V enters slice 0's t-tile 0 and
+        // slice 1's t-tile 1)
+        f4_t x[2][2];
+        x[0][0] = hf == 0 ? uc0 : zero;
+        x[0][1] = zero;
+        x[1][0] = zero;
+        x[1][1] = hf == 0 ? uc1 : zero;
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-            x[sl][0] = sl == 0 ? __builtin_bit_cast(f4_t, o.v[RW_U + (wv * 2 + 0) * 64 + lane]) : zero;
-            x[sl][1] = sl == 1 ? __builtin_bit_cast(f4_t, o.v[RW_U + (wv * 2 + 1) * 64 + lane]) : zero;
-        }
-#pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
+        for (int j = 0; j < 2; ++j) {
+            const int sl = 2 * hf + j;
             f4_t wf[2][2];
 #pragma unroll
             for (int jt = 0; jt < 2; ++jt) {
@@ -1456,64 +1475,69 @@ __global__ __launch_bounds__(RW_THREADS) void chunk_seq_rows_kernel(SeqIn in, co
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                x[sl][0] = mma_f32(wf[0][e >> 2][e & 3], S[2 * sl + (e >> 2)][e & 3], x[sl][0]);
-                x[sl][1] = mma_f32(wf[1][e >> 2][e & 3], S[2 * sl + (e >> 2)][e & 3], x[sl][1]);
+                x[j][0] = mma_f32(wf[0][e >> 2][e & 3], S[2 * j + (e >> 2)][e & 3], x[j][0]);
+                x[j][1] = mma_f32(wf[1][e >> 2][e & 3], S[2 * j + (e >> 2)][e & 3], x[j][1]);
             }
         }
-        // S Q^T shares per slice from the state's two leading planes, summed in slice order
-        f4_t ys[2];
+        // S Q^T shares of the two slices from the state's two leading planes
+        f4_t yp[2][2];
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
+        for (int j = 0; j < 2; ++j) {
+            const int sl = 2 * hf + j;
             u4_t s_h, s_m;
-            split8hm(no, S[2 * sl], S[2 * sl + 1], s_h, s_m);
-            const u4_t q0 = o.v[RW_Q + (sl * 2) * 64 + lane], q1 = o.v[RW_Q + (sl * 2 + 1) * 64 + lane];
-            f4_t y0v = mma(s_m, q0, zero), y1v = mma(s_m, q1, zero);
-            y0v = mma(s_h, q0, y0v);
-            y1v = mma(s_h, q1, y1v);
-            ys[0] = sl == 0 ? y0v : ys[0] + y0v;
-            ys[1] = sl == 0 ? y1v : ys[1] + y1v;
+            split8hm(no, S[2 * j], S[2 * j + 1], s_h, s_m);
+            const u4_t q0 = o.v[PW_Q + (sl * 2) * 64 + lane], q1 = o.v[PW_Q + (sl * 2 + 1) * 64 + lane];
+            yp[j][0] = mma(s_m, q0, zero);
+            yp[j][1] = mma(s_m, q1, zero);
+            yp[j][0] = mma(s_h, q0, yp[j][0]);
+            yp[j][1] = mma(s_h, q1, yp[j][1]);
         }
-        // D = W S^T - Tb V = -Delta, summed in slice order
-        const f4_t d0 = ((x[0][0] + x[1][0]) + x[2][0]) + x[3][0];
-        const f4_t d1 = ((x[0][1] + x[1][1]) + x[2][1]) + x[3][1];
+        const f4_t xh0 = x[0][0] + x[1][0], xh1 = x[0][1] + x[1][1];
+        const f4_t yh0 = yp[0][0] + yp[1][0], yh1 = yp[0][1] + yp[1][1];
+        f4_t(*ex)[64] = sm.ex[c & 1][wv];
+        ex[0][lane] = xh0;
+        ex[1][lane] = xh1;
+        ex[2][lane] = hf == 0 ? yh1 : yh0;        // for the other half's t-tile
+        __syncthreads();
 
-        // S = gamma_{C-1} S + K^T (diag(rho) Delta)
+        // D = W S^T - Tb V = -Delta: (slices 0 + 1) + (slices 2 + 3); the
+        // two halves add the same two sums (addition commutes exactly)
+        const f4_t(*px)[64] = sm.ex[c & 1][wv ^ PW_TILES];
+        const f4_t d0 = xh0 + px[0][lane], d1 = xh1 + px[1][lane];
+        const f4_t ys = (hf == 0 ? yh0 : yh1) + px[2][lane];
+
+        // S = gamma_{C-1} S + K^T (diag(rho) Delta) over this half's columns
         const f4_t rh0 = *reinterpret_cast<const f4_t*>(o.rg + 8 * lq);
         const f4_t rh1 = *reinterpret_cast<const f4_t*>(o.rg + 8 * lq + 4);
         const float gc = o.rg[2 * CK - 1];
         const Planes bs = split8(no, rh0 * d0, rh1 * d1);
 #pragma unroll
-        for (int tt = 0; tt < 8; ++tt) {
+        for (int tt = 0; tt < 4; ++tt) {
             S[tt] = S[tt] * gc;
-            S[tt] = mma3b(o.v[RW_K + tt * 64 + lane], bs, S[tt]);
+            S[tt] = mma3b(o.v[PW_K + (4 * hf + tt) * 64 + lane], bs, S[tt]);
         }
 
-        // y of the chunk: Y^T = gamma_t (S Q^T) + D^T (-P)^T, leading planes of D and P
+        // y of t-tile hf: Y^T = gamma_t (S Q^T) + D^T (-P)^T, leading planes of D and P
         u4_t dh, dm;
         split8hm(no, d0, d1, dh, dm);
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-            const int yt = 16 * jt + lr;
-            f4_t yv = ys[jt] * o.rg[CK + yt];
-            const u4_t ch = o.v[RW_P + (jt * 2) * 64 + lane], cm = o.v[RW_P + (jt * 2 + 1) * 64 + lane];
-            yv = mma(dm, ch, yv);
-            yv = mma(dh, cm, yv);
-            yv = mma(dh, ch, yv);
-            const int t = c * CK + yt;
-            if (t < T) {
-                u2_t w = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
-                if (!keep[jt]) w = u2_t{0, 0};   // masked step
-                *reinterpret_cast<u2_t*>(yw + (int64_t)t * vstride) = w;
-            }
+        f4_t yv = ys * o.rg[CK + yt];
+        const u4_t ch = o.v[PW_P + (hf * 2) * 64 + lane], cm = o.v[PW_P + (hf * 2 + 1) * 64 + lane];
+        yv = mma(dm, ch, yv);
+        yv = mma(dh, cm, yv);
+        yv = mma(dh, ch, yv);
+        const int t = c * CK + yt;
+        if (t < T) {
+            u2_t w = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
+            if (!keep) w = u2_t{0, 0};   // masked step
+            *reinterpret_cast<u2_t*>(yw + (int64_t)t * vstride) = w;
         }
 
         if (pre) stage_store(slot == 0 ? 2 : slot - 1);    // slot of chunk c + 2, last read in step c - 1
-        __syncthreads();
         slot = slot == 2 ? 0 : slot + 1;
     }
 
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) *reinterpret_cast<f4_t*>(state_out + soff + 16 * tt) = S[tt];
+    for (int tt = 0; tt < 4; ++tt) *reinterpret_cast<f4_t*>(state_out + soff + 16 * tt) = S[tt];
 }
 
 // ================================================================== launch
@@ -1643,15 +1667,15 @@ static hipError_t launch_chunked(const RecurrentArgs& a, const PrologueIn* pin, 
     in.qsw = o.qsw;
     in.ksw = o.ksw;
     // two row tiles per block once one tile per block would need more blocks
-    // than the device has CUs (the sequential blocks run one per CU); one
-    // wave per row tile (chunk_seq_rows_kernel) once two tiles per block
-    // would still need more
+    // than the device has CUs (the sequential blocks run one per CU); two
+    // waves per row tile, four tiles per block (chunk_seq_pairs_kernel), once
+    // two tiles per block would still need more
     const int cus = device_cu_count();
     const int64_t tiles = (int64_t)a.B * a.Hv * (a.Dv / RB);
-    if (!a.g_per_key && a.Dv % (RWW * RB) == 0 && cus > 0 && tiles > 2 * (int64_t)cus) {
-        const int rb = a.Dv / (RWW * RB);
+    if (!a.g_per_key && a.Dv % (PW_TILES * RB) == 0 && cus > 0 && tiles > 2 * (int64_t)cus) {
+        const int rb = a.Dv / (PW_TILES * RB);
         const int64_t nb = (int64_t)a.B * a.Hv * rb;
-        hipLaunchKernelGGL(chunk_seq_rows_kernel, dim3((unsigned)nb), dim3(RW_THREADS), 0, stream, in, a.state_in,
+        hipLaunchKernelGGL(chunk_seq_pairs_kernel, dim3((unsigned)nb), dim3(PW_THREADS), 0, stream, in, a.state_in,
                            a.state_out, a.y, a.mask, a.T, a.Hk, a.Hv, a.Dv, L.nc, rb, (int)nb);
         return hipGetLastError();
     }

@@ -647,17 +647,17 @@ def test_recurrent_chunked_matches_oracle(case):
 
 @pytest.mark.parametrize("B,Hv,Dv,zero_state", [(2, 32, 128, False), (3, 32, 64, False), (3, 32, 128, False),
                                                   (5, 32, 64, False), (4, 32, 128, True)],
-                         ids=["two_tiles_B2", "two_tiles_B3_Dv64", "row_waves_B3", "row_waves_B5_Dv64",
-                              "row_waves_B4_zero_state"])
+                         ids=["two_tiles_B2", "two_tiles_B3_Dv64", "wave_pairs_B3", "wave_pairs_B5_Dv64",
+                              "wave_pairs_B4_zero_state"])
 def test_recurrent_chunked_two_row_tiles(B, Hv, Dv, zero_state):
     """Once B*Hv*Dv/16 exceeds the CU count the sequential pass serves two
-    16-row tiles per block, and once it exceeds twice the CU count one wave
-    per tile over all key columns (chunk_seq_rows_kernel); one tile per block
-    below that.  Sequences of a batch are independent, so each must be
+    16-row tiles per block, and once it exceeds twice the CU count two waves
+    per tile, one per half of the key columns, four tiles per block
+    (chunk_seq_pairs_kernel); one tile per block below that.  Sequences of a batch are independent, so each must be
     bit-identical to itself run alone (one tile per block), and the batch
     must meet the oracle.  T = 100 ends in a partial chunk; the last
     sequence has masked steps."""
-    say("recurrent_chunked two row tiles / row waves", B, Hv, Dv, zero_state)
+    say("recurrent_chunked two row tiles / wave pairs", B, Hv, Dv, zero_state)
     ri = rec_inputs(B, 100, Hv // 2, Hv, 128, Dv, 421)
     if zero_state:
         ri["state"] = None
@@ -672,8 +672,8 @@ def test_recurrent_chunked_two_row_tiles(B, Hv, Dv, zero_state):
     st = np.zeros(s.shape) if ri["state"] is None else ri["state"].astype(np.float64)
     y_ref, s_ref = oracle.recurrent(*[oracle.bf16_to_f64(ri[k]) for k in ("q", "k", "v")],
                                     ri["g"].astype(np.float64), ri["beta"].astype(np.float64), st, mask=mask)
-    H.check_y(y, y_ref, "two tiles / row waves")
-    H.check_state(s, s_ref, 1e-4, "two tiles / row waves")
+    H.check_y(y, y_ref, "two tiles / wave pairs")
+    H.check_state(s, s_ref, 1e-4, "two tiles / wave pairs")
 
 
 def test_recurrent_chunked_properties():
