@@ -212,15 +212,16 @@ __device__ __forceinline__ f4_t mma6(const Planes& a, const Planes& b, f4_t c) {
 // ========================================================= chunk preparation
 
 // Inputs of the per-key form's preparation: k and q rows in f32, the gate
-// rows (then the suffix decays within each half chunk) and the prefix decays
-// within each half chunk, per key column.  Nothing in the per-head form.
+// rows (then the suffix decays within each quarter chunk) and the prefix
+// decays within each quarter chunk, per key column.  Nothing in the per-head
+// form.
 template <bool PK>
 struct PkIn {
     float kf[CK][DKC + 4];
     float qf[CK][DKC + 4];
     float ge[CK][DKC + 4];
     float gam[CK][DKC + 4];
-    float gb[2][DKC];          // the product of each half chunk's gates
+    float gq[4][DKC];          // the product of each quarter chunk's gates
 };
 template <>
 struct PkIn<false> {};
@@ -598,19 +599,20 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) 
         // 3'. per-key decay ratios R_j(t, s) = g_{s+1}[j] ... g_t[j]:
         //     A[t][s] = beta_t sum_j k_t[j] k_s[j] R_j(t, s)   (s < t)
         //     P[t][s] = sum_j q_t[j] k_s[j] R_j(t, s)          (s <= t)
-        //     Within each half chunk (s, t both below 16 or both from 16 on)
-        //     thread (s, jg) carries u = k_s o R(t, s) over key columns
-        //     16 jg .. 16 jg + 15 while t runs up from s to the half's end (a
-        //     running product, never a quotient of cumulative decays); the
-        //     eight column groups of a row s are adjacent lanes, summed by DPP.
-        //     A wave's rows s start at s_lo, so its loop starts there.  Across
-        //     the halves (t >= 16 > s) R(t, s) = R(t, 15) o R(15, s), two
-        //     factors <= 1: that block is one f32 product on the matrix cores.
+        //     Within each quarter chunk of eight steps (s, t in the same
+        //     quarter) thread (s, jg) carries u = k_s o R(t, s) over key
+        //     columns 16 jg .. 16 jg + 15 while t runs up from s to the
+        //     quarter's end (a running product, never a quotient of cumulative
+        //     decays); the eight column groups of a row s are adjacent lanes,
+        //     summed by DPP.  Wave w holds the rows of quarter w.  Across
+        //     quarters (s in an earlier one) R(t, s) splits at the boundary
+        //     into factors <= 1, R(t, s) = R(t, m) o R(m, s): those blocks are
+        //     f32 products on the matrix cores (below).
         auto& sw = sh.w.s[0];
         const int s = tl >> 3, jg = tl & 7;
-        // a wave's eight rows s share s_lo and the half's end: scalar bounds
+        // a wave's eight rows s share their quarter: scalar bounds
         const int s_lo = __builtin_amdgcn_readfirstlane(s & ~7);
-        const int t_hi = __builtin_amdgcn_readfirstlane(s < CK / 2 ? CK / 2 : CK);
+        const int t_hi = s_lo + 8;
         float u[16];
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
@@ -667,16 +669,14 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) 
                 sw.tm[t][s] = t >= s ? pp : 0.f;       // P, kept here until its planes are cut
             }
         };
-        // steps s_lo .. t_hi - 1 in pairs (8 or 16 of them); the first eight
-        // cover the wave's own rows, where the decay starts row by row
+        // steps s_lo .. s_lo + 7 in pairs, the wave's own rows, where the
+        // decay starts row by row
         RowOps ra = row_ops(s_lo);
         for (int t = s_lo; t < t_hi; t += 2) {
             const RowOps rb = row_ops(t + 1);
-            if (t < s_lo + 8) pk_step(t, ra, std::true_type{});
-            else pk_step(t, ra, std::false_type{});
+            pk_step(t, ra, std::true_type{});
             ra = row_ops(min(t + 2, t_hi - 1));
-            if (t + 1 < s_lo + 8) pk_step(t + 1, rb, std::true_type{});
-            else pk_step(t + 1, rb, std::false_type{});
+            pk_step(t + 1, rb, std::true_type{});
         }
         if (jg == 0)
             for (int t = 0; t < s_lo; ++t) {
@@ -684,54 +684,101 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) 
                 sw.tm[t][s] = 0.f;
             }
         __syncthreads();
-        // decays per key column within each half chunk: prefix products
-        // (gam) and suffix products (ge, over the gate rows), and the product
-        // of each half's gates
-        constexpr int CH2 = CK / 2;
-        if (tl < DKC) {
-            float gc[CK];
+        // decays per key column within each quarter chunk: prefix products
+        // (gam), suffix products (ge, over the gate rows), and the product
+        // of each quarter's gates; thread (j, h) takes column j in half h
+        constexpr int CQ = CK / 4, CH2 = CK / 2;
+        {
+            const int j = tl & (DKC - 1), h = tl / DKC;
+            float gc[2 * CQ];
 #pragma unroll
-            for (int t = 0; t < CK; ++t) gc[t] = sh.u.pk.ge[t][tl];
+            for (int i = 0; i < 2 * CQ; ++i) gc[i] = sh.u.pk.ge[2 * CQ * h + i][j];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int qq = 0; qq < 2; ++qq) {
                 float gp = 1.f, ep = 1.f;
 #pragma unroll
-                for (int i = 0; i < CH2; ++i) {
-                    const int t = CH2 * h + i, r = CH2 * h + CH2 - 1 - i;
-                    gp *= gc[t];
-                    sh.u.pk.gam[t][tl] = gp;
-                    sh.u.pk.ge[r][tl] = ep;
-                    ep *= gc[r];
+                for (int i = 0; i < CQ; ++i) {
+                    const int t = CQ * (2 * h + qq) + i, r = CQ * (2 * h + qq) + CQ - 1 - i;
+                    gp *= gc[CQ * qq + i];
+                    sh.u.pk.gam[t][j] = gp;
+                    sh.u.pk.ge[r][j] = ep;
+                    ep *= gc[CQ * qq + CQ - 1 - i];
                 }
-                sh.u.pk.gb[h][tl] = gp;
+                sh.u.pk.gq[2 * h + qq][j] = gp;
             }
-            o.rg[unit * rg_floats<PK>() + 2 * CK + tl] = sh.u.pk.gb[0][tl] * sh.u.pk.gb[1][tl];   // Gamma_{C-1}
         }
         __syncthreads();
-        // across the halves: A21 = diag(beta) (K2 o G2)(K1 o E1)^T (wave 1) and
-        // P21 = (Q2 o G2)(K1 o E1)^T (wave 3), G2 the second half's prefix and
-        // E1 the first half's suffix decays; f32 operands as planes, six products
-        if (wl == 1 || wl == 3) {
-            f4_t acc = {0.f, 0.f, 0.f, 0.f};
+        // Gamma_{C-1} and the blocks of A and P across quarters, each one 16 x 16
+        // f32 product over the key columns on the f32 matrix instruction
+        // (product e of a 32-column block takes element e of the lane's eight
+        // columns, as in W S^T of the sequential pass):
+        //   waves 0, 2: A, P of steps t in quarter 1 (3) against s in quarter 0
+        //     (2), R(t, s) = G(t) o E(s) with G the prefix decays of t's quarter
+        //     and E the suffix decays of s's (the other two 8 x 8 blocks of the
+        //     tile pair unrelated steps and are dropped);
+        //   waves 1, 3: A, P of t in the second half against s in the first,
+        //     R(t, s) = (G(t) [o g_q2 for t in quarter 3]) o (E(s) [o g_q1 for
+        //     s in quarter 0]), g_q the product of quarter q's gates.
+        if (tl < DKC)
+            o.rg[unit * rg_floats<PK>() + 2 * CK + tl] =
+                ((sh.u.pk.gq[0][tl] * sh.u.pk.gq[1][tl]) * sh.u.pk.gq[2][tl]) * sh.u.pk.gq[3][tl];   // Gamma_{C-1}
+        {
+            const bool xh = (wl & 1) != 0;     // across the halves
+            const bool isp = wl >= 2;          // P (q rows) instead of A (k rows)
+            const int tm = xh ? CH2 + lr : (lr < CQ ? CQ + lr : CH2 + lr);     // left operand row lr: step t
+            const int sn = xh ? lr : (lr < CQ ? lr : CQ + lr);                // right operand row lr: step s
+            const float* xr = isp ? &sh.u.pk.qf[tm][0] : &sh.u.pk.kf[tm][0];
+            const bool in3 = xh && tm >= CH2 + CQ, in0 = xh && sn < CQ;
+            auto ld4 = [](const float* p) { return *reinterpret_cast<const f4_t*>(p); };
+            f4_t acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int ks = 0; ks < DKC / 32; ++ks) {
                 const int c = 32 * ks + 8 * lq;
-                float av[8], bv[8];
+                f4_t av[2], bv[2];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = wl == 1 ? sh.u.pk.kf[CH2 + lr][c + e] : sh.u.pk.qf[CH2 + lr][c + e];
-                    av[e] = x * sh.u.pk.gam[CH2 + lr][c + e];
-                    bv[e] = sh.u.pk.kf[lr][c + e] * sh.u.pk.ge[lr][c + e];
+                for (int h = 0; h < 2; ++h) {
+                    const int ch = c + 4 * h;
+                    f4_t gt = ld4(&sh.u.pk.gam[tm][ch]), es = ld4(&sh.u.pk.ge[sn][ch]);
+                    if (xh) {
+                        const f4_t g2 = ld4(&sh.u.pk.gq[2][ch]), g1 = ld4(&sh.u.pk.gq[1][ch]);
+                        const f4_t gt3 = g2 * gt, es0 = es * g1;
+                        gt = in3 ? gt3 : gt;
+                        es = in0 ? es0 : es;
+                    }
+                    av[h] = ld4(xr + ch) * gt;
+                    bv[h] = ld4(&sh.u.pk.kf[sn][ch]) * es;
                 }
-                const Planes pa = split8(no, f4_t{av[0], av[1], av[2], av[3]}, f4_t{av[4], av[5], av[6], av[7]});
-                const Planes pb = split8(no, f4_t{bv[0], bv[1], bv[2], bv[3]}, f4_t{bv[4], bv[5], bv[6], bv[7]});
-                acc = mma6(pa, pb, acc);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc2[ks & 1] = mma_f32(av[e >> 2][e & 3], bv[e >> 2][e & 3], acc2[ks & 1]);
             }
+            const f4_t acc = acc2[0] + acc2[1];
+            // output row 4 lq + i (a left row, step t), column lr (a right row, step s)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = CH2 + 4 * lq + i;
-                if (wl == 1) sw.a[t][lr] = sh.bs[0][t] * acc[i];
-                else sw.tm[t][lr] = acc[i];
+                const int m = 4 * lq + i;
+                const int t = xh ? CH2 + m : (m < CQ ? CQ + m : CH2 + m);
+                if (xh || (m < CQ) == (lr < CQ)) {
+                    if (!isp) sw.a[t][sn] = sh.bs[0][t] * acc[i];
+                    else sw.tm[t][sn] = acc[i];
+                }
+            }
+        }
+        __syncthreads();
+        // the chunk's decays from the quarter ones, in place: Gamma_t = g_0 ... g_t
+        // is the product of the earlier quarters' gates times t's prefix in its
+        // quarter, E_t = g_{t+1} ... g_{C-1} t's suffix in its quarter times the
+        // later quarters' gates
+        {
+            const int j = tl & (DKC - 1), h = tl / DKC;
+            const float g0 = sh.u.pk.gq[0][j], g1 = sh.u.pk.gq[1][j], g2 = sh.u.pk.gq[2][j], g3 = sh.u.pk.gq[3][j];
+            const float g01 = g0 * g1, g23 = g2 * g3;
+            const float pre[4] = {1.f, g0, g01, g01 * g2};
+            const float suf[4] = {g1 * g23, g23, g3, 1.f};
+#pragma unroll
+            for (int i = 0; i < 2 * CQ; ++i) {
+                const int t = 2 * CQ * h + i, q = t / CQ;
+                if (q > 0) sh.u.pk.gam[t][j] = pre[q] * sh.u.pk.gam[t][j];
+                if (q < 3) sh.u.pk.ge[t][j] = sh.u.pk.ge[t][j] * suf[q];
             }
         }
         __syncthreads();
@@ -744,14 +791,8 @@ __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) 
             if (tl < CK) sh.gm[0][tl] = 1.f;
             if (tl < 2 * CK) o.rg[unit * rg_floats<PK>() + tl] = tl < CK ? -1.f : 1.f;
         }
-        // the chunk's decays from the half ones: Gamma_t = g_0 ... g_t and
-        // E_t = g_{t+1} ... g_{C-1}
-        auto gamma_at = [&](int t, int j) {
-            return t < CH2 ? sh.u.pk.gam[t][j] : sh.u.pk.gb[0][j] * sh.u.pk.gam[t][j];
-        };
-        auto e_at = [&](int t, int j) {
-            return t < CH2 ? sh.u.pk.ge[t][j] * sh.u.pk.gb[1][j] : sh.u.pk.ge[t][j];
-        };
+        auto gamma_at = [&](int t, int j) { return sh.u.pk.gam[t][j]; };
+        auto e_at = [&](int t, int j) { return sh.u.pk.ge[t][j]; };
         // operands: (K o Gamma)^T planes for W (kept in registers until step
         // 6), -(K o E)^T in f32 and Q o Gamma planes for the sequential pass
 #pragma unroll
