@@ -63,8 +63,10 @@
 //   W = T diag(beta) (K o Gamma),   Y = (Q o Gamma) S_0^T + P Delta,
 //   S_C = S_0 diag(Gamma_{C-1}) + Delta^T (K o E),
 // Gamma_t = g_0 o ... o g_t, E_t = g_{t+1} o ... o g_{C-1}; chunk_prep_kernel
-// <0, 1, true> forms the ratios as running products and chunk_seq_kernel
-// <1, true> takes Q o Gamma, (K o E)^T and Gamma_{C-1} per v-head.
+// <0, 1, true> forms the ratios as running products inside each quarter
+// chunk and as f32 products of prefix- and suffix-scaled rows across
+// quarters, and chunk_seq_kernel <1, true> takes Q o Gamma, (K o E)^T and
+// Gamma_{C-1} per v-head.
 #include <algorithm>
 #include <cstddef>
 #include <type_traits>
@@ -279,9 +281,10 @@ constexpr int rg_floats() { return PK ? 2 * CK + DKC : 2 * CK; }
 // A two-head block takes just under 50 KB of LDS (the k rows share space
 // with the T planes), so three fit a CU where the registers allow it.
 // PK: the per-key gate g [B, T, Hv, Dk] (KF = 0, NH = 1): the decay ratios
-// are per key column, so A and P are formed as running products instead of
-// scaled k k^T, q k^T; K o Gamma enters W, and the sequential pass gets
-// Q o Gamma, (K o E)^T and Gamma_{C-1} in place of q, k and gamma.
+// are per key column, so A and P are formed from running products and
+// decay-scaled row products instead of scaled k k^T, q k^T; K o Gamma enters
+// W, and the sequential pass gets Q o Gamma, (K o E)^T and Gamma_{C-1} in
+// place of q, k and gamma.
 template <int KF, int NH, bool PK = false>
 __global__ __launch_bounds__(256 * NH, PK ? 2 : NH == 2 ? (KF > 0 ? 6 : 3) : 4) void chunk_prep_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
