@@ -19,9 +19,10 @@
 // the same arithmetic as the per-step loop up to rounding order: dense
 // products replace the per-step dot products.
 //
-// fp32 products on the matrix cores.  W S^T (and the per-key form's state
-// update) run on the f32 matrix instruction (16x16x4, f32 in, f32 out).  The
-// other products run on bf16 MFMAs: every f32 operand x is cut into three
+// fp32 products on the matrix cores.  W S^T of the sequential pass and the
+// per-key preparation's cross-quarter blocks run on the f32 matrix
+// instruction (16x16x4, f32 in, f32 out).  The other products run on bf16
+// MFMAs: every f32 operand x is cut into three
 // bf16 planes x = h + m + l exactly (h is x rounded to bf16, m the remainder
 // rounded, l what is left), so that a product of an f32 matrix with an exact
 // bf16 matrix (q, k, v) is three bf16 MFMAs with f32 accumulation, and a
@@ -1318,18 +1319,18 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
         }
 
         if constexpr (PK) {
-            // per-key: S = S diag(Gamma_{C-1}) + Delta^T (K o E) on the f32
-            // matrix instruction, Delta = -D: product 4 jt + i takes steps
-            // 16 jt + 4 q + i, element i of D's t-tile jt and of -(K o E)^T's
+            // per-key: S = S diag(Gamma_{C-1}) + Delta^T (K o E), Delta = -D,
+            // as the six plane products of -(K o E)^T (cut here from its f32
+            // operand, off the state chain) with D: element e of both is step
+            // kperm(q, e), the contraction layout of the bf16 products
 #pragma unroll
             for (int rt = 0; rt < NR; ++rt) {
+                const Planes dp = split8(no, d0[rt], d1[rt]);
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
+                    const Planes kp = split8(no, o.kf[tt][0], o.kf[tt][1]);
                     S[rt][tt] = S[rt][tt] * o.gd[tt];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) S[rt][tt] = mma_f32(o.kf[tt][0][i], d0[rt][i], S[rt][tt]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) S[rt][tt] = mma_f32(o.kf[tt][1][i], d1[rt][i], S[rt][tt]);
+                    S[rt][tt] = mma6(kp, dp, S[rt][tt]);
                 }
             }
         } else {

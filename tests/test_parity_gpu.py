@@ -646,17 +646,18 @@ def test_recurrent_chunked_matches_oracle(case):
 
 
 @pytest.mark.parametrize("B,Hv,Dv,zero_state", [(2, 32, 128, False), (3, 32, 64, False), (3, 32, 128, False),
-                                                  (5, 32, 64, False), (4, 32, 128, True)],
+                                                  (5, 32, 64, False), (4, 32, 128, True), (2, 32, 192, False)],
                          ids=["two_tiles_B2", "two_tiles_B3_Dv64", "wave_pairs_B3", "wave_pairs_B5_Dv64",
-                              "wave_pairs_B4_zero_state"])
+                              "wave_pairs_B4_zero_state", "wave_pairs_B2_Dv192"])
 def test_recurrent_chunked_two_row_tiles(B, Hv, Dv, zero_state):
     """Once B*Hv*Dv/16 exceeds the CU count the sequential pass serves two
     16-row tiles per block, and once it exceeds twice the CU count two waves
     per tile, one per half of the key columns, four tiles per block
-    (chunk_seq_pairs_kernel); one tile per block below that.  Sequences of a batch are independent, so each must be
-    bit-identical to itself run alone (one tile per block), and the batch
-    must meet the oracle.  T = 100 ends in a partial chunk; the last
-    sequence has masked steps."""
+    (chunk_seq_pairs_kernel); one tile per block below that.  Sequences of a
+    batch are independent, so each must be bit-identical to itself run alone
+    (a smaller grid: one or two tiles per block), and the batch must meet
+    the oracle.  T = 100 ends in a partial chunk; the last sequence has
+    masked steps."""
     say("recurrent_chunked two row tiles / wave pairs", B, Hv, Dv, zero_state)
     ri = rec_inputs(B, 100, Hv // 2, Hv, 128, Dv, 421)
     if zero_state:
