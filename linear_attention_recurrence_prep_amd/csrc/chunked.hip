@@ -1292,32 +1292,6 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
             d1[rt] = (p01 + p11) + (p21 + p31);
         }
 
-        // this wave's share of S Q^T (rows r, columns t), formed after the
-        // barrier, beside the D sums and split (the output waves read it one
-        // chunk later); y is rounded to bf16, so the state's two leading
-        // planes suffice (2^-16)
-#pragma unroll
-        for (int rt = 0; rt < NR; ++rt) {
-            f4_t y0v, y1v;
-            if constexpr (PK) {
-                // Q o Gamma in two planes: h.h, h.m and m.h
-                y0v = mma(s_m[rt], o.q[0], zero);
-                y1v = mma(s_m[rt], o.q[1], zero);
-                y0v = mma(s_h[rt], o.qm[0], y0v);
-                y1v = mma(s_h[rt], o.qm[1], y1v);
-                y0v = mma(s_h[rt], o.q[0], y0v);
-                y1v = mma(s_h[rt], o.q[1], y1v);
-            } else {
-                y0v = mma(s_m[rt], o.q[0], zero);
-                y1v = mma(s_m[rt], o.q[1], zero);
-                y0v = mma(s_h[rt], o.q[0], y0v);
-                y1v = mma(s_h[rt], o.q[1], y1v);
-            }
-            f4_t* yb = sh.y[b3][rt];
-            yb[(2 * wv) * 64 + lane] = y0v;
-            yb[(2 * wv + 1) * 64 + lane] = y1v;
-        }
-
         if constexpr (PK) {
             // per-key: S = S diag(Gamma_{C-1}) + Delta^T (K o E), Delta = -D,
             // as the six plane products of -(K o E)^T (cut here from its f32
@@ -1349,6 +1323,33 @@ __global__ __launch_bounds__(SEQ_THREADS) void chunk_seq_kernel(SeqIn in, const 
                 S[rt][1] = mma3b(o.k[1], bs[rt], S[rt][1]);
             }
         }
+        // this wave's share of S Q^T (rows r, columns t) from the planes of the
+        // state before the update, issued after the update's products so
+        // that they fill the matrix pipe while the update completes (the
+        // output waves read it one chunk later); y is rounded to bf16, so the
+        // state's two leading planes suffice (2^-16)
+#pragma unroll
+        for (int rt = 0; rt < NR; ++rt) {
+            f4_t y0v, y1v;
+            if constexpr (PK) {
+                // Q o Gamma in two planes: h.h, h.m and m.h
+                y0v = mma(s_m[rt], o.q[0], zero);
+                y1v = mma(s_m[rt], o.q[1], zero);
+                y0v = mma(s_h[rt], o.qm[0], y0v);
+                y1v = mma(s_h[rt], o.qm[1], y1v);
+                y0v = mma(s_h[rt], o.q[0], y0v);
+                y1v = mma(s_h[rt], o.q[1], y1v);
+            } else {
+                y0v = mma(s_m[rt], o.q[0], zero);
+                y1v = mma(s_m[rt], o.q[1], zero);
+                y0v = mma(s_h[rt], o.q[0], y0v);
+                y1v = mma(s_h[rt], o.q[1], y1v);
+            }
+            f4_t* yb = sh.y[b3][rt];
+            yb[(2 * wv) * 64 + lane] = y0v;
+            yb[(2 * wv + 1) * 64 + lane] = y1v;
+        }
+
         if (wv == 0) {
 #pragma unroll
             for (int rt = 0; rt < NR; ++rt) {
