@@ -284,8 +284,10 @@ gdn_status gdn_recurrent_per_key(const gdn_bf16 *q, const gdn_bf16 *k, const gdn
  * gdn_recurrent_chunked (the same precision: fp32 state path, y from two
  * bf16 planes before its bf16 rounding).
  * Within a chunk the decay from step s to step t is per key column,
- * g_{s+1}[j] ... g_t[j]; it is formed as running products, never as a
- * quotient of cumulative decays, so any gate values in [0, 1] are safe.
+ * g_{s+1}[j] ... g_t[j]; it is formed as running products inside each
+ * quarter of the chunk and as a product of two such factors across quarters,
+ * never as a quotient of cumulative decays, so any gate values in [0, 1] are
+ * safe.
  * Arguments as gdn_recurrent_per_key (mask: 0 = inactive step, y written +0,
  * state untouched; NULL = every step active) plus a caller-owned device
  * workspace of at least gdn_recurrent_chunked_per_key_workspace_bytes(...)
