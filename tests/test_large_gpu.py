@@ -14,6 +14,7 @@ import pytest
 import torch
 
 from linear_attention_recurrence_prep_amd import binding, inputs
+from tests import helpers as H
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +91,7 @@ def test_layer_core_prefill_past_2_31_elements():
     gdn_prep followed by gdn_recurrent_chunked bit for bit."""
     B, T = B_LONG, T_LONG
     assert B * T * C > 2**31 > T * C and B * T * HV * DV > 2**31
+    assert H.layer_uses_chunked(B, T, HV, DK, DV) and H.layer_uses_chunked(1, T, HV, DK, DV)
     nws = binding.layer_core_workspace_bytes(B, T, HK, HV, DK, DV)
     assert nws == binding.recurrent_chunked_workspace_bytes(B, T, HK, HV, DK, DV)
     # qkv + y (layer core and composition) + q, k, v + workspace, with room
@@ -131,18 +133,22 @@ def test_layer_core_prefill_past_2_31_elements():
     assert torch.equal(y2, y), "y differs from the composition"
 
 
-def test_decode_past_2_31_state_elements():
-    """Single-step layer core (prologue, then the per-step recurrence) at
-    B = 4100: the state holds 2.15e9 elements, so sequences from 4096 on sit
-    past 2^31.  Sequences 4095 and 4099 equal one-sequence calls bit for
-    bit."""
-    B, T = B_DEC, 1
+@pytest.mark.parametrize("T", [1, 12, 64], ids=["decode", "per_step_T12", "chunked_T64"])
+def test_state_past_2_31_elements(T):
+    """The layer core at B = 4100: the state holds 2.15e9 elements, so
+    sequences from 4096 on sit past 2^31.  T = 1 takes the single-step
+    kernel, T = 12 the per-step form with staged chunks, T = 64 the chunked
+    form (fused preparation, two waves per state tile).  Sequences 4095 and
+    4099 equal one-sequence calls bit for bit."""
+    B = B_DEC
     n_state = B * HV * DV * DK
     assert n_state > 2**31 > 4096 * HV * DV * DK - 1
+    assert H.layer_uses_chunked(B, T, HV, DK, DV) == (T >= 64) == H.layer_uses_chunked(1, T, HV, DK, DV)
     nws = binding.layer_core_workspace_bytes(B, T, HK, HV, DK, DV)
-    need_free(int((3 * 4 * n_state + nws) * 1.1))
-    say("decode past 2^31 state elements", B)
-    d = device_inputs(B, T, 2032)
+    need = 8 * n_state + 2 * B * T * C + 2 * B * T * HV * DV + nws
+    need_free(int(need * 1.25))
+    say("state past 2^31 elements", B, T)
+    d = device_inputs(B, T, 2032 + T)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV)
     y, s, cs = run_layer_core(d, slice(0, B), ws)
     assert not (y == NAN_BF16).any().item(), "y not written everywhere"
