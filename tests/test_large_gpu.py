@@ -181,3 +181,95 @@ def test_gated_rmsnorm_past_2_31_elements():
     binding.gated_rmsnorm(y[2:3], z[2:3], w, out1)
     torch.cuda.synchronize()
     assert torch.equal(out1[0], out[2]), "sequence 2 differs from its one-sequence call"
+
+
+def unit_rows(x):
+    """Rows scaled to unit norm over the last axis (keys as the prologue's
+    normalisation leaves them), stored as bf16."""
+    xf = x.float()
+    return (xf / xf.norm(dim=-1, keepdim=True).clamp_min(1e-6)).to(torch.bfloat16)
+
+
+def recurrence_inputs(B, T, seed, per_key):
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    bf = dict(dtype=torch.bfloat16, device=DEV, generator=gen)
+    f32 = dict(dtype=torch.float32, device=DEV, generator=gen)
+    gshape = (B, T, HV, DK) if per_key else (B, T, HV)
+    return {
+        "q": unit_rows(torch.randn(B, T, HK, DK, **bf)),
+        "k": unit_rows(torch.randn(B, T, HK, DK, **bf)),
+        "v": torch.randn(B, T, HV, DV, **bf),
+        "g": torch.rand(*gshape, **f32).mul_(0.7).add_(0.3),
+        "beta": torch.rand(B, T, HV, **f32),
+        "state": torch.randn(B, HV, DV, DK, **f32).mul_(0.02),
+    }
+
+
+def test_per_key_chunked_past_2_31_elements():
+    """The chunked recurrence with the per-key gate at B = 3, T = 196608: the
+    gate rows (2.4e9 elements), v and y pass 2^31 inside sequence 1, the
+    workspace is about 40 GB.  Sequences 1 and 2 equal one-sequence calls bit
+    for bit."""
+    B, T = B_LONG, T_LONG
+    ng = B * T * HV * DK
+    assert ng > 2**31 and B * T * HV * DV > 2**31
+    nws = binding.recurrent_chunked_per_key_workspace_bytes(B, T, HK, HV, DK, DV)
+    need = 4 * ng + 2 * (2 * B * T * HK * DK) + 2 * (2 * B * T * HV * DV) + 2 * T * HV * DV + nws
+    need_free(int(need * 1.25))
+    say("per-key chunked past 2^31 elements", B, T)
+    d = recurrence_inputs(B, T, 2041, per_key=True)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+
+    def run(sl):
+        x = {k_: v_[sl] for k_, v_ in d.items()}
+        n = x["q"].shape[0]
+        y = torch.full((n, T, HV, DV), NAN_BF16, dtype=torch.int16, device=DEV)
+        s = torch.full((n, HV, DV, DK), float("nan"), dtype=torch.float32, device=DEV)
+        binding.recurrent_chunked_per_key(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"], s, y, ws)
+        torch.cuda.synchronize()
+        return y, s
+
+    y, s = run(slice(0, B))
+    assert not (y == NAN_BF16).any().item(), "y not written everywhere"
+    assert torch.isfinite(s).all().item()
+    for b in (1, 2):
+        say("one-sequence call", b)
+        y1, s1 = run(slice(b, b + 1))
+        assert torch.equal(y1[0], y[b]), f"sequence {b}: y differs from its one-sequence call"
+        assert torch.equal(s1[0], s[b]), f"sequence {b}: state differs from its one-sequence call"
+        del y1, s1
+
+
+@pytest.mark.parametrize("per_key", [False, True], ids=["per_head_gate", "per_key_gate"])
+def test_snapshots_past_2_31_elements(per_key):
+    """gdn_recurrent_snapshots at B = 4100, T = 2 with the state after steps 1
+    and 2: the state and each snapshot hold 2.15e9 elements.  Sequences 4095
+    and 4099 equal one-sequence calls bit for bit, snapshots included."""
+    B, T = B_DEC, 2
+    n_state = B * HV * DV * DK
+    assert n_state > 2**31
+    steps = [1, 2]
+    need_free(int(4 * n_state * (2 + len(steps)) * 1.25))
+    say("snapshots past 2^31 elements", B, "per-key" if per_key else "per-head")
+    d = recurrence_inputs(B, T, 2042 + per_key, per_key)
+
+    def run(sl):
+        x = {k_: v_[sl] for k_, v_ in d.items()}
+        n = x["q"].shape[0]
+        y = torch.full((n, T, HV, DV), NAN_BF16, dtype=torch.int16, device=DEV)
+        s = torch.full((n, HV, DV, DK), float("nan"), dtype=torch.float32, device=DEV)
+        snaps = torch.full((len(steps), n, HV, DV, DK), float("nan"), dtype=torch.float32, device=DEV)
+        binding.recurrent_snapshots(x["q"], x["k"], x["v"], x["g"], x["beta"], x["state"], s, y, steps, snaps)
+        torch.cuda.synchronize()
+        return y, s, snaps
+
+    y, s, snaps = run(slice(0, B))
+    assert not (y == NAN_BF16).any().item(), "y not written everywhere"
+    assert torch.equal(snaps[-1], s), "the snapshot after the last step is the final state"
+    for b in (4095, 4099):
+        say("one-sequence call", b)
+        y1, s1, sn1 = run(slice(b, b + 1))
+        assert torch.equal(y1[0], y[b]), f"sequence {b}: y differs from its one-sequence call"
+        assert torch.equal(s1[0], s[b]), f"sequence {b}: state differs from its one-sequence call"
+        assert torch.equal(sn1[:, 0], snaps[:, b]), f"sequence {b}: snapshots differ from its one-sequence call"
