@@ -12,8 +12,10 @@
  * - Pointers are DEVICE pointers (HIP device memory of the current device),
  *   row-major and contiguous.  bf16 tensors are raw bfloat16 bit patterns
  *   (gdn_bf16).  Every tensor pointer must be 16-byte aligned.
- * - Ownership: the caller owns every buffer.  The library never allocates,
- *   frees or retains device memory and keeps no pointer after returning.
+ * - Ownership: the caller owns every buffer.  The library never allocates or
+ *   frees device memory and keeps no caller pointer after returning; the
+ *   only device memory it holds is the scratch array of
+ *   gdn_layer_core_no_alloc (reserved by the code object, see there).
  * - Execution: every call only enqueues kernels on `stream` (a hipStream_t
  *   passed as void*; NULL is the null stream) and returns without
  *   synchronising.  Outputs are valid once the stream reaches that point.
@@ -30,8 +32,11 @@
  *   hk = hv / (Hv / Hk), the repeat order of the pages); Dk in
  *   {32, 64, 128, 256}; Dv a multiple of 8 in [8, 4096]; conv kernel size K
  *   in {2, 3, 4}.
- * - Concurrency: calls on different streams or threads are independent; the
- *   library holds no global mutable state other than the thread-local error.
+ * - Concurrency: calls on different streams or threads are independent,
+ *   except gdn_layer_core_no_alloc calls on one device, which share that
+ *   device's scratch array.  The library's other global state is the
+ *   thread-local error and a per-device cache of the compute-unit count
+ *   (read once; it picks between kernels whose results are bit-identical).
  */
 #ifndef GDN_H
 #define GDN_H

@@ -71,6 +71,28 @@ def build(verbose: bool = False, extra_flags=None, lib=LIB, obj_dir=OUT_DIR, lin
     return lib
 
 
+C_DEMO_SRC = os.path.join(ROOT, "tests", "c_abi_demo.c")
+C_DEMO = os.path.join(ROOT, "tests", "c_abi_demo")
+
+
+def build_c_abi_demo(verbose: bool = False) -> str:
+    """Compile the C99 test program of the ABI (tests/c_abi_demo.c) with gcc
+    against the in-tree libgdn.so and the HIP runtime (no HIP device code)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = C_DEMO + ".tmp"
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"), C_DEMO_SRC,
+           "-L", PKG, "-lgdn", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../linear_attention_recurrence_prep_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, C_DEMO)
+    return C_DEMO
+
+
 if __name__ == "__main__":
     build(verbose="-v" in sys.argv)
+    build_c_abi_demo(verbose="-v" in sys.argv)
     print(LIB)

@@ -390,3 +390,34 @@ def test_no_alloc_rejects_before_set_up(L):
     assert call(Hk=3) == DIMS
     assert call(Dk=100) == UNSUP
     assert call(B=-1) == DIMS
+
+
+def _c_demo():
+    """The C99 test program of the ABI, (re)built when missing or older than
+    its source (gcc only, no device code)."""
+    import shutil
+    from linear_attention_recurrence_prep_amd import build as B
+    if not os.path.exists(B.C_DEMO) or os.path.getmtime(B.C_DEMO) < os.path.getmtime(B.C_DEMO_SRC):
+        if shutil.which("gcc") is None:
+            pytest.skip("gcc not available to build the C test program")
+        B.build_c_abi_demo()
+    return B.C_DEMO
+
+
+def test_c_program_against_the_abi(L):
+    """tests/c_abi_demo.c, plain C99 linked against libgdn.so (the header
+    compiles as C), gets the documented status for bad calls (bad dims, an
+    unsupported Dk, a NULL input, a misaligned pointer, an output overlapping
+    an input, a missing workspace; B = 0 is valid) and the workspace sizes
+    the Python binding reports."""
+    import subprocess
+    r = subprocess.run([_c_demo(), "check"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "check ok" in r.stdout
+    got = dict(line.rsplit(" ", 1) for line in r.stdout.splitlines() if "workspace_bytes" in line)
+    assert int(got["layer_core_workspace_bytes(1,4096,16,32,128,128)"]) == \
+        binding.layer_core_workspace_bytes(1, 4096, 16, 32, 128, 128)
+    assert int(got["recurrent_chunked_workspace_bytes(1,4096,16,32,128,128)"]) == \
+        binding.recurrent_chunked_workspace_bytes(1, 4096, 16, 32, 128, 128)
+    assert int(got["layer_core_workspace_bytes(64,1,16,32,128,128)"]) == \
+        binding.layer_core_workspace_bytes(64, 1, 16, 32, 128, 128)

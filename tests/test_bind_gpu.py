@@ -1,6 +1,7 @@
 """binding.bind: a call marshalled once and issued again gives the same bits
 as the direct call, picks up new buffer contents, and keeps its tensors
-alive."""
+alive.  And the C ABI driven from a plain C program (tests/c_abi_demo.c)
+gives the bits of the same call made through the binding."""
 import numpy as np
 import pytest
 import torch
@@ -71,3 +72,39 @@ def test_bound_recurrent_in_place_decode_loop():
         call()
     torch.cuda.synchronize()
     assert torch.equal(sa, sb) and torch.equal(ya, yb)
+
+
+@pytest.mark.parametrize("T", [20, 100], ids=["per_step", "chunked"])
+def test_c_program_layer_core_matches_binding(T, tmp_path):
+    """A plain C99 program (tests/c_abi_demo.c: hipMalloc, hipMemcpy and one
+    gdn_layer_core call on the null stream, no Python in between) gives the
+    bits of the same call made through the Python binding."""
+    import os
+    import subprocess
+    from linear_attention_recurrence_prep_amd import build as bld
+    demo = bld.C_DEMO
+    assert os.path.exists(demo), "the C test program is built by build()"
+    B, Hk, Hv, Dk, Dv, K = 2, 2, 4, 128, 64, 4
+    raw, d = _layer(B, T, Hk, Hv, Dk, Dv, K)
+    for name in ("qkv", "conv_w", "conv_state", "a", "b", "A_log", "dt_bias", "state"):
+        np.ascontiguousarray(raw[name]).tofile(tmp_path / name)
+    qs, ks = 1.0 / Dk, Dk ** -0.5
+    print("[case] C program layer core", T, flush=True)
+    r = subprocess.run([demo, "run", str(tmp_path), str(B), str(T), str(Hk), str(Hv), str(Dk), str(Dv), str(K),
+                        repr(qs), repr(ks)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    C = 2 * Hk * Dk + Hv * Dv
+    y_c = np.fromfile(tmp_path / "y", dtype=np.int16).reshape(B, T, Hv, Dv)
+    s_c = np.fromfile(tmp_path / "state_out", dtype=np.float32).reshape(B, Hv, Dv, Dk)
+    cs_c = np.fromfile(tmp_path / "conv_state_out", dtype=np.int16).reshape(B, K - 1, C)
+    ws = torch.empty(max(binding.layer_core_workspace_bytes(B, T, Hk, Hv, Dk, Dv), 1), dtype=torch.uint8,
+                     device=H.DEV)
+    s = torch.empty(B, Hv, Dv, Dk, device=H.DEV)
+    y = torch.empty(B, T, Hv, Dv, dtype=torch.int16, device=H.DEV)
+    cs = torch.empty(B, K - 1, C, dtype=torch.int16, device=H.DEV)
+    binding.layer_core(d["qkv"], d["conv_w"], d["conv_state"], cs, d["a"], d["b"], d["A_log"], d["dt_bias"],
+                       d["state"], s, y, ws, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs, k_scale=ks)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), y_c)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_c.view(np.uint32))
+    assert np.array_equal(cs.cpu().numpy(), cs_c)
