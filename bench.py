@@ -121,7 +121,7 @@ def parse():
     ap.add_argument("--no-long", action="store_true", help="skip the B=4 T=32768 long-prefill leg")
     ap.add_argument("--kernel-only", default=None,
                     choices=[None, "recurrent", "prep", "decode", "copy", "chunked", "epilogue", "layer", "verify",
-                             "per_key_decode"],
+                             "per_key_decode", "long", "per_key"],
                     help="launch only this kernel (for counter collection)")
     return ap.parse_args()
 
@@ -149,6 +149,13 @@ def main():
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).to(dev)
         return torch.from_numpy(a).to(dev)
+
+    if args.kernel_only == "long":       # the long-prefill layer-core step alone
+        bench_long_prefill(args, torch, dev, up, inputs, binding, np, launches=max(args.steps, 1))
+        return
+    if args.kernel_only == "per_key":    # the per-key chunked recurrence alone
+        bench_per_key_prefill(args, torch, dev, up, inputs, binding, np, launches=max(args.steps, 1))
+        return
 
     # ------------------------------------------------------------ prefill
     w = inputs.WORKLOADS["prefill"]
@@ -582,12 +589,13 @@ def serving_kernel(name, torch, dev, up, inputs, binding):
     return fn
 
 
-def bench_per_key_prefill(args, torch, dev, up, inputs, binding, np):
+def bench_per_key_prefill(args, torch, dev, up, inputs, binding, np, launches=None):
     """The per-key decay gate g [B,T,Hv,Dk] over a prefill-length sequence
     (B=1 T=4096 Hk=16 Hv=32 Dk=Dv=128): the chunked matrix-core form, the
     per-step form with k, q and the gate rows staged through LDS, and the
     staging-free per-step kernel (reached through the snapshot entry point
-    with one snapshot, of the final state)."""
+    with one snapshot, of the final state).  With ``launches``: only that
+    many chunked calls (for counter passes)."""
     B, T, Hk, Hv, Dk, Dv = 1, 4096, 16, 32, 128, 128
     raw = inputs.recurrence_raw(B=B, T=T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, workload_id=8, state=True)
     # unit-norm-scale keys and queries, beta in (0, 1)
@@ -613,6 +621,12 @@ def bench_per_key_prefill(args, torch, dev, up, inputs, binding, np):
     def staging_free():
         binding.recurrent_snapshots(q, k, v, g, beta, st, s_out, y, [T], snap)
 
+    if launches is not None:
+        for _ in range(launches):
+            chunked()
+        torch.cuda.synchronize()
+        print(f"[bench] kernel-only per_key: {launches} launches", file=sys.stderr, flush=True)
+        return None
     out = {}
     for name, fn in (("chunked", chunked), ("staged", staged), ("staging_free", staging_free)):
         fn()
@@ -623,8 +637,13 @@ def bench_per_key_prefill(args, torch, dev, up, inputs, binding, np):
     tf = flops / (out["chunked"] * 1e-6) / 1e12
     print(f"[bench] per-key prefill B=1 T=4096: chunked {out['chunked']:.1f} us ({tf:.1f} TFLOP/s), per-step "
           f"staged {out['staged']:.1f} us, staging-free {out['staging_free']:.1f} us", file=sys.stderr, flush=True)
+    # algorithmic bytes: q, k, v, the gate rows, beta and the state read; y and the state written
+    alg = (2 * B * T * Hk * Dk * 2 + B * T * Hv * Dv * 2 + B * T * Hv * Dk * 4 + B * T * Hv * 4
+           + 2 * B * Hv * Dv * Dk * 4 + B * T * Hv * Dv * 2)
     return {"workload": f"B={B} T={T} Hk={Hk} Hv={Hv} Dk=Dv={Dk}, per-key gate U[0.3, 1), random state",
             "kernel": "chunk_prep_kernel<0, 1, true> + chunk_seq_kernel<1, true> (gdn_recurrent_chunked_per_key)",
+            "traffic": measured_traffic("chunked_recurrence", "per_key_prefill_B1_T4096"),
+            "traffic_algorithmic": alg,
             "avg_launch_us": out["chunked"], "achieved_TFLOPs": tf, "frac_fp32_peak": tf / FP32_PEAK_TFLOPS,
             "per_step_staged_us": out["staged"], "per_step_staging_free_us": out["staging_free"]}
 
@@ -773,10 +792,11 @@ def bench_decode_b1(args, torch, dev, up, inputs, binding, np):
     return out
 
 
-def bench_long_prefill(args, torch, dev, up, inputs, binding, np):
+def bench_long_prefill(args, torch, dev, up, inputs, binding, np, launches=None):
     """Long batched prefill B=4, T=32768 (Hk=16 Hv=32 Dk=Dv=128, random
     recurrent state): the layer core per step, and its chunked recurrence
-    alone against the fp32 peak."""
+    alone against the fp32 peak.  With ``launches``: only that many
+    layer-core steps (for counter passes)."""
     w = inputs.WORKLOADS["long"]
     B, T, Hk, Hv, Dk, Dv, K = (w[k] for k in ("B", "T", "Hk", "Hv", "Dk", "Dv", "K"))
     C = 2 * Hk * Dk + Hv * Dv
@@ -803,6 +823,12 @@ def bench_long_prefill(args, torch, dev, up, inputs, binding, np):
     def chunked():
         binding.recurrent_chunked(pq, pk, pv, pg, pb, d["state"], s_out, y, cws)
 
+    if launches is not None:
+        for _ in range(launches):
+            step()
+        torch.cuda.synchronize()
+        print(f"[bench] kernel-only long: {launches} launches", file=sys.stderr, flush=True)
+        return None
     binding.prep(d["qkv"], d["conv_w"], d["conv_state"], None, d["a"], d["b"], d["A_log"], d["dt_bias"], pq, pk,
                  pv, pg, pb, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, q_scale=qs, k_scale=ks)
     stream = torch.cuda.current_stream(dev)
@@ -814,8 +840,13 @@ def bench_long_prefill(args, torch, dev, up, inputs, binding, np):
     print(f"[bench] long prefill B=4 T=32768: layer core {step_us / 1e3:.2f} ms/step; chunked recurrence "
           f"{chunk_us / 1e3:.2f} ms ({tf:.1f} TFLOP/s, {tf / FP32_PEAK_TFLOPS:.1%} of fp32 peak)",
           file=sys.stderr, flush=True)
+    # algorithmic bytes of the layer-core step: qkv, a, b, conv weights and the state read; y, the state and
+    # the conv state written
+    alg = (B * T * C * 2 + 2 * B * T * Hv * 2 + C * K * 2 + B * Hv * Dv * Dk * 4
+           + B * T * Hv * Dv * 2 + B * Hv * Dv * Dk * 4 + B * (K - 1) * C * 2)
     return {"workload": "long prefill B=4 T=32768 Hk=16 Hv=32 Dk=Dv=128 K=4, random recurrent state",
             "kernel": "chunk_prep_kernel<4, 2> + chunk_seq_pairs_kernel (two waves per 16-row state tile)",
+            "traffic": measured_traffic("layer_core", "long_prefill_B4_T32768"), "traffic_algorithmic": alg,
             "ms_per_step": step_us / 1e3, "value": B * T * Hv / (step_us * 1e-6), "unit": "token*head/s",
             "chunked_recurrence_ms": chunk_us / 1e3, "chunked_TFLOPs": tf, "frac_fp32_peak": tf / FP32_PEAK_TFLOPS,
             "steps_timed": n}
