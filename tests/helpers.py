@@ -4,6 +4,8 @@ from __future__ import annotations
 
 import math
 
+import sys
+
 import numpy as np
 import torch
 
@@ -97,10 +99,24 @@ def state_err(s_gpu, s_ref):
     return float(np.max(d / np.maximum(n, 1e-300))) if d.size else 0.0
 
 
+def state_err_elementwise(s_gpu, s_ref, floor=1e-3):
+    """For information only: the largest elementwise relative error over the
+    entries with |S_ref| >= floor * max |S_ref| of their (b, v-head) (the
+    elementwise ratio is unbounded at entries near zero, so it is not a
+    tolerance)."""
+    ref = s_ref.reshape(s_ref.shape[0], s_ref.shape[1], -1)
+    d = np.abs(s_gpu.astype(np.float64).reshape(ref.shape) - ref)
+    n = np.abs(ref).max(-1, keepdims=True)
+    big = np.abs(ref) >= floor * n
+    return float((d[big] / np.abs(ref[big])).max()) if big.any() else 0.0
+
+
 def check_state(s_gpu, s_ref, tol, label=""):
     assert not np.isnan(s_gpu).any(), f"{label}: NaN in state"
     e = state_err(s_gpu, s_ref)
     assert e <= tol, f"{label}: state normwise error {e:.3e} > {tol:.1e}"
+    print(f"[state] {label}: normwise {e:.2e} (bound {tol:.0e}); elementwise relative "
+          f"{state_err_elementwise(s_gpu, s_ref):.2e} where |S| >= 1e-3 of its head's max", file=sys.stderr)
     return e
 
 
