@@ -107,7 +107,7 @@ def state_err_elementwise(s_gpu, s_ref, floor=1e-3):
     ref = s_ref.reshape(s_ref.shape[0], s_ref.shape[1], -1)
     d = np.abs(s_gpu.astype(np.float64).reshape(ref.shape) - ref)
     n = np.abs(ref).max(-1, keepdims=True)
-    big = np.abs(ref) >= floor * n
+    big = (np.abs(ref) >= floor * n) & (ref != 0)     # (an all-zero head has no such entries)
     return float((d[big] / np.abs(ref[big])).max()) if big.any() else 0.0
 
 
