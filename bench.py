@@ -867,22 +867,28 @@ def cpu_baseline(raw, Hk, Hv, Dk, Dv, qs, ks, eps):
     except (AttributeError, OSError):
         pass
     oracle.lib()
+    # whole passes over the workload until at least 10 s of CPU time (one pass
+    # takes a few seconds on the host)
+    passes = 0
     t0 = time.perf_counter()
-    for hv in heads:
-        hk = hv // (Hv // Hk)
-        ch = (list(range(hk * Dk, (hk + 1) * Dk)) + list(range(Hk * Dk + hk * Dk, Hk * Dk + (hk + 1) * Dk))
-              + list(range(2 * Hk * Dk + hv * Dv, 2 * Hk * Dk + (hv + 1) * Dv)))
-        oracle.layer_core(np.ascontiguousarray(raw["qkv"][..., ch]), np.ascontiguousarray(raw["conv_w"][ch]),
-                          None, np.ascontiguousarray(raw["a"][..., hv:hv + 1]),
-                          np.ascontiguousarray(raw["b"][..., hv:hv + 1]), raw["A_log"][hv:hv + 1].copy(),
-                          raw["dt_bias"][hv:hv + 1].copy(), None, Hk=1, Hv=1, Dk=Dk, Dv=Dv,
-                          q_scale=qs, k_scale=ks, eps=eps)
+    while passes == 0 or time.perf_counter() - t0 < 10.0:
+        for hv in heads:
+            hk = hv // (Hv // Hk)
+            ch = (list(range(hk * Dk, (hk + 1) * Dk)) + list(range(Hk * Dk + hk * Dk, Hk * Dk + (hk + 1) * Dk))
+                  + list(range(2 * Hk * Dk + hv * Dv, 2 * Hk * Dk + (hv + 1) * Dv)))
+            oracle.layer_core(np.ascontiguousarray(raw["qkv"][..., ch]), np.ascontiguousarray(raw["conv_w"][ch]),
+                              None, np.ascontiguousarray(raw["a"][..., hv:hv + 1]),
+                              np.ascontiguousarray(raw["b"][..., hv:hv + 1]), raw["A_log"][hv:hv + 1].copy(),
+                              raw["dt_bias"][hv:hv + 1].copy(), None, Hk=1, Hv=1, Dk=Dk, Dv=Dv,
+                              q_scale=qs, k_scale=ks, eps=eps)
+        passes += 1
     dt = time.perf_counter() - t0
-    print(f"[bench] cpu oracle: {len(heads)} heads x {T} tokens in {dt:.1f} s", file=sys.stderr, flush=True)
-    return {"value": len(heads) * T / dt, "unit": "token*head/s", "cores": 1, "kind": "oracle",
-            "sample": f"the whole prefill workload, computed per v-head (all {len(heads)}): prologue of the head's channels + recurrence "
-                      f"over all {T} tokens, fp64, one thread",
-            "seconds": dt, "host": host_cpu_model(), "host_cpus": os.cpu_count()}
+    print(f"[bench] cpu oracle: {passes} passes of {len(heads)} heads x {T} tokens in {dt:.1f} s",
+          file=sys.stderr, flush=True)
+    return {"value": passes * len(heads) * T / dt, "unit": "token*head/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} whole passes over the prefill workload, each computed per v-head (all {len(heads)}): "
+                      f"prologue of the head's channels + recurrence over all {T} tokens, fp64, one thread",
+            "seconds": dt, "passes": passes, "host": host_cpu_model(), "host_cpus": os.cpu_count()}
 
 
 def kernel_only(args, torch, dev, prep_rot, rec_only, up, inputs, binding, np, chunked_only, epilogue_rot,
