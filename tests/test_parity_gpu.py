@@ -574,22 +574,26 @@ def test_prefill_workload_chunked_recurrence_strict():
     say("prefill chunked state normwise err", worst)
 
 
-def test_long_workload_full_size_sampled():
+@pytest.mark.parametrize("q_scale", ["mlex", "rms_x_dk_half"])
+def test_long_workload_full_size_sampled(q_scale):
     """B=4, T=32768 with random initial state: the full layer core on the GPU;
     8 rows of 3 (b, hv) heads over the whole sequence against the oracle's
     recurrence on the device's own prologue outputs (long-horizon drift:
-    state 1e-3, strict y bounds) and against the oracle's own prologue."""
-    say("long workload full size")
+    state 1e-3, strict y bounds) and against the oracle's own prologue.  Both
+    readings of the q scale, as at the prefill workload."""
+    say("long workload full size", q_scale)
     w = inputs.WORKLOADS["long"]
     Hk, Hv, Dk, Dv, T = w["Hk"], w["Hv"], w["Dk"], w["Dv"], w["T"]
     raw = inputs.workload("long")
     qs, ks = inputs.scales(Dk)
+    if q_scale == "rms_x_dk_half":
+        qs = Dk ** -0.5
     y, s, cs = gpu_layer_core(raw, Hk, Hv, Dk, Dv, qs, ks)
     assert not np.isnan(s).any()
     p = gpu_prep(raw, Hk, Hv, Dk, Dv, qs, ks)
     rows = [0, 9, 31, 64, 77, 100, 126, 127]
-    worst = check_core_heads("long", y, s, p, raw, ((0, 0), (1, 13), (3, 31)), rows, Hk, Hv, Dk, Dv, qs, ks,
-                             state_tol_for(T))
+    worst = check_core_heads("long " + q_scale, y, s, p, raw, ((0, 0), (1, 13), (3, 31)), rows, Hk, Hv, Dk, Dv,
+                             qs, ks, state_tol_for(T))
     say("long state normwise err", worst)
 
 
